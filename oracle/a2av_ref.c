@@ -1,0 +1,246 @@
+/*
+ * a2av_ref.c — CPU oracle (plain, slow, single-threaded C).
+ *
+ * TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the
+ * benchmark's CPU-baseline leg, never by the product path. Shares no code with
+ * the HIP library. Each function writes out the definition it follows, step by
+ * step, with no blocking, fusion or reordering.
+ *
+ * Reading of the operation (the pages name nvshmem_all_to_all_vdev in the
+ * "Problem" section of "[a2av] Improve tuning for 4 GPUs" but never define
+ * it): all-to-all-v with device-held counts.
+ *   1. splits must be valid (non-negative, at most REF_MAX_SPLIT rows);
+ *   2. output splits O[d][s] = S[s][d];
+ *   3. send_off[s][d] = sum_{d' < d} S[s][d'], total at index W;
+ *      the total may not exceed the rows rank s holds;
+ *   4. recv_off[d][s] = sum_{s' < s} O[d][s'], total at index W;
+ *      the total may not exceed the rows rank d can hold;
+ *   5. for each d, for each s in ascending order, copy S[s][d] rows from
+ *      rank s's input at send_off[s][d] to rank d's output at recv_off[d][s];
+ *   6. nothing past a destination's total is touched; on any failure no
+ *      payload byte is written.
+ */
+#include "a2av_ref.h"
+
+#include <stdlib.h>
+#include <string.h>
+
+static int split_is_valid(int64_t v) { return v >= 0 && v <= REF_MAX_SPLIT; }
+
+/* Host-side argument checks shared by the payload functions of this file. */
+static int check_rank_sizes(int W, size_t R, const void *const *bufs,
+                            const int64_t *rows) {
+    if (W < 1 || W > REF_MAX_W || R == 0 || bufs == NULL || rows == NULL)
+        return REF_EARG;
+    for (int r = 0; r < W; r++) {
+        if (rows[r] < 0) return REF_EARG;
+        if ((uint64_t)rows[r] > (uint64_t)INT64_MAX / R) return REF_EARG;
+        if (rows[r] > 0 && bufs[r] == NULL) return REF_EARG;
+    }
+    return 0;
+}
+
+int ref_exchange_splits(int W, const int64_t *S, int64_t *O) {
+    if (W < 1 || W > REF_MAX_W || S == NULL || O == NULL) return REF_EARG;
+    for (int s = 0; s < W; s++)
+        for (int d = 0; d < W; d++)
+            if (!split_is_valid(S[s * W + d])) return REF_BAD_SPLIT;
+    /* Step 2: the receive counts are the transpose of the send counts. */
+    for (int d = 0; d < W; d++)
+        for (int s = 0; s < W; s++)
+            O[d * W + s] = S[s * W + d];
+    return 0;
+}
+
+int ref_offsets(int W, const int64_t *S, const int64_t *O,
+                int64_t *send_off, int64_t *recv_off) {
+    if (W < 1 || W > REF_MAX_W || !S || !O || !send_off || !recv_off)
+        return REF_EARG;
+    for (int i = 0; i < W * W; i++)
+        if (!split_is_valid(S[i]) || !split_is_valid(O[i])) return REF_BAD_SPLIT;
+    /* Step 3: exclusive scan of each send row; the total lands at index W. */
+    for (int s = 0; s < W; s++) {
+        int64_t run = 0;
+        for (int d = 0; d < W; d++) {
+            send_off[s * (W + 1) + d] = run;
+            run += S[s * W + d];
+        }
+        send_off[s * (W + 1) + W] = run;
+    }
+    /* Step 4: exclusive scan of each receive row. */
+    for (int d = 0; d < W; d++) {
+        int64_t run = 0;
+        for (int s = 0; s < W; s++) {
+            recv_off[d * (W + 1) + s] = run;
+            run += O[d * W + s];
+        }
+        recv_off[d * (W + 1) + W] = run;
+    }
+    return 0;
+}
+
+/* Step 5 alone, once every check has passed. */
+static void copy_chunks(int W, size_t R, const void *const *in,
+                        void *const *out, const int64_t *S,
+                        const int64_t *send_off, const int64_t *recv_off) {
+    for (int d = 0; d < W; d++) {
+        for (int s = 0; s < W; s++) {
+            int64_t rows = S[s * W + d];
+            if (rows == 0) continue;
+            const unsigned char *src =
+                (const unsigned char *)in[s] + (size_t)send_off[s * (W + 1) + d] * R;
+            unsigned char *dst =
+                (unsigned char *)out[d] + (size_t)recv_off[d * (W + 1) + s] * R;
+            memcpy(dst, src, (size_t)rows * R);
+        }
+    }
+}
+
+int ref_copy(int W, size_t R,
+             const void *const *in, const int64_t *in_rows,
+             void *const *out, const int64_t *out_cap_rows,
+             const int64_t *S, const int64_t *send_off, const int64_t *recv_off) {
+    if (check_rank_sizes(W, R, in, in_rows) || check_rank_sizes(W, R, (const void *const *)out, out_cap_rows))
+        return REF_EARG;
+    if (!S || !send_off || !recv_off) return REF_EARG;
+
+    int st = 0;
+    for (int i = 0; i < W * W; i++)
+        if (!split_is_valid(S[i])) st |= REF_BAD_SPLIT;
+
+    /* The given offsets must be the scans of step 3 and 4 (compared modulo
+     * 2^64 so that garbage input cannot overflow a signed add). */
+    for (int s = 0; s < W; s++) {
+        if (send_off[s * (W + 1)] != 0) st |= REF_BAD_OFFSETS;
+        for (int d = 0; d < W; d++) {
+            uint64_t step = (uint64_t)send_off[s * (W + 1) + d + 1] -
+                            (uint64_t)send_off[s * (W + 1) + d];
+            if (step != (uint64_t)S[s * W + d]) st |= REF_BAD_OFFSETS;
+        }
+    }
+    for (int d = 0; d < W; d++) {
+        if (recv_off[d * (W + 1)] != 0) st |= REF_BAD_OFFSETS;
+        for (int s = 0; s < W; s++) {
+            uint64_t step = (uint64_t)recv_off[d * (W + 1) + s + 1] -
+                            (uint64_t)recv_off[d * (W + 1) + s];
+            if (step != (uint64_t)S[s * W + d]) st |= REF_BAD_OFFSETS;
+        }
+    }
+    /* Step 3 and 4 bounds, on the totals as given. */
+    for (int s = 0; s < W; s++)
+        if (send_off[s * (W + 1) + W] > in_rows[s]) st |= REF_SEND_OVERRUN;
+    for (int d = 0; d < W; d++)
+        if (recv_off[d * (W + 1) + W] > out_cap_rows[d]) st |= REF_RECV_OVERFLOW;
+    if (st) return st;
+
+    copy_chunks(W, R, in, out, S, send_off, recv_off);
+    return 0;
+}
+
+int ref_a2av(int W, size_t R,
+             const void *const *in, const int64_t *in_rows,
+             void *const *out, const int64_t *out_cap_rows,
+             const int64_t *S, int64_t *O, int64_t *send_off, int64_t *recv_off) {
+    if (check_rank_sizes(W, R, in, in_rows) || check_rank_sizes(W, R, (const void *const *)out, out_cap_rows))
+        return REF_EARG;
+    if (!S || !O || !send_off || !recv_off) return REF_EARG;
+
+    int st = ref_exchange_splits(W, S, O);
+    if (st) return st;
+    st = ref_offsets(W, S, O, send_off, recv_off);
+    if (st) return st;
+    for (int s = 0; s < W; s++)
+        if (send_off[s * (W + 1) + W] > in_rows[s]) st |= REF_SEND_OVERRUN;
+    for (int d = 0; d < W; d++)
+        if (recv_off[d * (W + 1) + W] > out_cap_rows[d]) st |= REF_RECV_OVERFLOW;
+    if (st) return st;
+    copy_chunks(W, R, in, out, S, send_off, recv_off);
+    return 0;
+}
+
+int ref_source_of(int W, const int64_t *S, int d, int64_t j,
+                  int *src_rank, int64_t *src_row) {
+    if (W < 1 || W > REF_MAX_W || !S || d < 0 || d >= W || j < 0 ||
+        !src_rank || !src_row)
+        return REF_EARG;
+    for (int i = 0; i < W * W; i++)
+        if (!split_is_valid(S[i])) return REF_EARG;
+    /* Walk rank d's receive row in source order (step 4) until row j falls
+     * inside source s's chunk; then step 3 gives the row inside in[s]. */
+    int64_t recv_start = 0;
+    for (int s = 0; s < W; s++) {
+        int64_t rows = S[s * W + d];
+        if (j < recv_start + rows) {
+            int64_t send_start = 0;
+            for (int dd = 0; dd < d; dd++) send_start += S[s * W + dd];
+            *src_rank = s;
+            *src_row = send_start + (j - recv_start);
+            return 0;
+        }
+        recv_start += rows;
+    }
+    return 1;
+}
+
+/*
+ * MoE dispatch pack of one rank, as a stable counting sort of the T*k routing
+ * slots by expert id (tokens routed to experts, then grouped by the rank that
+ * owns each expert; the page's "MoE related region" is the message this
+ * builds). Experts are owned in contiguous blocks: owner(e) = e / (E / W),
+ * so sorting by expert also groups by destination rank.
+ */
+int ref_moe_pack(int64_t T, int k, int E, int W, size_t R,
+                 const void *tokens, const int32_t *ids,
+                 void *send, int64_t *perm, int64_t *splits,
+                 int64_t *expert_counts) {
+    if (T < 0 || k < 1 || E < 1 || W < 1 || W > REF_MAX_W || E % W != 0 || R == 0)
+        return REF_EARG;
+    if (T > INT64_MAX / k) return REF_EARG;
+    const int64_t Q = T * k;
+    if (Q > 0 && (!tokens || !ids || !send || !perm)) return REF_EARG;
+    if (!splits || !expert_counts) return REF_EARG;
+
+    /* Every id must name an expert before anything is written. */
+    for (int64_t q = 0; q < Q; q++)
+        if (ids[q] < 0 || ids[q] >= E) return REF_BAD_EXPERT;
+
+    int64_t *count = calloc((size_t)E, sizeof(int64_t));
+    int64_t *next = calloc((size_t)E, sizeof(int64_t));
+    if (!count || !next) { free(count); free(next); return REF_EARG; }
+
+    /* count[e] = number of slots routed to expert e. */
+    for (int64_t q = 0; q < Q; q++) count[ids[q]] += 1;
+    /* base[e] = slots of all smaller experts; next[e] starts at base[e]. */
+    int64_t run = 0;
+    for (int e = 0; e < E; e++) { next[e] = run; run += count[e]; }
+    /* perm[q] = base[e(q)] + number of earlier slots with the same expert. */
+    for (int64_t q = 0; q < Q; q++) perm[q] = next[ids[q]]++;
+    /* send[perm[q]] = the token of slot q. */
+    for (int64_t q = 0; q < Q; q++)
+        memcpy((unsigned char *)send + (size_t)perm[q] * R,
+               (const unsigned char *)tokens + (size_t)(q / k) * R, R);
+    /* splits[d] = slots whose expert rank d owns. */
+    const int per_rank = E / W;
+    for (int d = 0; d < W; d++) splits[d] = 0;
+    for (int e = 0; e < E; e++) splits[e / per_rank] += count[e];
+    for (int e = 0; e < E; e++) expert_counts[e] = count[e];
+
+    free(count);
+    free(next);
+    return 0;
+}
+
+int ref_moe_unpack(int64_t T, int k, size_t R,
+                   const void *back, const int64_t *perm, void *out) {
+    if (T < 0 || k < 1 || R == 0) return REF_EARG;
+    if (T > INT64_MAX / k) return REF_EARG;
+    const int64_t Q = T * k;
+    if (Q > 0 && (!back || !perm || !out)) return REF_EARG;
+    for (int64_t q = 0; q < Q; q++)
+        if (perm[q] < 0 || perm[q] >= Q) return REF_BAD_PERM;
+    /* out[q] = back[perm[q]]: the row that slot q was packed to comes home. */
+    for (int64_t q = 0; q < Q; q++)
+        memcpy((unsigned char *)out + (size_t)q * R,
+               (const unsigned char *)back + (size_t)perm[q] * R, R);
+    return 0;
+}

@@ -1,0 +1,97 @@
+/*
+ * a2av_ref.h — CPU oracle for the device-split all-to-all-v and the MoE
+ * pack/unpack around it.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link,
+ * load or call this code: only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it. It shares no source, header, table or helper with
+ * the HIP library.
+ *
+ * Every function is plain, single-threaded C over host pointers. Status bits
+ * have the same meaning as the device status bits of the HIP library, but the
+ * values are defined here again, on purpose, so the two sides share nothing.
+ *
+ * Source of the operation: the page "[a2av] Improve tuning for 4 GPUs"
+ * (pytorch/pytorch pull 154580), section "Problem", names the op
+ * nvshmem_all_to_all_vdev and times it; it does not spell out what it
+ * computes. The plain reading used here is MPI all-to-all-v with the counts
+ * held on the device: rank s sends S[s][d] rows to rank d, the receive counts
+ * are the transpose, send and receive displacements are exclusive scans of
+ * the counts, and each destination receives its chunks in source-rank order.
+ */
+#ifndef A2AV_REF_H
+#define A2AV_REF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Returned status bits (OR-ed together); 0 = success. */
+#define REF_BAD_SPLIT     1  /* a split is negative or above REF_MAX_SPLIT      */
+#define REF_SEND_OVERRUN  2  /* a rank sends more rows than its input holds     */
+#define REF_RECV_OVERFLOW 4  /* a rank receives more rows than its output holds */
+#define REF_BAD_EXPERT    8  /* an expert id is outside [0, E)                  */
+#define REF_BAD_OFFSETS  16  /* given offsets are not the scans of the splits   */
+#define REF_BAD_PERM     32  /* a permutation entry is outside its range        */
+
+/* Host argument error (nothing computed, nothing written). */
+#define REF_EARG (-1)
+
+#define REF_MAX_SPLIT ((int64_t)1 << 40)
+#define REF_MAX_W 64
+
+/* O[d][s] = S[s][d] for a W x W row-major matrix (row s = rank s's splits). */
+int ref_exchange_splits(int W, const int64_t *S, int64_t *O);
+
+/* send_off[s][0..W] = exclusive scan of row s of S, with the total at index W;
+ * recv_off[d][0..W] = exclusive scan of row d of O, with the total at index W.
+ * Both outputs are W x (W+1) row-major. */
+int ref_offsets(int W, const int64_t *S, const int64_t *O,
+                int64_t *send_off, int64_t *recv_off);
+
+/* Payload step: for every destination d and source s (ascending), copy
+ * S[s][d] rows of R bytes from in[s] at row send_off[s][d] to out[d] at row
+ * recv_off[d][s]. Checks every condition first; writes nothing on failure. */
+int ref_copy(int W, size_t R,
+             const void *const *in, const int64_t *in_rows,
+             void *const *out, const int64_t *out_cap_rows,
+             const int64_t *S, const int64_t *send_off, const int64_t *recv_off);
+
+/* The whole definition from S alone: exchange, offsets, payload. O,
+ * send_off and recv_off are written when the splits are valid; the payload
+ * only when every check passes. */
+int ref_a2av(int W, size_t R,
+             const void *const *in, const int64_t *in_rows,
+             void *const *out, const int64_t *out_cap_rows,
+             const int64_t *S, int64_t *O, int64_t *send_off, int64_t *recv_off);
+
+/* Inverse map for one output row: output row j of rank d came from input row
+ * *src_row of rank *src_rank. Returns 0, or 1 when j is past rank d's total,
+ * or REF_EARG. Lets a test check sampled rows of a workload too large to run
+ * whole. */
+int ref_source_of(int W, const int64_t *S, int d, int64_t j,
+                  int *src_rank, int64_t *src_row);
+
+/* MoE dispatch pack for ONE rank. T tokens of R bytes, k expert ids each
+ * (ids is T x k, slot q = t*k + j), E experts spread over W ranks in
+ * contiguous blocks of E/W. Outputs: perm[q] = row of slot q in send (a
+ * stable counting sort by expert id), send[perm[q]] = token q/k,
+ * splits[d] = slots bound for rank d, expert_counts[e] = slots for expert e. */
+int ref_moe_pack(int64_t T, int k, int E, int W, size_t R,
+                 const void *tokens, const int32_t *ids,
+                 void *send, int64_t *perm, int64_t *splits,
+                 int64_t *expert_counts);
+
+/* Inverse of the pack after the return trip, for ONE rank:
+ * out[q] = back[perm[q]] for q < T*k (rows of R bytes). */
+int ref_moe_unpack(int64_t T, int k, size_t R,
+                   const void *back, const int64_t *perm, void *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* A2AV_REF_H */

@@ -1,0 +1,165 @@
+"""ctypes wrapper of the CPU oracle (``liba2av_ref.so``), over numpy arrays.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg call this module; the product path never does. It loads only
+the oracle's own shared library, built from ``a2av_ref.c`` by :func:`build`.
+
+Payload buffers are numpy ``uint8`` arrays (byte views of whatever dtype the
+rows hold); splits, offsets and permutations are ``int64`` arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "a2av_ref.c")
+LIB = os.path.join(HERE, "liba2av_ref.so")
+
+BAD_SPLIT = 1
+SEND_OVERRUN = 2
+RECV_OVERFLOW = 4
+BAD_EXPERT = 8
+BAD_OFFSETS = 16
+BAD_PERM = 32
+EARG = -1
+MAX_SPLIT = 1 << 40
+
+_lib = None
+
+
+def build(out: str = LIB, extra_flags: tuple = ()) -> str:
+    """Compile the oracle with gcc into a shared library and return its path."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror", "-fPIC", "-shared",
+           "-ffp-contract=off", *extra_flags, "-o", out, SRC]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def _bind(lib):
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    vpp = ctypes.POINTER(ctypes.c_void_p)
+    sz = ctypes.c_size_t
+    lib.ref_exchange_splits.argtypes = [ctypes.c_int, i64p, i64p]
+    lib.ref_offsets.argtypes = [ctypes.c_int, i64p, i64p, i64p, i64p]
+    lib.ref_copy.argtypes = [ctypes.c_int, sz, vpp, i64p, vpp, i64p, i64p, i64p, i64p]
+    lib.ref_a2av.argtypes = [ctypes.c_int, sz, vpp, i64p, vpp, i64p, i64p, i64p, i64p, i64p]
+    lib.ref_source_of.argtypes = [ctypes.c_int, i64p, ctypes.c_int, ctypes.c_int64,
+                                  ctypes.POINTER(ctypes.c_int), i64p]
+    lib.ref_moe_pack.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, sz,
+                                 ctypes.c_void_p, i32p, ctypes.c_void_p, i64p, i64p, i64p]
+    lib.ref_moe_unpack.argtypes = [ctypes.c_int64, ctypes.c_int, sz, ctypes.c_void_p, i64p,
+                                   ctypes.c_void_p]
+    for name in ("ref_exchange_splits", "ref_offsets", "ref_copy", "ref_a2av", "ref_source_of",
+                 "ref_moe_pack", "ref_moe_unpack"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+def load(path: str | None = None):
+    """Load the oracle library (building it first if it is missing)."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build()
+        _lib = _bind(ctypes.CDLL(LIB))
+    return _lib
+
+
+def _i64(a):
+    assert a.dtype == np.int64 and a.flags.c_contiguous
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def _ptrs(bufs):
+    arr = (ctypes.c_void_p * len(bufs))()
+    for i, b in enumerate(bufs):
+        if b is None:
+            arr[i] = None
+        else:
+            assert b.flags.c_contiguous
+            arr[i] = b.ctypes.data
+    return arr
+
+
+class Oracle:
+    """Thin numpy front end of one loaded oracle library."""
+
+    def __init__(self, lib=None):
+        self.lib = lib if lib is not None else load()
+
+    def exchange_splits(self, S):
+        S = np.ascontiguousarray(S, dtype=np.int64)
+        W = S.shape[0]
+        O = np.zeros((W, W), dtype=np.int64)
+        st = self.lib.ref_exchange_splits(W, _i64(S), _i64(O))
+        return st, O
+
+    def offsets(self, S, O):
+        S = np.ascontiguousarray(S, dtype=np.int64)
+        O = np.ascontiguousarray(O, dtype=np.int64)
+        W = S.shape[0]
+        send_off = np.zeros((W, W + 1), dtype=np.int64)
+        recv_off = np.zeros((W, W + 1), dtype=np.int64)
+        st = self.lib.ref_offsets(W, _i64(S), _i64(O), _i64(send_off), _i64(recv_off))
+        return st, send_off, recv_off
+
+    def copy(self, R, ins, in_rows, outs, out_cap, S, send_off, recv_off):
+        """Payload step into ``outs`` (modified in place); returns the status."""
+        W = len(ins)
+        in_rows = np.ascontiguousarray(in_rows, dtype=np.int64)
+        out_cap = np.ascontiguousarray(out_cap, dtype=np.int64)
+        S = np.ascontiguousarray(S, dtype=np.int64)
+        send_off = np.ascontiguousarray(send_off, dtype=np.int64)
+        recv_off = np.ascontiguousarray(recv_off, dtype=np.int64)
+        return self.lib.ref_copy(W, R, _ptrs(ins), _i64(in_rows), _ptrs(outs), _i64(out_cap),
+                                 _i64(S), _i64(send_off), _i64(recv_off))
+
+    def a2av(self, R, ins, in_rows, outs, out_cap, S):
+        """Whole definition from S alone; payload lands in ``outs`` in place."""
+        W = len(ins)
+        in_rows = np.ascontiguousarray(in_rows, dtype=np.int64)
+        out_cap = np.ascontiguousarray(out_cap, dtype=np.int64)
+        S = np.ascontiguousarray(S, dtype=np.int64)
+        O = np.zeros((W, W), dtype=np.int64)
+        send_off = np.zeros((W, W + 1), dtype=np.int64)
+        recv_off = np.zeros((W, W + 1), dtype=np.int64)
+        st = self.lib.ref_a2av(W, R, _ptrs(ins), _i64(in_rows), _ptrs(outs), _i64(out_cap),
+                               _i64(S), _i64(O), _i64(send_off), _i64(recv_off))
+        return st, O, send_off, recv_off
+
+    def source_of(self, S, d, j):
+        S = np.ascontiguousarray(S, dtype=np.int64)
+        s = ctypes.c_int(-1)
+        i = ctypes.c_int64(-1)
+        st = self.lib.ref_source_of(S.shape[0], _i64(S), d, j, ctypes.byref(s), ctypes.byref(i))
+        if st == 1:
+            return None
+        if st != 0:
+            raise ValueError(f"ref_source_of failed with {st}")
+        return s.value, i.value
+
+    def moe_pack(self, T, k, E, W, R, tokens, ids):
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        tokens = np.ascontiguousarray(tokens).view(np.uint8)
+        send = np.zeros(T * k * R, dtype=np.uint8)
+        perm = np.zeros(T * k, dtype=np.int64)
+        splits = np.zeros(W, dtype=np.int64)
+        counts = np.zeros(E, dtype=np.int64)
+        st = self.lib.ref_moe_pack(T, k, E, W, R, tokens.ctypes.data,
+                                   ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                   send.ctypes.data, _i64(perm), _i64(splits), _i64(counts))
+        return st, send, perm, splits, counts
+
+    def moe_unpack(self, T, k, R, back, perm):
+        back = np.ascontiguousarray(back).view(np.uint8)
+        perm = np.ascontiguousarray(perm, dtype=np.int64)
+        out = np.zeros(T * k * R, dtype=np.uint8)
+        st = self.lib.ref_moe_unpack(T, k, R, back.ctypes.data, _i64(perm), out.ctypes.data)
+        return st, out

@@ -1,0 +1,120 @@
+"""The pins have teeth: plant plausible mistakes in a copy of the oracle and
+check that at least one pin fails for each (no GPU).
+
+Each mutant is a textual edit of ``oracle/a2av_ref.c`` (a swapped index, a
+dropped term, an inclusive instead of exclusive scan, an unstable order, an
+off-by-one bound, a transposed operand). Some planted mistakes move a
+chunk past the end of its buffer, so every mutant runs in a child process: the
+child reports the first pin that fails, and a child killed by the memory error
+before any pin fails counts as caught by that crash (reported as such).
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle.ref as R
+import oracle_pins
+
+SRC = open(R.SRC).read()
+
+MUTANTS = {
+    "exchange_not_transposed": [
+        ("O[d * W + s] = S[s * W + d];", "O[d * W + s] = S[d * W + s];", 0)],
+    "send_scan_inclusive": [
+        ("send_off[s * (W + 1) + d] = run;\n            run += S[s * W + d];",
+         "run += S[s * W + d];\n            send_off[s * (W + 1) + d] = run;", 0)],
+    "recv_scan_reads_S_not_O": [("run += O[d * W + s];", "run += S[d * W + s];", 0)],
+    "copy_src_offset_transposed": [
+        ("(size_t)send_off[s * (W + 1) + d] * R;", "(size_t)send_off[d * (W + 1) + s] * R;", 0)],
+    "copy_dst_offset_transposed": [
+        ("(size_t)recv_off[d * (W + 1) + s] * R;", "(size_t)recv_off[s * (W + 1) + d] * R;", 0)],
+    "copy_count_transposed": [
+        ("int64_t rows = S[s * W + d];\n            if (rows == 0) continue;",
+         "int64_t rows = S[d * W + s];\n            if (rows == 0) continue;", 0)],
+    "overrun_off_by_one": [
+        ("if (send_off[s * (W + 1) + W] > in_rows[s]) st |= REF_SEND_OVERRUN;",
+         "if (send_off[s * (W + 1) + W] >= in_rows[s]) st |= REF_SEND_OVERRUN;", 1)],
+    "overflow_check_slack": [
+        ("if (recv_off[d * (W + 1) + W] > out_cap_rows[d]) st |= REF_RECV_OVERFLOW;",
+         "if (recv_off[d * (W + 1) + W] > out_cap_rows[d] + 1) st |= REF_RECV_OVERFLOW;", 1)],
+    "copy_ignores_bad_offsets": [
+        ("if (step != (uint64_t)S[s * W + d]) st |= REF_BAD_OFFSETS;", "(void)step;", 0)],
+    "split_range_not_checked": [
+        ("return v >= 0 && v <= REF_MAX_SPLIT;", "return v >= 0;", 0)],
+    "pack_unstable": [
+        ("for (int64_t q = 0; q < Q; q++) perm[q] = next[ids[q]]++;",
+         "for (int64_t q = Q - 1; q >= 0; q--) perm[q] = next[ids[q]]++;", 0)],
+    "pack_owner_modulo": [("splits[e / per_rank] += count[e];", "splits[e % W] += count[e];", 0)],
+    "pack_wrong_token": [("(size_t)(q / k) * R, R);", "(size_t)(q % T) * R, R);", 0)],
+    "unpack_scatter_not_gather": [
+        ("memcpy((unsigned char *)out + (size_t)q * R,\n"
+         "               (const unsigned char *)back + (size_t)perm[q] * R, R);",
+         "memcpy((unsigned char *)out + (size_t)perm[q] * R,\n"
+         "               (const unsigned char *)back + (size_t)q * R, R);", 0)],
+    "source_of_drops_send_start": [
+        ("*src_row = send_start + (j - recv_start);", "*src_row = (j - recv_start); (void)send_start;", 0)],
+    "bad_expert_upper_bound": [("if (ids[q] < 0 || ids[q] >= E) return REF_BAD_EXPERT;",
+                                "if (ids[q] < 0 || ids[q] > E) return REF_BAD_EXPERT;", 0)],
+}
+
+# cheap pins first; the brute-force enumeration last
+PIN_ORDER = sorted(oracle_pins.ALL_PINS,
+                   key=lambda f: (f.__name__ in ("pin_brute_force_tiny", "pin_emb_two_call_consistency"),
+                                  f.__name__))
+
+
+def _apply(src, edits):
+    for old, new, nth in edits:
+        parts = src.split(old)
+        assert len(parts) > nth + 1, f"pattern not found ({nth}): {old!r}"
+        src = old.join(parts[:nth + 1]) + new + old.join(parts[nth + 1:])
+    return src
+
+
+def _run_pins_in_child(so_path):
+    """Run the pins on a library in a child process; returns (how, detail)."""
+    code = ("import sys, os; sys.path[:0] = [%r, %r]\n"
+            "import oracle.ref as R, test_oracle_mutants as M\n"
+            "o = R.Oracle(R.load(%r))\n"
+            "for pin in M.PIN_ORDER:\n"
+            "    try:\n"
+            "        pin(o)\n"
+            "    except AssertionError:\n"
+            "        print('CAUGHT', pin.__name__, flush=True); os._exit(0)\n"
+            "print('MISSED', flush=True); os._exit(0)\n") % (
+                os.path.dirname(R.HERE), os.path.dirname(os.path.abspath(__file__)), str(so_path))
+    p = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    out = p.stdout.strip().splitlines()
+    if out and out[-1].startswith("CAUGHT"):
+        return "pin", out[-1].split()[1]
+    if out and out[-1] == "MISSED":
+        return "missed", ""
+    return "crash", f"rc={p.returncode} {p.stderr[-300:]}"
+
+
+def _build(tmp_path, src, name):
+    c = tmp_path / "a2av_ref.c"
+    c.write_text(src)
+    (tmp_path / "a2av_ref.h").write_text(open(os.path.join(R.HERE, "a2av_ref.h")).read())
+    so = tmp_path / f"{name}.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-o", str(so), str(c)],
+                   check=True)
+    return so
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    src = _apply(SRC, MUTANTS[name])
+    assert src != SRC
+    how, detail = _run_pins_in_child(_build(tmp_path, src, f"mut_{name}"))
+    print(f"{name}: {how} {detail}")
+    assert how != "missed", f"no pin caught the planted mistake {name!r}"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    """The same build route without an edit passes every pin (so a caught
+    mutant is caught for its mistake, not for the build)."""
+    how, detail = _run_pins_in_child(_build(tmp_path, SRC, "plain"))
+    assert how == "missed", (how, detail)
