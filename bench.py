@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Benchmark of the device-split all-to-all-v on one MI355X.
+
+One step = the whole a2av on W virtual ranks held in one GPU's HBM: splits
+exchange -> offsets -> payload copy, three C-ABI calls on one stream. The
+default workload is W=4 ranks x 32 MiB (4096 rows x 4096 bf16, 8 KiB rows)
+with multinomial splits, the message size of the MoE region on the tuning
+page. The printed value is effective HBM throughput: payload bytes read plus
+bytes written (2 x row bytes x rows moved) per second of wall clock over the
+timed steps, inputs resident in HBM.
+
+Several independent buffer sets are cycled so that no step finds its inputs
+in the 256 MB Infinity Cache left behind by the step before.
+
+Also reported on the same JSON line:
+  roofline      payload kernel alone, timed with HIP events on its stream,
+                against the 8 TB/s HBM peak; `traffic` is the HBM byte count
+                from rocprofv3 counters when they were taken on this exact
+                kernel source (else null)
+  cpu_baseline  the CPU oracle on the same workload on this host
+  headline      W in {4, 8} x {32 MiB, 1 GiB} per rank, payload kernel and step
+  ceilings      plain device copy of the same bytes (this library's copy loop
+                and torch's D2D copy)
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "a2av_copy_w4_32mib_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "embeddings_a2av_virtual_amd", "csrc", f)
+                  for f in ("a2av.hip", "common.hpp")]
+
+
+def gbps(nbytes: float, seconds: float) -> float:
+    """Decimal GB/s (10^9 bytes per second)."""
+    return nbytes / seconds / 1e9
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class VSet:
+    """One independent set of W virtual ranks: payload, outputs, device
+    splits/offsets/status, and pre-marshalled C-ABI argument tuples."""
+
+    def __init__(self, torch, B, I, W, rows, cols, seed, stream_handle):
+        from embeddings_a2av_virtual_amd.vranks import A2av
+        self.W, self.rows, self.R = W, rows, cols * 2
+        g = I.rng(seed)
+        self.S_host = I.uniform_splits(g, W, rows)
+        self.ins = [I.payload_bf16(rows, cols, seed * 1000 + r, device="cuda") for r in range(W)]
+        cap = self.S_host.sum(axis=0)
+        self.cap = [int(c) for c in cap]
+        self.outs = [torch.empty((c, cols), dtype=torch.bfloat16, device="cuda") for c in self.cap]
+        self.st = A2av(W)
+        self.st.set_splits(self.S_host)
+        self.moved = 2 * self.R * int(self.S_host.sum())
+        vp = ctypes.c_void_p
+        st = self.st
+        hs = vp(stream_handle)
+        self.ex_args = (W, vp(st.S.data_ptr()), vp(st.O.data_ptr()), vp(st.status.data_ptr()), hs)
+        self.off_args = (W, vp(st.S.data_ptr()), vp(st.O.data_ptr()), vp(st.send_off.data_ptr()),
+                         vp(st.recv_off.data_ptr()), vp(st.status.data_ptr()), hs)
+        ins = (ctypes.c_void_p * W)(*[t.data_ptr() for t in self.ins])
+        outs = (ctypes.c_void_p * W)(*[t.data_ptr() for t in self.outs])
+        in_rows = (ctypes.c_int64 * W)(*([rows] * W))
+        caps = (ctypes.c_int64 * W)(*self.cap)
+        self._keep = (ins, outs, in_rows, caps)
+        self.copy_args = (W, self.R, ins, in_rows, outs, caps, vp(st.S.data_ptr()),
+                          vp(st.send_off.data_ptr()), vp(st.recv_off.data_ptr()),
+                          vp(st.status.data_ptr()), hs)
+
+
+def run_config(torch, B, I, W, mib, steps, warmup, nsets):
+    """Time `steps` whole a2av steps over `nsets` rotating buffer sets.
+    Returns a dict of wall-clock step throughput and event-timed copy kernel
+    throughput."""
+    L = B.lib()
+    stream = torch.cuda.current_stream()
+    hs = stream.cuda_stream
+    cols = 4096
+    rows = I.rows_for_mib(mib, cols * 2)
+    sets = [VSet(torch, B, I, W, rows, cols, seed=100 + 17 * W + mib + s, stream_handle=hs)
+            for s in range(nsets)]
+    torch.cuda.synchronize()
+
+    def step(vs, ev=None):
+        assert L.a2av_exchange_splits(*vs.ex_args) == 0
+        assert L.a2av_offsets(*vs.off_args) == 0
+        if ev is not None:
+            ev[0].record(stream)
+        assert L.a2av_copy(*vs.copy_args) == 0
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(warmup):
+        step(sets[i % nsets])
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(sets[i % nsets], evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for vs in sets:
+        st = int(vs.st.status.item())
+        if st != 0:
+            raise RuntimeError(f"status word {st}: {B.a2av_strerror(st)}")
+    moved = [sets[i % nsets].moved for i in range(steps)]
+    copy_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)]
+    wall = t1 - t0
+    res = {
+        "W": W, "mib_per_rank": mib, "row_bytes": cols * 2, "steps": steps,
+        "bytes_per_step": statistics.mean(moved),
+        "step_ms": wall / steps * 1e3,
+        "step_gbs": gbps(sum(moved), wall),
+        "copy_ms_mean": statistics.mean(copy_ms),
+        "copy_ms_median": statistics.median(copy_ms),
+        "copy_gbs": gbps(sum(moved), sum(copy_ms) / 1e3),
+    }
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def ceilings(torch, B, nbytes, reps=50, nsets=8):
+    """Plain contiguous copies of the same byte count (read n + write n)."""
+    half = nbytes // 2
+    srcs = [torch.empty(half, dtype=torch.uint8, device="cuda").fill_(i) for i in range(nsets)]
+    dsts = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+    out = {}
+    for name, fn in (("device_copy", lambda d, s: B.a2av_device_copy(d, s, half)),
+                     ("torch_d2d", lambda d, s: d.copy_(s))):
+        for i in range(5):
+            fn(dsts[i % nsets], srcs[i % nsets])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(reps):
+            fn(dsts[i % nsets], srcs[i % nsets])
+        b.record()
+        torch.cuda.synchronize()
+        out[name + "_gbs"] = gbps(2 * half * reps, a.elapsed_time(b) / 1e3)
+    del srcs, dsts
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(torch, I, W=4, mib=32, budget_s=10.0):
+    """The CPU oracle on one full set of the workload, repeated for about
+    budget_s seconds (at least 3 runs); single-threaded C."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    from oracle.ref import Oracle
+    o = Oracle()
+    cols = 4096
+    R = cols * 2
+    rows = I.rows_for_mib(mib, R)
+    seed = 100 + 17 * W + mib   # the first buffer set of the GPU run
+    g = I.rng(seed)
+    S = I.uniform_splits(g, W, rows)
+    X = [I.payload_bf16(rows, cols, seed * 1000 + r, device="cuda").view(torch.uint8).cpu().numpy()
+         .reshape(-1) for r in range(W)]
+    cap = S.sum(axis=0)
+    Y = [np.empty(int(c) * R, dtype=np.uint8) for c in cap]
+    in_rows = np.full(W, rows, dtype=np.int64)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 or (time.perf_counter() - t_start < budget_s and len(times) < 500):
+        t0 = time.perf_counter()
+        st = o.a2av(R, X, in_rows, Y, cap, S)[0]
+        times.append(time.perf_counter() - t0)
+        assert st == 0
+    moved = 2 * R * int(S.sum())
+    med = statistics.median(times)
+    return {"value": round(gbps(moved, med), 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole W={W} x {mib} MiB/rank a2av (exchange+offsets+copy), "
+                      f"{len(times)} runs, median {med * 1e3:.1f} ms"}
+
+
+def traffic_entry(bytes_per_launch):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--sets", type=int, default=8, help="rotating buffer sets (32 MiB case)")
+    ap.add_argument("--no-headline", action="store_true", help="skip the W x size matrix")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} requested, but this build runs on ONE GPU: the "
+              "W ranks are virtual (partitions of one GPU's HBM) and there is no multi-GPU "
+              "path; run with --gpus 1.", file=sys.stderr)
+        return 2
+    if int(os.environ.get("RANK", "0")) != 0:
+        return 0
+
+    sys.path.insert(0, ROOT)
+    import torch
+    from embeddings_a2av_virtual_amd import _binding as B
+    from embeddings_a2av_virtual_amd import inputs as I
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    B.lib()
+
+    log("bench: W=4 x 32 MiB/rank, steps", args.steps, "warmup", args.warmup, "sets", args.sets)
+    main_res = run_config(torch, B, I, 4, 32, args.steps, args.warmup, args.sets)
+    log("bench: main", json.dumps(main_res))
+
+    headline = {}
+    if not args.no_headline:
+        for W, mib, steps, nsets in ((4, 32, 200, 8), (8, 32, 200, 8), (4, 1024, 20, 2),
+                                     (8, 1024, 10, 2)):
+            r = run_config(torch, B, I, W, mib, steps, 5, nsets)
+            headline[f"w{W}_{mib}mib"] = {
+                "copy_gbs": round(r["copy_gbs"], 1),
+                "copy_frac": round(r["copy_gbs"] / HBM_PEAK_GBS, 4),
+                "step_gbs": round(r["step_gbs"], 1),
+                "copy_us": round(r["copy_ms_mean"] * 1e3, 2),
+                "step_us": round(r["step_ms"] * 1e3, 2)}
+            log("bench: headline", W, mib, json.dumps(headline[f"w{W}_{mib}mib"]))
+    ceil = ceilings(torch, B, int(main_res["bytes_per_step"]))
+    log("bench: ceilings", json.dumps(ceil))
+
+    cpu = None if args.no_cpu else cpu_baseline(torch, I)
+    if cpu:
+        log("bench: cpu", json.dumps(cpu))
+
+    per_launch = main_res["bytes_per_step"]
+    achieved = gbps(per_launch, main_res["copy_ms_mean"] / 1e3)
+    line = {
+        "metric": "a2av effective HBM GB/s @32 MiB & 1 GiB per rank, W=4/8; % of HBM peak",
+        "value": round(main_res["step_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "a2av W=4 virtual ranks x 32 MiB/rank (4096 rows x 4096 bf16), "
+                               "uniform multinomial splits; step = splits exchange + offsets + copy",
+                   "W": 4, "rows_per_rank": 4096, "row_bytes": 8192,
+                   "rotating_sets": args.sets, "frac_of_hbm_peak": round(
+                       main_res["step_gbs"] / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "a2av_copy", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_entry(per_launch),
+                     "algorithmic_bytes_per_launch": int(per_launch),
+                     "avg_launch_us": round(main_res["copy_ms_mean"] * 1e3, 3)},
+        "cpu_baseline": cpu,
+        "headline": headline,
+        "ceilings": {k: round(v, 1) for k, v in ceil.items()},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

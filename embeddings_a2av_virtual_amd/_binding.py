@@ -1,1 +1,184 @@
-__all__ = []
+"""ctypes binding of ``liba2av.so`` (the C ABI in ``include/a2av.h``).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, passes their device pointers and the stream to the C entry
+point of the same name, and raises :class:`A2avError` for a nonzero host
+return code. All computation runs in the library's HIP kernels; if the library
+is missing the first call raises, there is no fallback.
+
+torch is used for device memory and streams only. The stream defaults to
+torch's current stream on the tensors' device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "A2avError", "lib", "LIB_PATH",
+    "OK", "EARG", "EHIP", "MAX_W", "MAX_SPLIT", "MAX_EXPERTS",
+    "ST_BAD_SPLIT", "ST_SEND_OVERRUN", "ST_RECV_OVERFLOW", "ST_BAD_EXPERT", "ST_BAD_OFFSETS",
+    "ST_BAD_PERM",
+    "a2av_abi_version", "a2av_strerror", "a2av_exchange_splits", "a2av_offsets", "a2av_copy",
+    "moe_pack_workspace_bytes", "moe_pack", "moe_unpack", "a2av_device_copy",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liba2av.so")
+
+OK, EARG, EHIP = 0, -1, -2
+MAX_W = 64
+MAX_SPLIT = 1 << 40
+MAX_EXPERTS = 4096
+ST_BAD_SPLIT = 1
+ST_SEND_OVERRUN = 2
+ST_RECV_OVERFLOW = 4
+ST_BAD_EXPERT = 8
+ST_BAD_OFFSETS = 16
+ST_BAD_PERM = 32
+
+_lib = None
+
+
+class A2avError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} returned {code}: {a2av_strerror(code)}")
+        self.code = code
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m embeddings_a2av_virtual_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        vpp = ctypes.POINTER(ctypes.c_void_p)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        L.a2av_abi_version.argtypes = []
+        L.a2av_abi_version.restype = i32
+        L.a2av_strerror.argtypes = [i32]
+        L.a2av_strerror.restype = ctypes.c_char_p
+        L.a2av_exchange_splits.argtypes = [i32, vp, vp, vp, vp]
+        L.a2av_offsets.argtypes = [i32, vp, vp, vp, vp, vp, vp]
+        L.a2av_copy.argtypes = [i32, sz, vpp, i64p, vpp, i64p, vp, vp, vp, vp, vp]
+        L.moe_pack_workspace_bytes.argtypes = [i32, i64, i32, i32]
+        L.moe_pack_workspace_bytes.restype = sz
+        L.moe_pack.argtypes = [i32, i64, i32, i32, sz, vpp, vpp, vpp, vpp, vp, vp, vp, sz, vp, vp]
+        L.moe_unpack.argtypes = [i32, i64, i32, sz, vpp, vpp, vpp, vp, vp]
+        L.a2av_device_copy.argtypes = [vp, vp, sz, vp]
+        for f in ("a2av_exchange_splits", "a2av_offsets", "a2av_copy", "moe_pack", "moe_unpack",
+                  "a2av_device_copy"):
+            getattr(L, f).restype = i32
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------------ marshalling helpers
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, like: torch.Tensor) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(like.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr_array(tensors, name):
+    arr = (ctypes.c_void_p * len(tensors))()
+    for i, t in enumerate(tensors):
+        arr[i] = None if t is None else _dev(t, f"{name}[{i}]")
+    return arr
+
+
+def _i64_array(vals):
+    arr = (ctypes.c_int64 * len(vals))()
+    for i, v in enumerate(vals):
+        arr[i] = int(v)
+    return arr
+
+
+def _check(fn, rc):
+    if rc != OK:
+        raise A2avError(fn, rc)
+
+
+# ------------------------------------------------------------------ entry points
+def a2av_abi_version() -> int:
+    return lib().a2av_abi_version()
+
+
+def a2av_strerror(code: int) -> str:
+    return lib().a2av_strerror(int(code)).decode()
+
+
+def a2av_exchange_splits(S, O, status, stream=None):
+    """O[d][s] = S[s][d]; S, O: int64 [W, W] on the GPU; status: int32 [1]."""
+    W = S.shape[0]
+    _check("a2av_exchange_splits",
+           lib().a2av_exchange_splits(W, _dev(S, "S"), _dev(O, "O"), _dev(status, "status"),
+                                      _stream(stream, S)))
+
+
+def a2av_offsets(S, O, send_off, recv_off, status, stream=None):
+    """Exclusive scans of the rows of S and O into [W, W+1] int64 offsets."""
+    W = S.shape[0]
+    _check("a2av_offsets",
+           lib().a2av_offsets(W, _dev(S, "S"), _dev(O, "O"), _dev(send_off, "send_off"),
+                              _dev(recv_off, "recv_off"), _dev(status, "status"),
+                              _stream(stream, S)))
+
+
+def a2av_copy(row_bytes, ins, in_rows, outs, out_cap_rows, S, send_off, recv_off, status,
+              stream=None):
+    """Payload step. ``ins``/``outs``: W GPU tensors (any dtype, contiguous);
+    ``in_rows``/``out_cap_rows``: W host integers (rows each buffer holds)."""
+    W = len(ins)
+    if len(outs) != W or len(in_rows) != W or len(out_cap_rows) != W:
+        raise ValueError("ins, outs, in_rows and out_cap_rows need W entries each")
+    _check("a2av_copy",
+           lib().a2av_copy(W, int(row_bytes), _ptr_array(ins, "ins"), _i64_array(in_rows),
+                           _ptr_array(outs, "outs"), _i64_array(out_cap_rows), _dev(S, "S"),
+                           _dev(send_off, "send_off"), _dev(recv_off, "recv_off"),
+                           _dev(status, "status"), _stream(stream, S)))
+
+
+def moe_pack_workspace_bytes(W, T, k, E) -> int:
+    return int(lib().moe_pack_workspace_bytes(int(W), int(T), int(k), int(E)))
+
+
+def moe_pack(W, T, k, E, row_bytes, tokens, ids, send, perm, S, expert_counts, workspace,
+             status, stream=None):
+    """Stable pack of every rank's routing slots by expert id (see a2av.h)."""
+    _check("moe_pack",
+           lib().moe_pack(int(W), int(T), int(k), int(E), int(row_bytes),
+                          _ptr_array(tokens, "tokens"), _ptr_array(ids, "ids"),
+                          _ptr_array(send, "send"), _ptr_array(perm, "perm"), _dev(S, "S"),
+                          _dev(expert_counts, "expert_counts"), _dev(workspace, "workspace"),
+                          workspace.numel() * workspace.element_size(), _dev(status, "status"),
+                          _stream(stream, S)))
+
+
+def moe_unpack(W, T, k, row_bytes, back, perm, out, status, stream=None):
+    """out[r][q] = back[r][perm[r][q]] for every rank r."""
+    _check("moe_unpack",
+           lib().moe_unpack(int(W), int(T), int(k), int(row_bytes), _ptr_array(back, "back"),
+                            _ptr_array(perm, "perm"), _ptr_array(out, "out"),
+                            _dev(status, "status"), _stream(stream, status)))
+
+
+def a2av_device_copy(dst, src, nbytes, stream=None):
+    """Plain contiguous copy of nbytes from src to dst (bandwidth ceiling)."""
+    _check("a2av_device_copy",
+           lib().a2av_device_copy(_dev(dst, "dst"), _dev(src, "src"), int(nbytes),
+                                  _stream(stream, dst)))

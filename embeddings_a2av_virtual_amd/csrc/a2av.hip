@@ -1,0 +1,350 @@
+// a2av.hip — device-split all-to-all-v over W virtual ranks in one GPU's HBM
+// (gfx950): splits exchange, offset scans and the payload copy.
+//
+// The operation is the one the page "[a2av] Improve tuning for 4 GPUs" times
+// in its "Problem" section (nvshmem_all_to_all_vdev), read as all-to-all-v
+// with device-held counts. That page's "Change" section keeps the thread-block
+// count fixed when the peer count drops and moves blocks into the
+// data-parallel dimension; the payload kernel here goes one step further and
+// drops the peer dimension from the grid altogether: the destination byte
+// space of all ranks is cut into equal contiguous pieces, one per workgroup.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "common.hpp"
+
+namespace a2av {
+
+// ====================================================================== host helpers
+int device_cu_count(hipStream_t stream) {
+    static std::mutex mu;
+    static int cache[256] = {0};
+    int dev = 0;
+    if (stream == nullptr || hipStreamGetDevice(stream, &dev) != hipSuccess) {
+        if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev >= 0 && dev < 256 && cache[dev] > 0) return cache[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev >= 0 && dev < 256) cache[dev] = n;
+    return n;
+}
+
+long env_long(const char *name, long dflt, long lo, long hi) {
+    const char *v = std::getenv(name);
+    if (v == nullptr || *v == 0) return dflt;
+    char *end = nullptr;
+    long x = std::strtol(v, &end, 0);
+    if (end == v || x < lo || x > hi) return dflt;
+    return x;
+}
+
+// ====================================================================== exchange
+__global__ __launch_bounds__(256) void k_exchange(int W, const int64_t *__restrict__ S,
+                                                  int64_t *__restrict__ O, int32_t *status) {
+    if (status_poisoned(status)) return;
+    const int n = W * W;
+    int bad = 0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) bad |= split_invalid(S[i]);
+    if (__syncthreads_or(bad)) {
+        if (threadIdx.x == 0) atomicOr(status, A2AV_ST_BAD_SPLIT);
+        return;
+    }
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int s = i / W, d = i - s * W;
+        O[d * W + s] = S[i];
+    }
+}
+
+// ====================================================================== offsets
+// Row r < W scans S row r into send_off; row W + r scans O row r into
+// recv_off. One wave per row (W <= 64 entries fit one wave64 scan).
+__global__ __launch_bounds__(1024) void k_offsets(int W, const int64_t *__restrict__ S,
+                                                  const int64_t *__restrict__ O,
+                                                  int64_t *__restrict__ send_off,
+                                                  int64_t *__restrict__ recv_off,
+                                                  int32_t *status) {
+    if (status_poisoned(status)) return;
+    const int n = W * W;
+    int bad = 0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) bad |= split_invalid(S[i]) | split_invalid(O[i]);
+    if (__syncthreads_or(bad)) {
+        if (threadIdx.x == 0) atomicOr(status, A2AV_ST_BAD_SPLIT);
+        return;
+    }
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nwaves = blockDim.x / kWave;
+    for (int row = wave; row < 2 * W; row += nwaves) {
+        const int64_t *src = row < W ? S + (size_t)row * W : O + (size_t)(row - W) * W;
+        int64_t *dst = row < W ? send_off + (size_t)row * (W + 1) : recv_off + (size_t)(row - W) * (W + 1);
+        const int64_t v = lane < W ? src[lane] : 0;
+        const int64_t incl = wave_incl_scan(v);
+        if (lane < W) dst[lane] = incl - v;
+        if (lane == W - 1) dst[W] = incl;
+    }
+}
+
+// ====================================================================== payload copy
+struct CopyArgs {
+    const unsigned char *in[A2AV_MAX_W];
+    unsigned char *out[A2AV_MAX_W];
+    int64_t in_rows[A2AV_MAX_W];
+    int64_t cap[A2AV_MAX_W];
+    const int64_t *S;
+    const int64_t *send_off;
+    const int64_t *recv_off;
+    int32_t *status;
+    uint64_t R;          // row bytes
+    uint64_t min_piece;  // smallest piece of the destination space per block
+    int W;
+    int xcd_remap;       // 1: give each XCD a contiguous eighth of the pieces
+};
+
+// Every workgroup validates the whole split/offset set before any byte moves,
+// so a failure found by one is found by all and nothing is written.
+template <int BS>
+__device__ __forceinline__ int validate_all(const CopyArgs &a) {
+    __shared__ int s_bits;
+    if (threadIdx.x == 0) s_bits = 0;
+    __syncthreads();
+    const int W = a.W, W1 = W + 1;
+    int bits = 0;
+    for (int i = threadIdx.x; i < W * W; i += BS) {
+        const int s = i / W, d = i - s * W;
+        const int64_t v = a.S[i];
+        if (split_invalid(v)) bits |= A2AV_ST_BAD_SPLIT;
+        const int64_t so0 = a.send_off[s * W1 + d], so1 = a.send_off[s * W1 + d + 1];
+        const int64_t ro0 = a.recv_off[d * W1 + s], ro1 = a.recv_off[d * W1 + s + 1];
+        if ((uint64_t)so1 - (uint64_t)so0 != (uint64_t)v) bits |= A2AV_ST_BAD_OFFSETS;
+        if ((uint64_t)ro1 - (uint64_t)ro0 != (uint64_t)v) bits |= A2AV_ST_BAD_OFFSETS;
+        if (d == 0 && so0 != 0) bits |= A2AV_ST_BAD_OFFSETS;
+        if (s == 0 && ro0 != 0) bits |= A2AV_ST_BAD_OFFSETS;
+    }
+    // row totals against capacities: uniform index, so the kernel-argument
+    // arrays are read with scalar loads
+    if (threadIdx.x < kWave) {
+        for (int r = 0; r < W; r++) {
+            if (a.send_off[r * W1 + W] > a.in_rows[r]) bits |= A2AV_ST_SEND_OVERRUN;
+            if (a.recv_off[r * W1 + W] > a.cap[r]) bits |= A2AV_ST_RECV_OVERFLOW;
+        }
+    }
+    if (bits) atomicOr(&s_bits, bits);
+    __syncthreads();
+    return s_bits;
+}
+
+template <int BS, int U, bool NT>
+__global__ __launch_bounds__(BS) void k_a2av_copy(const CopyArgs a) {
+    if (status_poisoned(a.status)) return;
+    const int bits = validate_all<BS>(a);
+    if (bits) {
+        if (threadIdx.x == 0) atomicOr(a.status, bits);
+        return;
+    }
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int W = a.W, W1 = W + 1;
+    const uint64_t R = a.R;
+
+    // Destination byte space: out[0] rows, then out[1] rows, ... Rows before
+    // destination `lane` (lane < W) and the grand total.
+    const int64_t tot = lane < W ? a.recv_off[lane * W1 + W] : 0;
+    const int64_t incl = wave_incl_scan(tot);
+    const int64_t pre = incl - tot;
+    const uint64_t B = (uint64_t)__shfl(incl, kWave - 1) * R;
+
+    const uint64_t G = gridDim.x;
+    uint64_t piece = (B + G - 1) / G;
+    if (piece < a.min_piece) piece = a.min_piece;
+    piece = (piece + 4095) & ~(uint64_t)4095;
+    uint64_t g = blockIdx.x;
+    if (a.xcd_remap) g = (g & 7) * (G >> 3) + (g >> 3);
+    const uint64_t lo = g * piece;
+    if (lo >= B) return;
+    const uint64_t hi = lo + piece < B ? lo + piece : B;
+
+    // First destination whose space starts at or before lo, then first source
+    // chunk inside it (largest index with start <= lo).
+    const uint64_t mask_d = __ballot(lane < W && (uint64_t)pre * R <= lo);
+    int d = 63 - __clzll(mask_d);
+    uint64_t dbase = (uint64_t)__shfl(pre, d) * R;
+    const int64_t roff = lane < W ? a.recv_off[d * W1 + lane] : 0;
+    const uint64_t mask_s = __ballot(lane < W && dbase + (uint64_t)roff * R <= lo);
+    int s = 63 - __clzll(mask_s);
+
+    uint64_t x = lo;
+    while (x < hi && d < W) {
+        const int64_t r0 = a.recv_off[d * W1 + s];
+        const int64_t n = a.S[s * W + d];
+        const uint64_t F = dbase + (uint64_t)r0 * R;
+        const uint64_t L = (uint64_t)n * R;
+        if (n > 0 && x < F + L) {
+            const uint64_t e = hi < F + L ? hi : F + L;
+            const uint64_t off = x - F;
+            const int64_t so = a.send_off[s * W1 + d];
+            copy_segment<BS, U, NT>(a.out[d] + (uint64_t)r0 * R + off,
+                                    a.in[s] + (uint64_t)so * R + off, e - x, tid);
+            x = e;
+        }
+        if (++s == W) {
+            s = 0;
+            ++d;
+            if (d < W) dbase = (uint64_t)__shfl(pre, d) * R;
+        }
+    }
+}
+
+// ====================================================================== plain copy
+template <int BS, int U, bool NT>
+__global__ __launch_bounds__(BS) void k_device_copy(unsigned char *dst, const unsigned char *src,
+                                                    uint64_t bytes, uint64_t min_piece) {
+    const uint64_t G = gridDim.x;
+    uint64_t piece = (bytes + G - 1) / G;
+    if (piece < min_piece) piece = min_piece;
+    piece = (piece + 4095) & ~(uint64_t)4095;
+    const uint64_t lo = (uint64_t)blockIdx.x * piece;
+    if (lo >= bytes) return;
+    const uint64_t hi = lo + piece < bytes ? lo + piece : bytes;
+    copy_segment<BS, U, NT>(dst + lo, src + lo, hi - lo, threadIdx.x);
+}
+
+// ====================================================================== launch config
+struct CopyTuning {
+    int blocks_per_cu;
+    int unroll;
+    int nontemporal;
+    int xcd_remap;
+    long min_piece;
+};
+
+static CopyTuning copy_tuning() {
+    CopyTuning t;
+    t.blocks_per_cu = (int)env_long("A2AV_BLOCKS_PER_CU", 8, 1, 64);
+    t.unroll = (int)env_long("A2AV_UNROLL", 4, 1, 8);
+    t.nontemporal = (int)env_long("A2AV_NT", 1, 0, 1);
+    t.xcd_remap = (int)env_long("A2AV_XCD_REMAP", 0, 0, 1);
+    t.min_piece = env_long("A2AV_MIN_PIECE", 16384, 4096, 1L << 30);
+    return t;
+}
+
+template <int BS, int U>
+static void launch_copy_u(const CopyArgs &a, int grid, bool nt, hipStream_t st) {
+    if (nt) hipLaunchKernelGGL((k_a2av_copy<BS, U, true>), dim3(grid), dim3(BS), 0, st, a);
+    else hipLaunchKernelGGL((k_a2av_copy<BS, U, false>), dim3(grid), dim3(BS), 0, st, a);
+}
+
+template <int BS, int U>
+static void launch_dcopy_u(unsigned char *d, const unsigned char *s, uint64_t n, uint64_t mp,
+                           int grid, bool nt, hipStream_t st) {
+    if (nt) hipLaunchKernelGGL((k_device_copy<BS, U, true>), dim3(grid), dim3(BS), 0, st, d, s, n, mp);
+    else hipLaunchKernelGGL((k_device_copy<BS, U, false>), dim3(grid), dim3(BS), 0, st, d, s, n, mp);
+}
+
+static int launch_status() {
+    return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
+}
+
+}  // namespace a2av
+
+using namespace a2av;
+
+// ====================================================================== C ABI
+A2AV_API int a2av_abi_version(void) { return A2AV_ABI_VERSION; }
+
+A2AV_API const char *a2av_strerror(int code) {
+    switch (code) {
+    case A2AV_OK: return "ok";
+    case A2AV_EARG: return "invalid argument (nothing enqueued)";
+    case A2AV_EHIP: return "HIP runtime refused a launch";
+    case A2AV_ST_BAD_SPLIT: return "a split is negative or too large";
+    case A2AV_ST_SEND_OVERRUN: return "a rank sends more rows than its input holds";
+    case A2AV_ST_RECV_OVERFLOW: return "a rank receives more rows than its output holds";
+    case A2AV_ST_BAD_EXPERT: return "an expert id is out of range";
+    case A2AV_ST_BAD_OFFSETS: return "offsets are not the exclusive scans of the splits";
+    case A2AV_ST_BAD_PERM: return "a permutation entry is out of range";
+    default: return "unknown code";
+    }
+}
+
+A2AV_API int a2av_exchange_splits(int W, const int64_t *S, int64_t *O, int32_t *status,
+                                  hipStream_t stream) {
+    if (W < 1 || W > A2AV_MAX_W || !S || !O || !status) return A2AV_EARG;
+    hipLaunchKernelGGL(k_exchange, dim3(1), dim3(256), 0, stream, W, S, O, status);
+    return launch_status();
+}
+
+A2AV_API int a2av_offsets(int W, const int64_t *S, const int64_t *O, int64_t *send_off,
+                          int64_t *recv_off, int32_t *status, hipStream_t stream) {
+    if (W < 1 || W > A2AV_MAX_W || !S || !O || !send_off || !recv_off || !status) return A2AV_EARG;
+    const int threads = 2 * W * kWave < 1024 ? 2 * W * kWave : 1024;
+    hipLaunchKernelGGL(k_offsets, dim3(1), dim3(threads), 0, stream, W, S, O, send_off, recv_off,
+                       status);
+    return launch_status();
+}
+
+A2AV_API int a2av_copy(int W, size_t row_bytes, const void *const *in, const int64_t *in_rows,
+                       void *const *out, const int64_t *out_cap_rows, const int64_t *S,
+                       const int64_t *send_off, const int64_t *recv_off, int32_t *status,
+                       hipStream_t stream) {
+    if (W < 1 || W > A2AV_MAX_W || row_bytes == 0 || !in || !in_rows || !out || !out_cap_rows ||
+        !S || !send_off || !recv_off || !status)
+        return A2AV_EARG;
+    CopyArgs a;
+    std::memset(&a, 0, sizeof(a));
+    uint64_t cap_bytes = 0;  // the kernel's flat destination space must fit 62 bits
+    for (int r = 0; r < W; r++) {
+        if (in_rows[r] < 0 || out_cap_rows[r] < 0) return A2AV_EARG;
+        if ((uint64_t)in_rows[r] > (uint64_t)INT64_MAX / row_bytes) return A2AV_EARG;
+        if ((uint64_t)out_cap_rows[r] > (uint64_t)INT64_MAX / row_bytes) return A2AV_EARG;
+        if (in_rows[r] > 0 && in[r] == nullptr) return A2AV_EARG;
+        if (out_cap_rows[r] > 0 && out[r] == nullptr) return A2AV_EARG;
+        a.in[r] = (const unsigned char *)in[r];
+        a.out[r] = (unsigned char *)out[r];
+        a.in_rows[r] = in_rows[r];
+        a.cap[r] = out_cap_rows[r];
+        cap_bytes += (uint64_t)out_cap_rows[r] * row_bytes;
+        if (cap_bytes > ((uint64_t)1 << 62)) return A2AV_EARG;
+    }
+    a.S = S;
+    a.send_off = send_off;
+    a.recv_off = recv_off;
+    a.status = status;
+    a.R = row_bytes;
+    a.W = W;
+    const CopyTuning t = copy_tuning();
+    a.min_piece = (uint64_t)t.min_piece;
+    int grid = device_cu_count(stream) * t.blocks_per_cu;
+    grid = (grid + 7) & ~7;
+    a.xcd_remap = t.xcd_remap;
+    const bool nt = t.nontemporal != 0;
+    switch (t.unroll) {
+    case 1: launch_copy_u<256, 1>(a, grid, nt, stream); break;
+    case 2: launch_copy_u<256, 2>(a, grid, nt, stream); break;
+    case 8: launch_copy_u<256, 8>(a, grid, nt, stream); break;
+    default: launch_copy_u<256, 4>(a, grid, nt, stream); break;
+    }
+    return launch_status();
+}
+
+A2AV_API int a2av_device_copy(void *dst, const void *src, size_t bytes, hipStream_t stream) {
+    if (bytes == 0) return A2AV_OK;
+    if (!dst || !src) return A2AV_EARG;
+    const CopyTuning t = copy_tuning();
+    int grid = device_cu_count(stream) * t.blocks_per_cu;
+    const bool nt = t.nontemporal != 0;
+    unsigned char *d = (unsigned char *)dst;
+    const unsigned char *s = (const unsigned char *)src;
+    switch (t.unroll) {
+    case 1: launch_dcopy_u<256, 1>(d, s, bytes, t.min_piece, grid, nt, stream); break;
+    case 2: launch_dcopy_u<256, 2>(d, s, bytes, t.min_piece, grid, nt, stream); break;
+    case 8: launch_dcopy_u<256, 8>(d, s, bytes, t.min_piece, grid, nt, stream); break;
+    default: launch_dcopy_u<256, 4>(d, s, bytes, t.min_piece, grid, nt, stream); break;
+    }
+    return launch_status();
+}

@@ -1,0 +1,365 @@
+// moe.hip — MoE dispatch pack and un-pack around the a2av (gfx950).
+//
+// The pack is a stable counting sort of the T*k routing slots of each rank
+// by expert id; experts are owned by ranks in contiguous blocks, so sorting by
+// expert also groups the send buffer by destination rank, which is the
+// message layout of the MoE region the tuning page measures at 32 MiB.
+//
+//   k_moe_hist    LDS histogram of expert ids per segment of kSeg slots
+//   k_moe_scan    expert-major exclusive scan of the histograms (per rank):
+//                 base[e][seg] = slots of smaller experts + slots of expert e
+//                 in earlier segments; also the expert counts and splits
+//   k_moe_rank    stable rank inside a segment from wave64 ballots:
+//                 perm[q] = base[e][seg] + earlier slots of e in the segment
+//   k_moe_scatter token-major row scatter: read each token once, write it to
+//                 its k packed rows
+//   k_perm_check + k_moe_gather   the un-pack: out[q] = back[perm[q]]
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "common.hpp"
+
+namespace a2av {
+
+constexpr int kSeg = 1024;       // routing slots per segment
+constexpr int kRankWaves = 4;    // waves in a k_moe_rank block
+constexpr int kSlotsPerWave = kSeg / kRankWaves;
+
+struct MoeArgs {
+    const unsigned char *tokens[A2AV_MAX_W];
+    const int32_t *ids[A2AV_MAX_W];
+    unsigned char *send[A2AV_MAX_W];
+    int64_t *perm[A2AV_MAX_W];
+    int64_t *S;
+    int64_t *expert_counts;
+    int32_t *hist;   // workspace: [W][E][nseg] int32
+    int32_t *status;
+    uint64_t R;
+    int64_t T;
+    int64_t Q;       // T * k
+    int k;
+    int E;
+    int W;
+    int nseg;
+};
+
+// ------------------------------------------------------------------ histogram
+__global__ __launch_bounds__(256) void k_moe_hist(const MoeArgs a) {
+    extern __shared__ int32_t hist[];
+    if (status_poisoned(a.status)) return;
+    const int r = blockIdx.y, seg = blockIdx.x, E = a.E;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+    __syncthreads();
+    const int32_t *ids = a.ids[r];
+    const int64_t q0 = (int64_t)seg * kSeg;
+    int bad = 0;
+    for (int i = threadIdx.x; i < kSeg; i += blockDim.x) {
+        const int64_t q = q0 + i;
+        if (q < a.Q) {
+            const int e = ids[q];
+            if ((unsigned)e >= (unsigned)E) bad = 1;
+            else atomicAdd(&hist[e], 1);
+        }
+    }
+    bad = __syncthreads_or(bad);
+    int32_t *H = a.hist + (size_t)r * E * a.nseg;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) H[(size_t)e * a.nseg + seg] = hist[e];
+    if (bad && threadIdx.x == 0) atomicOr(a.status, A2AV_ST_BAD_EXPERT);
+}
+
+// ------------------------------------------------------------------ scan
+// One block per rank. Each thread scans a contiguous run of the E*nseg
+// counters; run totals are scanned across the block through LDS.
+__global__ __launch_bounds__(1024) void k_moe_scan(const MoeArgs a) {
+    __shared__ int32_t wave_tot[1024 / kWave];
+    if (status_poisoned(a.status)) return;
+    const int r = blockIdx.x;
+    const int64_t N = (int64_t)a.E * a.nseg;
+    int32_t *H = a.hist + (size_t)r * N;
+    const int nthr = blockDim.x;
+    const int64_t per = (N + nthr - 1) / nthr;
+    const int64_t b0 = (int64_t)threadIdx.x * per;
+    const int64_t b1 = b0 + per < N ? b0 + per : N;
+    int32_t sum = 0;
+    for (int64_t i = b0; i < b1; i++) sum += H[i];
+    // block exclusive scan of `sum`
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int32_t incl = wave_incl_scan32(sum);
+    if (lane == kWave - 1) wave_tot[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        const int nw = nthr / kWave;
+        const int32_t t = lane < nw ? wave_tot[lane] : 0;
+        const int32_t ti = wave_incl_scan32(t);
+        if (lane < nw) wave_tot[lane] = ti - t;
+    }
+    __syncthreads();
+    int32_t run = wave_tot[wave] + incl - sum;
+    for (int64_t i = b0; i < b1; i++) {
+        const int32_t c = H[i];
+        H[i] = run;
+        run += c;
+    }
+    __syncthreads();
+    // base of expert e = H[e][0]; the count is the gap to the next base
+    const int E = a.E;
+    for (int e = threadIdx.x; e < E; e += nthr) {
+        const int64_t b = H[(size_t)e * a.nseg];
+        const int64_t nb = e + 1 < E ? (int64_t)H[(size_t)(e + 1) * a.nseg] : a.Q;
+        a.expert_counts[(size_t)r * E + e] = nb - b;
+    }
+    const int per_rank = E / a.W;
+    for (int d = threadIdx.x; d < a.W; d += nthr) {
+        const int64_t b = H[(size_t)d * per_rank * a.nseg];
+        const int64_t nb = d + 1 < a.W ? (int64_t)H[(size_t)(d + 1) * per_rank * a.nseg] : a.Q;
+        a.S[(size_t)r * a.W + d] = nb - b;
+    }
+}
+
+// ------------------------------------------------------------------ stable rank
+// Wave w of the block owns slots [w*256, (w+1)*256) of the segment and walks
+// them 64 at a time in order. Lanes holding the same expert find each other
+// with one ballot per bit of the id; the lowest such lane bumps the wave's LDS
+// counter. After a barrier, the counts of earlier waves are added.
+__global__ __launch_bounds__(256) void k_moe_rank(const MoeArgs a) {
+    extern __shared__ int32_t cnt[];  // [kRankWaves][E]
+    if (status_poisoned(a.status)) return;
+    const int r = blockIdx.y, seg = blockIdx.x, E = a.E;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    for (int i = threadIdx.x; i < kRankWaves * E; i += blockDim.x) cnt[i] = 0;
+    __syncthreads();
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    const uint64_t below = (1ull << lane) - 1;
+    const int32_t *ids = a.ids[r];
+    int32_t *mine = cnt + wave * E;
+    int e_of[kSlotsPerWave / kWave];
+    int rank_of[kSlotsPerWave / kWave];
+    const int64_t qbase = (int64_t)seg * kSeg + wave * kSlotsPerWave;
+#pragma unroll
+    for (int c = 0; c < kSlotsPerWave / kWave; c++) {
+        const int64_t q = qbase + c * kWave + lane;
+        const bool ok = q < a.Q;
+        const int e = ok ? ids[q] : 0;
+        uint64_t peers = __ballot(ok);
+        for (int b = 0; b < nbits; b++) {
+            const int bit = (e >> b) & 1;
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        e_of[c] = e;
+        rank_of[c] = 0;
+        if (ok) {
+            const int before = mine[e];
+            const int rk = __popcll(peers & below);
+            rank_of[c] = before + rk;
+            if (rk == 0) mine[e] = before + __popcll(peers);
+        }
+    }
+    __syncthreads();
+    const int32_t *H = a.hist + (size_t)r * E * a.nseg;
+    int64_t *perm = a.perm[r];
+#pragma unroll
+    for (int c = 0; c < kSlotsPerWave / kWave; c++) {
+        const int64_t q = qbase + c * kWave + lane;
+        if (q < a.Q) {
+            const int e = e_of[c];
+            int32_t pre = 0;
+            for (int w = 0; w < wave; w++) pre += cnt[w * E + e];
+            perm[q] = (int64_t)H[(size_t)e * a.nseg + seg] + pre + rank_of[c];
+        }
+    }
+}
+
+// ------------------------------------------------------------------ scatter
+// One block per (token, rank): the row is read once into registers and
+// stored to the k packed rows of its slots (16-byte path when rows and bases
+// allow it, otherwise k block copies of the row).
+template <int BS, int U, bool ALIGNED>
+__global__ __launch_bounds__(BS) void k_moe_scatter(const MoeArgs a) {
+    if (status_poisoned(a.status)) return;
+    const int r = blockIdx.y;
+    const int64_t t = blockIdx.x;
+    const uint64_t R = a.R;
+    const unsigned char *src = a.tokens[r] + (uint64_t)t * R;
+    const int64_t *perm = a.perm[r] + t * a.k;
+    unsigned char *send = a.send[r];
+    if constexpr (ALIGNED) {
+        const uint64_t nv = R / 16;
+        const u32x4 *s16 = (const u32x4 *)src;
+        for (uint64_t base = 0; base < nv; base += (uint64_t)BS * U) {
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const uint64_t i = base + threadIdx.x + (uint64_t)u * BS;
+                if (i < nv) v[u] = ld<true>(s16 + i);
+            }
+            for (int j = 0; j < a.k; j++) {
+                const int64_t p = perm[j];
+                if (p < 0 || p >= a.Q) continue;
+                u32x4 *d16 = (u32x4 *)(send + (uint64_t)p * R);
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    const uint64_t i = base + threadIdx.x + (uint64_t)u * BS;
+                    if (i < nv) st<true>(d16 + i, v[u]);
+                }
+            }
+        }
+    } else {
+        for (int j = 0; j < a.k; j++) {
+            const int64_t p = perm[j];
+            if (p < 0 || p >= a.Q) continue;
+            copy_segment<BS, 2, false>(send + (uint64_t)p * R, src, R, threadIdx.x);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ un-pack
+struct UnpackArgs {
+    const unsigned char *back[A2AV_MAX_W];
+    const int64_t *perm[A2AV_MAX_W];
+    unsigned char *out[A2AV_MAX_W];
+    int32_t *status;
+    uint64_t R;
+    int64_t Q;
+    int64_t rows_per_block;
+};
+
+__global__ __launch_bounds__(256) void k_perm_check(const UnpackArgs a) {
+    if (status_poisoned(a.status)) return;
+    const int r = blockIdx.y;
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int bad = 0;
+    if (q < a.Q) {
+        const int64_t p = a.perm[r][q];
+        bad = p < 0 || p >= a.Q;
+    }
+    if (__ballot(bad) != 0 && (threadIdx.x & (kWave - 1)) == 0) atomicOr(a.status, A2AV_ST_BAD_PERM);
+}
+
+template <int BS, bool ALIGNED>
+__global__ __launch_bounds__(BS) void k_moe_gather(const UnpackArgs a) {
+    if (status_poisoned(a.status)) return;
+    const int r = blockIdx.y;
+    const int64_t q0 = (int64_t)blockIdx.x * a.rows_per_block;
+    const int64_t q1 = q0 + a.rows_per_block < a.Q ? q0 + a.rows_per_block : a.Q;
+    const uint64_t R = a.R;
+    const int64_t *perm = a.perm[r];
+    for (int64_t q = q0; q < q1; q++) {
+        const int64_t p = perm[q];
+        const unsigned char *src = a.back[r] + (uint64_t)p * R;
+        unsigned char *dst = a.out[r] + (uint64_t)q * R;
+        if constexpr (ALIGNED)
+            copy_elems<u32x4, BS, 4, true>((u32x4 *)dst, (const u32x4 *)src, R / 16, threadIdx.x);
+        else
+            copy_segment<BS, 2, false>(dst, src, R, threadIdx.x);
+    }
+}
+
+static int64_t n_segments(int64_t Q) { return (Q + kSeg - 1) / kSeg; }
+
+static bool moe_sizes_ok(int W, int64_t T, int k, int E) {
+    if (W < 1 || W > A2AV_MAX_W || T < 0 || k < 1 || E < 1 || E > A2AV_MAX_EXPERTS) return false;
+    if (E % W != 0) return false;
+    if (T > ((int64_t)1 << 31) / k) return false;
+    return T * k < ((int64_t)1 << 31);
+}
+
+}  // namespace a2av
+
+using namespace a2av;
+
+A2AV_API size_t moe_pack_workspace_bytes(int W, int64_t T, int k, int E) {
+    if (!moe_sizes_ok(W, T, k, E)) return 0;
+    const int64_t nseg = n_segments(T * k);
+    size_t b = (size_t)W * (size_t)E * (size_t)(nseg > 0 ? nseg : 1) * sizeof(int32_t);
+    return (b + 255) & ~(size_t)255;
+}
+
+A2AV_API int moe_pack(int W, int64_t T, int k, int E, size_t row_bytes,
+                      const void *const *tokens, const int32_t *const *ids, void *const *send,
+                      int64_t *const *perm, int64_t *S, int64_t *expert_counts, void *workspace,
+                      size_t workspace_bytes, int32_t *status, hipStream_t stream) {
+    if (!moe_sizes_ok(W, T, k, E) || row_bytes == 0 || !tokens || !ids || !send || !perm || !S ||
+        !expert_counts || !status)
+        return A2AV_EARG;
+    if (!workspace || workspace_bytes < moe_pack_workspace_bytes(W, T, k, E)) return A2AV_EARG;
+    if ((uint64_t)T * (uint64_t)k > (uint64_t)INT64_MAX / row_bytes) return A2AV_EARG;
+    MoeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    bool aligned = (row_bytes % 16) == 0;
+    for (int r = 0; r < W; r++) {
+        if (T > 0 && (!tokens[r] || !ids[r] || !send[r] || !perm[r])) return A2AV_EARG;
+        a.tokens[r] = (const unsigned char *)tokens[r];
+        a.ids[r] = ids[r];
+        a.send[r] = (unsigned char *)send[r];
+        a.perm[r] = perm[r];
+        aligned = aligned && ((uintptr_t)tokens[r] % 16 == 0) && ((uintptr_t)send[r] % 16 == 0);
+    }
+    a.S = S;
+    a.expert_counts = expert_counts;
+    a.hist = (int32_t *)workspace;
+    a.status = status;
+    a.R = row_bytes;
+    a.T = T;
+    a.k = k;
+    a.Q = T * k;
+    a.E = E;
+    a.W = W;
+    a.nseg = (int)n_segments(a.Q);
+    const int nseg_grid = a.nseg > 0 ? a.nseg : 1;
+    if (a.nseg > 0) {
+        hipLaunchKernelGGL(k_moe_hist, dim3(a.nseg, W), dim3(256), E * sizeof(int32_t), stream, a);
+    } else {
+        a.nseg = 1;  // no slots: one empty segment so counts and splits come out zero
+        hipLaunchKernelGGL(k_moe_hist, dim3(1, W), dim3(256), E * sizeof(int32_t), stream, a);
+    }
+    hipLaunchKernelGGL(k_moe_scan, dim3(W), dim3(1024), 0, stream, a);
+    if (a.Q > 0) {
+        hipLaunchKernelGGL(k_moe_rank, dim3(nseg_grid, W), dim3(kRankWaves * kWave),
+                           kRankWaves * E * sizeof(int32_t), stream, a);
+        if (aligned)
+            hipLaunchKernelGGL((k_moe_scatter<256, 4, true>), dim3(T, W), dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_moe_scatter<256, 4, false>), dim3(T, W), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
+}
+
+A2AV_API int moe_unpack(int W, int64_t T, int k, size_t row_bytes, const void *const *back,
+                        const int64_t *const *perm, void *const *out, int32_t *status,
+                        hipStream_t stream) {
+    if (W < 1 || W > A2AV_MAX_W || T < 0 || k < 1 || row_bytes == 0 || !back || !perm || !out ||
+        !status)
+        return A2AV_EARG;
+    if (T > INT64_MAX / k || (uint64_t)T * (uint64_t)k > (uint64_t)INT64_MAX / row_bytes)
+        return A2AV_EARG;
+    UnpackArgs a;
+    std::memset(&a, 0, sizeof(a));
+    bool aligned = (row_bytes % 16) == 0;
+    for (int r = 0; r < W; r++) {
+        if (T > 0 && (!back[r] || !perm[r] || !out[r])) return A2AV_EARG;
+        a.back[r] = (const unsigned char *)back[r];
+        a.perm[r] = perm[r];
+        a.out[r] = (unsigned char *)out[r];
+        aligned = aligned && ((uintptr_t)back[r] % 16 == 0) && ((uintptr_t)out[r] % 16 == 0);
+    }
+    a.status = status;
+    a.R = row_bytes;
+    a.Q = T * k;
+    if (a.Q == 0) return A2AV_OK;
+    int64_t rpb = (int64_t)((65536 + row_bytes - 1) / row_bytes);
+    if (rpb < 1) rpb = 1;
+    a.rows_per_block = rpb;
+    const int64_t check_blocks = (a.Q + 255) / 256;
+    const int64_t gather_blocks = (a.Q + rpb - 1) / rpb;
+    if (check_blocks > INT32_MAX || gather_blocks > INT32_MAX) return A2AV_EARG;
+    hipLaunchKernelGGL(k_perm_check, dim3((unsigned)check_blocks, W), dim3(256), 0, stream, a);
+    if (aligned)
+        hipLaunchKernelGGL((k_moe_gather<256, true>), dim3((unsigned)gather_blocks, W), dim3(256), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((k_moe_gather<256, false>), dim3((unsigned)gather_blocks, W), dim3(256),
+                           0, stream, a);
+    return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
+}

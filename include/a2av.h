@@ -1,0 +1,191 @@
+/*
+ * a2av.h — C ABI of liba2av.so: device-split all-to-all-v (a2av) and the MoE
+ * dispatch pack/unpack around it, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed. The page "[a2av] Improve tuning for 4 GPUs" (pytorch
+ * pull 154580), section "Problem", times nvshmem_all_to_all_vdev on 4 GPUs
+ * with per-rank messages of 0.5..4096 MiB; its section "Change" re-balances
+ * the thread blocks of that exchange between the peer dimension and the
+ * data-parallel dimension. The page does not spell out the operation; it is
+ * read here as MPI all-to-all-v with device-resident counts:
+ *   - rank s holds an input buffer and an int64 split vector S[s][0..W-1]
+ *     (rows it sends to each rank d);
+ *   - the output splits are the transpose O[d][s] = S[s][d];
+ *   - send and receive offsets are exclusive scans of S and O rows;
+ *   - rank d's output is the concatenation of the chunks sent to it, in
+ *     source-rank order.
+ * The W ranks are W partitions of one GPU's HBM: rank r is the pair of device
+ * buffers (in[r], out[r]) and row r of the split matrices.
+ *
+ * Conventions for every call:
+ *   - Matrices are row-major int64 in device memory: S and O are W x W, offsets
+ *     are W x (W+1) with the row total at index W.
+ *   - Pointer arrays (in, out, tokens, ...) and row-count arrays (in_rows,
+ *     out_cap_rows) are HOST arrays of length W holding device pointers / host
+ *     integers; they are read during the call and not kept.
+ *   - The caller owns every buffer. Nothing is allocated by the library
+ *     except as stated; scratch comes from a caller-provided workspace.
+ *   - Every call enqueues its kernels on `stream` and returns without
+ *     synchronising. Stream order carries the dependencies between calls.
+ *   - Return value (host side): 0 = enqueued; A2AV_EARG = a bad argument
+ *     (nothing enqueued); A2AV_EHIP = the HIP runtime refused a launch.
+ *   - Device-side failures are reported through `status`, a caller-zeroed
+ *     device int32. Kernels OR status bits into it. An op that finds the word
+ *     nonzero on entry writes nothing, and an op that detects a failure writes
+ *     no output byte (all-or-nothing), so a failed op poisons the rest of a
+ *     sequence that shares the word. Read it after synchronising the stream.
+ *   - Calls that overlap in time on buffers they share race; calls on
+ *     disjoint buffers may run concurrently on different streams.
+ */
+#ifndef A2AV_H
+#define A2AV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define A2AV_ABI_VERSION 1
+#define A2AV_MAX_W 64                        /* virtual ranks per call        */
+#define A2AV_MAX_SPLIT ((int64_t)1 << 40)    /* largest valid split (rows)    */
+#define A2AV_MAX_EXPERTS 4096                /* experts per moe_pack call     */
+
+/* host return codes */
+#define A2AV_OK 0
+#define A2AV_EARG (-1)
+#define A2AV_EHIP (-2)
+
+/* device status bits */
+#define A2AV_ST_BAD_SPLIT 1      /* a split is negative or above A2AV_MAX_SPLIT */
+#define A2AV_ST_SEND_OVERRUN 2   /* a rank sends more rows than in_rows        */
+#define A2AV_ST_RECV_OVERFLOW 4  /* a rank receives more rows than out_cap_rows */
+#define A2AV_ST_BAD_EXPERT 8     /* an expert id is outside [0, E)              */
+#define A2AV_ST_BAD_OFFSETS 16   /* offsets are not the exclusive scans of S    */
+#define A2AV_ST_BAD_PERM 32      /* a permutation entry is outside [0, T*k)     */
+
+/* ABI version of the loaded library (A2AV_ABI_VERSION it was built with). */
+int a2av_abi_version(void);
+
+/* Static text for a host return code or a status bit; never NULL. */
+const char *a2av_strerror(int code);
+
+/*
+ * Splits exchange: O[d][s] = S[s][d] (the output split matrix is the
+ * transpose of the input splits; row d of O is what rank d receives from
+ * each source).
+ *   W      1..A2AV_MAX_W
+ *   S      device int64 [W][W], row s = rank s's split vector (rows per peer)
+ *   O      device int64 [W][W], written
+ *   status device int32; sets A2AV_ST_BAD_SPLIT (and writes nothing) if any
+ *          split is negative or above A2AV_MAX_SPLIT.
+ * One single-workgroup kernel.
+ */
+int a2av_exchange_splits(int W, const int64_t *S, int64_t *O, int32_t *status,
+                         hipStream_t stream);
+
+/*
+ * Offsets: send_off[s][d] = sum_{d'<d} S[s][d'] and recv_off[d][s] =
+ * sum_{s'<s} O[d][s'] (exclusive scans), with the row totals at index W.
+ *   S, O      device int64 [W][W]
+ *   send_off  device int64 [W][W+1], written
+ *   recv_off  device int64 [W][W+1], written
+ *   status    sets A2AV_ST_BAD_SPLIT (writes nothing) for an invalid entry.
+ * One single-workgroup kernel; one wave64 prefix scan per row.
+ */
+int a2av_offsets(int W, const int64_t *S, const int64_t *O, int64_t *send_off,
+                 int64_t *recv_off, int32_t *status, hipStream_t stream);
+
+/*
+ * Payload: for every (s, d), rows [send_off[s][d], +S[s][d]) of in[s] are
+ * copied to out[d] at row recv_off[d][s]; rows are row_bytes wide and copied
+ * bit-for-bit. Output bytes past recv_off[d][W] rows are not touched; input
+ * rows past send_off[s][W] are not sent.
+ *   row_bytes     >= 1, same for every rank; any alignment is accepted, the
+ *                 fast path wants source and destination congruent mod 16
+ *   in[W]         host array of device pointers, in[s] holds in_rows[s] rows
+ *                 (may be NULL when in_rows[s] == 0)
+ *   out[W]        host array of device pointers, out[d] holds out_cap_rows[d]
+ *   S, send_off, recv_off  device matrices as produced by
+ *                 a2av_exchange_splits + a2av_offsets
+ *   status        checked before any byte moves, in every workgroup:
+ *                 A2AV_ST_BAD_SPLIT, A2AV_ST_BAD_OFFSETS (offsets are not the
+ *                 scans of S and S^T), A2AV_ST_SEND_OVERRUN
+ *                 (send_off[s][W] > in_rows[s]), A2AV_ST_RECV_OVERFLOW
+ *                 (recv_off[d][W] > out_cap_rows[d]); any of them => no byte
+ *                 of any out[d] is written.
+ * One persistent kernel: the destination byte space of all ranks is cut into
+ * equal contiguous pieces, one per workgroup, so skewed or zero splits leave
+ * no compute unit idle; each piece is copied with 16-byte coalesced accesses.
+ */
+int a2av_copy(int W, size_t row_bytes, const void *const *in,
+              const int64_t *in_rows, void *const *out,
+              const int64_t *out_cap_rows, const int64_t *S,
+              const int64_t *send_off, const int64_t *recv_off,
+              int32_t *status, hipStream_t stream);
+
+/*
+ * Workspace bytes moe_pack needs for these sizes (0 for invalid sizes).
+ */
+size_t moe_pack_workspace_bytes(int W, int64_t T, int k, int E);
+
+/*
+ * MoE dispatch pack, for every rank r at once: the T*k routing slots
+ * (slot q = t*k + j routes token t to expert ids[r][q]) are ordered by a
+ * stable counting sort on the expert id. Experts are owned in contiguous
+ * blocks of E/W per rank, so the order is (destination rank, expert, token,
+ * slot), the layout a following a2av sends.
+ *   T, k, E       tokens per rank, experts per token, experts in total;
+ *                 E % W == 0, 1 <= E <= A2AV_MAX_EXPERTS, T*k < 2^31
+ *   row_bytes     token row width in bytes (>= 1)
+ *   tokens[W]     device [T][row_bytes] per rank
+ *   ids[W]        device int32 [T][k] per rank
+ *   send[W]       device [T*k][row_bytes] per rank, written: send[perm[q]] =
+ *                 tokens[q / k]
+ *   perm[W]       device int64 [T*k] per rank, written: row of slot q in send
+ *   S             device int64 [W][W], written: S[r][d] = slots of rank r bound
+ *                 for rank d (the split matrix of the dispatch a2av)
+ *   expert_counts device int64 [W][E], written: slots per (rank, expert)
+ *   workspace     device scratch of >= moe_pack_workspace_bytes() bytes
+ *   status        A2AV_ST_BAD_EXPERT for an id outside [0, E): nothing but
+ *                 the workspace is written.
+ * Four kernels: an LDS histogram per slot segment, an expert-major scan of the
+ * histograms, a stable in-segment rank (wave ballots), and a token-major row
+ * scatter that reads each token once and writes it k times.
+ */
+int moe_pack(int W, int64_t T, int k, int E, size_t row_bytes,
+             const void *const *tokens, const int32_t *const *ids,
+             void *const *send, int64_t *const *perm, int64_t *S,
+             int64_t *expert_counts, void *workspace, size_t workspace_bytes,
+             int32_t *status, hipStream_t stream);
+
+/*
+ * MoE un-pack after the return trip ("inverse combine" without weights):
+ * out[r][q] = back[r][perm[r][q]] for q < T*k, i.e. every slot gets back the
+ * row it was packed to. back is what the return a2av (splits O, the
+ * transpose of the dispatch splits) delivered to rank r.
+ *   back[W], out[W]  device [T*k][row_bytes] per rank
+ *   perm[W]          device int64 [T*k] per rank, from moe_pack
+ *   status           A2AV_ST_BAD_PERM if an entry is outside [0, T*k):
+ *                    nothing is written.
+ * Two kernels: a range check of perm, then a row gather.
+ */
+int moe_unpack(int W, int64_t T, int k, size_t row_bytes,
+               const void *const *back, const int64_t *const *perm,
+               void *const *out, int32_t *status, hipStream_t stream);
+
+/*
+ * Plain contiguous device copy of `bytes` bytes (dst and src device pointers,
+ * not overlapping), with the same copy loop as a2av_copy. A bandwidth
+ * ceiling for the payload kernel and the reference for counter scaling.
+ */
+int a2av_device_copy(void *dst, const void *src, size_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* A2AV_H */

@@ -1,0 +1,89 @@
+"""The C ABI library loads, exports every symbol its header declares, and
+rejects bad host arguments before touching the GPU (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "a2av.h")
+
+
+def declared_functions(path):
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = "\n".join(l for l in text.splitlines() if not l.lstrip().startswith("#"))
+    return sorted(set(re.findall(r"\b([A-Za-z_]\w*)\s*\([^;{}]*\)\s*;", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from embeddings_a2av_virtual_amd import _binding
+    return _binding.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions(HEADER)
+    for must in ("a2av_exchange_splits", "a2av_offsets", "a2av_copy", "moe_pack", "moe_unpack",
+                 "moe_pack_workspace_bytes", "a2av_abi_version", "a2av_strerror"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions(HEADER):
+        assert hasattr(L, name), f"{name} declared in a2av.h but not exported"
+
+
+def test_only_declared_symbols_are_exported():
+    import subprocess
+    from embeddings_a2av_virtual_amd._binding import LIB_PATH
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.split()[1] in ("T", "W")}
+    exported = {n for n in exported if not n.startswith("_")}
+    assert exported == set(declared_functions(HEADER))
+
+
+def test_version_and_strerror(L):
+    from embeddings_a2av_virtual_amd import _binding as B
+    assert B.a2av_abi_version() == 1
+    for code in (0, -1, -2, 1, 2, 4, 8, 16, 32, 12345):
+        assert isinstance(B.a2av_strerror(code), str) and B.a2av_strerror(code)
+
+
+def test_host_argument_errors(L):
+    """Checks that return A2AV_EARG before any HIP call is made."""
+    EARG = -1
+    vp = ctypes.c_void_p
+    assert L.a2av_exchange_splits(0, vp(8), vp(8), vp(8), None) == EARG
+    assert L.a2av_exchange_splits(65, vp(8), vp(8), vp(8), None) == EARG
+    assert L.a2av_exchange_splits(4, None, vp(8), vp(8), None) == EARG
+    assert L.a2av_offsets(4, vp(8), vp(8), None, vp(8), vp(8), None) == EARG
+    arr = (ctypes.c_void_p * 4)(8, 8, 8, 8)
+    rows = (ctypes.c_int64 * 4)(1, 1, 1, 1)
+    neg = (ctypes.c_int64 * 4)(1, -1, 1, 1)
+    # row_bytes 0, negative rows, rows * row_bytes overflowing, null buffers with rows
+    assert L.a2av_copy(4, 0, arr, rows, arr, rows, vp(8), vp(8), vp(8), vp(8), None) == EARG
+    assert L.a2av_copy(4, 8, arr, neg, arr, rows, vp(8), vp(8), vp(8), vp(8), None) == EARG
+    big = (ctypes.c_int64 * 4)(1, 1 << 62, 1, 1)
+    assert L.a2av_copy(4, 8, arr, big, arr, rows, vp(8), vp(8), vp(8), vp(8), None) == EARG
+    nul = (ctypes.c_void_p * 4)(8, None, 8, 8)
+    assert L.a2av_copy(4, 8, nul, rows, arr, rows, vp(8), vp(8), vp(8), vp(8), None) == EARG
+    # MoE size rules: E % W, E above the maximum, T*k past 2^31, small workspace
+    assert L.moe_pack_workspace_bytes(8, 8192, 8, 256) > 0
+    assert L.moe_pack_workspace_bytes(3, 10, 2, 8) == 0
+    assert L.moe_pack_workspace_bytes(1, 10, 2, 4097) == 0
+    assert L.moe_pack_workspace_bytes(1, 1 << 29, 8, 8) == 0
+    ptrs = (ctypes.c_void_p * 2)(8, 8)
+    ws = L.moe_pack_workspace_bytes(2, 10, 2, 8)
+    assert L.moe_pack(2, 10, 2, 8, 16, ptrs, ptrs, ptrs, ptrs, vp(8), vp(8), vp(8), ws - 1,
+                      vp(8), None) == EARG
+    assert L.moe_unpack(2, 10, 0, 16, ptrs, ptrs, ptrs, vp(8), None) == EARG
+
+
+def test_workspace_formula(L):
+    # one int32 counter per (rank, expert, segment of 1024 slots), 256-byte rounded
+    assert L.moe_pack_workspace_bytes(8, 8192, 8, 256) == 8 * 256 * 64 * 4
+    assert L.moe_pack_workspace_bytes(2, 0, 2, 8) == 256
