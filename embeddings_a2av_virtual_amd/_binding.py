@@ -22,6 +22,7 @@ __all__ = [
     "ST_BAD_SPLIT", "ST_SEND_OVERRUN", "ST_RECV_OVERFLOW", "ST_BAD_EXPERT", "ST_BAD_OFFSETS",
     "ST_BAD_PERM",
     "a2av_abi_version", "a2av_strerror", "a2av_exchange_splits", "a2av_offsets", "a2av_copy",
+    "a2av_all_to_all_vdev",
     "moe_pack_workspace_bytes", "moe_pack", "moe_unpack", "a2av_device_copy",
 ]
 
@@ -65,13 +66,14 @@ def lib():
         L.a2av_exchange_splits.argtypes = [i32, vp, vp, vp, vp]
         L.a2av_offsets.argtypes = [i32, vp, vp, vp, vp, vp, vp]
         L.a2av_copy.argtypes = [i32, sz, vpp, i64p, vpp, i64p, vp, vp, vp, vp, vp]
+        L.a2av_all_to_all_vdev.argtypes = [i32, sz, vpp, i64p, vpp, i64p, vp, vp, vp, vp, vp, vp]
         L.moe_pack_workspace_bytes.argtypes = [i32, i64, i32, i32]
         L.moe_pack_workspace_bytes.restype = sz
         L.moe_pack.argtypes = [i32, i64, i32, i32, sz, vpp, vpp, vpp, vpp, vp, vp, vp, sz, vp, vp]
         L.moe_unpack.argtypes = [i32, i64, i32, sz, vpp, vpp, vpp, vp, vp]
         L.a2av_device_copy.argtypes = [vp, vp, sz, vp]
-        for f in ("a2av_exchange_splits", "a2av_offsets", "a2av_copy", "moe_pack", "moe_unpack",
-                  "a2av_device_copy"):
+        for f in ("a2av_exchange_splits", "a2av_offsets", "a2av_copy", "a2av_all_to_all_vdev",
+                  "moe_pack", "moe_unpack", "a2av_device_copy"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -151,6 +153,20 @@ def a2av_copy(row_bytes, ins, in_rows, outs, out_cap_rows, S, send_off, recv_off
                            _ptr_array(outs, "outs"), _i64_array(out_cap_rows), _dev(S, "S"),
                            _dev(send_off, "send_off"), _dev(recv_off, "recv_off"),
                            _dev(status, "status"), _stream(stream, S)))
+
+
+def a2av_all_to_all_vdev(row_bytes, ins, in_rows, outs, out_cap_rows, S, O, send_off, recv_off,
+                         status, stream=None):
+    """Exchange, offsets and payload in one call (one launch for W <= 16)."""
+    W = len(ins)
+    if len(outs) != W or len(in_rows) != W or len(out_cap_rows) != W:
+        raise ValueError("ins, outs, in_rows and out_cap_rows need W entries each")
+    _check("a2av_all_to_all_vdev",
+           lib().a2av_all_to_all_vdev(W, int(row_bytes), _ptr_array(ins, "ins"),
+                                      _i64_array(in_rows), _ptr_array(outs, "outs"),
+                                      _i64_array(out_cap_rows), _dev(S, "S"), _dev(O, "O"),
+                                      _dev(send_off, "send_off"), _dev(recv_off, "recv_off"),
+                                      _dev(status, "status"), _stream(stream, S)))
 
 
 def moe_pack_workspace_bytes(W, T, k, E) -> int:

@@ -91,111 +91,195 @@ __global__ __launch_bounds__(1024) void k_offsets(int W, const int64_t *__restri
 }
 
 // ====================================================================== payload copy
+// A block stages the split and offset matrices in LDS when W <= kMetaW (one
+// global round trip for all of its metadata); above that it reads them from
+// global memory (they are a few KiB and stay in L2).
+constexpr int kMetaW = 16;
+
 struct CopyArgs {
     const unsigned char *in[A2AV_MAX_W];
     unsigned char *out[A2AV_MAX_W];
     int64_t in_rows[A2AV_MAX_W];
     int64_t cap[A2AV_MAX_W];
     const int64_t *S;
-    const int64_t *send_off;
+    const int64_t *send_off;   // copy modes: input; fused mode: unused
     const int64_t *recv_off;
+    int64_t *O_out;            // fused mode: outputs written by block 0
+    int64_t *send_off_out;
+    int64_t *recv_off_out;
     int32_t *status;
     uint64_t R;          // row bytes
     uint64_t min_piece;  // smallest piece of the destination space per block
+    uint64_t piece;      // 0: one contiguous piece per block; else fixed piece
+                         // size, pieces dealt to blocks round-robin
     int W;
-    int xcd_remap;       // 1: give each XCD a contiguous eighth of the pieces
 };
 
-// Every workgroup validates the whole split/offset set before any byte moves,
-// so a failure found by one is found by all and nothing is written.
-template <int BS>
-__device__ __forceinline__ int validate_all(const CopyArgs &a) {
-    __shared__ int s_bits;
-    if (threadIdx.x == 0) s_bits = 0;
-    __syncthreads();
-    const int W = a.W, W1 = W + 1;
+template <int MW>
+struct MetaLds {
+    int64_t S[MW * MW];
+    int64_t so[MW * (MW + 1)];
+    int64_t ro[MW * (MW + 1)];
+    int64_t pre[A2AV_MAX_W + 1];  // rows of destinations before d; [W] = total
+    int bits;
+};
+
+enum PayloadMode {
+    kCopyStaged = 0,  // a2av_copy, W <= kMetaW: S and offsets staged in LDS
+    kCopyGlobal = 1,  // a2av_copy, W > kMetaW: metadata read from global
+    kFused = 2,       // a2av_all_to_all_vdev, W <= kMetaW: offsets computed here
+};
+
+// Consistency of one (s, d) pair of the given offsets with S: the checks the
+// payload step makes before any byte moves.
+__device__ __forceinline__ int pair_bits(int64_t v, int64_t so0, int64_t so1, int64_t ro0,
+                                         int64_t ro1, int s, int d) {
     int bits = 0;
-    for (int i = threadIdx.x; i < W * W; i += BS) {
-        const int s = i / W, d = i - s * W;
-        const int64_t v = a.S[i];
-        if (split_invalid(v)) bits |= A2AV_ST_BAD_SPLIT;
-        const int64_t so0 = a.send_off[s * W1 + d], so1 = a.send_off[s * W1 + d + 1];
-        const int64_t ro0 = a.recv_off[d * W1 + s], ro1 = a.recv_off[d * W1 + s + 1];
-        if ((uint64_t)so1 - (uint64_t)so0 != (uint64_t)v) bits |= A2AV_ST_BAD_OFFSETS;
-        if ((uint64_t)ro1 - (uint64_t)ro0 != (uint64_t)v) bits |= A2AV_ST_BAD_OFFSETS;
-        if (d == 0 && so0 != 0) bits |= A2AV_ST_BAD_OFFSETS;
-        if (s == 0 && ro0 != 0) bits |= A2AV_ST_BAD_OFFSETS;
-    }
-    // row totals against capacities: uniform index, so the kernel-argument
-    // arrays are read with scalar loads
-    if (threadIdx.x < kWave) {
-        for (int r = 0; r < W; r++) {
-            if (a.send_off[r * W1 + W] > a.in_rows[r]) bits |= A2AV_ST_SEND_OVERRUN;
-            if (a.recv_off[r * W1 + W] > a.cap[r]) bits |= A2AV_ST_RECV_OVERFLOW;
-        }
-    }
-    if (bits) atomicOr(&s_bits, bits);
-    __syncthreads();
-    return s_bits;
+    if (split_invalid(v)) bits |= A2AV_ST_BAD_SPLIT;
+    if ((uint64_t)so1 - (uint64_t)so0 != (uint64_t)v) bits |= A2AV_ST_BAD_OFFSETS;
+    if ((uint64_t)ro1 - (uint64_t)ro0 != (uint64_t)v) bits |= A2AV_ST_BAD_OFFSETS;
+    if (d == 0 && so0 != 0) bits |= A2AV_ST_BAD_OFFSETS;
+    if (s == 0 && ro0 != 0) bits |= A2AV_ST_BAD_OFFSETS;
+    return bits;
 }
 
-template <int BS, int U, bool NT>
-__global__ __launch_bounds__(BS) void k_a2av_copy(const CopyArgs a) {
-    if (status_poisoned(a.status)) return;
-    const int bits = validate_all<BS>(a);
-    if (bits) {
-        if (threadIdx.x == 0) atomicOr(a.status, bits);
-        return;
-    }
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
+// Wave 0: rows before each destination (pre) and the totals against the
+// capacities. The capacity arrays are read with a uniform index (scalar
+// loads from the kernel arguments).
+template <int MW>
+__device__ __forceinline__ int totals_and_pre(const CopyArgs &a, MetaLds<MW> &m,
+                                              const int64_t *so, const int64_t *ro) {
     const int W = a.W, W1 = W + 1;
-    const uint64_t R = a.R;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t t = lane < W ? ro[lane * W1 + W] : 0;
+    const int64_t incl = wave_incl_scan(t);
+    if (lane < W) m.pre[lane] = incl - t;
+    if (lane == W - 1) m.pre[W] = incl;
+    int bits = 0;
+    for (int r = 0; r < W; r++) {
+        if (so[r * W1 + W] > a.in_rows[r]) bits |= A2AV_ST_SEND_OVERRUN;
+        if (ro[r * W1 + W] > a.cap[r]) bits |= A2AV_ST_RECV_OVERFLOW;
+    }
+    return bits;
+}
 
-    // Destination byte space: out[0] rows, then out[1] rows, ... Rows before
-    // destination `lane` (lane < W) and the grand total.
-    const int64_t tot = lane < W ? a.recv_off[lane * W1 + W] : 0;
-    const int64_t incl = wave_incl_scan(tot);
-    const int64_t pre = incl - tot;
-    const uint64_t B = (uint64_t)__shfl(incl, kWave - 1) * R;
+template <int BS, int U, bool NT, int MODE>
+__global__ __launch_bounds__(BS) void k_a2av_payload(const CopyArgs a) {
+    constexpr int MW = MODE == kCopyGlobal ? 1 : kMetaW;
+    __shared__ MetaLds<MW> m;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const int W = a.W, W1 = W + 1;
 
-    const uint64_t G = gridDim.x;
-    uint64_t piece = (B + G - 1) / G;
-    if (piece < a.min_piece) piece = a.min_piece;
-    piece = (piece + 4095) & ~(uint64_t)4095;
-    uint64_t g = blockIdx.x;
-    if (a.xcd_remap) g = (g & 7) * (G >> 3) + (g >> 3);
-    const uint64_t lo = g * piece;
-    if (lo >= B) return;
-    const uint64_t hi = lo + piece < B ? lo + piece : B;
-
-    // First destination whose space starts at or before lo, then first source
-    // chunk inside it (largest index with start <= lo).
-    const uint64_t mask_d = __ballot(lane < W && (uint64_t)pre * R <= lo);
-    int d = 63 - __clzll(mask_d);
-    uint64_t dbase = (uint64_t)__shfl(pre, d) * R;
-    const int64_t roff = lane < W ? a.recv_off[d * W1 + lane] : 0;
-    const uint64_t mask_s = __ballot(lane < W && dbase + (uint64_t)roff * R <= lo);
-    int s = 63 - __clzll(mask_s);
-
-    uint64_t x = lo;
-    while (x < hi && d < W) {
-        const int64_t r0 = a.recv_off[d * W1 + s];
-        const int64_t n = a.S[s * W + d];
-        const uint64_t F = dbase + (uint64_t)r0 * R;
-        const uint64_t L = (uint64_t)n * R;
-        if (n > 0 && x < F + L) {
-            const uint64_t e = hi < F + L ? hi : F + L;
-            const uint64_t off = x - F;
-            const int64_t so = a.send_off[s * W1 + d];
-            copy_segment<BS, U, NT>(a.out[d] + (uint64_t)r0 * R + off,
-                                    a.in[s] + (uint64_t)so * R + off, e - x, tid);
-            x = e;
+    // ---- prologue: the status word and the metadata loads go out together
+    const bool poisoned = status_poisoned(a.status);
+    if constexpr (MODE != kCopyGlobal) {
+        for (int i = tid; i < W * W; i += BS) m.S[i] = a.S[i];
+    }
+    if constexpr (MODE == kCopyStaged) {
+        for (int i = tid; i < W * W1; i += BS) {
+            m.so[i] = a.send_off[i];
+            m.ro[i] = a.recv_off[i];
         }
-        if (++s == W) {
-            s = 0;
-            ++d;
-            if (d < W) dbase = (uint64_t)__shfl(pre, d) * R;
+    }
+    if (tid == 0) m.bits = 0;
+    if (poisoned) return;
+    __syncthreads();
+
+    const int64_t *Sp = MODE == kCopyGlobal ? a.S : m.S;
+    const int64_t *sop = MODE == kCopyGlobal ? a.send_off : m.so;
+    const int64_t *rop = MODE == kCopyGlobal ? a.recv_off : m.ro;
+    int bits = 0;
+    if constexpr (MODE == kFused) {
+        // splits valid; then send rows (S rows) and receive rows (S columns)
+        // scanned, one wave64 scan per row
+        for (int i = tid; i < W * W; i += BS)
+            if (split_invalid(m.S[i])) bits |= A2AV_ST_BAD_SPLIT;
+        for (int r = wave; r < 2 * W; r += BS / kWave) {
+            int64_t v = 0;
+            if (lane < W) v = r < W ? m.S[r * W + lane] : m.S[lane * W + (r - W)];
+            const int64_t incl = wave_incl_scan(v);
+            int64_t *dst = r < W ? m.so + r * W1 : m.ro + (r - W) * W1;
+            if (lane < W) dst[lane] = incl - v;
+            if (lane == W - 1) dst[W] = incl;
+        }
+        __syncthreads();
+    } else {
+        for (int i = tid; i < W * W; i += BS) {
+            const int s = i / W, d = i - s * W;
+            bits |= pair_bits(Sp[i], sop[s * W1 + d], sop[s * W1 + d + 1], rop[d * W1 + s],
+                              rop[d * W1 + s + 1], s, d);
+        }
+    }
+    if (wave == 0) bits |= totals_and_pre(a, m, sop, rop);
+    if (bits) atomicOr(&m.bits, bits);
+    __syncthreads();
+    bits = m.bits;
+    // fused: invalid splits stop the sequence at the exchange, as three
+    // separate calls would, so the totals of bad scans are not reported
+    if (MODE == kFused && (bits & A2AV_ST_BAD_SPLIT)) bits = A2AV_ST_BAD_SPLIT;
+
+    if constexpr (MODE == kFused) {
+        // block 0 publishes the exchange and offsets (when the splits are valid)
+        if (blockIdx.x == 0) {
+            if (!(bits & A2AV_ST_BAD_SPLIT)) {
+                for (int i = tid; i < W * W; i += BS) {
+                    const int s = i / W, d = i - s * W;
+                    a.O_out[d * W + s] = m.S[i];
+                }
+                for (int i = tid; i < W * W1; i += BS) {
+                    a.send_off_out[i] = m.so[i];
+                    a.recv_off_out[i] = m.ro[i];
+                }
+            }
+            if (bits && tid == 0) atomicOr(a.status, bits);
+        }
+    } else {
+        if (bits && tid == 0) atomicOr(a.status, bits);
+    }
+    if (bits) return;
+
+    // ---- the destination byte space: out[0] rows, then out[1] rows, ...
+    const uint64_t R = a.R;
+    const uint64_t B = (uint64_t)m.pre[W] * R;
+    const uint64_t G = gridDim.x;
+    uint64_t piece = a.piece;
+    if (piece == 0) {
+        piece = (B + G - 1) / G;
+        if (piece < a.min_piece) piece = a.min_piece;
+        piece = (piece + 4095) & ~(uint64_t)4095;
+    }
+    for (uint64_t p = blockIdx.x; p * piece < B; p += G) {
+        const uint64_t lo = p * piece;
+        const uint64_t hi = lo + piece < B ? lo + piece : B;
+        // last destination whose space starts at or before lo, then the last
+        // source chunk inside it that starts at or before lo
+        const int64_t pre_l = lane < W ? m.pre[lane] : 0;
+        const uint64_t mask_d = __ballot(lane < W && (uint64_t)pre_l * R <= lo);
+        int d = 63 - __clzll(mask_d);
+        uint64_t dbase = (uint64_t)m.pre[d] * R;
+        const int64_t roff = lane < W ? rop[d * W1 + lane] : 0;
+        const uint64_t mask_s = __ballot(lane < W && dbase + (uint64_t)roff * R <= lo);
+        int s = 63 - __clzll(mask_s);
+        uint64_t x = lo;
+        while (x < hi && d < W) {
+            const int64_t r0 = rop[d * W1 + s];
+            const int64_t n = Sp[s * W + d];
+            const uint64_t F = dbase + (uint64_t)r0 * R;
+            const uint64_t L = (uint64_t)n * R;
+            if (n > 0 && x < F + L) {
+                const uint64_t e = hi < F + L ? hi : F + L;
+                const uint64_t off = x - F;
+                const int64_t so = sop[s * W1 + d];
+                copy_segment<BS, U, NT>(a.out[d] + (uint64_t)r0 * R + off,
+                                        a.in[s] + (uint64_t)so * R + off, e - x, tid);
+                x = e;
+            }
+            if (++s == W) {
+                s = 0;
+                ++d;
+                if (d < W) dbase = (uint64_t)m.pre[d] * R;
+            }
         }
     }
 }
@@ -203,15 +287,20 @@ __global__ __launch_bounds__(BS) void k_a2av_copy(const CopyArgs a) {
 // ====================================================================== plain copy
 template <int BS, int U, bool NT>
 __global__ __launch_bounds__(BS) void k_device_copy(unsigned char *dst, const unsigned char *src,
-                                                    uint64_t bytes, uint64_t min_piece) {
+                                                    uint64_t bytes, uint64_t min_piece,
+                                                    uint64_t fixed_piece) {
     const uint64_t G = gridDim.x;
-    uint64_t piece = (bytes + G - 1) / G;
-    if (piece < min_piece) piece = min_piece;
-    piece = (piece + 4095) & ~(uint64_t)4095;
-    const uint64_t lo = (uint64_t)blockIdx.x * piece;
-    if (lo >= bytes) return;
-    const uint64_t hi = lo + piece < bytes ? lo + piece : bytes;
-    copy_segment<BS, U, NT>(dst + lo, src + lo, hi - lo, threadIdx.x);
+    uint64_t piece = fixed_piece;
+    if (piece == 0) {
+        piece = (bytes + G - 1) / G;
+        if (piece < min_piece) piece = min_piece;
+        piece = (piece + 4095) & ~(uint64_t)4095;
+    }
+    for (uint64_t p = blockIdx.x; p * piece < bytes; p += G) {
+        const uint64_t lo = p * piece;
+        const uint64_t hi = lo + piece < bytes ? lo + piece : bytes;
+        copy_segment<BS, U, NT>(dst + lo, src + lo, hi - lo, threadIdx.x);
+    }
 }
 
 // ====================================================================== launch config
@@ -219,35 +308,79 @@ struct CopyTuning {
     int blocks_per_cu;
     int unroll;
     int nontemporal;
-    int xcd_remap;
     long min_piece;
+    long piece;
 };
 
 static CopyTuning copy_tuning() {
     CopyTuning t;
-    t.blocks_per_cu = (int)env_long("A2AV_BLOCKS_PER_CU", 8, 1, 64);
+    t.blocks_per_cu = (int)env_long("A2AV_BLOCKS_PER_CU", 16, 1, 64);
     t.unroll = (int)env_long("A2AV_UNROLL", 4, 1, 8);
     t.nontemporal = (int)env_long("A2AV_NT", 1, 0, 1);
-    t.xcd_remap = (int)env_long("A2AV_XCD_REMAP", 0, 0, 1);
     t.min_piece = env_long("A2AV_MIN_PIECE", 16384, 4096, 1L << 30);
+    t.piece = env_long("A2AV_PIECE", 0, 0, 1L << 34);
+    if (t.piece != 0) t.piece = (t.piece + 4095) & ~4095L;
     return t;
 }
 
-template <int BS, int U>
-static void launch_copy_u(const CopyArgs &a, int grid, bool nt, hipStream_t st) {
-    if (nt) hipLaunchKernelGGL((k_a2av_copy<BS, U, true>), dim3(grid), dim3(BS), 0, st, a);
-    else hipLaunchKernelGGL((k_a2av_copy<BS, U, false>), dim3(grid), dim3(BS), 0, st, a);
+template <int BS, int U, int MODE>
+static void launch_payload_u(const CopyArgs &a, int grid, bool nt, hipStream_t st) {
+    if (nt) hipLaunchKernelGGL((k_a2av_payload<BS, U, true, MODE>), dim3(grid), dim3(BS), 0, st, a);
+    else hipLaunchKernelGGL((k_a2av_payload<BS, U, false, MODE>), dim3(grid), dim3(BS), 0, st, a);
+}
+
+template <int MODE>
+static void launch_payload(const CopyArgs &a, int grid, const CopyTuning &t, hipStream_t st) {
+    const bool nt = t.nontemporal != 0;
+    switch (t.unroll) {
+    case 1: launch_payload_u<256, 1, MODE>(a, grid, nt, st); break;
+    case 2: launch_payload_u<256, 2, MODE>(a, grid, nt, st); break;
+    case 8: launch_payload_u<256, 8, MODE>(a, grid, nt, st); break;
+    default: launch_payload_u<256, 4, MODE>(a, grid, nt, st); break;
+    }
 }
 
 template <int BS, int U>
-static void launch_dcopy_u(unsigned char *d, const unsigned char *s, uint64_t n, uint64_t mp,
-                           int grid, bool nt, hipStream_t st) {
-    if (nt) hipLaunchKernelGGL((k_device_copy<BS, U, true>), dim3(grid), dim3(BS), 0, st, d, s, n, mp);
-    else hipLaunchKernelGGL((k_device_copy<BS, U, false>), dim3(grid), dim3(BS), 0, st, d, s, n, mp);
+static void launch_dcopy_u(unsigned char *d, const unsigned char *s, uint64_t n, const CopyTuning &t,
+                           int grid, hipStream_t st) {
+    if (t.nontemporal)
+        hipLaunchKernelGGL((k_device_copy<BS, U, true>), dim3(grid), dim3(BS), 0, st, d, s, n,
+                           (uint64_t)t.min_piece, (uint64_t)t.piece);
+    else
+        hipLaunchKernelGGL((k_device_copy<BS, U, false>), dim3(grid), dim3(BS), 0, st, d, s, n,
+                           (uint64_t)t.min_piece, (uint64_t)t.piece);
 }
 
 static int launch_status() {
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
+}
+
+// Host checks shared by a2av_copy and a2av_all_to_all_vdev; fills the buffer
+// part of the kernel arguments.
+static int fill_buffers(CopyArgs &a, int W, size_t row_bytes, const void *const *in,
+                        const int64_t *in_rows, void *const *out, const int64_t *out_cap_rows) {
+    std::memset(&a, 0, sizeof(a));
+    uint64_t cap_bytes = 0;  // the flat destination space must fit 62 bits
+    for (int r = 0; r < W; r++) {
+        if (in_rows[r] < 0 || out_cap_rows[r] < 0) return A2AV_EARG;
+        if ((uint64_t)in_rows[r] > (uint64_t)INT64_MAX / row_bytes) return A2AV_EARG;
+        if ((uint64_t)out_cap_rows[r] > (uint64_t)INT64_MAX / row_bytes) return A2AV_EARG;
+        if (in_rows[r] > 0 && in[r] == nullptr) return A2AV_EARG;
+        if (out_cap_rows[r] > 0 && out[r] == nullptr) return A2AV_EARG;
+        a.in[r] = (const unsigned char *)in[r];
+        a.out[r] = (unsigned char *)out[r];
+        a.in_rows[r] = in_rows[r];
+        a.cap[r] = out_cap_rows[r];
+        cap_bytes += (uint64_t)out_cap_rows[r] * row_bytes;
+        if (cap_bytes > ((uint64_t)1 << 62)) return A2AV_EARG;
+    }
+    a.R = row_bytes;
+    a.W = W;
+    return A2AV_OK;
+}
+
+static int payload_grid(const CopyTuning &t, hipStream_t stream) {
+    return device_cu_count(stream) * t.blocks_per_cu;
 }
 
 }  // namespace a2av
@@ -296,39 +429,50 @@ A2AV_API int a2av_copy(int W, size_t row_bytes, const void *const *in, const int
         !S || !send_off || !recv_off || !status)
         return A2AV_EARG;
     CopyArgs a;
-    std::memset(&a, 0, sizeof(a));
-    uint64_t cap_bytes = 0;  // the kernel's flat destination space must fit 62 bits
-    for (int r = 0; r < W; r++) {
-        if (in_rows[r] < 0 || out_cap_rows[r] < 0) return A2AV_EARG;
-        if ((uint64_t)in_rows[r] > (uint64_t)INT64_MAX / row_bytes) return A2AV_EARG;
-        if ((uint64_t)out_cap_rows[r] > (uint64_t)INT64_MAX / row_bytes) return A2AV_EARG;
-        if (in_rows[r] > 0 && in[r] == nullptr) return A2AV_EARG;
-        if (out_cap_rows[r] > 0 && out[r] == nullptr) return A2AV_EARG;
-        a.in[r] = (const unsigned char *)in[r];
-        a.out[r] = (unsigned char *)out[r];
-        a.in_rows[r] = in_rows[r];
-        a.cap[r] = out_cap_rows[r];
-        cap_bytes += (uint64_t)out_cap_rows[r] * row_bytes;
-        if (cap_bytes > ((uint64_t)1 << 62)) return A2AV_EARG;
-    }
+    const int rc = fill_buffers(a, W, row_bytes, in, in_rows, out, out_cap_rows);
+    if (rc != A2AV_OK) return rc;
     a.S = S;
     a.send_off = send_off;
     a.recv_off = recv_off;
     a.status = status;
-    a.R = row_bytes;
-    a.W = W;
     const CopyTuning t = copy_tuning();
     a.min_piece = (uint64_t)t.min_piece;
-    int grid = device_cu_count(stream) * t.blocks_per_cu;
-    grid = (grid + 7) & ~7;
-    a.xcd_remap = t.xcd_remap;
-    const bool nt = t.nontemporal != 0;
-    switch (t.unroll) {
-    case 1: launch_copy_u<256, 1>(a, grid, nt, stream); break;
-    case 2: launch_copy_u<256, 2>(a, grid, nt, stream); break;
-    case 8: launch_copy_u<256, 8>(a, grid, nt, stream); break;
-    default: launch_copy_u<256, 4>(a, grid, nt, stream); break;
+    a.piece = (uint64_t)t.piece;
+    const int grid = payload_grid(t, stream);
+    if (W <= kMetaW) launch_payload<kCopyStaged>(a, grid, t, stream);
+    else launch_payload<kCopyGlobal>(a, grid, t, stream);
+    return launch_status();
+}
+
+A2AV_API int a2av_all_to_all_vdev(int W, size_t row_bytes, const void *const *in,
+                                  const int64_t *in_rows, void *const *out,
+                                  const int64_t *out_cap_rows, const int64_t *S, int64_t *O,
+                                  int64_t *send_off, int64_t *recv_off, int32_t *status,
+                                  hipStream_t stream) {
+    if (W < 1 || W > A2AV_MAX_W || row_bytes == 0 || !in || !in_rows || !out || !out_cap_rows ||
+        !S || !O || !send_off || !recv_off || !status)
+        return A2AV_EARG;
+    CopyArgs a;
+    const int rc = fill_buffers(a, W, row_bytes, in, in_rows, out, out_cap_rows);
+    if (rc != A2AV_OK) return rc;
+    if (W > kMetaW) {
+        // the three steps as separate launches, in stream order
+        int r = a2av_exchange_splits(W, S, O, status, stream);
+        if (r == A2AV_OK) r = a2av_offsets(W, S, O, send_off, recv_off, status, stream);
+        if (r == A2AV_OK)
+            r = a2av_copy(W, row_bytes, in, in_rows, out, out_cap_rows, S, send_off, recv_off,
+                          status, stream);
+        return r;
     }
+    a.S = S;
+    a.O_out = O;
+    a.send_off_out = send_off;
+    a.recv_off_out = recv_off;
+    a.status = status;
+    const CopyTuning t = copy_tuning();
+    a.min_piece = (uint64_t)t.min_piece;
+    a.piece = (uint64_t)t.piece;
+    launch_payload<kFused>(a, payload_grid(t, stream), t, stream);
     return launch_status();
 }
 
@@ -336,15 +480,14 @@ A2AV_API int a2av_device_copy(void *dst, const void *src, size_t bytes, hipStrea
     if (bytes == 0) return A2AV_OK;
     if (!dst || !src) return A2AV_EARG;
     const CopyTuning t = copy_tuning();
-    int grid = device_cu_count(stream) * t.blocks_per_cu;
-    const bool nt = t.nontemporal != 0;
+    const int grid = payload_grid(t, stream);
     unsigned char *d = (unsigned char *)dst;
     const unsigned char *s = (const unsigned char *)src;
     switch (t.unroll) {
-    case 1: launch_dcopy_u<256, 1>(d, s, bytes, t.min_piece, grid, nt, stream); break;
-    case 2: launch_dcopy_u<256, 2>(d, s, bytes, t.min_piece, grid, nt, stream); break;
-    case 8: launch_dcopy_u<256, 8>(d, s, bytes, t.min_piece, grid, nt, stream); break;
-    default: launch_dcopy_u<256, 4>(d, s, bytes, t.min_piece, grid, nt, stream); break;
+    case 1: launch_dcopy_u<256, 1>(d, s, bytes, t, grid, stream); break;
+    case 2: launch_dcopy_u<256, 2>(d, s, bytes, t, grid, stream); break;
+    case 8: launch_dcopy_u<256, 8>(d, s, bytes, t, grid, stream); break;
+    default: launch_dcopy_u<256, 4>(d, s, bytes, t, grid, stream); break;
     }
     return launch_status();
 }

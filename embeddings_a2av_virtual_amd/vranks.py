@@ -41,8 +41,13 @@ class A2av:
         B.a2av_copy(row_bytes, ins, in_rows, outs, out_cap_rows, self.S, self.send_off,
                     self.recv_off, self.status, stream)
 
-    def __call__(self, row_bytes, ins, in_rows, outs, out_cap_rows, stream=None):
-        """Whole a2av on the device-resident splits ``self.S``."""
+    def __call__(self, row_bytes, ins, in_rows, outs, out_cap_rows, stream=None, fused=False):
+        """Whole a2av on the device-resident splits ``self.S``: three calls, or
+        the single a2av_all_to_all_vdev call when ``fused``."""
+        if fused:
+            B.a2av_all_to_all_vdev(row_bytes, ins, in_rows, outs, out_cap_rows, self.S, self.O,
+                                   self.send_off, self.recv_off, self.status, stream)
+            return
         self.exchange_and_offsets(stream)
         self.copy(row_bytes, ins, in_rows, outs, out_cap_rows, stream)
 

@@ -128,6 +128,23 @@ int a2av_copy(int W, size_t row_bytes, const void *const *in,
               int32_t *status, hipStream_t stream);
 
 /*
+ * The whole a2av in one call: a2av_exchange_splits, a2av_offsets and
+ * a2av_copy with the same arguments, same outputs and same status bits
+ * (BAD_SPLIT alone stops it before O and the offsets are written; SEND_OVERRUN
+ * / RECV_OVERFLOW leave O and the offsets written and no payload byte).
+ *   S                      device int64 [W][W] (input splits)
+ *   O, send_off, recv_off  device outputs as in the separate calls
+ * For W <= 16 this is ONE kernel launch: every workgroup stages S in LDS and
+ * scans it itself (workgroup 0 also writes O and the offsets), then copies
+ * its piece of the destination space; larger W runs the three launches.
+ */
+int a2av_all_to_all_vdev(int W, size_t row_bytes, const void *const *in,
+                         const int64_t *in_rows, void *const *out,
+                         const int64_t *out_cap_rows, const int64_t *S, int64_t *O,
+                         int64_t *send_off, int64_t *recv_off, int32_t *status,
+                         hipStream_t stream);
+
+/*
  * Workspace bytes moe_pack needs for these sizes (0 for invalid sizes).
  */
 size_t moe_pack_workspace_bytes(int W, int64_t T, int k, int E);

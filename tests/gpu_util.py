@@ -43,10 +43,10 @@ def upload_rows(x: np.ndarray, pad=0) -> GuardedBuffer:
     return b
 
 
-def gpu_a2av(R, X, S, cap=None, in_pad=0, out_pad=0, state=None, status_init=0):
-    """Run exchange -> offsets -> copy on the GPU. X: list of host uint8 [n, R]
-    arrays. Returns (status, O, send_off, recv_off, [Y_d host uint8 [cap_d, R]],
-    guards_ok)."""
+def gpu_a2av(R, X, S, cap=None, in_pad=0, out_pad=0, state=None, status_init=0, fused=False):
+    """Run exchange -> offsets -> copy on the GPU (three calls, or the single
+    fused call). X: list of host uint8 [n, R] arrays. Returns (status, O,
+    send_off, recv_off, [Y_d host uint8 [cap_d, R]], guards_ok)."""
     W = len(X)
     S = np.asarray(S, dtype=np.int64)
     if cap is None:
@@ -57,7 +57,7 @@ def gpu_a2av(R, X, S, cap=None, in_pad=0, out_pad=0, state=None, status_init=0):
     st.set_splits(S)
     st.status.fill_(status_init)
     st(R, [b.view for b in ins], [x.shape[0] for x in X], [b.view for b in outs],
-       [int(c) for c in cap])
+       [int(c) for c in cap], fused=fused)
     torch.cuda.synchronize()
     Y = [b.host().reshape(-1, R) if R else b.host() for b in outs]
     guards = all(b.guards_intact() for b in outs) and all(b.guards_intact() for b in ins)

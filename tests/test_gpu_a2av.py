@@ -24,8 +24,9 @@ def test_device_is_there():
 
 
 # ------------------------------------------------------------------ the tiny workload
+@pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
 @pytest.mark.parametrize("seed", [0, 1, 2])
-def test_tiny_workload_and_round_trip(ref, seed):
+def test_tiny_workload_and_round_trip(ref, seed, fused):
     """W=4, 256 rows x 64 bf16 per rank, multinomial splits, then back home."""
     _say("tiny seed", seed)
     g = I.rng(seed)
@@ -34,12 +35,12 @@ def test_tiny_workload_and_round_trip(ref, seed):
     X = [I.payload_bf16(n, cols, seed * 100 + r).view(torch.uint8).numpy().reshape(n, R)
          for r in range(W)]
     S = I.uniform_splits(g, W, n)
-    gpu = gpu_a2av(R, X, S)
+    gpu = gpu_a2av(R, X, S, fused=fused)
     want = ref_a2av(ref, R, X, S)
     assert_same(gpu, want, f"tiny seed {seed}")
     # round trip: the received rows go home with the transposed splits
     Y = gpu[4]
-    gpu2 = gpu_a2av(R, Y, gpu[1])
+    gpu2 = gpu_a2av(R, Y, gpu[1], fused=fused)
     want2 = ref_a2av(ref, R, want[4], want[1])
     assert_same(gpu2, want2, "tiny round trip")
     for r in range(W):
@@ -55,31 +56,34 @@ def test_tiny_workload_and_round_trip(ref, seed):
     (16, 512, 257, 0.5, 7),
     (64, 48, 40, 0.3, 8),
 ])
-def test_random_splits_many_tiles(ref, W, R, max_rows, zero_frac, seed):
+@pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
+def test_random_splits_many_tiles(ref, W, R, max_rows, zero_frac, seed, fused):
     _say("random", W, R, max_rows, zero_frac, seed)
     g = I.rng(seed)
     S = I.random_splits(g, W, max_rows, zero_frac)
     n = S.sum(axis=1) + g.integers(0, 5, size=W)      # some trailing rows stay home
     X = [random_rows(g, n[s], R) for s in range(W)]
     cap = S.sum(axis=0) + g.integers(0, 3, size=W)     # some room left over
-    assert_same(gpu_a2av(R, X, S, cap=cap), ref_a2av(ref, R, X, S, cap=cap), "random")
+    assert_same(gpu_a2av(R, X, S, cap=cap, fused=fused), ref_a2av(ref, R, X, S, cap=cap), "random")
 
 
 # ------------------------------------------------------------------ widths and alignment
 @pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 7, 8, 12, 16, 24, 100, 8196])
 @pytest.mark.parametrize("in_pad,out_pad", [(0, 0), (1, 0), (0, 3), (4, 8), (8, 0), (6, 6)])
-def test_row_widths_and_misaligned_bases(ref, R, in_pad, out_pad):
+@pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
+def test_row_widths_and_misaligned_bases(ref, R, in_pad, out_pad, fused):
     g = I.rng(1000 + R * 10 + in_pad)
     W = 4
     max_rows = max(1, 40000 // R)
     S = I.random_splits(g, W, max_rows, 0.2)
     X = [random_rows(g, S[s].sum(), R) for s in range(W)]
-    assert_same(gpu_a2av(R, X, S, in_pad=in_pad, out_pad=out_pad), ref_a2av(ref, R, X, S),
+    assert_same(gpu_a2av(R, X, S, in_pad=in_pad, out_pad=out_pad, fused=fused), ref_a2av(ref, R, X, S),
                 f"R={R} pads={in_pad},{out_pad}")
 
 
 # ------------------------------------------------------------------ degenerate cases
-def test_degenerate_cases(ref):
+@pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
+def test_degenerate_cases(ref, fused):
     g = I.rng(9)
     R = 64
     cases = {
@@ -98,11 +102,12 @@ def test_degenerate_cases(ref):
             n = S.sum(axis=1)
         X = [random_rows(g, n[s], R) for s in range(S.shape[0])]
         _say("degenerate", name)
-        assert_same(gpu_a2av(R, X, S), ref_a2av(ref, R, X, S), name)
+        assert_same(gpu_a2av(R, X, S, fused=fused), ref_a2av(ref, R, X, S), name)
 
 
 # ------------------------------------------------------------------ error paths
-def test_error_paths_match_oracle(ref):
+@pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
+def test_error_paths_match_oracle(ref, fused):
     g = I.rng(10)
     W, R, n = 4, 32, 40
     X = [random_rows(g, n, R) for _ in range(W)]
@@ -120,7 +125,7 @@ def test_error_paths_match_oracle(ref):
              ("exact_fit", good, good.sum(axis=0))]
     for name, S, cap in cases:
         _say("error case", name)
-        gpu = gpu_a2av(R, X, S, cap=cap)
+        gpu = gpu_a2av(R, X, S, cap=cap, fused=fused)
         want = ref_a2av(ref, R, X, S, cap=cap)
         assert_same(gpu, want, name)
         if want[0]:
@@ -158,12 +163,13 @@ def test_copy_rejects_foreign_offsets(ref):
         assert all(bool((b.view == SENT).all().item()) and b.guards_intact() for b in outs)
 
 
-def test_poisoned_status_blocks_every_op(ref):
+@pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
+def test_poisoned_status_blocks_every_op(ref, fused):
     g = I.rng(12)
     W, R, n = 4, 16, 20
     X = [random_rows(g, n, R) for _ in range(W)]
     S = np.full((W, W), n // W, dtype=np.int64)
-    st, O, so, ro, Y, guards = gpu_a2av(R, X, S, status_init=64)
+    st, O, so, ro, Y, guards = gpu_a2av(R, X, S, status_init=64, fused=fused)
     assert st == 64 and guards
     assert not O.any() and not so.any() and not ro.any()
     assert all(np.all(y == SENT) for y in Y)
@@ -174,8 +180,11 @@ def test_poisoned_status_blocks_every_op(ref):
     {"A2AV_BLOCKS_PER_CU": "1"}, {"A2AV_BLOCKS_PER_CU": "3", "A2AV_UNROLL": "1"},
     {"A2AV_UNROLL": "2", "A2AV_NT": "0"}, {"A2AV_UNROLL": "8", "A2AV_XCD_REMAP": "1"},
     {"A2AV_MIN_PIECE": "4096", "A2AV_BLOCKS_PER_CU": "16"}, {"A2AV_MIN_PIECE": "1048576"},
+    {"A2AV_PIECE": "4096"}, {"A2AV_PIECE": "65536", "A2AV_BLOCKS_PER_CU": "2"},
+    {"A2AV_PIECE": "1000000"},
 ])
-def test_launch_shapes_give_identical_bytes(ref, monkeypatch, env):
+@pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
+def test_launch_shapes_give_identical_bytes(ref, monkeypatch, env, fused):
     g = I.rng(13)
     W, R = 8, 1040
     S = I.random_splits(g, W, 600, 0.25)
@@ -183,11 +192,12 @@ def test_launch_shapes_give_identical_bytes(ref, monkeypatch, env):
     want = ref_a2av(ref, R, X, S)
     for k, v in env.items():
         monkeypatch.setenv(k, v)
-    assert_same(gpu_a2av(R, X, S), want, str(env))
+    assert_same(gpu_a2av(R, X, S, fused=fused), want, str(env))
 
 
 # ------------------------------------------------------------------ the 32 MiB workload
-def test_moe32_workload_full(ref):
+@pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
+def test_moe32_workload_full(ref, fused):
     """W=4, 4096 rows x 4096 bf16 (32 MiB) per rank, multinomial splits, every
     byte compared."""
     g = I.rng(20)
@@ -196,13 +206,14 @@ def test_moe32_workload_full(ref):
     X = [I.payload_bf16(n, cols, 2000 + r).view(torch.uint8).numpy().reshape(n, R)
          for r in range(W)]
     S = I.uniform_splits(g, W, n)
-    assert_same(gpu_a2av(R, X, S), ref_a2av(ref, R, X, S), "moe32")
+    assert_same(gpu_a2av(R, X, S, fused=fused), ref_a2av(ref, R, X, S), "moe32")
 
 
 @pytest.mark.parametrize("W", [4, 8])
 @pytest.mark.parametrize("mib", [1, 16, 32, 64, 256])
 @pytest.mark.parametrize("kind", ["uniform", "half_zero"])
-def test_sweep_sizes_full(ref, W, mib, kind):
+@pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
+def test_sweep_sizes_full(ref, W, mib, kind, fused):
     """8 KiB rows, 1..256 MiB per rank, uniform or 50 % zero splits."""
     _say("sweep", W, mib, kind)
     g = I.rng(30 + mib + W)
@@ -211,4 +222,4 @@ def test_sweep_sizes_full(ref, W, mib, kind):
     S = I.uniform_splits(g, W, n) if kind == "uniform" else I.half_zero_splits(g, W, n)
     X = [random_rows(g, n, R) if mib <= 16 else
          I.payload_bytes(n, R, 4000 + s, device="cuda").cpu().numpy() for s in range(W)]
-    assert_same(gpu_a2av(R, X, S), ref_a2av(ref, R, X, S), f"sweep {W} {mib} {kind}")
+    assert_same(gpu_a2av(R, X, S, fused=fused), ref_a2av(ref, R, X, S), f"sweep {W} {mib} {kind}")
