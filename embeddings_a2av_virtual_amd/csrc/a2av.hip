@@ -122,6 +122,7 @@ struct MetaLds {
     int64_t ro[MW * (MW + 1)];
     int64_t pre[A2AV_MAX_W + 1];  // rows of destinations before d; [W] = total
     int bits;
+    int poisoned;
 };
 
 enum PayloadMode {
@@ -171,8 +172,14 @@ __global__ __launch_bounds__(BS) void k_a2av_payload(const CopyArgs a) {
     const int lane = tid & (kWave - 1), wave = tid / kWave;
     const int W = a.W, W1 = W + 1;
 
-    // ---- prologue: the status word and the metadata loads go out together
-    const bool poisoned = status_poisoned(a.status);
+    // ---- prologue: the status word and the metadata loads go out together.
+    // One thread reads the word and the block decides together: a failing
+    // block of this same launch may set it at any moment, and waves of one
+    // block must not disagree about it.
+    if (tid == 0) {
+        m.bits = 0;
+        m.poisoned = status_poisoned(a.status);
+    }
     if constexpr (MODE != kCopyGlobal) {
         for (int i = tid; i < W * W; i += BS) m.S[i] = a.S[i];
     }
@@ -182,9 +189,8 @@ __global__ __launch_bounds__(BS) void k_a2av_payload(const CopyArgs a) {
             m.ro[i] = a.recv_off[i];
         }
     }
-    if (tid == 0) m.bits = 0;
-    if (poisoned) return;
     __syncthreads();
+    if (m.poisoned) return;
 
     const int64_t *Sp = MODE == kCopyGlobal ? a.S : m.S;
     const int64_t *sop = MODE == kCopyGlobal ? a.send_off : m.so;
@@ -256,10 +262,12 @@ __global__ __launch_bounds__(BS) void k_a2av_payload(const CopyArgs a) {
         // source chunk inside it that starts at or before lo
         const int64_t pre_l = lane < W ? m.pre[lane] : 0;
         const uint64_t mask_d = __ballot(lane < W && (uint64_t)pre_l * R <= lo);
+        if (mask_d == 0) break;  // cannot happen after validation (pre[0] == 0)
         int d = 63 - __clzll(mask_d);
         uint64_t dbase = (uint64_t)m.pre[d] * R;
         const int64_t roff = lane < W ? rop[d * W1 + lane] : 0;
         const uint64_t mask_s = __ballot(lane < W && dbase + (uint64_t)roff * R <= lo);
+        if (mask_s == 0) break;  // cannot happen after validation (offsets start at 0)
         int s = 63 - __clzll(mask_s);
         uint64_t x = lo;
         while (x < hi && d < W) {
@@ -271,8 +279,11 @@ __global__ __launch_bounds__(BS) void k_a2av_payload(const CopyArgs a) {
                 const uint64_t e = hi < F + L ? hi : F + L;
                 const uint64_t off = x - F;
                 const int64_t so = sop[s * W1 + d];
-                copy_segment<BS, U, NT>(a.out[d] + (uint64_t)r0 * R + off,
-                                        a.in[s] + (uint64_t)so * R + off, e - x, tid);
+                // validated metadata always passes; the check keeps every
+                // access inside the caller's buffers regardless
+                if (r0 >= 0 && so >= 0 && r0 + n <= a.cap[d] && so + n <= a.in_rows[s])
+                    copy_segment<BS, U, NT>(a.out[d] + (uint64_t)r0 * R + off,
+                                            a.in[s] + (uint64_t)so * R + off, e - x, tid);
                 x = e;
             }
             if (++s == W) {

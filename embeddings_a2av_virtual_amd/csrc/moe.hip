@@ -47,10 +47,14 @@ struct MoeArgs {
 // ------------------------------------------------------------------ histogram
 __global__ __launch_bounds__(256) void k_moe_hist(const MoeArgs a) {
     extern __shared__ int32_t hist[];
-    if (status_poisoned(a.status)) return;
+    __shared__ int poisoned;
+    // blocks of this launch set the word; one read per block keeps its waves
+    // in agreement
+    if (threadIdx.x == 0) poisoned = status_poisoned(a.status);
     const int r = blockIdx.y, seg = blockIdx.x, E = a.E;
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
     __syncthreads();
+    if (poisoned) return;
     const int32_t *ids = a.ids[r];
     const int64_t q0 = (int64_t)seg * kSeg;
     int bad = 0;
