@@ -72,7 +72,7 @@ __global__ __launch_bounds__(1024) void k_offsets(int W, const int64_t *__restri
     if (status_poisoned(status)) return;
     const int n = W * W;
     int bad = 0;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) bad |= split_invalid(S[i]) | split_invalid(O[i]);
+    for (int i = threadIdx.x; i < n; i += blockDim.x) bad |= (int)split_invalid(S[i]) | (int)split_invalid(O[i]);
     if (__syncthreads_or(bad)) {
         if (threadIdx.x == 0) atomicOr(status, A2AV_ST_BAD_SPLIT);
         return;
@@ -126,7 +126,7 @@ struct MetaLds {
 };
 
 enum PayloadMode {
-    kCopyStaged = 0,  // a2av_copy, W <= kMetaW: S and offsets staged in LDS
+    kCopyGiven = 0,  // a2av_copy: offsets given (staged in LDS by the block kernel)
     kCopyGlobal = 1,  // a2av_copy, W > kMetaW: metadata read from global
     kFused = 2,       // a2av_all_to_all_vdev, W <= kMetaW: offsets computed here
 };
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(BS) void k_a2av_payload(const CopyArgs a) {
     if constexpr (MODE != kCopyGlobal) {
         for (int i = tid; i < W * W; i += BS) m.S[i] = a.S[i];
     }
-    if constexpr (MODE == kCopyStaged) {
+    if constexpr (MODE == kCopyGiven) {
         for (int i = tid; i < W * W1; i += BS) {
             m.so[i] = a.send_off[i];
             m.ro[i] = a.recv_off[i];
@@ -314,6 +314,197 @@ __global__ __launch_bounds__(BS) void k_device_copy(unsigned char *dst, const un
     }
 }
 
+// ====================================================================== wave-level payload (W <= 8)
+// For up to 8 ranks every wave is self-contained. It reads the status word
+// and the split matrix through the scalar cache (a few s_load bursts; the
+// scalar path does not queue behind the vector stream that older waves keep
+// in flight on the same CU, which starves the vector loads of a young wave),
+// computes every offset it needs with wave64 shuffles in registers (lane
+// s*W + d holds the (s, d) entry), and copies one piece of the destination
+// space. No LDS and no barrier: the grid is sized to the traffic so that the
+// hardware dispatcher hands pieces to waves as older ones retire, which evens
+// out the unequal bandwidth that waves of different age get.
+constexpr int kWaveMaxW = 8;
+
+typedef __attribute__((address_space(4))) const int64_t const_i64;
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Wave-cooperative copy of n bytes, n a multiple of 16, both ends 16-aligned.
+template <int U>
+__device__ __forceinline__ void wave_copy16(unsigned char *dst, const unsigned char *src,
+                                            uint64_t n, int lane) {
+    copy_elems<u32x4, kWave, U, true>((u32x4 *)dst, (const u32x4 *)src, n / 16, lane);
+}
+
+template <int W, int U, bool ALIGNED, int MODE>
+__global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
+    static_assert(W >= 1 && W <= kWaveMaxW, "one (s, d) entry per lane");
+    constexpr int N = W * W;
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t wpb = blockDim.x / kWave;
+    const uint64_t gw = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave;
+    const uint64_t TW = (uint64_t)gridDim.x * wpb;
+
+    // ---- scalar loads: status word, S, and in copy mode the given offsets
+    const int32_t st0 = *(const const_i32 *)a.status;
+    const const_i64 *Sc = (const const_i64 *)a.S;
+    uint64_t v = 0;
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+        const uint64_t x = (uint64_t)Sc[i];
+        v = lane == i ? x : v;
+    }
+    uint64_t gso = 0, gro = 0, gso_t = 0, gro_t = 0;  // given send_off[s][d], recv_off[d][s], totals
+    if constexpr (MODE == kCopyGiven) {
+        const const_i64 *soc = (const const_i64 *)a.send_off;
+        const const_i64 *roc = (const const_i64 *)a.recv_off;
+        // one row of each matrix per iteration keeps the scalar registers in budget
+#pragma unroll 1
+        for (int r = 0; r < W; r++) {
+#pragma unroll
+            for (int c = 0; c <= W; c++) {
+                const uint64_t x = (uint64_t)soc[r * (W + 1) + c];  // send_off[s=r][d=c]
+                const uint64_t y = (uint64_t)roc[r * (W + 1) + c];  // recv_off[d=r][s=c]
+                if (c < W) {
+                    gso = lane == r * W + c ? x : gso;
+                    gro = lane == c * W + r ? y : gro;
+                } else {
+                    gso_t = lane == r * W + W - 1 ? x : gso_t;
+                    gro_t = lane == (W - 1) * W + r ? y : gro_t;
+                }
+            }
+        }
+    }
+    if (st0) return;
+
+    // ---- offsets from S, in registers (wrapping arithmetic, as the checks
+    // compare modulo 2^64)
+    const int s_ = lane / W, d_ = lane - (lane / W) * W;
+    const bool act = lane < N;
+    uint64_t inc = v;   // send_off[s][d + 1]
+#pragma unroll
+    for (int o = 1; o < W; o <<= 1) {
+        const uint64_t t = __shfl_up(inc, o, kWave);
+        if (d_ >= o) inc += t;
+    }
+    uint64_t inc2 = v;  // recv_off[d][s + 1]
+#pragma unroll
+    for (int o = 1; o < W; o <<= 1) {
+        const uint64_t t = __shfl_up(inc2, o * W, kWave);
+        if (s_ >= o) inc2 += t;
+    }
+    const uint64_t so = inc - v, ro = inc2 - v;
+    const uint64_t ct = __shfl(inc2, (W - 1) * W + d_, kWave);  // rows destination d_ receives
+    uint64_t pinc = ct;
+#pragma unroll
+    for (int o = 1; o < W; o <<= 1) {
+        const uint64_t t = __shfl_up(pinc, o, kWave);
+        if (d_ >= o) pinc += t;
+    }
+    const uint64_t pre = pinc - ct;  // rows of destinations before d_
+    const uint64_t total = readlane_u64(pinc, W - 1);
+
+    // ---- checks, identical in every wave
+    int bits = __ballot(act && split_invalid((int64_t)v)) ? A2AV_ST_BAD_SPLIT : 0;
+    if constexpr (MODE == kCopyGiven) {
+        const bool bad_off = act && (gso != so || gro != ro || (d_ == W - 1 && gso_t != inc) ||
+                                     (s_ == W - 1 && gro_t != inc2));
+        if (__ballot(bad_off)) bits |= A2AV_ST_BAD_OFFSETS;
+#pragma unroll
+        for (int r = 0; r < W; r++) {
+            if ((int64_t)readlane_u64(gso_t, r * W + W - 1) > a.in_rows[r]) bits |= A2AV_ST_SEND_OVERRUN;
+            if ((int64_t)readlane_u64(gro_t, (W - 1) * W + r) > a.cap[r]) bits |= A2AV_ST_RECV_OVERFLOW;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < W; r++) {
+            if ((int64_t)readlane_u64(inc, r * W + W - 1) > a.in_rows[r]) bits |= A2AV_ST_SEND_OVERRUN;
+            if ((int64_t)readlane_u64(inc2, (W - 1) * W + r) > a.cap[r]) bits |= A2AV_ST_RECV_OVERFLOW;
+        }
+        // invalid splits stop the sequence at the exchange
+        if (bits & A2AV_ST_BAD_SPLIT) bits = A2AV_ST_BAD_SPLIT;
+    }
+    if (gw == 0) {
+        if constexpr (MODE == kFused) {
+            if (!(bits & A2AV_ST_BAD_SPLIT) && act) {
+                a.O_out[d_ * W + s_] = (int64_t)v;
+                a.send_off_out[s_ * (W + 1) + d_] = (int64_t)so;
+                if (d_ == W - 1) a.send_off_out[s_ * (W + 1) + W] = (int64_t)inc;
+                a.recv_off_out[d_ * (W + 1) + s_] = (int64_t)ro;
+                if (s_ == W - 1) a.recv_off_out[d_ * (W + 1) + W] = (int64_t)inc2;
+            }
+        }
+        if (bits && lane == 0) atomicOr(a.status, bits);
+    }
+    if (bits) return;
+
+    // ---- pieces of the destination space: out[0] rows, then out[1] rows, ...
+    const uint64_t R = a.R;
+    const uint64_t B = total * R;
+    const uint64_t piece = a.piece;
+    for (uint64_t p = gw; p * piece < B; p += TW) {
+        const uint64_t lo = p * piece;
+        const uint64_t hi = lo + piece < B ? lo + piece : B;
+        // last destination starting at or before lo (lanes 0..W-1 hold pre[d]),
+        // then the last source chunk inside it starting at or before lo
+        const uint64_t mask_d = __ballot(lane < W && pre * R <= lo);
+        if (mask_d == 0) break;  // cannot happen: pre[0] == 0
+        int d = 63 - __clzll(mask_d);
+        uint64_t dbase = readlane_u64(pre, d) * R;
+        const uint64_t mask_s = __ballot(act && d_ == d && dbase + ro * R <= lo);
+        if (mask_s == 0) break;  // cannot happen: recv_off[d][0] == 0
+        int s = (63 - __clzll(mask_s)) / W;
+        uint64_t x = lo;
+        while (x < hi && d < W) {
+            const int li = s * W + d;
+            const uint64_t n = readlane_u64(v, li);
+            const uint64_t r0 = readlane_u64(ro, li);
+            const uint64_t F = dbase + r0 * R;
+            const uint64_t L = n * R;
+            if (n > 0 && x < F + L) {
+                const uint64_t e = hi < F + L ? hi : F + L;
+                const uint64_t off = x - F;
+                const uint64_t s0 = readlane_u64(so, li);
+                // validated offsets always pass; the check keeps every access
+                // inside the caller's buffers regardless
+                if ((int64_t)(r0 + n) <= a.cap[d] && (int64_t)(s0 + n) <= a.in_rows[s]) {
+                    unsigned char *dst = a.out[d] + r0 * R + off;
+                    const unsigned char *src = a.in[s] + s0 * R + off;
+                    if constexpr (ALIGNED) wave_copy16<U>(dst, src, e - x, lane);
+                    else copy_segment<kWave, U, true>(dst, src, e - x, lane);
+                }
+                x = e;
+            }
+            if (++s == W) {
+                s = 0;
+                ++d;
+                if (d < W) dbase = readlane_u64(pre, d) * R;
+            }
+        }
+    }
+}
+
+// Plain copy with the same one-piece-per-wave structure.
+template <int U, bool ALIGNED>
+__global__ __launch_bounds__(256) void k_device_copy_wave(unsigned char *dst, const unsigned char *src,
+                                                          uint64_t bytes, uint64_t piece) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t wpb = blockDim.x / kWave;
+    const uint64_t TW = (uint64_t)gridDim.x * wpb;
+    for (uint64_t p = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave; p * piece < bytes; p += TW) {
+        const uint64_t lo = p * piece;
+        const uint64_t hi = lo + piece < bytes ? lo + piece : bytes;
+        if constexpr (ALIGNED) wave_copy16<U>(dst + lo, src + lo, hi - lo, lane);
+        else copy_segment<kWave, U, true>(dst + lo, src + lo, hi - lo, lane);
+    }
+}
+
 // ====================================================================== launch config
 struct CopyTuning {
     int blocks_per_cu;
@@ -321,6 +512,7 @@ struct CopyTuning {
     int nontemporal;
     long min_piece;
     long piece;
+    int block_kernel;  // 1: use the workgroup (LDS) kernel for W <= 8 too
 };
 
 static CopyTuning copy_tuning() {
@@ -331,6 +523,7 @@ static CopyTuning copy_tuning() {
     t.min_piece = env_long("A2AV_MIN_PIECE", 16384, 4096, 1L << 30);
     t.piece = env_long("A2AV_PIECE", 0, 0, 1L << 34);
     if (t.piece != 0) t.piece = (t.piece + 4095) & ~4095L;
+    t.block_kernel = (int)env_long("A2AV_BLOCK_KERNEL", 0, 0, 1);
     return t;
 }
 
@@ -360,6 +553,68 @@ static void launch_dcopy_u(unsigned char *d, const unsigned char *s, uint64_t n,
     else
         hipLaunchKernelGGL((k_device_copy<BS, U, false>), dim3(grid), dim3(BS), 0, st, d, s, n,
                            (uint64_t)t.min_piece, (uint64_t)t.piece);
+}
+
+// Wave kernel: traffic up to kSmallTraffic moves in 8 KiB pieces with 8
+// loads in flight per lane; larger traffic in 32 KiB pieces with 16.
+constexpr uint64_t kSmallTraffic = 512ull << 20;
+
+struct WaveTuning {
+    int unroll;
+    uint64_t piece;
+};
+
+static WaveTuning wave_tuning(uint64_t bmax) {
+    WaveTuning t;
+    const bool small = bmax <= kSmallTraffic;
+    t.unroll = (int)env_long("A2AV_WAVE_UNROLL", small ? 8 : 16, 8, 16);
+    if (t.unroll != 8 && t.unroll != 16) t.unroll = 8;
+    t.piece = (uint64_t)env_long("A2AV_WAVE_PIECE", small ? 8192 : 32768, 4096, 1L << 30);
+    t.piece = (t.piece + 4095) & ~(uint64_t)4095;
+    return t;
+}
+
+static int wave_grid(uint64_t bmax, uint64_t piece) {
+    const uint64_t per_block = piece * 4;  // 4 waves per 256-thread block
+    uint64_t g = (bmax + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > (1u << 22)) g = 1u << 22;  // the piece loop strides over the rest
+    return (int)g;
+}
+
+template <int W, int MODE>
+static void launch_wave_w(const CopyArgs &a, bool aligned, int unroll, int grid, hipStream_t st) {
+    if (!aligned) hipLaunchKernelGGL((k_a2av_wave<W, 4, false, MODE>), dim3(grid), dim3(256), 0, st, a);
+    else if (unroll == 16) hipLaunchKernelGGL((k_a2av_wave<W, 16, true, MODE>), dim3(grid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_a2av_wave<W, 8, true, MODE>), dim3(grid), dim3(256), 0, st, a);
+}
+
+template <int MODE>
+static void launch_wave(const CopyArgs &a, bool aligned, int unroll, int grid, hipStream_t st) {
+    switch (a.W) {
+    case 1: launch_wave_w<1, MODE>(a, aligned, unroll, grid, st); break;
+    case 2: launch_wave_w<2, MODE>(a, aligned, unroll, grid, st); break;
+    case 3: launch_wave_w<3, MODE>(a, aligned, unroll, grid, st); break;
+    case 4: launch_wave_w<4, MODE>(a, aligned, unroll, grid, st); break;
+    case 5: launch_wave_w<5, MODE>(a, aligned, unroll, grid, st); break;
+    case 6: launch_wave_w<6, MODE>(a, aligned, unroll, grid, st); break;
+    case 7: launch_wave_w<7, MODE>(a, aligned, unroll, grid, st); break;
+    default: launch_wave_w<8, MODE>(a, aligned, unroll, grid, st); break;
+    }
+}
+
+// Largest possible traffic in bytes (what either side can hold) and whether
+// every base and row allows the 16-byte path.
+static void traffic_bound(const CopyArgs &a, uint64_t *bmax, bool *aligned) {
+    uint64_t in_total = 0, out_total = 0;
+    bool al = (a.R % 16) == 0;
+    for (int r = 0; r < a.W; r++) {
+        in_total += (uint64_t)a.in_rows[r];
+        out_total += (uint64_t)a.cap[r];
+        al = al && ((uintptr_t)a.in[r] % 16 == 0) && ((uintptr_t)a.out[r] % 16 == 0);
+    }
+    *bmax = (in_total < out_total ? in_total : out_total) * a.R;
+    *aligned = al;
 }
 
 static int launch_status() {
@@ -449,8 +704,17 @@ A2AV_API int a2av_copy(int W, size_t row_bytes, const void *const *in, const int
     const CopyTuning t = copy_tuning();
     a.min_piece = (uint64_t)t.min_piece;
     a.piece = (uint64_t)t.piece;
+    if (W <= kWaveMaxW && !t.block_kernel) {
+        uint64_t bmax;
+        bool aligned;
+        traffic_bound(a, &bmax, &aligned);
+        const WaveTuning wt = wave_tuning(bmax);
+        a.piece = wt.piece;
+        launch_wave<kCopyGiven>(a, aligned, wt.unroll, wave_grid(bmax, wt.piece), stream);
+        return launch_status();
+    }
     const int grid = payload_grid(t, stream);
-    if (W <= kMetaW) launch_payload<kCopyStaged>(a, grid, t, stream);
+    if (W <= kMetaW) launch_payload<kCopyGiven>(a, grid, t, stream);
     else launch_payload<kCopyGlobal>(a, grid, t, stream);
     return launch_status();
 }
@@ -483,6 +747,15 @@ A2AV_API int a2av_all_to_all_vdev(int W, size_t row_bytes, const void *const *in
     const CopyTuning t = copy_tuning();
     a.min_piece = (uint64_t)t.min_piece;
     a.piece = (uint64_t)t.piece;
+    if (W <= kWaveMaxW && !t.block_kernel) {
+        uint64_t bmax;
+        bool aligned;
+        traffic_bound(a, &bmax, &aligned);
+        const WaveTuning wt = wave_tuning(bmax);
+        a.piece = wt.piece;
+        launch_wave<kFused>(a, aligned, wt.unroll, wave_grid(bmax, wt.piece), stream);
+        return launch_status();
+    }
     launch_payload<kFused>(a, payload_grid(t, stream), t, stream);
     return launch_status();
 }
@@ -491,6 +764,23 @@ A2AV_API int a2av_device_copy(void *dst, const void *src, size_t bytes, hipStrea
     if (bytes == 0) return A2AV_OK;
     if (!dst || !src) return A2AV_EARG;
     const CopyTuning t = copy_tuning();
+    if (!t.block_kernel) {
+        const WaveTuning wt = wave_tuning(2 * (uint64_t)bytes);
+        const int grid = wave_grid(bytes, wt.piece);
+        const bool aligned = ((uintptr_t)dst % 16 == 0) && ((uintptr_t)src % 16 == 0) && bytes % 16 == 0;
+        unsigned char *d = (unsigned char *)dst;
+        const unsigned char *s = (const unsigned char *)src;
+        if (!aligned)
+            hipLaunchKernelGGL((k_device_copy_wave<4, false>), dim3(grid), dim3(256), 0, stream, d, s,
+                               (uint64_t)bytes, wt.piece);
+        else if (wt.unroll == 16)
+            hipLaunchKernelGGL((k_device_copy_wave<16, true>), dim3(grid), dim3(256), 0, stream, d, s,
+                               (uint64_t)bytes, wt.piece);
+        else
+            hipLaunchKernelGGL((k_device_copy_wave<8, true>), dim3(grid), dim3(256), 0, stream, d, s,
+                               (uint64_t)bytes, wt.piece);
+        return launch_status();
+    }
     const int grid = payload_grid(t, stream);
     unsigned char *d = (unsigned char *)dst;
     const unsigned char *s = (const unsigned char *)src;

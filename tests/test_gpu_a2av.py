@@ -182,11 +182,15 @@ def test_poisoned_status_blocks_every_op(ref, fused):
     {"A2AV_MIN_PIECE": "4096", "A2AV_BLOCKS_PER_CU": "16"}, {"A2AV_MIN_PIECE": "1048576"},
     {"A2AV_PIECE": "4096"}, {"A2AV_PIECE": "65536", "A2AV_BLOCKS_PER_CU": "2"},
     {"A2AV_PIECE": "1000000"},
+    {"A2AV_BLOCK_KERNEL": "1"}, {"A2AV_BLOCK_KERNEL": "1", "A2AV_PIECE": "65536"},
+    {"A2AV_WAVE_PIECE": "4096"}, {"A2AV_WAVE_PIECE": "65536", "A2AV_WAVE_UNROLL": "16"},
+    {"A2AV_WAVE_PIECE": "1052672", "A2AV_WAVE_UNROLL": "8"},
 ])
 @pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
-def test_launch_shapes_give_identical_bytes(ref, monkeypatch, env, fused):
-    g = I.rng(13)
-    W, R = 8, 1040
+@pytest.mark.parametrize("W", [3, 8, 12])
+def test_launch_shapes_give_identical_bytes(ref, monkeypatch, env, fused, W):
+    g = I.rng(13 + W)
+    R = 1040
     S = I.random_splits(g, W, 600, 0.25)
     X = [random_rows(g, S[s].sum(), R) for s in range(W)]
     want = ref_a2av(ref, R, X, S)
