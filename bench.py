@@ -226,6 +226,141 @@ def cpu_baseline(torch, I, W=4, mib=32, budget_s=10.0):
                       f"{len(times)} runs, median {med * 1e3:.1f} ms"}
 
 
+def time_events(torch, fn, reps, warmup=2):
+    """Average GPU ms of fn() over reps launches bracketed by two events."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def time_cpu(fn, budget_s=2.0, min_runs=2):
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < min_runs or time.perf_counter() - t_start < budget_s:
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 50:
+            break
+    return statistics.median(times)
+
+
+def row_entry(nbytes, ms, cpu_bytes=None, cpu_s=None, note=""):
+    gbs = gbps(nbytes, ms / 1e3)
+    e = {"bytes": int(nbytes), "us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+         "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    if cpu_bytes is not None:
+        e["oracle_gbs"] = round(gbps(cpu_bytes, cpu_s), 3)
+        e["oracle_sample"] = note
+    return e
+
+
+def row_benchmarks(torch, B, I, with_cpu=True):
+    """The other steps of the path, each at its full size: the MoE dispatch
+    pack, the dispatch and return a2av, the un-pack, and the embedding-key
+    exchange (keys and lengths). GB/s counts algorithmic bytes (payload read
+    + written, index bytes for the pack and un-pack)."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    from embeddings_a2av_virtual_amd.vranks import A2av
+    out = {}
+    o = None
+    if with_cpu:
+        from oracle.ref import Oracle
+        o = Oracle()
+    # ---- MoE dispatch: W=8, 8192 tokens x 7168 bf16, top-8 of 256 Zipf(1.1) experts
+    W, T, k, E, hidden = 8, 8192, 8, 256, 7168
+    R, Q = hidden * 2, T * k
+    g = I.rng(900)
+    ids_h = [I.topk_ids(g, T, k, E, 1.1) for _ in range(W)]
+    tok = [I.payload_bf16(T, hidden, 9000 + r, device="cuda") for r in range(W)]
+    ids = [torch.from_numpy(i.reshape(-1)).cuda() for i in ids_h]
+    send = [torch.empty((Q, hidden), dtype=torch.bfloat16, device="cuda") for _ in range(W)]
+    perm = [torch.empty(Q, dtype=torch.int64, device="cuda") for _ in range(W)]
+    S = torch.empty((W, W), dtype=torch.int64, device="cuda")
+    counts = torch.empty((W, E), dtype=torch.int64, device="cuda")
+    ws = torch.empty(B.moe_pack_workspace_bytes(W, T, k, E), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pack = lambda: B.moe_pack(W, T, k, E, R, tok, ids, send, perm, S, counts, ws, status)
+    ms = time_events(torch, pack, 5)
+    pack_bytes = W * (T * R + Q * R + Q * (4 + 8))
+    cpu = {}
+    if o is not None:
+        Ts = 1024   # one rank, the first 1024 tokens
+        th = tok[0][:Ts].view(torch.uint8).cpu().numpy()
+        ih = ids_h[0][:Ts]
+        cs = time_cpu(lambda: o.moe_pack(Ts, k, E, W, R, th, ih))
+        cpu = dict(cpu_bytes=Ts * R + Ts * k * R + Ts * k * 12, cpu_s=cs,
+                   note="one rank, 1024 tokens")
+    out["moe_pack"] = row_entry(pack_bytes, ms, **cpu)
+    # ---- dispatch a2av with the pack's splits (rank 0 receives ~66 % of all rows)
+    fwd = A2av(W)
+    fwd.S.copy_(S)
+    fwd.exchange_and_offsets()
+    torch.cuda.synchronize()
+    cap = [int(c) for c in fwd.recv_off[:, W].cpu().numpy()]
+    recv = [torch.empty((c, hidden), dtype=torch.bfloat16, device="cuda") for c in cap]
+    disp = lambda: fwd(R, send, [Q] * W, recv, cap, fused=True)
+    ms = time_events(torch, disp, 5)
+    moved = 2 * R * sum(cap)
+    out["dispatch_a2av"] = row_entry(moved, ms)
+    out["dispatch_a2av"]["rows_received_per_rank"] = cap
+    del send
+    bk = A2av(W)
+    bk.S.copy_(fwd.O)
+    back = [torch.empty((Q, hidden), dtype=torch.bfloat16, device="cuda") for _ in range(W)]
+    ret = lambda: bk(R, recv, cap, back, [Q] * W, fused=True)
+    ms = time_events(torch, ret, 5)
+    out["return_a2av"] = row_entry(moved, ms)
+    del recv
+    outb = [torch.empty((Q, hidden), dtype=torch.bfloat16, device="cuda") for _ in range(W)]
+    ust = torch.zeros(1, dtype=torch.int32, device="cuda")
+    unpack = lambda: B.moe_unpack(W, T, k, R, back, perm, outb, ust)
+    ms = time_events(torch, unpack, 5)
+    out["moe_unpack"] = row_entry(W * (2 * Q * R + 8 * Q), ms)
+    torch.cuda.synchronize()
+    for name, st in (("pack", status), ("dispatch", fwd.status), ("return", bk.status),
+                     ("unpack", ust)):
+        if int(st.item()) != 0:
+            raise RuntimeError(f"{name} status {int(st.item())}")
+    del back, outb, tok, perm
+    torch.cuda.empty_cache()
+    # ---- embedding-key exchange: W=8, 26 tables, batch 8192
+    g = I.rng(901)
+    ranks = [I.emb_keys_rank(g, W=W) for _ in range(W)]
+    res = {}
+    for what, R2 in (("keys", 8), ("lengths", 4)):
+        Sx = np.stack([r.split_keys if what == "keys" else r.split_lengths for r in ranks])
+        data = [torch.from_numpy(r.keys if what == "keys" else r.lengths).cuda() for r in ranks]
+        capx = [int(c) for c in Sx.sum(axis=0)]
+        outs = [torch.empty(c * R2, dtype=torch.uint8, device="cuda") for c in capx]
+        st = A2av(W)
+        st.set_splits(Sx)
+        call = lambda: st(R2, data, [int(x.numel()) for x in data], outs, capx, fused=True)
+        ms = time_events(torch, call, 20)
+        torch.cuda.synchronize()
+        if int(st.status.item()) != 0:
+            raise RuntimeError("key exchange status")
+        cpu = {}
+        if o is not None:
+            xh = [x.view(torch.uint8).cpu().numpy() for x in data]
+            yh = [np.empty(c * R2, dtype=np.uint8) for c in capx]
+            rows_in = np.array([x.numel() for x in data], dtype=np.int64)
+            cs = time_cpu(lambda: o.a2av(R2, xh, rows_in, yh, np.array(capx), Sx))
+            cpu = dict(cpu_bytes=2 * R2 * int(Sx.sum()), cpu_s=cs, note="whole exchange")
+        res[what] = row_entry(2 * R2 * int(Sx.sum()), ms, **cpu)
+    out["emb_keys_exchange"] = res
+    return out
+
+
 def traffic_entry(bytes_per_launch):
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -244,6 +379,8 @@ def main(argv=None):
     ap.add_argument("--sets", type=int, default=8, help="rotating buffer sets (32 MiB case)")
     ap.add_argument("--no-headline", action="store_true", help="skip the W x size matrix")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the MoE pack / un-pack and key-exchange measurements")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -287,6 +424,11 @@ def main(argv=None):
     ceil = ceilings(torch, B, int(main_res["bytes_per_step"]))
     log("bench: ceilings", json.dumps(ceil))
 
+    rows = {}
+    if not args.no_rows:
+        rows = row_benchmarks(torch, B, I, with_cpu=not args.no_cpu)
+        log("bench: rows", json.dumps(rows))
+
     cpu = None if args.no_cpu else cpu_baseline(torch, I)
     if cpu:
         log("bench: cpu", json.dumps(cpu))
@@ -324,6 +466,7 @@ def main(argv=None):
                      "avg_launch_us": round(main_res["kernel_ms_mean"] * 1e3, 3)},
         "cpu_baseline": cpu,
         "headline": headline,
+        "rows": rows,
         "ceilings": {k: round(v, 1) for k, v in ceil.items()},
     }
     print(json.dumps(line), flush=True)

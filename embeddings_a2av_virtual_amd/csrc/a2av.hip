@@ -477,7 +477,7 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
                     unsigned char *dst = a.out[d] + r0 * R + off;
                     const unsigned char *src = a.in[s] + s0 * R + off;
                     if constexpr (ALIGNED) wave_copy16<U>(dst, src, e - x, lane);
-                    else copy_segment<kWave, U, true>(dst, src, e - x, lane);
+                    else wave_copy_any<U>(dst, src, e - x, lane);
                 }
                 x = e;
             }
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(256) void k_device_copy_wave(unsigned char *dst, co
         const uint64_t lo = p * piece;
         const uint64_t hi = lo + piece < bytes ? lo + piece : bytes;
         if constexpr (ALIGNED) wave_copy16<U>(dst + lo, src + lo, hi - lo, lane);
-        else copy_segment<kWave, U, true>(dst + lo, src + lo, hi - lo, lane);
+        else wave_copy_any<U>(dst + lo, src + lo, hi - lo, lane);
     }
 }
 
@@ -584,9 +584,13 @@ static int wave_grid(uint64_t bmax, uint64_t piece) {
 
 template <int W, int MODE>
 static void launch_wave_w(const CopyArgs &a, bool aligned, int unroll, int grid, hipStream_t st) {
-    if (!aligned) hipLaunchKernelGGL((k_a2av_wave<W, 4, false, MODE>), dim3(grid), dim3(256), 0, st, a);
-    else if (unroll == 16) hipLaunchKernelGGL((k_a2av_wave<W, 16, true, MODE>), dim3(grid), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_a2av_wave<W, 8, true, MODE>), dim3(grid), dim3(256), 0, st, a);
+    if (unroll == 16) {
+        if (aligned) hipLaunchKernelGGL((k_a2av_wave<W, 16, true, MODE>), dim3(grid), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((k_a2av_wave<W, 16, false, MODE>), dim3(grid), dim3(256), 0, st, a);
+    } else {
+        if (aligned) hipLaunchKernelGGL((k_a2av_wave<W, 8, true, MODE>), dim3(grid), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((k_a2av_wave<W, 8, false, MODE>), dim3(grid), dim3(256), 0, st, a);
+    }
 }
 
 template <int MODE>
@@ -771,7 +775,7 @@ A2AV_API int a2av_device_copy(void *dst, const void *src, size_t bytes, hipStrea
         unsigned char *d = (unsigned char *)dst;
         const unsigned char *s = (const unsigned char *)src;
         if (!aligned)
-            hipLaunchKernelGGL((k_device_copy_wave<4, false>), dim3(grid), dim3(256), 0, stream, d, s,
+            hipLaunchKernelGGL((k_device_copy_wave<8, false>), dim3(grid), dim3(256), 0, stream, d, s,
                                (uint64_t)bytes, wt.piece);
         else if (wt.unroll == 16)
             hipLaunchKernelGGL((k_device_copy_wave<16, true>), dim3(grid), dim3(256), 0, stream, d, s,

@@ -63,22 +63,38 @@ __device__ __forceinline__ void st(V *p, V v) {
     else *p = v;
 }
 
-// Block-cooperative copy of nv elements of V: thread `tid` of BS moves
-// elements tid, tid + BS, ...; U loads are issued before their U stores so
-// each lane keeps U accesses in flight.
+// Cooperative copy of nv elements of V by BS threads: thread `tid` moves
+// elements tid, tid + BS, ...; each step issues U loads before their U
+// stores, so every lane keeps U accesses in flight. Full steps carry no
+// per-lane guard. The last, partial step clamps the index to nv - 1 instead
+// of branching: a lane past the end re-copies the last element, and every
+// such lane writes the same bytes to the same place. (Guards in this loop
+// make the compiler wait for each load before the next one.)
 template <typename V, int BS, int U, bool NT>
 __device__ __forceinline__ void copy_elems(V *__restrict__ d, const V *__restrict__ s,
                                            uint64_t nv, int tid) {
-    uint64_t i = (uint64_t)tid;
     constexpr uint64_t step = (uint64_t)BS * U;
-    for (; i + (uint64_t)(U - 1) * BS < nv; i += step) {
+    uint64_t base = 0;
+    for (; base + step <= nv; base += step) {
         V r[U];
 #pragma unroll
-        for (int u = 0; u < U; u++) r[u] = ld<NT>(s + i + (uint64_t)u * BS);
+        for (int u = 0; u < U; u++) r[u] = ld<NT>(s + base + (uint64_t)u * BS + tid);
 #pragma unroll
-        for (int u = 0; u < U; u++) st<NT>(d + i + (uint64_t)u * BS, r[u]);
+        for (int u = 0; u < U; u++) st<NT>(d + base + (uint64_t)u * BS + tid, r[u]);
     }
-    for (; i < nv; i += BS) st<NT>(d + i, ld<NT>(s + i));
+    if (base < nv) {
+        V r[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const uint64_t i = base + (uint64_t)u * BS + tid;
+            r[u] = ld<NT>(s + (i < nv ? i : nv - 1));
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const uint64_t i = base + (uint64_t)u * BS + tid;
+            st<NT>(d + (i < nv ? i : nv - 1), r[u]);
+        }
+    }
 }
 
 // Block-cooperative copy of n bytes between non-overlapping device ranges.
@@ -108,6 +124,77 @@ __device__ __forceinline__ void copy_segment(unsigned char *dst, const unsigned 
     }
     const uint64_t done = nv * w;
     if ((uint64_t)tid < n - done) dst[done + tid] = src[done + tid];
+}
+
+// Funnel 16 bytes out of the 32-byte pair (a, b) starting at byte `delta`
+// (1..15): dword j of the result is bytes [delta + 4j, delta + 4j + 4).
+__device__ __forceinline__ u32x4 funnel16(const u32x4 &a, const u32x4 &b, uint32_t delta) {
+    const uint32_t c[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const uint32_t q = delta >> 2, sh = delta & 3;
+    u32x4 o;
+    // q and sh are the same in every lane, so the branches do not diverge
+#define A2AV_FUNNEL(Q)                                                                       \
+    if (sh == 0) {                                                                         \
+        o.x = c[Q]; o.y = c[Q + 1]; o.z = c[Q + 2]; o.w = c[Q + 3];                       \
+    } else {                                                                               \
+        o.x = __builtin_amdgcn_alignbyte(c[Q + 1], c[Q], sh);                              \
+        o.y = __builtin_amdgcn_alignbyte(c[Q + 2], c[Q + 1], sh);                          \
+        o.z = __builtin_amdgcn_alignbyte(c[Q + 3], c[Q + 2], sh);                          \
+        o.w = __builtin_amdgcn_alignbyte(c[Q + 4], c[Q + 3], sh);                          \
+    }
+    switch (q) {
+    case 0: A2AV_FUNNEL(0) break;
+    case 1: A2AV_FUNNEL(1) break;
+    case 2: A2AV_FUNNEL(2) break;
+    default: A2AV_FUNNEL(3) break;
+    }
+#undef A2AV_FUNNEL
+    return o;
+}
+
+// Wave-cooperative copy of n bytes at any alignment (64 lanes, all calling
+// with the same arguments). A head of < 16 bytes brings the destination to a
+// 16-byte boundary; then every lane stores one aligned 16-byte block per
+// step, cut out of the two aligned 16-byte source blocks that hold its bytes
+// (the second one is the block its right neighbour loads, so it comes from
+// cache). Every source block read holds at least one byte of the source
+// range, so no read leaves the pages the range lives on. The last step clamps
+// its index like copy_elems; the tail of < 16 bytes goes byte by byte.
+template <int U>
+__device__ __forceinline__ void wave_copy_any(unsigned char *dst, const unsigned char *src,
+                                              uint64_t n, int lane) {
+    uint64_t head = (16 - ((uintptr_t)dst & 15)) & 15;
+    if (head > n) head = n;
+    if ((uint64_t)lane < head) dst[lane] = src[lane];
+    dst += head;
+    src += head;
+    n -= head;
+    const uint64_t nv = n / 16;
+    const uint32_t delta = (uint32_t)((uintptr_t)src & 15);
+    u32x4 *d16 = (u32x4 *)dst;
+    if (delta == 0) {
+        copy_elems<u32x4, kWave, U, true>(d16, (const u32x4 *)src, nv, lane);
+    } else if (nv > 0) {
+        const u32x4 *sa = (const u32x4 *)(src - delta);
+        for (uint64_t base = 0; base < nv; base += (uint64_t)kWave * U) {
+            u32x4 lo[U], hi[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                uint64_t i = base + (uint64_t)u * kWave + lane;
+                i = i < nv ? i : nv - 1;
+                lo[u] = ld<true>(sa + i);
+                hi[u] = ld<true>(sa + i + 1);  // block nv still holds source bytes
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                uint64_t i = base + (uint64_t)u * kWave + lane;
+                i = i < nv ? i : nv - 1;
+                st<true>(d16 + i, funnel16(lo[u], hi[u], delta));
+            }
+        }
+    }
+    const uint64_t done = nv * 16;
+    if ((uint64_t)lane < n - done) dst[done + lane] = src[done + lane];
 }
 
 // ------------------------------------------------------------ host helpers

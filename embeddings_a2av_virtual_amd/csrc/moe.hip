@@ -176,44 +176,52 @@ __global__ __launch_bounds__(256) void k_moe_rank(const MoeArgs a) {
 }
 
 // ------------------------------------------------------------------ scatter
-// One block per (token, rank): the row is read once into registers and
-// stored to the k packed rows of its slots (16-byte path when rows and bases
-// allow it, otherwise k block copies of the row).
-template <int BS, int U, bool ALIGNED>
-__global__ __launch_bounds__(BS) void k_moe_scatter(const MoeArgs a) {
+// One wave per (rank, token): the token row is read once into registers (up
+// to 64 x 16 x U bytes per pass) and stored to the k packed rows of its
+// slots. Rows or bases that are not 16-byte aligned take k realigning wave
+// copies of the row instead (the re-reads hit in L2).
+template <int U, bool ALIGNED>
+__global__ __launch_bounds__(256) void k_moe_scatter(const MoeArgs a) {
     if (status_poisoned(a.status)) return;
-    const int r = blockIdx.y;
-    const int64_t t = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t wpb = blockDim.x / kWave;
+    const uint64_t nwork = (uint64_t)a.W * (uint64_t)a.T;
     const uint64_t R = a.R;
-    const unsigned char *src = a.tokens[r] + (uint64_t)t * R;
-    const int64_t *perm = a.perm[r] + t * a.k;
-    unsigned char *send = a.send[r];
-    if constexpr (ALIGNED) {
-        const uint64_t nv = R / 16;
-        const u32x4 *s16 = (const u32x4 *)src;
-        for (uint64_t base = 0; base < nv; base += (uint64_t)BS * U) {
-            u32x4 v[U];
+    for (uint64_t w = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave; w < nwork;
+         w += (uint64_t)gridDim.x * wpb) {
+        const int r = (int)(w / (uint64_t)a.T);
+        const int64_t t = (int64_t)(w - (uint64_t)r * (uint64_t)a.T);
+        const unsigned char *src = a.tokens[r] + (uint64_t)t * R;
+        const int64_t *perm = a.perm[r] + t * a.k;
+        unsigned char *send = a.send[r];
+        if constexpr (ALIGNED) {
+            const uint64_t nv = R / 16;
+            const u32x4 *s16 = (const u32x4 *)src;
+            // indices past the row end are clamped to its last vector (no
+            // per-lane branch; the clamped lanes store identical bytes)
+            for (uint64_t base = 0; base < nv; base += (uint64_t)kWave * U) {
+                u32x4 v[U];
+                uint64_t idx[U];
 #pragma unroll
-            for (int u = 0; u < U; u++) {
-                const uint64_t i = base + threadIdx.x + (uint64_t)u * BS;
-                if (i < nv) v[u] = ld<true>(s16 + i);
+                for (int u = 0; u < U; u++) {
+                    const uint64_t i = base + (uint64_t)u * kWave + lane;
+                    idx[u] = i < nv ? i : nv - 1;
+                    v[u] = ld<true>(s16 + idx[u]);
+                }
+                for (int j = 0; j < a.k; j++) {
+                    const int64_t p = perm[j];
+                    if (p < 0 || p >= a.Q) continue;
+                    u32x4 *d16 = (u32x4 *)(send + (uint64_t)p * R);
+#pragma unroll
+                    for (int u = 0; u < U; u++) st<true>(d16 + idx[u], v[u]);
+                }
             }
+        } else {
             for (int j = 0; j < a.k; j++) {
                 const int64_t p = perm[j];
                 if (p < 0 || p >= a.Q) continue;
-                u32x4 *d16 = (u32x4 *)(send + (uint64_t)p * R);
-#pragma unroll
-                for (int u = 0; u < U; u++) {
-                    const uint64_t i = base + threadIdx.x + (uint64_t)u * BS;
-                    if (i < nv) st<true>(d16 + i, v[u]);
-                }
+                wave_copy_any<4>(send + (uint64_t)p * R, src, R, lane);
             }
-        }
-    } else {
-        for (int j = 0; j < a.k; j++) {
-            const int64_t p = perm[j];
-            if (p < 0 || p >= a.Q) continue;
-            copy_segment<BS, 2, false>(send + (uint64_t)p * R, src, R, threadIdx.x);
         }
     }
 }
@@ -226,7 +234,7 @@ struct UnpackArgs {
     int32_t *status;
     uint64_t R;
     int64_t Q;
-    int64_t rows_per_block;
+    int W;
 };
 
 __global__ __launch_bounds__(256) void k_perm_check(const UnpackArgs a) {
@@ -241,22 +249,23 @@ __global__ __launch_bounds__(256) void k_perm_check(const UnpackArgs a) {
     if (__ballot(bad) != 0 && (threadIdx.x & (kWave - 1)) == 0) atomicOr(a.status, A2AV_ST_BAD_PERM);
 }
 
-template <int BS, bool ALIGNED>
-__global__ __launch_bounds__(BS) void k_moe_gather(const UnpackArgs a) {
+// One wave per (rank, slot): out[q] = back[perm[q]].
+template <int U, bool ALIGNED>
+__global__ __launch_bounds__(256) void k_moe_gather(const UnpackArgs a) {
     if (status_poisoned(a.status)) return;
-    const int r = blockIdx.y;
-    const int64_t q0 = (int64_t)blockIdx.x * a.rows_per_block;
-    const int64_t q1 = q0 + a.rows_per_block < a.Q ? q0 + a.rows_per_block : a.Q;
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t wpb = blockDim.x / kWave;
+    const uint64_t nwork = (uint64_t)a.W * (uint64_t)a.Q;
     const uint64_t R = a.R;
-    const int64_t *perm = a.perm[r];
-    for (int64_t q = q0; q < q1; q++) {
-        const int64_t p = perm[q];
+    for (uint64_t w = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave; w < nwork;
+         w += (uint64_t)gridDim.x * wpb) {
+        const int r = (int)(w / (uint64_t)a.Q);
+        const int64_t q = (int64_t)(w - (uint64_t)r * (uint64_t)a.Q);
+        const int64_t p = a.perm[r][q];
         const unsigned char *src = a.back[r] + (uint64_t)p * R;
         unsigned char *dst = a.out[r] + (uint64_t)q * R;
-        if constexpr (ALIGNED)
-            copy_elems<u32x4, BS, 4, true>((u32x4 *)dst, (const u32x4 *)src, R / 16, threadIdx.x);
-        else
-            copy_segment<BS, 2, false>(dst, src, R, threadIdx.x);
+        if constexpr (ALIGNED) copy_elems<u32x4, kWave, U, true>((u32x4 *)dst, (const u32x4 *)src, R / 16, lane);
+        else wave_copy_any<U>(dst, src, R, lane);
     }
 }
 
@@ -322,10 +331,13 @@ A2AV_API int moe_pack(int W, int64_t T, int k, int E, size_t row_bytes,
     if (a.Q > 0) {
         hipLaunchKernelGGL(k_moe_rank, dim3(nseg_grid, W), dim3(kRankWaves * kWave),
                            kRankWaves * E * sizeof(int32_t), stream, a);
+        const uint64_t waves = (uint64_t)W * (uint64_t)T;
+        uint64_t blocks = (waves + 3) / 4;
+        if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
         if (aligned)
-            hipLaunchKernelGGL((k_moe_scatter<256, 4, true>), dim3(T, W), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_moe_scatter<16, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
         else
-            hipLaunchKernelGGL((k_moe_scatter<256, 4, false>), dim3(T, W), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_moe_scatter<4, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     }
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
 }
@@ -351,19 +363,18 @@ A2AV_API int moe_unpack(int W, int64_t T, int k, size_t row_bytes, const void *c
     a.status = status;
     a.R = row_bytes;
     a.Q = T * k;
+    a.W = W;
     if (a.Q == 0) return A2AV_OK;
-    int64_t rpb = (int64_t)((65536 + row_bytes - 1) / row_bytes);
-    if (rpb < 1) rpb = 1;
-    a.rows_per_block = rpb;
     const int64_t check_blocks = (a.Q + 255) / 256;
-    const int64_t gather_blocks = (a.Q + rpb - 1) / rpb;
-    if (check_blocks > INT32_MAX || gather_blocks > INT32_MAX) return A2AV_EARG;
+    if (check_blocks > INT32_MAX) return A2AV_EARG;
+    uint64_t gather_blocks = ((uint64_t)W * (uint64_t)a.Q + 3) / 4;
+    if (gather_blocks > (1u << 22)) gather_blocks = 1u << 22;  // the wave loop strides over the rest
     hipLaunchKernelGGL(k_perm_check, dim3((unsigned)check_blocks, W), dim3(256), 0, stream, a);
     if (aligned)
-        hipLaunchKernelGGL((k_moe_gather<256, true>), dim3((unsigned)gather_blocks, W), dim3(256), 0,
+        hipLaunchKernelGGL((k_moe_gather<8, true>), dim3((unsigned)gather_blocks), dim3(256), 0,
                            stream, a);
     else
-        hipLaunchKernelGGL((k_moe_gather<256, false>), dim3((unsigned)gather_blocks, W), dim3(256),
-                           0, stream, a);
+        hipLaunchKernelGGL((k_moe_gather<8, false>), dim3((unsigned)gather_blocks), dim3(256), 0,
+                           stream, a);
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
 }
