@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) void k_moe_rank(const MoeArgs a) {
 // to 64 x 16 x U bytes per pass) and stored to the k packed rows of its
 // slots. Rows or bases that are not 16-byte aligned take k realigning wave
 // copies of the row instead (the re-reads hit in L2).
-template <int U, bool ALIGNED>
+template <int U, bool ALIGNED, bool SNT>
 __global__ __launch_bounds__(256) void k_moe_scatter(const MoeArgs a) {
     if (status_poisoned(a.status)) return;
     const int lane = threadIdx.x & (kWave - 1);
@@ -194,6 +194,9 @@ __global__ __launch_bounds__(256) void k_moe_scatter(const MoeArgs a) {
         const unsigned char *src = a.tokens[r] + (uint64_t)t * R;
         const int64_t *perm = a.perm[r] + t * a.k;
         unsigned char *send = a.send[r];
+        // the token's k packed rows, one per lane, fetched before any store
+        // (k <= 64 here; the host routes larger k to the unaligned form)
+        const int64_t pl = lane < a.k ? perm[lane] : -1;
         if constexpr (ALIGNED) {
             const uint64_t nv = R / 16;
             const u32x4 *s16 = (const u32x4 *)src;
@@ -209,14 +212,17 @@ __global__ __launch_bounds__(256) void k_moe_scatter(const MoeArgs a) {
                     v[u] = ld<true>(s16 + idx[u]);
                 }
                 for (int j = 0; j < a.k; j++) {
-                    const int64_t p = perm[j];
+                    const int64_t p = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                                                     (int)((uint64_t)pl >> 32), j) << 32) |
+                                                 (uint32_t)__builtin_amdgcn_readlane((int)pl, j));
                     if (p < 0 || p >= a.Q) continue;
                     u32x4 *d16 = (u32x4 *)(send + (uint64_t)p * R);
 #pragma unroll
-                    for (int u = 0; u < U; u++) st<true>(d16 + idx[u], v[u]);
+                    for (int u = 0; u < U; u++) st<SNT>(d16 + idx[u], v[u]);
                 }
             }
         } else {
+            (void)pl;
             for (int j = 0; j < a.k; j++) {
                 const int64_t p = perm[j];
                 if (p < 0 || p >= a.Q) continue;
@@ -334,10 +340,18 @@ A2AV_API int moe_pack(int W, int64_t T, int k, int E, size_t row_bytes,
         const uint64_t waves = (uint64_t)W * (uint64_t)T;
         uint64_t blocks = (waves + 3) / 4;
         if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
-        if (aligned)
-            hipLaunchKernelGGL((k_moe_scatter<16, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-        else
-            hipLaunchKernelGGL((k_moe_scatter<4, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+        // tuning knobs: A2AV_MOE_UNROLL (vectors per lane per pass, 4/8/16) and
+        // A2AV_MOE_STORE_NT (non-temporal stores, 0/1)
+        const int mu = (int)env_long("A2AV_MOE_UNROLL", 16, 4, 16);
+        const bool snt = env_long("A2AV_MOE_STORE_NT", 0, 0, 1) != 0;
+#define A2AV_SCATTER(UU, NT_) \
+    hipLaunchKernelGGL((k_moe_scatter<UU, true, NT_>), dim3((unsigned)blocks), dim3(256), 0, stream, a)
+        if (!aligned || k > kWave)
+            hipLaunchKernelGGL((k_moe_scatter<4, false, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+        else if (mu <= 4) { if (snt) A2AV_SCATTER(4, true); else A2AV_SCATTER(4, false); }
+        else if (mu <= 8) { if (snt) A2AV_SCATTER(8, true); else A2AV_SCATTER(8, false); }
+        else { if (snt) A2AV_SCATTER(16, true); else A2AV_SCATTER(16, false); }
+#undef A2AV_SCATTER
     }
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
 }
@@ -370,7 +384,14 @@ A2AV_API int moe_unpack(int W, int64_t T, int k, size_t row_bytes, const void *c
     uint64_t gather_blocks = ((uint64_t)W * (uint64_t)a.Q + 3) / 4;
     if (gather_blocks > (1u << 22)) gather_blocks = 1u << 22;  // the wave loop strides over the rest
     hipLaunchKernelGGL(k_perm_check, dim3((unsigned)check_blocks, W), dim3(256), 0, stream, a);
-    if (aligned)
+    const int gu = (int)env_long("A2AV_MOE_GATHER_UNROLL", 16, 4, 16);
+    if (aligned && gu >= 16)
+        hipLaunchKernelGGL((k_moe_gather<16, true>), dim3((unsigned)gather_blocks), dim3(256), 0,
+                           stream, a);
+    else if (aligned && gu <= 4)
+        hipLaunchKernelGGL((k_moe_gather<4, true>), dim3((unsigned)gather_blocks), dim3(256), 0,
+                           stream, a);
+    else if (aligned)
         hipLaunchKernelGGL((k_moe_gather<8, true>), dim3((unsigned)gather_blocks), dim3(256), 0,
                            stream, a);
     else

@@ -237,3 +237,25 @@ def test_embedding_key_exchange_full(ref):
         lv = gl[4][d].reshape(-1).view(np.int32)
         for s in range(W):
             assert lv[gl[3][d, s]:gl[3][d, s + 1]].sum() == gk[1][d, s]
+
+
+@pytest.mark.parametrize("env", [
+    {"A2AV_MOE_UNROLL": "4"}, {"A2AV_MOE_UNROLL": "8", "A2AV_MOE_STORE_NT": "1"},
+    {"A2AV_MOE_GATHER_UNROLL": "4"}, {"A2AV_MOE_GATHER_UNROLL": "8"},
+])
+def test_moe_launch_shapes_give_identical_bytes(ref, monkeypatch, env):
+    W, T, k, E, R = 4, 300, 4, 16, 1040
+    g = I.rng(31)
+    tokens, ids = _moe_inputs(g, W, T, k, E, R, "zipf")
+    for key, val in env.items():
+        monkeypatch.setenv(key, val)
+    run = MoeRun(W, T, k, E, R, tokens, ids)
+    assert run.pack() == 0
+    for r in range(W):
+        st, send, perm, splits, counts = ref.moe_pack(T, k, E, W, R, tokens[r], ids[r])
+        assert np.array_equal(run.send[r].host(), send)
+        assert np.array_equal(run.perm[r].cpu().numpy(), perm)
+    assert run.round_trip()[:3] == (0, 0, 0)
+    for r in range(W):
+        got = run.out[r].host().reshape(T, k, R)
+        assert np.array_equal(got, np.repeat(tokens[r][:, None, :], k, axis=1))
