@@ -117,9 +117,18 @@ int a2av_offsets(int W, const int64_t *S, const int64_t *O, int64_t *send_off,
  *                 (send_off[s][W] > in_rows[s]), A2AV_ST_RECV_OVERFLOW
  *                 (recv_off[d][W] > out_cap_rows[d]); any of them => no byte
  *                 of any out[d] is written.
- * One persistent kernel: the destination byte space of all ranks is cut into
- * equal contiguous pieces, one per workgroup, so skewed or zero splits leave
- * no compute unit idle; each piece is copied with 16-byte coalesced accesses.
+ * One kernel. The destination byte space of all ranks (out[0]'s rows, then
+ * out[1]'s, ...) is cut into equal pieces, so skewed or zero splits leave no
+ * compute unit idle. For W <= 8 every wave reads S and the offsets through the
+ * scalar cache, checks them, and copies one piece with 16-byte coalesced
+ * non-temporal accesses (realigned in registers when source and destination
+ * differ mod 16); the grid is sized to min(sum in_rows, sum out_cap_rows) *
+ * row_bytes. For larger W each workgroup stages the matrices in LDS (W <= 16)
+ * or reads them from global memory, then copies its piece.
+ * Tuning (read on every call; defaults are compiled in): A2AV_WAVE_PIECE,
+ * A2AV_WAVE_UNROLL (wave kernel); A2AV_BLOCK_KERNEL=1 forces the workgroup
+ * kernel; A2AV_BLOCKS_PER_CU, A2AV_UNROLL, A2AV_NT, A2AV_PIECE,
+ * A2AV_MIN_PIECE (workgroup kernel). Every setting gives identical bytes.
  */
 int a2av_copy(int W, size_t row_bytes, const void *const *in,
               const int64_t *in_rows, void *const *out,
@@ -134,9 +143,10 @@ int a2av_copy(int W, size_t row_bytes, const void *const *in,
  * / RECV_OVERFLOW leave O and the offsets written and no payload byte).
  *   S                      device int64 [W][W] (input splits)
  *   O, send_off, recv_off  device outputs as in the separate calls
- * For W <= 16 this is ONE kernel launch: every workgroup stages S in LDS and
- * scans it itself (workgroup 0 also writes O and the offsets), then copies
- * its piece of the destination space; larger W runs the three launches.
+ * For W <= 16 this is ONE kernel launch: every wave (W <= 8) or workgroup
+ * (W <= 16) reads S, computes O and both offset matrices itself (the first
+ * one also writes them out), checks them, and copies its piece of the
+ * destination space; larger W runs the three launches.
  */
 int a2av_all_to_all_vdev(int W, size_t row_bytes, const void *const *in,
                          const int64_t *in_rows, void *const *out,
@@ -171,7 +181,8 @@ size_t moe_pack_workspace_bytes(int W, int64_t T, int k, int E);
  *                 the workspace is written.
  * Four kernels: an LDS histogram per slot segment, an expert-major scan of the
  * histograms, a stable in-segment rank (wave ballots), and a token-major row
- * scatter that reads each token once and writes it k times.
+ * scatter (one wave per token) that reads each token once and writes it k
+ * times. Tuning: A2AV_MOE_UNROLL, A2AV_MOE_STORE_NT.
  */
 int moe_pack(int W, int64_t T, int k, int E, size_t row_bytes,
              const void *const *tokens, const int32_t *const *ids,
@@ -188,7 +199,8 @@ int moe_pack(int W, int64_t T, int k, int E, size_t row_bytes,
  *   perm[W]          device int64 [T*k] per rank, from moe_pack
  *   status           A2AV_ST_BAD_PERM if an entry is outside [0, T*k):
  *                    nothing is written.
- * Two kernels: a range check of perm, then a row gather.
+ * Two kernels: a range check of perm, then a row gather (one wave per row).
+ * Tuning: A2AV_MOE_GATHER_UNROLL.
  */
 int moe_unpack(int W, int64_t T, int k, size_t row_bytes,
                const void *const *back, const int64_t *const *perm,

@@ -1,0 +1,102 @@
+/*
+ * Drives the CPU oracle under AddressSanitizer and UndefinedBehaviorSanitizer
+ * (built and run by test_oracle_sanitized.py, host only). Every buffer is
+ * allocated at exactly the size the definition allows, so any read or write
+ * past a rank's rows, past an output's capacity or past a permutation is
+ * reported. Also checks the round trip and the pack/unpack identity.
+ */
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "a2av_ref.h"
+
+static uint64_t rng_state = 0x9e3779b97f4a7c15ull;
+static uint64_t next_u64(void) {  /* splitmix64 */
+    uint64_t z = (rng_state += 0x9e3779b97f4a7c15ull);
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
+
+#define CHECK(c) do { if (!(c)) { fprintf(stderr, "check failed: %s (line %d)\n", #c, __LINE__); exit(1); } } while (0)
+
+static void one_exchange(int W, size_t R, int zero_pct) {
+    int64_t *S = malloc(sizeof(int64_t) * W * W), *S2 = malloc(sizeof(int64_t) * W * W);
+    int64_t *O = malloc(sizeof(int64_t) * W * W);
+    int64_t *so = malloc(sizeof(int64_t) * W * (W + 1)), *ro = malloc(sizeof(int64_t) * W * (W + 1));
+    int64_t *rows = malloc(sizeof(int64_t) * W), *cap = calloc(W, sizeof(int64_t));
+    unsigned char **in = malloc(sizeof(void *) * W), **out = malloc(sizeof(void *) * W), **back = malloc(sizeof(void *) * W);
+    for (int i = 0; i < W * W; i++) S[i] = (int)(next_u64() % 100) < zero_pct ? 0 : (int64_t)(next_u64() % 40);
+    for (int s = 0; s < W; s++) {
+        rows[s] = 0;
+        for (int d = 0; d < W; d++) { rows[s] += S[s * W + d]; cap[d] += S[s * W + d]; }
+    }
+    for (int s = 0; s < W; s++) {
+        in[s] = malloc(rows[s] * R + 1);
+        for (int64_t b = 0; b < rows[s] * (int64_t)R; b++) in[s][b] = (unsigned char)next_u64();
+        out[s] = malloc(cap[s] * R + 1);
+        back[s] = malloc(rows[s] * R + 1);
+    }
+    CHECK(ref_a2av(W, R, (const void *const *)in, rows, (void *const *)out, cap, S, O, so, ro) == 0);
+    CHECK(ref_copy(W, R, (const void *const *)in, rows, (void *const *)out, cap, S, so, ro) == 0);
+    memcpy(S2, O, sizeof(int64_t) * W * W);
+    CHECK(ref_a2av(W, R, (const void *const *)out, cap, (void *const *)back, rows, S2, O, so, ro) == 0);
+    for (int s = 0; s < W; s++) CHECK(memcmp(back[s], in[s], rows[s] * R) == 0);
+    for (int d = 0; d < W; d++) {
+        for (int64_t j = 0; j < cap[d]; j++) {
+            int sr; int64_t i;
+            CHECK(ref_source_of(W, S, d, j, &sr, &i) == 0);
+            CHECK(memcmp(out[d] + j * R, in[sr] + i * R, R) == 0);
+        }
+        int sr; int64_t i;
+        CHECK(ref_source_of(W, S, d, cap[d], &sr, &i) == 1);
+    }
+    /* one row too many for rank 0 and one row too few room for rank 0 */
+    if (rows[0] > 0) {
+        rows[0] -= 1;
+        CHECK(ref_a2av(W, R, (const void *const *)in, rows, (void *const *)out, cap, S, O, so, ro) == REF_SEND_OVERRUN);
+        rows[0] += 1;
+    }
+    if (cap[0] > 0) {
+        cap[0] -= 1;
+        CHECK(ref_a2av(W, R, (const void *const *)in, rows, (void *const *)out, cap, S, O, so, ro) == REF_RECV_OVERFLOW);
+        cap[0] += 1;
+    }
+    for (int s = 0; s < W; s++) { free(in[s]); free(out[s]); free(back[s]); }
+    free(in); free(out); free(back); free(S); free(S2); free(O); free(so); free(ro); free(rows); free(cap);
+}
+
+static void one_pack(int64_t T, int k, int E, int W, size_t R) {
+    int64_t Q = T * k;
+    unsigned char *tok = malloc(T * R + 1), *send = malloc(Q * R + 1), *out = malloc(Q * R + 1);
+    int32_t *ids = malloc(sizeof(int32_t) * (Q + 1));
+    int64_t *perm = malloc(sizeof(int64_t) * (Q + 1)), *splits = malloc(sizeof(int64_t) * W);
+    int64_t *counts = malloc(sizeof(int64_t) * E);
+    for (int64_t b = 0; b < T * (int64_t)R; b++) tok[b] = (unsigned char)next_u64();
+    for (int64_t q = 0; q < Q; q++) ids[q] = (int32_t)(next_u64() % E);
+    CHECK(ref_moe_pack(T, k, E, W, R, tok, ids, send, perm, splits, counts) == 0);
+    CHECK(ref_moe_unpack(T, k, R, send, perm, out) == 0);
+    for (int64_t q = 0; q < Q; q++) CHECK(memcmp(out + q * R, tok + (q / k) * R, R) == 0);
+    if (Q > 0) {
+        ids[Q / 2] = E;
+        CHECK(ref_moe_pack(T, k, E, W, R, tok, ids, send, perm, splits, counts) == REF_BAD_EXPERT);
+    }
+    free(tok); free(send); free(out); free(ids); free(perm); free(splits); free(counts);
+}
+
+int main(void) {
+    const size_t widths[] = {1, 3, 8, 16, 100};
+    for (int W = 1; W <= 9; W++)
+        for (int wi = 0; wi < 5; wi++)
+            for (int z = 0; z <= 80; z += 40) one_exchange(W, widths[wi], z);
+    one_exchange(64, 4, 50);
+    one_exchange(64, 1, 0);
+    one_pack(200, 8, 256, 8, 16);
+    one_pack(333, 3, 12, 4, 5);
+    one_pack(1, 1, 1, 1, 1);
+    one_pack(0, 2, 8, 2, 4);
+    printf("oracle sanitized: ok\n");
+    return 0;
+}
