@@ -348,33 +348,6 @@ def row_benchmarks(torch, B, I, with_cpu=True):
             raise RuntimeError(f"{name} status {int(st.item())}")
     del back, outb, tok, perm
     torch.cuda.empty_cache()
-    # ---- embedding-key exchange: W=8, 26 tables, batch 8192
-    g = I.rng(901)
-    ranks = [I.emb_keys_rank(g, W=W) for _ in range(W)]
-    res = {}
-    for what, R2 in (("keys", 8), ("lengths", 4)):
-        Sx = np.stack([r.split_keys if what == "keys" else r.split_lengths for r in ranks])
-        data = [torch.from_numpy(r.keys if what == "keys" else r.lengths).cuda() for r in ranks]
-        capx = [int(c) for c in Sx.sum(axis=0)]
-        outs = [torch.empty(c * R2, dtype=torch.uint8, device="cuda") for c in capx]
-        st = A2av(W)
-        st.set_splits(Sx)
-        args = fused_args(st, R2, data, [int(x.numel()) for x in data], outs, capx)
-        L = B.lib()
-        call = lambda: L.a2av_all_to_all_vdev(*args)
-        ms = time_events(torch, call, 50)
-        torch.cuda.synchronize()
-        if int(st.status.item()) != 0:
-            raise RuntimeError("key exchange status")
-        cpu = {}
-        if o is not None:
-            xh = [x.view(torch.uint8).cpu().numpy() for x in data]
-            yh = [np.empty(c * R2, dtype=np.uint8) for c in capx]
-            rows_in = np.array([x.numel() for x in data], dtype=np.int64)
-            cs = time_cpu(lambda: o.a2av(R2, xh, rows_in, yh, np.array(capx), Sx))
-            cpu = dict(cpu_bytes=2 * R2 * int(Sx.sum()), cpu_s=cs, note="whole exchange")
-        res[what] = row_entry(2 * R2 * int(Sx.sum()), ms, **cpu)
-    out["emb_keys_exchange"] = res
     return out
 
 

@@ -18,7 +18,8 @@ Workloads (sizes per virtual rank):
   (32 per rank), expert ids Zipf(s=1.1).
 - ``sweep``: W=4, 8 KiB rows, 1..4096 MiB per rank, uniform or 50 % zero splits.
 - ``emb_keys``: W=8, 26 tables, batch 8192, lengths min(Poisson(20), 100), int64
-  keys uniform in [0, 1e7), table t owned by rank t mod 8.
+  keys uniform in [0, 1e7), in table order (the exchange buckets them by
+  owning rank, t mod 8).
 """
 from __future__ import annotations
 
@@ -104,34 +105,31 @@ def uniform_ids(g: np.random.Generator, T: int, k: int, E: int) -> np.ndarray:
 
 # ---------------------------------------------------------------- embedding keys
 class EmbKeysRank:
-    """One rank's embedding-key exchange input in send order.
+    """One rank's sparse features for one batch, in table order.
 
-    Tables are laid out by (owner = t mod W, t), samples in order inside a
-    table. ``keys`` is int64 (8-byte rows), ``lengths`` int32 (4-byte rows).
-    ``split_keys[d]`` / ``split_lengths[d]`` are the rows bound for rank d.
+    ``lengths`` is [tables][batch] int32 (keys per sample); ``keys`` holds the
+    keys of table 0 (sample 0, 1, ...), then table 1, ... as int64.
     """
 
-    def __init__(self, keys, lengths, split_keys, split_lengths, table_order):
-        self.keys = keys
+    def __init__(self, lengths, keys):
         self.lengths = lengths
-        self.split_keys = split_keys
-        self.split_lengths = split_lengths
-        self.table_order = table_order
+        self.keys = keys
 
 
-def emb_keys_rank(g: np.random.Generator, W: int = 8, tables: int = 26, batch: int = 8192,
+def emb_keys_rank(g: np.random.Generator, tables: int = 26, batch: int = 8192,
                   lam: float = 20.0, cap: int = 100, key_range: int = 10_000_000) -> EmbKeysRank:
+    """lengths ~ min(Poisson(lam), cap) per (table, sample); keys uniform int64
+    in [0, key_range)."""
     lengths = np.minimum(g.poisson(lam, size=(tables, batch)), cap).astype(np.int32)
-    order = sorted(range(tables), key=lambda t: (t % W, t))
-    lens_sent = np.ascontiguousarray(lengths[order].reshape(-1))
-    total = int(lengths.sum())
-    keys = g.integers(0, key_range, size=total, dtype=np.int64)
-    split_keys = np.zeros(W, dtype=np.int64)
-    split_lengths = np.zeros(W, dtype=np.int64)
-    for t in range(tables):
-        split_keys[t % W] += int(lengths[t].sum())
-        split_lengths[t % W] += batch
-    return EmbKeysRank(keys, lens_sent, split_keys, split_lengths, order)
+    keys = g.integers(0, key_range, size=int(lengths.sum()), dtype=np.int64)
+    return EmbKeysRank(lengths, keys)
+
+
+def gate_weights(g: np.random.Generator, T: int, k: int) -> np.ndarray:
+    """T x k float32 gate weights: a softmax over k N(0, 1) logits per token."""
+    z = g.standard_normal((T, k))
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
 
 
 # ---------------------------------------------------------------- workload table

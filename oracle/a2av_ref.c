@@ -22,6 +22,7 @@
  */
 #include "a2av_ref.h"
 
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -242,5 +243,139 @@ int ref_moe_unpack(int64_t T, int k, size_t R,
     for (int64_t q = 0; q < Q; q++)
         memcpy((unsigned char *)out + (size_t)q * R,
                (const unsigned char *)back + (size_t)perm[q] * R, R);
+    return 0;
+}
+
+/*
+ * Receive-side expert regroup of one rank: the step after the dispatch, so
+ * that each expert's rows sit together for its GEMM. Rank d receives from
+ * each source the rows routed to d's experts, ordered by expert; regrouping
+ * makes the order (expert, source) instead of (source, expert).
+ */
+int ref_moe_regroup(int W, int E, int d, size_t R, const int64_t *counts,
+                    const void *in, int64_t in_rows, void *out, int64_t out_cap,
+                    int64_t *expert_offsets, int direction) {
+    if (W < 1 || W > REF_MAX_W || E < 1 || E % W != 0 || d < 0 || d >= W || R == 0 ||
+        !counts || !expert_offsets || in_rows < 0 || out_cap < 0 ||
+        (direction != 0 && direction != 1))
+        return REF_EARG;
+    const int P = E / W;
+    /* the P owned columns of counts */
+    for (int s = 0; s < W; s++)
+        for (int j = 0; j < P; j++)
+            if (!split_is_valid(counts[s * E + d * P + j])) return REF_BAD_SPLIT;
+    int64_t total = 0;
+    for (int s = 0; s < W; s++)
+        for (int j = 0; j < P; j++) total += counts[s * E + d * P + j];
+    int st = 0;
+    if (total > in_rows) st |= REF_SEND_OVERRUN;
+    if (total > out_cap) st |= REF_RECV_OVERFLOW;
+    if (st) return st;
+    if (total > 0 && (!in || !out)) return REF_EARG;
+    /* expert-major offsets */
+    int64_t run = 0;
+    for (int j = 0; j < P; j++) {
+        expert_offsets[j] = run;
+        for (int s = 0; s < W; s++) run += counts[s * E + d * P + j];
+    }
+    expert_offsets[P] = run;
+    /* walk the blocks in source-major order, keeping both positions */
+    int64_t src_major = 0;
+    for (int s = 0; s < W; s++) {
+        for (int j = 0; j < P; j++) {
+            const int64_t n = counts[s * E + d * P + j];
+            int64_t expert_major = expert_offsets[j];
+            for (int s2 = 0; s2 < s; s2++) expert_major += counts[s2 * E + d * P + j];
+            const int64_t from = direction == 0 ? src_major : expert_major;
+            const int64_t to = direction == 0 ? expert_major : src_major;
+            if (n > 0)
+                memcpy((unsigned char *)out + (size_t)to * R,
+                       (const unsigned char *)in + (size_t)from * R, (size_t)n * R);
+            src_major += n;
+        }
+    }
+    return 0;
+}
+
+/* bfloat16 is the top half of an IEEE binary32. */
+static float bf16_to_float(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Round a binary32 to bfloat16, to nearest, ties to even; a NaN keeps its
+ * sign and top payload bits and becomes quiet. */
+static uint16_t float_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if (isnan(f)) return (uint16_t)((u >> 16) | 0x0040u);
+    const uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+int ref_moe_combine(int64_t T, int k, int64_t H, const uint16_t *back,
+                    const int64_t *perm, const float *w, uint16_t *out) {
+    if (T < 0 || k < 1 || H < 1) return REF_EARG;
+    if (T > INT64_MAX / k) return REF_EARG;
+    const int64_t Q = T * k;
+    if (Q > 0 && (!back || !perm || !w || !out)) return REF_EARG;
+    for (int64_t q = 0; q < Q; q++)
+        if (perm[q] < 0 || perm[q] >= Q) return REF_BAD_PERM;
+    for (int64_t t = 0; t < T; t++) {
+        for (int64_t h = 0; h < H; h++) {
+            float acc = 0.0f;
+            for (int j = 0; j < k; j++) {
+                const int64_t row = perm[t * k + j];
+                acc = fmaf(w[t * k + j], bf16_to_float(back[row * H + h]), acc);
+            }
+            out[t * H + h] = float_to_bf16(acc);
+        }
+    }
+    return 0;
+}
+
+/* Embedding keys bucketed by the rank that owns their table, before the key
+ * exchange: tables in (owner, table) order, samples in order inside a table. */
+int ref_keys_bucketize(int W, int n_tables, int64_t batch, const int32_t *lengths,
+                       const int64_t *keys, int64_t n_keys, int32_t *lengths_out,
+                       int64_t *keys_out, int64_t *split_keys, int64_t *split_lengths) {
+    if (W < 1 || W > REF_MAX_W || n_tables < 0 || batch < 0 || n_keys < 0 || !split_keys ||
+        !split_lengths)
+        return REF_EARG;
+    if (n_tables > 0 && batch > INT64_MAX / n_tables) return REF_EARG;
+    const int64_t nl = (int64_t)n_tables * batch;
+    if (nl > 0 && (!lengths || !lengths_out)) return REF_EARG;
+    for (int64_t i = 0; i < nl; i++)
+        if (lengths[i] < 0) return REF_BAD_SPLIT;
+    /* keys of each table and where they start in the input */
+    int64_t *tk = calloc((size_t)(n_tables > 0 ? n_tables : 1), sizeof(int64_t));
+    int64_t *tstart = calloc((size_t)(n_tables > 0 ? n_tables : 1), sizeof(int64_t));
+    if (!tk || !tstart) { free(tk); free(tstart); return REF_EARG; }
+    int64_t run = 0;
+    for (int t = 0; t < n_tables; t++) {
+        tstart[t] = run;
+        for (int64_t b = 0; b < batch; b++) tk[t] += lengths[(int64_t)t * batch + b];
+        run += tk[t];
+    }
+    if (run > n_keys) { free(tk); free(tstart); return REF_SEND_OVERRUN; }
+    if (run > 0 && (!keys || !keys_out)) { free(tk); free(tstart); return REF_EARG; }
+    for (int d = 0; d < W; d++) { split_keys[d] = 0; split_lengths[d] = 0; }
+    int64_t kpos = 0, lpos = 0;
+    for (int d = 0; d < W; d++) {
+        for (int t = d; t < n_tables; t += W) {  /* tables owned by d, ascending */
+            if (batch > 0)
+                memcpy(lengths_out + lpos, lengths + (int64_t)t * batch, (size_t)batch * 4);
+            if (tk[t] > 0)
+                memcpy(keys_out + kpos, keys + tstart[t], (size_t)tk[t] * 8);
+            lpos += batch;
+            kpos += tk[t];
+            split_keys[d] += tk[t];
+            split_lengths[d] += batch;
+        }
+    }
+    free(tk);
+    free(tstart);
     return 0;
 }

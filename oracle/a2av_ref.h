@@ -90,6 +90,34 @@ int ref_moe_pack(int64_t T, int k, int E, int W, size_t R,
 int ref_moe_unpack(int64_t T, int k, size_t R,
                    const void *back, const int64_t *perm, void *out);
 
+/* Receive-side expert regroup for ONE rank d. counts is the W x E matrix of
+ * rows each source s routed to each expert e (row s = source s). The rank
+ * owns experts d*P .. d*P+P-1 (P = E/W). Source-major order: for each source
+ * s, for each owned expert j, counts[s][d*P+j] rows. Expert-major order: for
+ * each owned expert j, for each source s, the same blocks. direction 0 turns
+ * source-major `in` into expert-major `out`; direction 1 the reverse.
+ * expert_offsets[j] = rows before owned expert j in expert-major order, with
+ * the total at index P. */
+int ref_moe_regroup(int W, int E, int d, size_t R, const int64_t *counts,
+                    const void *in, int64_t in_rows, void *out, int64_t out_cap,
+                    int64_t *expert_offsets, int direction);
+
+/* Gate-weighted combine for ONE rank: for token t and element h,
+ * acc = +0.0f; for j = 0..k-1: acc = fmaf(w[t][j], float(back[perm[t*k+j]][h]), acc);
+ * out[t][h] = acc rounded to bfloat16 (round to nearest even; NaN stays a quiet
+ * NaN). back is [T*k][H] bf16, w is [T][k] fp32, out is [T][H] bf16. */
+int ref_moe_combine(int64_t T, int k, int64_t H, const uint16_t *back,
+                    const int64_t *perm, const float *w, uint16_t *out);
+
+/* Bucketing of ONE rank's jagged embedding keys by owning rank (table t is
+ * owned by rank t mod W). lengths is [n_tables][batch] int32 in table order,
+ * keys are the keys of table 0, then table 1, ... (n_keys of them). Outputs
+ * lengths_out / keys_out hold the tables in (owner, t) order;
+ * split_keys[d] / split_lengths[d] = keys / lengths rows bound for rank d. */
+int ref_keys_bucketize(int W, int n_tables, int64_t batch, const int32_t *lengths,
+                       const int64_t *keys, int64_t n_keys, int32_t *lengths_out,
+                       int64_t *keys_out, int64_t *split_keys, int64_t *split_lengths);
+
 #ifdef __cplusplus
 }
 #endif

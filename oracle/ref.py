@@ -34,7 +34,7 @@ _lib = None
 def build(out: str = LIB, extra_flags: tuple = ()) -> str:
     """Compile the oracle with gcc into a shared library and return its path."""
     cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror", "-fPIC", "-shared",
-           "-ffp-contract=off", *extra_flags, "-o", out, SRC]
+           "-ffp-contract=off", *extra_flags, "-o", out, SRC, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 
@@ -54,8 +54,17 @@ def _bind(lib):
                                  ctypes.c_void_p, i32p, ctypes.c_void_p, i64p, i64p, i64p]
     lib.ref_moe_unpack.argtypes = [ctypes.c_int64, ctypes.c_int, sz, ctypes.c_void_p, i64p,
                                    ctypes.c_void_p]
+    lib.ref_moe_regroup.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, sz, i64p,
+                                    ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                    ctypes.c_int64, i64p, ctypes.c_int]
+    lib.ref_moe_combine.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
+                                    i64p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ref_keys_bucketize.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, i32p,
+                                       ctypes.c_void_p, ctypes.c_int64, i32p, ctypes.c_void_p,
+                                       i64p, i64p]
     for name in ("ref_exchange_splits", "ref_offsets", "ref_copy", "ref_a2av", "ref_source_of",
-                 "ref_moe_pack", "ref_moe_unpack"):
+                 "ref_moe_pack", "ref_moe_unpack", "ref_moe_regroup", "ref_moe_combine",
+                 "ref_keys_bucketize"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -163,3 +172,38 @@ class Oracle:
         out = np.zeros(T * k * R, dtype=np.uint8)
         st = self.lib.ref_moe_unpack(T, k, R, back.ctypes.data, _i64(perm), out.ctypes.data)
         return st, out
+
+    def moe_regroup(self, W, E, d, R, counts, inp, in_rows, out_cap, direction=0):
+        """Returns (status, out bytes [out_cap * R], expert_offsets [E/W + 1])."""
+        counts = np.ascontiguousarray(counts, dtype=np.int64)
+        inp = np.ascontiguousarray(inp).view(np.uint8).reshape(-1)
+        out = np.zeros(max(int(out_cap), 0) * R, dtype=np.uint8)
+        eoff = np.zeros(E // W + 1, dtype=np.int64)
+        st = self.lib.ref_moe_regroup(W, E, d, R, _i64(counts), inp.ctypes.data, int(in_rows),
+                                      out.ctypes.data, int(out_cap), _i64(eoff), direction)
+        return st, out, eoff
+
+    def moe_combine(self, T, k, H, back, perm, w):
+        """back: uint16 [T*k, H] (bf16 bits), w: float32 [T, k]; returns uint16 [T, H]."""
+        back = np.ascontiguousarray(back, dtype=np.uint16)
+        perm = np.ascontiguousarray(perm, dtype=np.int64)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        out = np.zeros((T, H), dtype=np.uint16)
+        st = self.lib.ref_moe_combine(T, k, H, back.ctypes.data, _i64(perm), w.ctypes.data,
+                                      out.ctypes.data)
+        return st, out
+
+    def keys_bucketize(self, W, n_tables, batch, lengths, keys):
+        """Returns (status, lengths_out, keys_out, split_keys, split_lengths)."""
+        lengths = np.ascontiguousarray(lengths, dtype=np.int32).reshape(-1)
+        keys = np.ascontiguousarray(keys, dtype=np.int64)
+        lo = np.zeros(n_tables * batch, dtype=np.int32)
+        ko = np.zeros(keys.size, dtype=np.int64)
+        sk = np.zeros(W, dtype=np.int64)
+        sl = np.zeros(W, dtype=np.int64)
+        st = self.lib.ref_keys_bucketize(W, n_tables, batch,
+                                         lengths.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                         keys.ctypes.data, keys.size,
+                                         lo.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                         ko.ctypes.data, _i64(sk), _i64(sl))
+        return st, lo, ko, sk, sl

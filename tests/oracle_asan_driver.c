@@ -86,6 +86,67 @@ static void one_pack(int64_t T, int k, int E, int W, size_t R) {
     free(tok); free(send); free(out); free(ids); free(perm); free(splits); free(counts);
 }
 
+/* pack on every rank, regroup each rank's received rows to expert-major and
+ * back, on buffers of exactly the received size */
+static void one_regroup(int W, int E, size_t R) {
+    int64_t *counts = malloc(sizeof(int64_t) * W * E);
+    const int P = E / W;
+    for (int i = 0; i < W * E; i++) counts[i] = (int64_t)(next_u64() % 5);
+    for (int d = 0; d < W; d++) {
+        int64_t n = 0;
+        for (int s = 0; s < W; s++)
+            for (int j = 0; j < P; j++) n += counts[s * E + d * P + j];
+        unsigned char *in = malloc(n * R + 1), *mid = malloc(n * R + 1), *back = malloc(n * R + 1);
+        int64_t *eoff = malloc(sizeof(int64_t) * (P + 1));
+        for (int64_t b = 0; b < n * (int64_t)R; b++) in[b] = (unsigned char)next_u64();
+        CHECK(ref_moe_regroup(W, E, d, R, counts, in, n, mid, n, eoff, 0) == 0);
+        CHECK(eoff[P] == n);
+        CHECK(ref_moe_regroup(W, E, d, R, counts, mid, n, back, n, eoff, 1) == 0);
+        CHECK(n == 0 || memcmp(in, back, n * R) == 0);
+        if (n > 0) {
+            CHECK(ref_moe_regroup(W, E, d, R, counts, in, n - 1, mid, n, eoff, 0) == REF_SEND_OVERRUN);
+            CHECK(ref_moe_regroup(W, E, d, R, counts, in, n, mid, n - 1, eoff, 0) == REF_RECV_OVERFLOW);
+        }
+        free(in); free(mid); free(back); free(eoff);
+    }
+    free(counts);
+}
+
+static void one_combine(int64_t T, int k, int64_t H) {
+    const int64_t Q = T * k;
+    uint16_t *back = malloc(sizeof(uint16_t) * (Q * H + 1)), *out = malloc(sizeof(uint16_t) * (T * H + 1));
+    int64_t *perm = malloc(sizeof(int64_t) * (Q + 1));
+    float *w = malloc(sizeof(float) * (Q + 1));
+    for (int64_t i = 0; i < Q * H; i++) back[i] = (uint16_t)next_u64();  /* any bits, NaNs too */
+    for (int64_t q = 0; q < Q; q++) { perm[q] = q; w[q] = (float)(next_u64() % 1000) / 999.0f; }
+    for (int64_t q = Q - 1; q > 0; q--) {
+        int64_t r = (int64_t)(next_u64() % (uint64_t)(q + 1)), t = perm[q];
+        perm[q] = perm[r]; perm[r] = t;
+    }
+    CHECK(ref_moe_combine(T, k, H, back, perm, w, out) == 0);
+    if (Q > 0) {
+        perm[Q - 1] = Q;
+        CHECK(ref_moe_combine(T, k, H, back, perm, w, out) == REF_BAD_PERM);
+    }
+    free(back); free(out); free(perm); free(w);
+}
+
+static void one_bucketize(int W, int n_tables, int64_t batch) {
+    const int64_t nl = (int64_t)n_tables * batch;
+    int32_t *len = malloc(sizeof(int32_t) * (nl + 1)), *lo = malloc(sizeof(int32_t) * (nl + 1));
+    int64_t n = 0;
+    for (int64_t i = 0; i < nl; i++) { len[i] = (int32_t)(next_u64() % 7); n += len[i]; }
+    int64_t *keys = malloc(sizeof(int64_t) * (n + 1)), *ko = malloc(sizeof(int64_t) * (n + 1));
+    int64_t *sk = malloc(sizeof(int64_t) * W), *sl = malloc(sizeof(int64_t) * W);
+    for (int64_t i = 0; i < n; i++) keys[i] = (int64_t)(next_u64() >> 1);
+    CHECK(ref_keys_bucketize(W, n_tables, batch, len, keys, n, lo, ko, sk, sl) == 0);
+    int64_t tk = 0, tl = 0;
+    for (int d = 0; d < W; d++) { tk += sk[d]; tl += sl[d]; }
+    CHECK(tk == n && tl == nl);
+    if (n > 0) CHECK(ref_keys_bucketize(W, n_tables, batch, len, keys, n - 1, lo, ko, sk, sl) == REF_SEND_OVERRUN);
+    free(len); free(lo); free(keys); free(ko); free(sk); free(sl);
+}
+
 int main(void) {
     const size_t widths[] = {1, 3, 8, 16, 100};
     for (int W = 1; W <= 9; W++)
@@ -97,6 +158,15 @@ int main(void) {
     one_pack(333, 3, 12, 4, 5);
     one_pack(1, 1, 1, 1, 1);
     one_pack(0, 2, 8, 2, 4);
+    one_regroup(8, 256, 16);
+    one_regroup(3, 12, 7);
+    one_regroup(1, 1, 1);
+    one_combine(50, 8, 33);
+    one_combine(0, 2, 4);
+    one_combine(7, 1, 1);
+    one_bucketize(8, 26, 64);
+    one_bucketize(3, 2, 0);
+    one_bucketize(5, 0, 10);
     printf("oracle sanitized: ok\n");
     return 0;
 }

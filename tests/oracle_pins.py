@@ -320,18 +320,62 @@ def pin_moe_errors(o):
 
 
 # ------------------------------------------------------------------ embedding keys
+def _tables_by_owner(W, tables):
+    """Table order after bucketing, written as a sort: by (t mod W, t)."""
+    return sorted(range(tables), key=lambda t: (t % W, t))
+
+
+def _bucketize_numpy(W, lengths, keys):
+    """Independent formulation of the bucketing: split the keys per table with
+    a cumulative sum, reorder tables with a sort, concatenate."""
+    tables, batch = lengths.shape
+    per_table = lengths.sum(axis=1)
+    bounds = np.concatenate([[0], np.cumsum(per_table)])
+    order = _tables_by_owner(W, tables)
+    lo = np.concatenate([lengths[t] for t in order]) if tables else np.zeros(0, np.int32)
+    ko = (np.concatenate([keys[bounds[t]:bounds[t + 1]] for t in order])
+          if tables else np.zeros(0, np.int64))
+    sk = np.bincount(np.arange(tables) % W, weights=per_table, minlength=W).astype(np.int64)
+    sl = np.bincount(np.arange(tables) % W, minlength=W).astype(np.int64) * batch
+    return lo, ko, sk, sl
+
+
+def pin_keys_bucketize_is_sort_by_owner(o):
+    from embeddings_a2av_virtual_amd.inputs import emb_keys_rank
+    g = np.random.default_rng(25)
+    for W, tables, batch in ((8, 26, 64), (4, 7, 16), (3, 1, 5), (5, 3, 0), (1, 4, 9), (6, 0, 4)):
+        r = emb_keys_rank(g, tables=tables, batch=batch)
+        st, lo, ko, sk, sl = o.keys_bucketize(W, tables, batch, r.lengths, r.keys)
+        assert st == 0
+        wlo, wko, wsk, wsl = _bucketize_numpy(W, r.lengths, r.keys)
+        assert np.array_equal(lo, wlo), "lengths order"
+        assert np.array_equal(ko[:wko.size], wko), "keys order"
+        assert np.array_equal(sk, wsk) and np.array_equal(sl, wsl), "splits"
+        assert sk.sum() == r.keys.size and sl.sum() == tables * batch
+    # errors: a negative length, keys shorter than the lengths say
+    r = emb_keys_rank(g, tables=4, batch=8)
+    bad = r.lengths.copy(); bad[2, 3] = -1
+    assert o.keys_bucketize(4, 4, 8, bad, r.keys)[0] == R.BAD_SPLIT
+    assert o.keys_bucketize(4, 4, 8, r.lengths, r.keys[:-1])[0] == R.SEND_OVERRUN
+    more = np.concatenate([r.keys, [7, 7]])  # spare keys are allowed and not sent
+    st, lo, ko, sk, sl = o.keys_bucketize(4, 4, 8, r.lengths, more)
+    assert st == 0 and sk.sum() == r.keys.size
+
+
 def pin_emb_two_call_consistency(o):
-    """Keys and lengths exchanged as two calls: for every (d, s) the received
-    lengths chunk sums to the keys chunk received from s, and keys received
-    from s are exactly the keys that s laid out for d's tables."""
+    """Keys and lengths bucketed, then exchanged as two calls: for every
+    (d, s) the received lengths chunk sums to the keys chunk received from s,
+    and the keys received from s are s's keys of the tables d owns."""
     from embeddings_a2av_virtual_amd.inputs import emb_keys_rank
     g = np.random.default_rng(24)
     W, tables, batch = 4, 7, 16
-    ranks = [emb_keys_rank(g, W=W, tables=tables, batch=batch) for _ in range(W)]
-    Sk = np.stack([r.split_keys for r in ranks]).astype(np.int64)
-    Sl = np.stack([r.split_lengths for r in ranks]).astype(np.int64)
-    keys = [r.keys.view(np.uint8).reshape(-1, 8) for r in ranks]
-    lens = [r.lengths.view(np.uint8).reshape(-1, 4) for r in ranks]
+    ranks = [emb_keys_rank(g, tables=tables, batch=batch) for _ in range(W)]
+    buck = [o.keys_bucketize(W, tables, batch, r.lengths, r.keys) for r in ranks]
+    assert all(b[0] == 0 for b in buck)
+    Sk = np.stack([b[3] for b in buck])
+    Sl = np.stack([b[4] for b in buck])
+    keys = [b[2].view(np.uint8).reshape(-1, 8) for b in buck]
+    lens = [b[1].view(np.uint8).reshape(-1, 4) for b in buck]
     st, Yk, Ok, _, rok = run_a2av(o, 8, keys, Sk)
     assert st == 0
     st, Yl, Ol, _, rol = run_a2av(o, 4, lens, Sl)
@@ -340,19 +384,180 @@ def pin_emb_two_call_consistency(o):
         lv = Yl[d].reshape(-1).view(np.int32)
         kv = Yk[d].reshape(-1).view(np.int64)
         for s in range(W):
-            chunk_lens = lv[rol[d, s]:rol[d, s + 1]]
-            assert chunk_lens.sum() == Ok[d, s]
-            # the keys of s's tables owned by d, in table then sample order
-            off = 0
-            mine = []
-            for p, t in enumerate(ranks[s].table_order):
-                n_t = int(ranks[s].lengths[p * batch:(p + 1) * batch].sum())
-                if t % W == d:
-                    mine.append(ranks[s].keys[off:off + n_t])
-                off += n_t
+            assert lv[rol[d, s]:rol[d, s + 1]].sum() == Ok[d, s]
+            bounds = np.concatenate([[0], np.cumsum(ranks[s].lengths.sum(axis=1))])
+            mine = [ranks[s].keys[bounds[t]:bounds[t + 1]] for t in range(d, tables, W)]
             want = np.concatenate(mine) if mine else np.zeros(0, np.int64)
             assert np.array_equal(kv[rok[d, s]:rok[d, s + 1]], want)
     assert sum(int(r.keys.size) for r in ranks) == int(rok[:, W].sum())
+
+
+# ------------------------------------------------------------------ expert regroup
+def _regroup_by_sort(W, E, d, R, counts, inp):
+    """Independent formulation: tag every source-major row with (source,
+    owned expert) by walking the counts, then stable-sort the rows by expert."""
+    P = E // W
+    tags = []
+    for s in range(W):
+        for j in range(P):
+            tags += [(j, s)] * int(counts[s, d * P + j])
+    rows = inp.reshape(-1, R)[:len(tags)]
+    order = sorted(range(len(tags)), key=lambda i: tags[i][0])  # sorted() is stable
+    return rows[order].reshape(-1) if tags else np.zeros(0, np.uint8)
+
+
+def pin_moe_regroup_is_stable_sort_by_expert(o):
+    g = np.random.default_rng(26)
+    for W, E, Rb in ((4, 16, 8), (8, 256, 4), (1, 3, 5), (3, 3, 2), (2, 8, 1)):
+        counts = g.integers(0, 6, size=(W, E)).astype(np.int64)
+        counts[g.random((W, E)) < 0.3] = 0
+        P = E // W
+        for d in range(W):
+            total = int(counts[:, d * P:(d + 1) * P].sum())
+            inp = g.integers(0, 256, size=total * Rb + 3 * Rb, dtype=np.uint8)
+            st, out, eoff = o.moe_regroup(W, E, d, Rb, counts, inp, total + 3, total + 1, 0)
+            assert st == 0
+            assert np.array_equal(out[:total * Rb], _regroup_by_sort(W, E, d, Rb, counts, inp))
+            assert not out[total * Rb:].any(), "bytes past the total were written"
+            col = counts[:, d * P:(d + 1) * P].sum(axis=0)
+            assert np.array_equal(eoff, np.concatenate([[0], np.cumsum(col)]))
+            st, back, eoff2 = o.moe_regroup(W, E, d, Rb, counts, out, total, total, 1)
+            assert st == 0 and np.array_equal(back, inp[:total * Rb]), "inverse"
+            assert np.array_equal(eoff2, eoff)
+    counts = np.ones((2, 4), np.int64)
+    inp = np.zeros(64, np.uint8)
+    assert o.moe_regroup(2, 4, 0, 4, counts, inp, 3, 16, 0)[0] == R.SEND_OVERRUN
+    assert o.moe_regroup(2, 4, 0, 4, counts, inp, 16, 3, 0)[0] == R.RECV_OVERFLOW
+    neg = counts.copy(); neg[1, 1] = -1
+    assert o.moe_regroup(2, 4, 0, 4, neg, inp, 16, 16, 0)[0] == R.BAD_SPLIT
+    assert o.moe_regroup(2, 4, 1, 4, neg, inp, 16, 16, 0)[0] == 0  # not an owned column
+
+
+def pin_moe_dispatch_regroup_closed_form(o):
+    """pack -> a2av -> regroup: rank d's rows of expert e are the tokens routed
+    to e by rank 0, then rank 1, ..., each in (token, slot) order."""
+    g = np.random.default_rng(27)
+    W, T, k, E, R_bytes = 4, 30, 3, 12, 6
+    toks, idss, sends, counts, S = [], [], [], [], np.zeros((W, W), np.int64)
+    for r in range(W):
+        tokens, ids = _moe_case(g, T, k, E, R_bytes, distinct=True)
+        st, send, perm, splits, cnt = o.moe_pack(T, k, E, W, R_bytes, tokens, ids)
+        assert st == 0
+        toks.append(tokens); idss.append(ids); sends.append(send.reshape(-1, R_bytes))
+        counts.append(cnt); S[r] = splits
+    counts = np.stack(counts)
+    st, Y, O, _, ro = run_a2av(o, R_bytes, sends, S)
+    assert st == 0
+    P = E // W
+    for d in range(W):
+        total = int(ro[d, W])
+        st, out, eoff = o.moe_regroup(W, E, d, R_bytes, counts, Y[d], total, total, 0)
+        assert st == 0
+        out = out.reshape(-1, R_bytes)
+        for j in range(P):
+            e = d * P + j
+            want = [toks[s][t] for s in range(W) for t in range(T) for jj in range(k)
+                    if idss[s][t, jj] == e]
+            got = out[eoff[j]:eoff[j + 1]]
+            assert len(want) == got.shape[0]
+            assert np.array_equal(got, np.array(want, np.uint8).reshape(-1, R_bytes))
+
+
+# ------------------------------------------------------------------ gate-weighted combine
+def _round_f32(x):
+    """A Fraction rounded to the nearest binary32, ties to even (finite, in
+    range): the rounding step of an IEEE fused multiply-add, from its
+    definition."""
+    from fractions import Fraction
+    import math
+    if x == 0:
+        return 0.0
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)                      # subnormals share the smallest exponent
+    q = a / Fraction(2) ** (e - 23)       # 24 significant bits
+    n = q.numerator // q.denominator
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * float(Fraction(n) * Fraction(2) ** (e - 23))
+
+
+def _bf16_bits_to_f32(b):
+    return (np.asarray(b, np.uint32) << 16).view(np.float32)
+
+
+def pin_moe_combine_is_exact_fma_chain(o):
+    """Each output element against the fma chain evaluated in exact rational
+    arithmetic with a round-to-nearest-even after every step, then rounded to
+    bfloat16 by torch (its own float32 -> bfloat16 conversion)."""
+    import torch
+    from fractions import Fraction
+    g = np.random.default_rng(28)
+    for T, k, H in ((5, 3, 7), (3, 8, 4), (2, 1, 9)):
+        back = torch.randn(T * k, H).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        perm = g.permutation(T * k).astype(np.int64)
+        w = g.random((T, k)).astype(np.float32) * 2 - 0.5
+        st, out = o.moe_combine(T, k, H, back, perm, w)
+        assert st == 0
+        xf = _bf16_bits_to_f32(back)
+        want = np.zeros((T, H), np.float32)
+        for t in range(T):
+            for h in range(H):
+                acc = 0.0
+                for j in range(k):
+                    acc = _round_f32(Fraction(float(w[t, j])) * Fraction(float(xf[perm[t * k + j], h]))
+                                     + Fraction(acc))
+                want[t, h] = acc
+        wb = torch.from_numpy(want).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(out, wb)
+
+
+def pin_moe_combine_special_cases(o):
+    g = np.random.default_rng(29)
+    T, k, H = 6, 4, 16
+    back = g.integers(0, 0x7F80, size=(T * k, H)).astype(np.uint16)  # finite, >= +0
+    perm = g.permutation(T * k).astype(np.int64)
+    # one-hot weights copy the chosen row exactly
+    w = np.zeros((T, k), np.float32)
+    pick = g.integers(0, k, size=T)
+    w[np.arange(T), pick] = 1.0
+    st, out = o.moe_combine(T, k, H, back, perm, w)
+    assert st == 0
+    for t in range(T):
+        assert np.array_equal(out[t], back[perm[t * k + pick[t]]])
+    # infinities and NaN propagate; NaN comes out quiet
+    b2 = back.copy()
+    b2[perm[0]] = 0x7F80          # +inf in slot 0 of token 0
+    b2[perm[k]] = 0x7FA0          # a signalling NaN in slot 0 of token 1
+    w2 = np.full((T, k), 0.25, np.float32)
+    st, out = o.moe_combine(T, k, H, b2, perm, w2)
+    assert st == 0
+    assert np.all(out[0] == 0x7F80)
+    assert np.all((out[1] & 0x7F80) == 0x7F80) and np.all(out[1] & 0x0040)
+    # zero weights over finite rows give +0 exactly
+    st, out = o.moe_combine(T, k, H, back, perm, np.zeros((T, k), np.float32))
+    assert st == 0 and not out.any()
+    # the order of the chain matters: 2^30 - 2^30 + 1 is 1 in slot order, while
+    # 1 - 2^30 rounds to -2^30 in float32, so the reverse order gives 0
+    ident = np.arange(3, dtype=np.int64)
+    b3 = np.array([[0x4E80], [0xCE80], [0x3F80]], np.uint16)   # 2^30, -2^30, 1
+    st, out = o.moe_combine(1, 3, 1, b3, ident, np.ones((1, 3), np.float32))
+    assert st == 0 and out[0, 0] == 0x3F80
+    # each step is one fused multiply-add: (1 + 2^-23)(1 + 2^-7) carries a 2^-30
+    # term that a rounded product would lose before it cancels against slot 0
+    b4 = np.array([[0x3F81], [0x3F81]], np.uint16)             # 1 + 2^-7, twice
+    w4 = np.array([[-(1 + 2.0 ** -23), 1 + 2.0 ** -23]], np.float32)
+    st, out = o.moe_combine(1, 2, 1, b4, ident[:2].copy(), w4)
+    assert st == 0 and out[0, 0] == 0x3080                     # 2^-30
+    # bad permutation entry
+    p2 = perm.copy(); p2[3] = T * k
+    assert o.moe_combine(T, k, H, back, p2, w)[0] == R.BAD_PERM
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -222,11 +222,15 @@ def test_embedding_key_exchange_full(ref):
     keys (8-byte rows) and lengths (4-byte rows) as two a2av calls."""
     W = 8
     g = I.rng(88)
-    ranks = [I.emb_keys_rank(g, W=W) for _ in range(W)]
-    Sk = np.stack([r.split_keys for r in ranks])
-    Sl = np.stack([r.split_lengths for r in ranks])
-    keys = [r.keys.view(np.uint8).reshape(-1, 8) for r in ranks]
-    lens = [r.lengths.view(np.uint8).reshape(-1, 4) for r in ranks]
+    ranks = [I.emb_keys_rank(g) for _ in range(W)]
+    # the owner-order layout comes from the oracle's bucketing here, so this
+    # test isolates the two exchanges
+    bk = [ref.keys_bucketize(W, 26, 8192, r.lengths, r.keys) for r in ranks]
+    assert all(b[0] == 0 for b in bk)
+    Sk = np.stack([b[3] for b in bk])
+    Sl = np.stack([b[4] for b in bk])
+    keys = [b[2].view(np.uint8).reshape(-1, 8) for b in bk]
+    lens = [b[1].view(np.uint8).reshape(-1, 4) for b in bk]
     _say("emb keys per rank", [k.shape[0] for k in keys])
     gk = gpu_a2av(8, keys, Sk)
     gl = gpu_a2av(4, lens, Sl)

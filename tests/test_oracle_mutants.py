@@ -57,6 +57,27 @@ MUTANTS = {
         ("*src_row = send_start + (j - recv_start);", "*src_row = (j - recv_start); (void)send_start;", 0)],
     "bad_expert_upper_bound": [("if (ids[q] < 0 || ids[q] >= E) return REF_BAD_EXPERT;",
                                 "if (ids[q] < 0 || ids[q] > E) return REF_BAD_EXPERT;", 0)],
+    "regroup_drops_earlier_sources": [
+        ("for (int s2 = 0; s2 < s; s2++) expert_major += counts[s2 * E + d * P + j];",
+         "(void)0;", 0)],
+    "regroup_directions_swapped": [
+        ("const int64_t from = direction == 0 ? src_major : expert_major;",
+         "const int64_t from = direction == 1 ? src_major : expert_major;", 0),
+        ("const int64_t to = direction == 0 ? expert_major : src_major;",
+         "const int64_t to = direction == 1 ? expert_major : src_major;", 0)],
+    "combine_unfused_multiply_add": [
+        ("acc = fmaf(w[t * k + j], bf16_to_float(back[row * H + h]), acc);",
+         "acc = w[t * k + j] * bf16_to_float(back[row * H + h]) + acc;", 0)],
+    "combine_reverse_order": [
+        ("for (int j = 0; j < k; j++) {\n                const int64_t row = perm[t * k + j];",
+         "for (int j = k - 1; j >= 0; j--) {\n                const int64_t row = perm[t * k + j];", 0)],
+    "combine_truncates_to_bf16": [
+        ("return (uint16_t)((u + 0x7FFFu + lsb) >> 16);", "(void)lsb; return (uint16_t)(u >> 16);", 0)],
+    "bucketize_reads_keys_at_output_position": [
+        ("memcpy(keys_out + kpos, keys + tstart[t], (size_t)tk[t] * 8);",
+         "memcpy(keys_out + kpos, keys + kpos, (size_t)tk[t] * 8);", 0)],
+    "bucketize_length_split_counts_keys": [
+        ("split_lengths[d] += batch;", "split_lengths[d] += tk[t];", 0)],
 }
 
 # cheap pins first; the brute-force enumeration last

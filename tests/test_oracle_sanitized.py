@@ -12,9 +12,9 @@ ROOT = os.path.dirname(HERE)
 def test_oracle_under_sanitizers(tmp_path):
     exe = tmp_path / "oracle_asan"
     cmd = ["gcc", "-std=c11", "-O1", "-g", "-fno-omit-frame-pointer",
-           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-ffp-contract=off",
            "-I", os.path.join(ROOT, "oracle"), os.path.join(ROOT, "oracle", "a2av_ref.c"),
-           os.path.join(HERE, "oracle_asan_driver.c"), "-o", str(exe)]
+           os.path.join(HERE, "oracle_asan_driver.c"), "-o", str(exe), "-lm"]
     try:
         subprocess.run(cmd, check=True, capture_output=True, text=True)
     except subprocess.CalledProcessError as e:
