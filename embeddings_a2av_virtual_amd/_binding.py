@@ -23,7 +23,9 @@ __all__ = [
     "ST_BAD_PERM",
     "a2av_abi_version", "a2av_strerror", "a2av_exchange_splits", "a2av_offsets", "a2av_copy",
     "a2av_all_to_all_vdev",
-    "moe_pack_workspace_bytes", "moe_pack", "moe_unpack", "a2av_device_copy",
+    "moe_pack_workspace_bytes", "moe_pack", "moe_unpack", "moe_combine",
+    "moe_regroup_workspace_bytes", "moe_regroup", "keys_bucketize_workspace_bytes",
+    "keys_bucketize", "a2av_device_copy", "MAX_TABLES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liba2av.so")
@@ -32,6 +34,7 @@ OK, EARG, EHIP = 0, -1, -2
 MAX_W = 64
 MAX_SPLIT = 1 << 40
 MAX_EXPERTS = 4096
+MAX_TABLES = 4096
 ST_BAD_SPLIT = 1
 ST_SEND_OVERRUN = 2
 ST_RECV_OVERFLOW = 4
@@ -71,9 +74,18 @@ def lib():
         L.moe_pack_workspace_bytes.restype = sz
         L.moe_pack.argtypes = [i32, i64, i32, i32, sz, vpp, vpp, vpp, vpp, vp, vp, vp, sz, vp, vp]
         L.moe_unpack.argtypes = [i32, i64, i32, sz, vpp, vpp, vpp, vp, vp]
+        L.moe_combine.argtypes = [i32, i64, i32, i64, vpp, vpp, vpp, vpp, vp, vp]
+        L.moe_regroup_workspace_bytes.argtypes = [i32, i32]
+        L.moe_regroup_workspace_bytes.restype = sz
+        L.moe_regroup.argtypes = [i32, i32, sz, vp, vpp, i64p, vpp, i64p, vp, i32, vp, sz, vp, vp]
+        L.keys_bucketize_workspace_bytes.argtypes = [i32, i32]
+        L.keys_bucketize_workspace_bytes.restype = sz
+        L.keys_bucketize.argtypes = [i32, i32, i64, vpp, vpp, i64p, vpp, vpp, vp, vp, vp, sz, vp,
+                                     vp]
         L.a2av_device_copy.argtypes = [vp, vp, sz, vp]
         for f in ("a2av_exchange_splits", "a2av_offsets", "a2av_copy", "a2av_all_to_all_vdev",
-                  "moe_pack", "moe_unpack", "a2av_device_copy"):
+                  "moe_pack", "moe_unpack", "moe_combine", "moe_regroup", "keys_bucketize",
+                  "a2av_device_copy"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -191,6 +203,53 @@ def moe_unpack(W, T, k, row_bytes, back, perm, out, status, stream=None):
            lib().moe_unpack(int(W), int(T), int(k), int(row_bytes), _ptr_array(back, "back"),
                             _ptr_array(perm, "perm"), _ptr_array(out, "out"),
                             _dev(status, "status"), _stream(stream, status)))
+
+
+def moe_combine(W, T, k, H, back, perm, weights, out, status, stream=None):
+    """Gate-weighted combine: out[r][t] = bf16(fma chain over j of
+    weights[r][t][j] * back[r][perm[r][t*k+j]]), in slot order."""
+    _check("moe_combine",
+           lib().moe_combine(int(W), int(T), int(k), int(H), _ptr_array(back, "back"),
+                             _ptr_array(perm, "perm"), _ptr_array(weights, "weights"),
+                             _ptr_array(out, "out"), _dev(status, "status"),
+                             _stream(stream, status)))
+
+
+def moe_regroup_workspace_bytes(W, E) -> int:
+    return int(lib().moe_regroup_workspace_bytes(int(W), int(E)))
+
+
+def moe_regroup(W, E, row_bytes, counts, ins, in_rows, outs, out_cap_rows, expert_offsets,
+                direction, workspace, status, stream=None):
+    """Per-rank regroup between (source, expert) and (expert, source) row order."""
+    if len(ins) != W or len(outs) != W or len(in_rows) != W or len(out_cap_rows) != W:
+        raise ValueError("ins, outs, in_rows and out_cap_rows need W entries each")
+    _check("moe_regroup",
+           lib().moe_regroup(int(W), int(E), int(row_bytes), _dev(counts, "counts"),
+                             _ptr_array(ins, "ins"), _i64_array(in_rows), _ptr_array(outs, "outs"),
+                             _i64_array(out_cap_rows), _dev(expert_offsets, "expert_offsets"),
+                             int(direction), _dev(workspace, "workspace"),
+                             workspace.numel() * workspace.element_size(),
+                             _dev(status, "status"), _stream(stream, status)))
+
+
+def keys_bucketize_workspace_bytes(W, n_tables) -> int:
+    return int(lib().keys_bucketize_workspace_bytes(int(W), int(n_tables)))
+
+
+def keys_bucketize(W, n_tables, batch, lengths, keys, n_keys, lengths_out, keys_out, split_keys,
+                   split_lengths, workspace, status, stream=None):
+    """Owner-order bucketing of every rank's jagged keys (table t -> rank t mod W)."""
+    if len(lengths) != W or len(keys) != W or len(n_keys) != W:
+        raise ValueError("lengths, keys and n_keys need W entries each")
+    _check("keys_bucketize",
+           lib().keys_bucketize(int(W), int(n_tables), int(batch), _ptr_array(lengths, "lengths"),
+                                _ptr_array(keys, "keys"), _i64_array(n_keys),
+                                _ptr_array(lengths_out, "lengths_out"),
+                                _ptr_array(keys_out, "keys_out"), _dev(split_keys, "split_keys"),
+                                _dev(split_lengths, "split_lengths"), _dev(workspace, "workspace"),
+                                workspace.numel() * workspace.element_size(),
+                                _dev(status, "status"), _stream(stream, status)))
 
 
 def a2av_device_copy(dst, src, nbytes, stream=None):

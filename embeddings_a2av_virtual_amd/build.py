@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "liba2av.so")
-SOURCES = ["a2av.hip", "moe.hip"]
+SOURCES = ["a2av.hip", "moe.hip", "blocks.hip"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -25,6 +25,8 @@ FLAGS = [
     "-shared",
     "-fvisibility=hidden",
     "-Wall",
+    # fp32 subnormals kept: the combine's results are defined bit for bit
+    "-fno-gpu-flush-denormals-to-zero",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",

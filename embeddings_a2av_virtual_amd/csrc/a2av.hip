@@ -326,22 +326,6 @@ __global__ __launch_bounds__(BS) void k_device_copy(unsigned char *dst, const un
 // out the unequal bandwidth that waves of different age get.
 constexpr int kWaveMaxW = 8;
 
-typedef __attribute__((address_space(4))) const int64_t const_i64;
-typedef __attribute__((address_space(4))) const int32_t const_i32;
-
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// Wave-cooperative copy of n bytes, n a multiple of 16, both ends 16-aligned.
-template <int U>
-__device__ __forceinline__ void wave_copy16(unsigned char *dst, const unsigned char *src,
-                                            uint64_t n, int lane) {
-    copy_elems<u32x4, kWave, U, true>((u32x4 *)dst, (const u32x4 *)src, n / 16, lane);
-}
-
 template <int W, int U, bool ALIGNED, int MODE>
 __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
     static_assert(W >= 1 && W <= kWaveMaxW, "one (s, d) entry per lane");

@@ -1,0 +1,554 @@
+// blocks.hip — block-permutation copies next to the a2av (gfx950): the
+// receive-side expert regroup after the MoE dispatch, and the bucketing of
+// jagged embedding keys by owning rank before the key exchange.
+//
+// Both reorder whole runs of rows ("blocks") inside each virtual rank. A
+// planning kernel writes, per rank, the blocks in destination order:
+//   dst_start[r][b]  first destination row of block b (exclusive scan, the
+//                    rank's total at b = B)
+//   src_start[r][b]  first source row of block b
+//   bits[r]          the rank's error bits (0 when it passed its checks)
+// and k_block_copy moves the bytes. The copy cuts the destination byte space
+// of all ranks (rank 0's rows, then rank 1's, ...) into equal pieces, one per
+// wave, like the a2av payload kernel; a wave finds the block holding its
+// piece with a 64-way search of dst_start (one ballot per level).
+//
+// Error protocol: a planning kernel never writes the status word (so every
+// block of it sees the word as it was when the operation began) and writes
+// its bits to the workspace; the copy kernel reads them, one wave ORs them
+// into the status word, and no byte moves when any rank failed.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "common.hpp"
+
+namespace a2av {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanPer = 4;  // blocks per planning thread: up to 4096 per rank
+
+struct BlockArgs {
+    const unsigned char *in[A2AV_MAX_W];
+    unsigned char *out[A2AV_MAX_W];
+    int64_t in_rows[A2AV_MAX_W];
+    int64_t cap[A2AV_MAX_W];
+    const int64_t *dst_start;  // [W][B + 1]
+    const int64_t *src_start;  // [W][B]
+    const int32_t *bits;       // [W]
+    int32_t *status;
+    uint64_t R;
+    uint64_t piece;
+    int W;
+    int B;
+};
+
+// Largest i in [0, n) with v[i] <= key, for v non-decreasing with v[0] <= key
+// (-1 if v[0] > key, which a valid plan never gives). One ballot per level of
+// a 64-way search: two levels cover 4096 entries.
+__device__ __forceinline__ int find_last_le(const int64_t *v, int n, uint64_t key, int lane) {
+    int lo = 0, len = n;
+    while (len > kWave) {
+        const int stride = (len + kWave - 1) / kWave;
+        const int off = lane * stride;
+        const bool ok = off < len && (uint64_t)v[lo + off] <= key;
+        const uint64_t m = __ballot(ok);
+        if (m == 0) return -1;
+        const int h = 63 - __clzll(m);
+        lo += h * stride;
+        len = stride < len - h * stride ? stride : len - h * stride;
+    }
+    const uint64_t m = __ballot(lane < len && (uint64_t)v[lo + lane] <= key);
+    if (m == 0) return -1;
+    return lo + 63 - __clzll(m);
+}
+
+template <int U, bool ALIGNED>
+__global__ __launch_bounds__(256) void k_block_copy(const BlockArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t wpb = blockDim.x / kWave;
+    const uint64_t gw = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave;
+    const uint64_t TW = (uint64_t)gridDim.x * wpb;
+    const int W = a.W, B = a.B;
+    const uint64_t R = a.R;
+
+    const int32_t st0 = *(const const_i32 *)a.status;
+    int32_t rb = 0;
+    uint64_t rows = 0;
+    if (lane < W) {
+        rb = a.bits[lane];
+        rows = (uint64_t)a.dst_start[(uint64_t)lane * (B + 1) + B];
+    }
+    if (st0) return;
+    const int32_t bad = wave_or(rb);
+    if (bad) {
+        if (gw == 0 && lane == 0) atomicOr(a.status, bad);
+        return;
+    }
+    // lane r: bytes of rank r and where they start in the flat space
+    const uint64_t bytes = rows * R;
+    const uint64_t incl = wave_incl_scan_u64(bytes);
+    const uint64_t base = incl - bytes;
+    const uint64_t total = readlane_u64(incl, kWave - 1);
+    const uint64_t piece = a.piece;
+    for (uint64_t p = gw; p * piece < total; p += TW) {
+        uint64_t x = p * piece;
+        const uint64_t hi = x + piece < total ? x + piece : total;
+        while (x < hi) {
+            // last rank starting at or before x: empty ranks share the base of
+            // the next one, so the highest match is the one holding x
+            const uint64_t md = __ballot(lane < W && base <= x);
+            const int d = 63 - __clzll(md);  // md has lane 0 (base 0)
+            const uint64_t rbase = readlane_u64(base, d);
+            const uint64_t rend = rbase + readlane_u64(bytes, d);
+            const uint64_t xr = x - rbase;
+            const uint64_t hr = (hi < rend ? hi : rend) - rbase;
+            const int64_t *ds = a.dst_start + (uint64_t)d * (B + 1);
+            const int b = find_last_le(ds, B, xr / R, lane);
+            if (b < 0) return;  // not a valid plan
+            const uint64_t r0 = (uint64_t)ds[b], r1 = (uint64_t)ds[b + 1];
+            const uint64_t s0 = (uint64_t)a.src_start[(uint64_t)d * B + b];
+            const uint64_t e = hr < r1 * R ? hr : r1 * R;
+            if (e <= xr) return;  // not a valid plan
+            // a valid plan always passes; the check keeps every access inside
+            // the caller's buffers regardless
+            if (r1 <= (uint64_t)a.cap[d] && s0 + (r1 - r0) <= (uint64_t)a.in_rows[d]) {
+                unsigned char *dst = a.out[d] + xr;
+                const unsigned char *src = a.in[d] + s0 * R + (xr - r0 * R);
+                if constexpr (ALIGNED) wave_copy16<U>(dst, src, e - xr, lane);
+                else wave_copy_any<U>(dst, src, e - xr, lane);
+            }
+            x = rbase + e;
+        }
+    }
+}
+
+// ------------------------------------------------------------ block scans
+// Exclusive scans of two sequences at once over a 1024-thread block: each
+// thread contributes its sums (va, vb) and gets the sums of the threads
+// before it; ta, tb receive the block totals.
+struct ScanLds {
+    int64_t a[kPlanThreads / kWave];
+    int64_t b[kPlanThreads / kWave];
+};
+
+__device__ __forceinline__ void block_excl_scan2(int64_t va, int64_t vb, ScanLds &l,
+                                                 int64_t *ea, int64_t *eb, int64_t *ta, int64_t *tb) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    constexpr int NW = kPlanThreads / kWave;
+    const int64_t ia = wave_incl_scan(va), ib = wave_incl_scan(vb);
+    if (lane == kWave - 1) {
+        l.a[wv] = ia;
+        l.b[wv] = ib;
+    }
+    __syncthreads();
+    int64_t pa = 0, pb = 0, sa = 0, sb = 0;
+#pragma unroll
+    for (int w = 0; w < NW; w++) {
+        const int64_t xa = l.a[w], xb = l.b[w];
+        if (w < wv) {
+            pa += xa;
+            pb += xb;
+        }
+        sa += xa;
+        sb += xb;
+    }
+    __syncthreads();  // the arrays may be reused by the caller
+    *ea = pa + ia - va;
+    *eb = pb + ib - vb;
+    *ta = sa;
+    *tb = sb;
+}
+
+// ------------------------------------------------------------ expert regroup plan
+struct RegroupPlanArgs {
+    const int64_t *counts;    // [W][E]
+    int64_t *dst_start;       // [W][E + 1]
+    int64_t *src_start;       // [W][E]
+    int32_t *bits;            // [W]
+    int64_t *expert_offsets;  // [W][P + 1]
+    const int32_t *status;
+    int64_t in_rows[A2AV_MAX_W];
+    int64_t cap[A2AV_MAX_W];
+    int W;
+    int E;
+    int direction;  // 0: (source, expert) -> (expert, source); 1: the reverse
+};
+
+// Rank d's blocks are the pairs (s, j), s a source rank and j one of the
+// P = E / W experts d owns, of counts[s][d*P + j] rows each. Source-major
+// order lists them as index s*P + j, expert-major as j*W + s.
+__global__ __launch_bounds__(kPlanThreads) void k_regroup_plan(const RegroupPlanArgs a) {
+    __shared__ ScanLds lds;
+    __shared__ int poisoned;
+    const int d = blockIdx.x, tid = threadIdx.x;
+    if (tid == 0) poisoned = *a.status != 0;
+    __syncthreads();
+    if (poisoned) return;
+    const int W = a.W, E = a.E, P = E / W;
+    const bool to_expert = a.direction == 0;
+    int64_t nd[kPlanPer], ns[kPlanPer];  // sizes in destination / source order
+    int64_t sd = 0, ss = 0;
+    int bad = 0;
+#pragma unroll
+    for (int u = 0; u < kPlanPer; u++) {
+        const int i = tid * kPlanPer + u;
+        nd[u] = ns[u] = 0;
+        if (i < E) {
+            const int sm_s = i / P, sm_j = i - (i / P) * P;  // i read source-major
+            const int em_j = i / W, em_s = i - (i / W) * W;  // i read expert-major
+            const int64_t c_sm = a.counts[(int64_t)sm_s * E + d * P + sm_j];
+            const int64_t c_em = a.counts[(int64_t)em_s * E + d * P + em_j];
+            bad |= (int)split_invalid(c_sm);
+            nd[u] = to_expert ? c_em : c_sm;
+            ns[u] = to_expert ? c_sm : c_em;
+        }
+        sd += nd[u];
+        ss += ns[u];
+    }
+    if (__syncthreads_or(bad)) {
+        if (tid == 0) a.bits[d] = A2AV_ST_BAD_SPLIT;
+        return;
+    }
+    int64_t ed, es, total, total2;
+    block_excl_scan2(sd, ss, lds, &ed, &es, &total, &total2);
+    int32_t bits = 0;
+    if (total > a.in_rows[d]) bits |= A2AV_ST_SEND_OVERRUN;
+    if (total > a.cap[d]) bits |= A2AV_ST_RECV_OVERFLOW;
+    int64_t *dst = a.dst_start + (int64_t)d * (E + 1);
+    int64_t *src = a.src_start + (int64_t)d * E;
+    int64_t *eoff = a.expert_offsets + (int64_t)d * (P + 1);
+#pragma unroll
+    for (int u = 0; u < kPlanPer; u++) {
+        const int i = tid * kPlanPer + u;
+        if (i < E) {
+            dst[i] = ed;
+            // source-order index i is the block (s, j); its destination index
+            const int b = to_expert ? (i - (i / P) * P) * W + i / P    // s*P+j -> j*W+s
+                                    : (i - (i / W) * W) * P + i / W;   // j*W+s -> s*P+j
+            src[b] = es;
+            if (bits == 0 && i % W == 0) eoff[i / W] = to_expert ? ed : es;
+        }
+        ed += nd[u];
+        es += ns[u];
+    }
+    if (tid == 0) {
+        dst[E] = total;
+        if (bits == 0) eoff[P] = total;
+        a.bits[d] = bits;
+    }
+}
+
+// ------------------------------------------------------------ key bucketing
+struct BucketArgs {
+    const int32_t *lengths[A2AV_MAX_W];  // [n_tables][batch] per rank
+    int64_t n_keys[A2AV_MAX_W];
+    int64_t *tk;            // [W][n_tables] keys per table, -1 for a negative length
+    int64_t *kdst;          // [W][n_tables + 1] plan of the keys
+    int64_t *ksrc;          // [W][n_tables]
+    int64_t *ldst;          // [W][n_tables + 1] plan of the lengths
+    int64_t *lsrc;          // [W][n_tables]
+    int32_t *bits;          // [W]
+    int64_t *split_keys;    // [W][W]
+    int64_t *split_lengths; // [W][W]
+    const int32_t *status;
+    int64_t batch;
+    int W;
+    int n_tables;
+};
+
+// One block per (table, rank): the table's key count, or -1 when a length is
+// negative.
+__global__ __launch_bounds__(256) void k_bucket_sums(const BucketArgs a) {
+    __shared__ int64_t part[256 / kWave];
+    __shared__ int neg[256 / kWave];
+    const int t = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+    const int32_t *L = a.lengths[r] + (int64_t)t * a.batch;
+    int64_t s = 0;
+    int n = 0;
+    for (int64_t i = tid; i < a.batch; i += 256) {
+        const int32_t v = L[i];
+        s += v;
+        n |= v < 0;
+    }
+    s = wave_incl_scan(s);
+    n = __ballot(n) != 0;
+    if ((tid & (kWave - 1)) == kWave - 1) {
+        part[tid / kWave] = s;
+        neg[tid / kWave] = n;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int64_t tot = 0;
+        int ng = 0;
+        for (int w = 0; w < 256 / kWave; w++) {
+            tot += part[w];
+            ng |= neg[w];
+        }
+        a.tk[(int64_t)r * a.n_tables + t] = ng ? -1 : tot;
+    }
+}
+
+// One block per rank: table t goes to rank t mod W; destination order is
+// owner-major, tables ascending inside an owner, so table t sits at position
+// (tables owned by ranks < t mod W) + t / W.
+__global__ __launch_bounds__(kPlanThreads) void k_bucket_plan(const BucketArgs a) {
+    __shared__ ScanLds lds;
+    __shared__ int poisoned;
+    __shared__ unsigned long long owner_keys[A2AV_MAX_W];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const int W = a.W, NT = a.n_tables;
+    if (tid == 0) poisoned = *a.status != 0;
+    if (tid < A2AV_MAX_W) owner_keys[tid] = 0;
+    __syncthreads();
+    if (poisoned) return;
+    const int64_t *tk = a.tk + (int64_t)r * NT;
+    // by position in destination order: the table there, its key count
+    int64_t nd[kPlanPer], nt[kPlanPer];
+    int64_t sd = 0, st = 0;
+    int bad = 0;
+#pragma unroll
+    for (int u = 0; u < kPlanPer; u++) {
+        const int i = tid * kPlanPer + u;
+        nd[u] = nt[u] = 0;
+        if (i < NT) {
+            // the table at position i: owner o is the largest with first(o) <= i,
+            // first(o) = sum over o' < o of ceil((NT - o') / W)
+            int o = 0, first = 0;
+            while (o + 1 < W) {
+                const int cnt = (NT - o + W - 1) / W;
+                if (first + cnt > i) break;
+                first += cnt;
+                o++;
+            }
+            const int t = o + (i - first) * W;
+            nd[u] = tk[t];
+            nt[u] = tk[i];  // table order, for the source starts
+            bad |= nt[u] < 0;
+        }
+        sd += nd[u];
+        st += nt[u];
+    }
+    if (__syncthreads_or(bad)) {
+        if (tid == 0) a.bits[r] = A2AV_ST_BAD_SPLIT;
+        return;
+    }
+    int64_t ed, et, total, total2;
+    block_excl_scan2(sd, st, lds, &ed, &et, &total, &total2);
+    const int32_t bits = total > a.n_keys[r] ? A2AV_ST_SEND_OVERRUN : 0;
+    int64_t *kdst = a.kdst + (int64_t)r * (NT + 1);
+    int64_t *ksrc = a.ksrc + (int64_t)r * NT;
+    int64_t *ldst = a.ldst + (int64_t)r * (NT + 1);
+    int64_t *lsrc = a.lsrc + (int64_t)r * NT;
+#pragma unroll
+    for (int u = 0; u < kPlanPer; u++) {
+        const int i = tid * kPlanPer + u;
+        if (i < NT) {
+            kdst[i] = ed;
+            ldst[i] = (int64_t)i * a.batch;
+            // table i (table order) starts at et in the input; its position
+            const int o = i % W;
+            int first = 0;
+            for (int o2 = 0; o2 < o; o2++) first += (NT - o2 + W - 1) / W;
+            const int pos = first + i / W;
+            ksrc[pos] = et;
+            lsrc[pos] = (int64_t)i * a.batch;
+            atomicAdd(&owner_keys[o], (unsigned long long)nt[u]);
+        }
+        ed += nd[u];
+        et += nt[u];
+    }
+    __syncthreads();
+    if (tid == 0) {
+        kdst[NT] = total;
+        ldst[NT] = (int64_t)NT * a.batch;
+        a.bits[r] = bits;
+    }
+    if (bits == 0 && tid < W) {
+        a.split_keys[(int64_t)r * W + tid] = (int64_t)owner_keys[tid];
+        a.split_lengths[(int64_t)r * W + tid] = (int64_t)((NT - tid + W - 1) / W) * a.batch;
+    }
+}
+
+// ------------------------------------------------------------ host side
+static void piece_policy(uint64_t bmax, int *unroll, uint64_t *piece) {
+    const bool small = bmax <= (512ull << 20);
+    *unroll = small ? 8 : 16;
+    *piece = small ? 8192 : 32768;
+}
+
+static int copy_grid(uint64_t bmax, uint64_t piece) {
+    uint64_t g = (bmax + piece * 4 - 1) / (piece * 4);  // 4 waves per block
+    if (g < 1) g = 1;  // one wave always runs, to report the planning bits
+    if (g > (1u << 22)) g = 1u << 22;  // the piece loop strides over the rest
+    return (int)g;
+}
+
+// Launch k_block_copy; bmax bounds the bytes any rank can move.
+static void launch_block_copy(const BlockArgs &a, uint64_t bmax, bool aligned, hipStream_t st) {
+    int unroll;
+    uint64_t piece;
+    piece_policy(bmax, &unroll, &piece);
+    BlockArgs b = a;
+    b.piece = piece;
+    const int grid = copy_grid(bmax, piece);
+    if (unroll == 16) {
+        if (aligned) hipLaunchKernelGGL((k_block_copy<16, true>), dim3(grid), dim3(256), 0, st, b);
+        else hipLaunchKernelGGL((k_block_copy<16, false>), dim3(grid), dim3(256), 0, st, b);
+    } else {
+        if (aligned) hipLaunchKernelGGL((k_block_copy<8, true>), dim3(grid), dim3(256), 0, st, b);
+        else hipLaunchKernelGGL((k_block_copy<8, false>), dim3(grid), dim3(256), 0, st, b);
+    }
+}
+
+static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+}  // namespace a2av
+
+using namespace a2av;
+
+A2AV_API size_t moe_regroup_workspace_bytes(int W, int E) {
+    if (W < 1 || W > A2AV_MAX_W || E < 1 || E > A2AV_MAX_EXPERTS || E % W != 0) return 0;
+    return round256((size_t)W * (2 * (size_t)E + 1) * 8) + round256((size_t)W * 4);
+}
+
+A2AV_API int moe_regroup(int W, int E, size_t row_bytes, const int64_t *counts,
+                         const void *const *in, const int64_t *in_rows, void *const *out,
+                         const int64_t *out_cap_rows, int64_t *expert_offsets, int direction,
+                         void *workspace, size_t workspace_bytes, int32_t *status,
+                         hipStream_t stream) {
+    if (W < 1 || W > A2AV_MAX_W || E < 1 || E > A2AV_MAX_EXPERTS || E % W != 0 || row_bytes == 0 ||
+        !counts || !in || !in_rows || !out || !out_cap_rows || !expert_offsets || !status ||
+        (direction != 0 && direction != 1))
+        return A2AV_EARG;
+    if (!workspace || workspace_bytes < moe_regroup_workspace_bytes(W, E)) return A2AV_EARG;
+    BlockArgs c;
+    RegroupPlanArgs p;
+    std::memset(&c, 0, sizeof(c));
+    std::memset(&p, 0, sizeof(p));
+    uint64_t bmax = 0, cap_bytes = 0;
+    bool aligned = (row_bytes % 16) == 0;
+    for (int r = 0; r < W; r++) {
+        if (in_rows[r] < 0 || out_cap_rows[r] < 0) return A2AV_EARG;
+        if ((uint64_t)in_rows[r] > (uint64_t)INT64_MAX / row_bytes ||
+            (uint64_t)out_cap_rows[r] > (uint64_t)INT64_MAX / row_bytes)
+            return A2AV_EARG;
+        if ((in_rows[r] > 0 && !in[r]) || (out_cap_rows[r] > 0 && !out[r])) return A2AV_EARG;
+        c.in[r] = (const unsigned char *)in[r];
+        c.out[r] = (unsigned char *)out[r];
+        c.in_rows[r] = p.in_rows[r] = in_rows[r];
+        c.cap[r] = p.cap[r] = out_cap_rows[r];
+        const int64_t m = in_rows[r] < out_cap_rows[r] ? in_rows[r] : out_cap_rows[r];
+        bmax += (uint64_t)m * row_bytes;
+        cap_bytes += (uint64_t)out_cap_rows[r] * row_bytes;
+        if (cap_bytes > ((uint64_t)1 << 62)) return A2AV_EARG;
+        aligned = aligned && ((uintptr_t)in[r] % 16 == 0) && ((uintptr_t)out[r] % 16 == 0);
+    }
+    unsigned char *ws = (unsigned char *)workspace;
+    int64_t *dst = (int64_t *)ws;
+    int64_t *src = dst + (size_t)W * (E + 1);
+    int32_t *bits = (int32_t *)(ws + round256((size_t)W * (2 * (size_t)E + 1) * 8));
+    p.counts = counts;
+    p.dst_start = dst;
+    p.src_start = src;
+    p.bits = bits;
+    p.expert_offsets = expert_offsets;
+    p.status = status;
+    p.W = W;
+    p.E = E;
+    p.direction = direction;
+    hipLaunchKernelGGL(k_regroup_plan, dim3(W), dim3(kPlanThreads), 0, stream, p);
+    c.dst_start = dst;
+    c.src_start = src;
+    c.bits = bits;
+    c.status = status;
+    c.R = row_bytes;
+    c.W = W;
+    c.B = E;
+    launch_block_copy(c, bmax, aligned, stream);
+    return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
+}
+
+A2AV_API size_t keys_bucketize_workspace_bytes(int W, int n_tables) {
+    if (W < 1 || W > A2AV_MAX_W || n_tables < 0 || n_tables > A2AV_MAX_TABLES) return 0;
+    const size_t nt = (size_t)n_tables;
+    return round256((size_t)W * (5 * nt + 2) * 8) + round256((size_t)W * 4);
+}
+
+A2AV_API int keys_bucketize(int W, int n_tables, int64_t batch, const int32_t *const *lengths,
+                            const int64_t *const *keys, const int64_t *n_keys,
+                            int32_t *const *lengths_out, int64_t *const *keys_out,
+                            int64_t *split_keys, int64_t *split_lengths, void *workspace,
+                            size_t workspace_bytes, int32_t *status, hipStream_t stream) {
+    if (W < 1 || W > A2AV_MAX_W || n_tables < 0 || n_tables > A2AV_MAX_TABLES || batch < 0 ||
+        !lengths || !keys || !n_keys || !lengths_out || !keys_out || !split_keys ||
+        !split_lengths || !status)
+        return A2AV_EARG;
+    if (!workspace || workspace_bytes < keys_bucketize_workspace_bytes(W, n_tables)) return A2AV_EARG;
+    if (n_tables > 0 && batch > ((int64_t)1 << 40) / n_tables) return A2AV_EARG;
+    const int64_t nl = (int64_t)n_tables * batch;
+    BucketArgs b;
+    BlockArgs ck, cl;
+    std::memset(&b, 0, sizeof(b));
+    std::memset(&ck, 0, sizeof(ck));
+    std::memset(&cl, 0, sizeof(cl));
+    uint64_t kmax = 0;
+    // the 16-byte path needs every block edge on a 16-byte boundary: never
+    // true for 8-byte keys in general, true for the lengths when batch % 4 == 0
+    const bool kal = false;
+    bool lal = (batch % 4) == 0;
+    for (int r = 0; r < W; r++) {
+        if (n_keys[r] < 0 || n_keys[r] > ((int64_t)1 << 59)) return A2AV_EARG;
+        if (nl > 0 && (!lengths[r] || !lengths_out[r])) return A2AV_EARG;
+        if (n_keys[r] > 0 && (!keys[r] || !keys_out[r])) return A2AV_EARG;
+        b.lengths[r] = lengths[r];
+        b.n_keys[r] = n_keys[r];
+        ck.in[r] = (const unsigned char *)keys[r];
+        ck.out[r] = (unsigned char *)keys_out[r];
+        ck.in_rows[r] = ck.cap[r] = n_keys[r];
+        cl.in[r] = (const unsigned char *)lengths[r];
+        cl.out[r] = (unsigned char *)lengths_out[r];
+        cl.in_rows[r] = cl.cap[r] = nl;
+        kmax += (uint64_t)n_keys[r] * 8;
+        lal = lal && ((uintptr_t)lengths[r] % 16 == 0) && ((uintptr_t)lengths_out[r] % 16 == 0);
+    }
+    const size_t nt = (size_t)n_tables;
+    int64_t *ws = (int64_t *)workspace;
+    b.tk = ws;
+    b.kdst = b.tk + (size_t)W * nt;
+    b.ksrc = b.kdst + (size_t)W * (nt + 1);
+    b.ldst = b.ksrc + (size_t)W * nt;
+    b.lsrc = b.ldst + (size_t)W * (nt + 1);
+    b.bits = (int32_t *)((unsigned char *)workspace + round256((size_t)W * (5 * nt + 2) * 8));
+    b.split_keys = split_keys;
+    b.split_lengths = split_lengths;
+    b.status = status;
+    b.batch = batch;
+    b.W = W;
+    b.n_tables = n_tables;
+    if (n_tables > 0)
+        hipLaunchKernelGGL(k_bucket_sums, dim3(n_tables, W), dim3(256), 0, stream, b);
+    hipLaunchKernelGGL(k_bucket_plan, dim3(W), dim3(kPlanThreads), 0, stream, b);
+    ck.dst_start = b.kdst;
+    ck.src_start = b.ksrc;
+    ck.bits = b.bits;
+    ck.status = status;
+    ck.R = 8;
+    ck.W = W;
+    ck.B = n_tables;
+    cl.dst_start = b.ldst;
+    cl.src_start = b.lsrc;
+    cl.bits = b.bits;
+    cl.status = status;
+    cl.R = 4;
+    cl.W = W;
+    cl.B = n_tables;
+    if (n_tables > 0) {
+        launch_block_copy(ck, kmax, kal, stream);
+        launch_block_copy(cl, (uint64_t)W * (uint64_t)nl * 4, lal, stream);
+    } else {
+        // no tables: nothing to move, but the planning bits still go out
+        launch_block_copy(ck, 0, kal, stream);
+    }
+    return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
+}

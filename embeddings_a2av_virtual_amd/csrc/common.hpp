@@ -197,6 +197,42 @@ __device__ __forceinline__ void wave_copy_any(unsigned char *dst, const unsigned
     if ((uint64_t)lane < n - done) dst[done + lane] = src[done + lane];
 }
 
+// Wave-cooperative copy of n bytes, n a multiple of 16, both ends 16-aligned.
+template <int U>
+__device__ __forceinline__ void wave_copy16(unsigned char *dst, const unsigned char *src,
+                                            uint64_t n, int lane) {
+    copy_elems<u32x4, kWave, U, true>((u32x4 *)dst, (const u32x4 *)src, n / 16, lane);
+}
+
+// ------------------------------------------------------------ wave-uniform values
+// Pointers into the constant address space: loads through them that the
+// compiler can prove uniform become scalar loads, which do not queue behind
+// the wave's vector memory traffic.
+typedef __attribute__((address_space(4))) const int64_t const_i64;
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint64_t t = __shfl_up(v, o, kWave);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int32_t wave_or(int32_t v) {
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) v |= __shfl_xor(v, o, kWave);
+    return v;
+}
+
 // ------------------------------------------------------------ host helpers
 int device_cu_count(hipStream_t stream);
 long env_long(const char *name, long dflt, long lo, long hi);

@@ -275,6 +275,142 @@ __global__ __launch_bounds__(256) void k_moe_gather(const UnpackArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ combine
+// Gate-weighted combine: out[r][t][h] = bf16( fma chain over j = 0..k-1 of
+// w[r][t][j] * back[r][perm[r][t*k+j]][h] ), accumulated in fp32 from +0 with
+// one fused multiply-add per slot, in slot order, rounded to bfloat16 to
+// nearest even at the end. One wave per (rank, token): lane j of the wave
+// holds perm and weight of slot j, and every lane owns 8 consecutive elements
+// (16 bytes) of the token's row per vector step.
+struct CombineArgs {
+    const unsigned char *back[A2AV_MAX_W];
+    const int64_t *perm[A2AV_MAX_W];
+    const float *w[A2AV_MAX_W];
+    unsigned char *out[A2AV_MAX_W];
+    int32_t *status;
+    int64_t T;
+    int64_t H;
+    int k;
+    int W;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
+
+// float -> bfloat16 bits, round to nearest even; every NaN becomes 0x7FC0
+// (the sign and payload of a NaN result are not fixed by IEEE 754 and differ
+// between processors).
+__device__ __forceinline__ uint32_t to_bf16(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+constexpr int kCombineGroup = 8;  // slots whose rows are loaded before their fmas
+
+template <int U>
+__global__ __launch_bounds__(256) void k_moe_combine(const CombineArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t wpb = blockDim.x / kWave;
+    if (*(const const_i32 *)a.status) return;  // written only by earlier kernels
+    const uint64_t nwork = (uint64_t)a.W * (uint64_t)a.T;
+    const int k = a.k;
+    const uint64_t rowb = (uint64_t)a.H * 2;
+    const uint64_t nv = (uint64_t)a.H / 8;  // 16-byte vectors per row
+    for (uint64_t wk = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave; wk < nwork;
+         wk += (uint64_t)gridDim.x * wpb) {
+        const int r = (int)(wk / (uint64_t)a.T);
+        const int64_t t = (int64_t)(wk - (uint64_t)r * (uint64_t)a.T);
+        const int64_t *pp = a.perm[r] + t * k;
+        const float *wp = a.w[r] + t * k;
+        const unsigned char *bk = a.back[r];
+        u32x4 *dst = (u32x4 *)(a.out[r] + (uint64_t)t * rowb);
+        for (uint64_t base = 0; base < nv; base += (uint64_t)kWave * U) {
+            float acc[U][8];
+#pragma unroll
+            for (int u = 0; u < U; u++)
+#pragma unroll
+                for (int e = 0; e < 8; e++) acc[u][e] = 0.0f;
+            uint64_t vi[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const uint64_t i = base + (uint64_t)u * kWave + lane;
+                vi[u] = i < nv ? i : nv - 1;  // clamped lanes redo the last vector
+            }
+            for (int c0 = 0; c0 < k; c0 += kWave) {
+                const int nc = k - c0 < kWave ? k - c0 : kWave;
+                const int64_t pl = lane < nc ? pp[c0 + lane] : 0;
+                const float wl = lane < nc ? wp[c0 + lane] : 0.0f;
+                for (int j0 = 0; j0 < nc; j0 += kCombineGroup) {
+                    u32x4 v[kCombineGroup][U];
+#pragma unroll
+                    for (int g = 0; g < kCombineGroup; g++) {
+                        // past the last slot the load repeats slot nc-1; its fma is skipped
+                        const int j = j0 + g < nc ? j0 + g : nc - 1;
+                        const u32x4 *row = (const u32x4 *)(bk + readlane_u64((uint64_t)pl, j) * rowb);
+#pragma unroll
+                        for (int u = 0; u < U; u++) v[g][u] = ld<true>(row + vi[u]);
+                    }
+#pragma unroll
+                    for (int g = 0; g < kCombineGroup; g++) {
+                        if (j0 + g < nc) {
+                            const float wt = __int_as_float(
+                                __builtin_amdgcn_readlane(__float_as_int(wl), j0 + g));
+#pragma unroll
+                            for (int u = 0; u < U; u++) {
+                                acc[u][0] = __builtin_fmaf(wt, bf16_lo(v[g][u].x), acc[u][0]);
+                                acc[u][1] = __builtin_fmaf(wt, bf16_hi(v[g][u].x), acc[u][1]);
+                                acc[u][2] = __builtin_fmaf(wt, bf16_lo(v[g][u].y), acc[u][2]);
+                                acc[u][3] = __builtin_fmaf(wt, bf16_hi(v[g][u].y), acc[u][3]);
+                                acc[u][4] = __builtin_fmaf(wt, bf16_lo(v[g][u].z), acc[u][4]);
+                                acc[u][5] = __builtin_fmaf(wt, bf16_hi(v[g][u].z), acc[u][5]);
+                                acc[u][6] = __builtin_fmaf(wt, bf16_lo(v[g][u].w), acc[u][6]);
+                                acc[u][7] = __builtin_fmaf(wt, bf16_hi(v[g][u].w), acc[u][7]);
+                            }
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                u32x4 o;
+                o.x = to_bf16(acc[u][0]) | (to_bf16(acc[u][1]) << 16);
+                o.y = to_bf16(acc[u][2]) | (to_bf16(acc[u][3]) << 16);
+                o.z = to_bf16(acc[u][4]) | (to_bf16(acc[u][5]) << 16);
+                o.w = to_bf16(acc[u][6]) | (to_bf16(acc[u][7]) << 16);
+                st<true>(dst + vi[u], o);
+            }
+        }
+    }
+}
+
+// Any row width or alignment: one element per lane per step.
+__global__ __launch_bounds__(256) void k_moe_combine_any(const CombineArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t wpb = blockDim.x / kWave;
+    if (*(const const_i32 *)a.status) return;
+    const uint64_t nwork = (uint64_t)a.W * (uint64_t)a.T;
+    const int k = a.k;
+    const uint64_t H = (uint64_t)a.H;
+    for (uint64_t wk = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave; wk < nwork;
+         wk += (uint64_t)gridDim.x * wpb) {
+        const int r = (int)(wk / (uint64_t)a.T);
+        const int64_t t = (int64_t)(wk - (uint64_t)r * (uint64_t)a.T);
+        const int64_t *pp = a.perm[r] + t * k;
+        const float *wp = a.w[r] + t * k;
+        const uint16_t *bk = (const uint16_t *)a.back[r];
+        uint16_t *dst = (uint16_t *)a.out[r] + (uint64_t)t * H;
+        for (uint64_t h = lane; h < H; h += kWave) {
+            float acc = 0.0f;
+            for (int j = 0; j < k; j++) {
+                const uint64_t row = (uint64_t)pp[j];
+                acc = __builtin_fmaf(wp[j], __uint_as_float((uint32_t)bk[row * H + h] << 16), acc);
+            }
+            dst[h] = (uint16_t)to_bf16(acc);
+        }
+    }
+}
+
 static int64_t n_segments(int64_t Q) { return (Q + kSeg - 1) / kSeg; }
 
 static bool moe_sizes_ok(int W, int64_t T, int k, int E) {
@@ -397,5 +533,51 @@ A2AV_API int moe_unpack(int W, int64_t T, int k, size_t row_bytes, const void *c
     else
         hipLaunchKernelGGL((k_moe_gather<8, false>), dim3((unsigned)gather_blocks), dim3(256), 0,
                            stream, a);
+    return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
+}
+
+A2AV_API int moe_combine(int W, int64_t T, int k, int64_t H, const void *const *back,
+                         const int64_t *const *perm, const float *const *weights,
+                         void *const *out, int32_t *status, hipStream_t stream) {
+    if (W < 1 || W > A2AV_MAX_W || T < 0 || k < 1 || H < 1 || !back || !perm || !weights ||
+        !out || !status)
+        return A2AV_EARG;
+    if (T > INT64_MAX / k || (uint64_t)T * (uint64_t)k > (uint64_t)INT64_MAX / (2 * (uint64_t)H))
+        return A2AV_EARG;
+    CombineArgs a;
+    UnpackArgs c;
+    std::memset(&a, 0, sizeof(a));
+    std::memset(&c, 0, sizeof(c));
+    bool aligned = (H % 8) == 0;
+    for (int r = 0; r < W; r++) {
+        if (T > 0 && (!back[r] || !perm[r] || !weights[r] || !out[r])) return A2AV_EARG;
+        a.back[r] = (const unsigned char *)back[r];
+        a.perm[r] = perm[r];
+        a.w[r] = weights[r];
+        a.out[r] = (unsigned char *)out[r];
+        c.perm[r] = perm[r];
+        aligned = aligned && ((uintptr_t)back[r] % 16 == 0) && ((uintptr_t)out[r] % 16 == 0);
+    }
+    a.status = c.status = status;
+    a.T = T;
+    a.H = H;
+    a.k = k;
+    a.W = W;
+    c.Q = T * k;
+    c.W = W;
+    c.R = 1;
+    if (T == 0) return A2AV_OK;
+    const int64_t check_blocks = (c.Q + 255) / 256;
+    if (check_blocks > INT32_MAX) return A2AV_EARG;
+    hipLaunchKernelGGL(k_perm_check, dim3((unsigned)check_blocks, W), dim3(256), 0, stream, c);
+    uint64_t blocks = ((uint64_t)W * (uint64_t)T + 3) / 4;
+    if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
+    const int cu = (int)env_long("A2AV_COMBINE_UNROLL", 2, 1, 2);
+    if (!aligned)
+        hipLaunchKernelGGL(k_moe_combine_any, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else if (cu == 1)
+        hipLaunchKernelGGL((k_moe_combine<1>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_moe_combine<2>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
 }

@@ -53,6 +53,7 @@ extern "C" {
 #define A2AV_MAX_W 64                        /* virtual ranks per call        */
 #define A2AV_MAX_SPLIT ((int64_t)1 << 40)    /* largest valid split (rows)    */
 #define A2AV_MAX_EXPERTS 4096                /* experts per moe_pack call     */
+#define A2AV_MAX_TABLES 4096                 /* tables per keys_bucketize call */
 
 /* host return codes */
 #define A2AV_OK 0
@@ -205,6 +206,106 @@ int moe_pack(int W, int64_t T, int k, int E, size_t row_bytes,
 int moe_unpack(int W, int64_t T, int k, size_t row_bytes,
                const void *const *back, const int64_t *const *perm,
                void *const *out, int32_t *status, hipStream_t stream);
+
+/*
+ * MoE gate-weighted combine after the return trip, the weighted half of what
+ * the MoE region on the page "[a2av] Improve tuning for 4 GPUs" (section
+ * "Change", its 32 MB remark) sends back: for every rank r, token t < T and
+ * element h < H,
+ *   acc = +0.0f; for j = 0..k-1: acc = fmaf(w[r][t][j], back[r][perm[r][t*k+j]][h], acc);
+ *   out[r][t][h] = acc rounded to bfloat16 (nearest even); a NaN result is
+ *                  written as the quiet NaN 0x7FC0, since IEEE 754 does not
+ *                  fix the sign or payload of a NaN.
+ * The order of the slots and the single rounding of each fused multiply-add
+ * fix every bit of the result; fp32 subnormals are kept, not flushed.
+ *   back[W]     device bf16 [T*k][H] per rank (the returned rows, in the
+ *               order moe_pack packed them)
+ *   perm[W]     device int64 [T*k] per rank, from moe_pack
+ *   weights[W]  device fp32 [T][k] per rank (gate weights)
+ *   out[W]      device bf16 [T][H] per rank
+ *   status      A2AV_ST_BAD_PERM if a perm entry is outside [0, T*k):
+ *               nothing is written.
+ * Two kernels: a range check of perm, then one wave per (rank, token) that
+ * loads the token's k rows 8 slots at a time and accumulates in registers
+ * (16-byte vectors when H % 8 == 0 and every base is 16-byte aligned, else
+ * one element per lane). Tuning: A2AV_COMBINE_UNROLL (1 or 2 vectors per
+ * lane per step).
+ */
+int moe_combine(int W, int64_t T, int k, int64_t H, const void *const *back,
+                const int64_t *const *perm, const float *const *weights,
+                void *const *out, int32_t *status, hipStream_t stream);
+
+/*
+ * Workspace bytes moe_regroup needs (0 for invalid sizes).
+ */
+size_t moe_regroup_workspace_bytes(int W, int E);
+
+/*
+ * Receive-side expert regroup, the step after the dispatch a2av of the MoE
+ * region on the page "[a2av] Improve tuning for 4 GPUs" (section "Change"):
+ * rank d owns experts d*P .. d*P+P-1 (P = E/W) and received, from each source
+ * s in turn, the rows s routed to those experts, expert by expert. With
+ * counts[s][e] the rows source s routed to expert e (the expert_counts matrix
+ * of moe_pack; rank d reads column block d of it, which is the exchange of
+ * the counts), rank d's blocks (s, j) of counts[s][d*P+j] rows are
+ *   source-major: s = 0..W-1 outer, j = 0..P-1 inner (how the a2av delivers)
+ *   expert-major: j outer, s inner (each expert's rows contiguous)
+ *   direction 0: in source-major -> out expert-major; 1: the reverse.
+ *   counts          device int64 [W][E]
+ *   in[W], out[W]   device [rows][row_bytes] per rank; not overlapping
+ *   in_rows[W], out_cap_rows[W]  host: rows each buffer holds
+ *   expert_offsets  device int64 [W][P+1]: rows before expert j in the
+ *                   expert-major order of rank d, the total at index P;
+ *                   written for every rank that passes its checks
+ *   workspace       device scratch of >= moe_regroup_workspace_bytes() bytes
+ *   status          A2AV_ST_BAD_SPLIT (an owned count outside [0, 2^40]),
+ *                   A2AV_ST_SEND_OVERRUN (a rank's total > in_rows),
+ *                   A2AV_ST_RECV_OVERFLOW (> out_cap_rows): no payload byte
+ *                   of any rank is written.
+ * Two kernels: a plan (one workgroup per rank: two block scans give every
+ * block's source and destination start), then a copy that cuts all ranks'
+ * destination bytes into equal pieces, one per wave.
+ */
+int moe_regroup(int W, int E, size_t row_bytes, const int64_t *counts,
+                const void *const *in, const int64_t *in_rows, void *const *out,
+                const int64_t *out_cap_rows, int64_t *expert_offsets, int direction,
+                void *workspace, size_t workspace_bytes, int32_t *status,
+                hipStream_t stream);
+
+/*
+ * Workspace bytes keys_bucketize needs (0 for invalid sizes).
+ */
+size_t keys_bucketize_workspace_bytes(int W, int n_tables);
+
+/*
+ * Owner-order bucketing of jagged embedding keys before the key exchange,
+ * the exchange that the page "Different nccl stream within EmbeddingKey
+ * alltoall and EmbeddingValue..." (TorchRec, description) moves to a stream
+ * of its own. Table t is owned by rank t mod W. For every rank r:
+ *   lengths[r]      device int32 [n_tables][batch]: keys per (table, sample)
+ *   keys[r]         device int64 [n_keys[r]]: table 0's keys (sample 0, 1, ..),
+ *                   then table 1's, ...
+ *   lengths_out[r]  device int32 [n_tables][batch], keys_out[r] device int64
+ *                   [n_keys[r]]: the same data with the tables in (owner,
+ *                   table) order
+ *   split_keys      device int64 [W][W]: keys rank r sends to rank d
+ *   split_lengths   device int64 [W][W]: lengths entries r sends to d
+ *                   (the two split matrices of the keys and lengths a2av)
+ *   n_keys          host int64 [W]
+ *   workspace       device scratch of >= keys_bucketize_workspace_bytes()
+ *   status          A2AV_ST_BAD_SPLIT (a negative length) or
+ *                   A2AV_ST_SEND_OVERRUN (the lengths add up to more than
+ *                   n_keys[r]): nothing but the workspace is written, except
+ *                   the splits of ranks that passed.
+ * Keys past the lengths' total are not read and not written.
+ * Four kernels: per-(table, rank) key counts, a per-rank plan, and a block
+ * copy each for keys and lengths.
+ */
+int keys_bucketize(int W, int n_tables, int64_t batch, const int32_t *const *lengths,
+                   const int64_t *const *keys, const int64_t *n_keys,
+                   int32_t *const *lengths_out, int64_t *const *keys_out,
+                   int64_t *split_keys, int64_t *split_lengths, void *workspace,
+                   size_t workspace_bytes, int32_t *status, hipStream_t stream);
 
 /*
  * Plain contiguous device copy of `bytes` bytes (dst and src device pointers,

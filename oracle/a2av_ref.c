@@ -305,12 +305,13 @@ static float bf16_to_float(uint16_t h) {
     return f;
 }
 
-/* Round a binary32 to bfloat16, to nearest, ties to even; a NaN keeps its
- * sign and top payload bits and becomes quiet. */
+/* Round a binary32 to bfloat16, to nearest, ties to even. Every NaN becomes
+ * the canonical quiet NaN 0x7FC0: IEEE 754 leaves the sign and payload of a
+ * NaN result open, so they are not part of the result. */
 static uint16_t float_to_bf16(float f) {
     uint32_t u;
     memcpy(&u, &f, 4);
-    if (isnan(f)) return (uint16_t)((u >> 16) | 0x0040u);
+    if (isnan(f)) return 0x7FC0u;
     const uint32_t lsb = (u >> 16) & 1u;
     return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
 }

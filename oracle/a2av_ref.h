@@ -104,8 +104,9 @@ int ref_moe_regroup(int W, int E, int d, size_t R, const int64_t *counts,
 
 /* Gate-weighted combine for ONE rank: for token t and element h,
  * acc = +0.0f; for j = 0..k-1: acc = fmaf(w[t][j], float(back[perm[t*k+j]][h]), acc);
- * out[t][h] = acc rounded to bfloat16 (round to nearest even; NaN stays a quiet
- * NaN). back is [T*k][H] bf16, w is [T][k] fp32, out is [T][H] bf16. */
+ * out[t][h] = acc rounded to bfloat16 (round to nearest even; any NaN is written
+ * as the quiet NaN 0x7FC0). back is [T*k][H] bf16, w is [T][k] fp32, out is
+ * [T][H] bf16. */
 int ref_moe_combine(int64_t T, int k, int64_t H, const uint16_t *back,
                     const int64_t *perm, const float *w, uint16_t *out);
 

@@ -531,7 +531,8 @@ def pin_moe_combine_special_cases(o):
     assert st == 0
     for t in range(T):
         assert np.array_equal(out[t], back[perm[t * k + pick[t]]])
-    # infinities and NaN propagate; NaN comes out quiet
+    # infinities and NaN propagate; every NaN comes out as the one quiet NaN
+    # 0x7FC0, whatever its sign and payload were
     b2 = back.copy()
     b2[perm[0]] = 0x7F80          # +inf in slot 0 of token 0
     b2[perm[k]] = 0x7FA0          # a signalling NaN in slot 0 of token 1
@@ -539,7 +540,12 @@ def pin_moe_combine_special_cases(o):
     st, out = o.moe_combine(T, k, H, b2, perm, w2)
     assert st == 0
     assert np.all(out[0] == 0x7F80)
-    assert np.all((out[1] & 0x7F80) == 0x7F80) and np.all(out[1] & 0x0040)
+    assert np.all(out[1] == 0x7FC0)
+    b2[perm[k]] = 0xFFC1          # a negative quiet NaN with a payload
+    b2[perm[2 * k]] = 0x7F80      # +inf - inf in token 2 makes a new NaN
+    b2[perm[2 * k + 1]] = 0xFF80
+    st, out = o.moe_combine(T, k, H, b2, perm, w2)
+    assert st == 0 and np.all(out[1] == 0x7FC0) and np.all(out[2] == 0x7FC0)
     # zero weights over finite rows give +0 exactly
     st, out = o.moe_combine(T, k, H, back, perm, np.zeros((T, k), np.float32))
     assert st == 0 and not out.any()

@@ -27,7 +27,9 @@ def L():
 def test_header_declares_the_boundary():
     names = declared_functions(HEADER)
     for must in ("a2av_exchange_splits", "a2av_offsets", "a2av_copy", "moe_pack", "moe_unpack",
-                 "moe_pack_workspace_bytes", "a2av_abi_version", "a2av_strerror"):
+                 "moe_pack_workspace_bytes", "a2av_abi_version", "a2av_strerror",
+                 "moe_combine", "moe_regroup", "moe_regroup_workspace_bytes", "keys_bucketize",
+                 "keys_bucketize_workspace_bytes"):
         assert must in names
 
 
@@ -81,6 +83,32 @@ def test_host_argument_errors(L):
     assert L.moe_pack(2, 10, 2, 8, 16, ptrs, ptrs, ptrs, ptrs, vp(8), vp(8), vp(8), ws - 1,
                       vp(8), None) == EARG
     assert L.moe_unpack(2, 10, 0, 16, ptrs, ptrs, ptrs, vp(8), None) == EARG
+    # combine: k = 0, H = 0, a null buffer for a rank with tokens
+    assert L.moe_combine(2, 10, 0, 16, ptrs, ptrs, ptrs, ptrs, vp(8), None) == EARG
+    assert L.moe_combine(2, 10, 2, 0, ptrs, ptrs, ptrs, ptrs, vp(8), None) == EARG
+    assert L.moe_combine(2, 10, 2, 16, nul, ptrs, ptrs, ptrs, vp(8), None) == EARG
+    # regroup: E % W, bad direction, small workspace, negative rows
+    two = (ctypes.c_int64 * 2)(4, 4)
+    wsr = L.moe_regroup_workspace_bytes(2, 8)
+    assert wsr > 0 and L.moe_regroup_workspace_bytes(3, 8) == 0
+    assert L.moe_regroup(3, 8, 16, vp(8), arr, rows, arr, rows, vp(8), 0, vp(8), 1 << 20,
+                         vp(8), None) == EARG
+    assert L.moe_regroup(2, 8, 16, vp(8), ptrs, two, ptrs, two, vp(8), 2, vp(8), wsr,
+                         vp(8), None) == EARG
+    assert L.moe_regroup(2, 8, 16, vp(8), ptrs, two, ptrs, two, vp(8), 0, vp(8), wsr - 1,
+                         vp(8), None) == EARG
+    negr = (ctypes.c_int64 * 2)(4, -4)
+    assert L.moe_regroup(2, 8, 16, vp(8), ptrs, negr, ptrs, two, vp(8), 0, vp(8), wsr,
+                         vp(8), None) == EARG
+    # bucketize: too many tables, negative batch, small workspace, negative key count
+    wsb = L.keys_bucketize_workspace_bytes(2, 26)
+    assert wsb > 0 and L.keys_bucketize_workspace_bytes(2, 4097) == 0
+    assert L.keys_bucketize(2, 26, -1, ptrs, ptrs, two, ptrs, ptrs, vp(8), vp(8), vp(8), wsb,
+                            vp(8), None) == EARG
+    assert L.keys_bucketize(2, 26, 8, ptrs, ptrs, two, ptrs, ptrs, vp(8), vp(8), vp(8), wsb - 1,
+                            vp(8), None) == EARG
+    assert L.keys_bucketize(2, 26, 8, ptrs, ptrs, negr, ptrs, ptrs, vp(8), vp(8), vp(8), wsb,
+                            vp(8), None) == EARG
 
 
 def test_workspace_formula(L):

@@ -1,6 +1,5 @@
 """GPU parity of the MoE dispatch pack, the dispatch and return a2av, and the
-un-pack, against the CPU oracle (bit-exact), plus the embedding-key exchange
-as two a2av calls."""
+un-pack, against the CPU oracle (bit-exact)."""
 import numpy as np
 import pytest
 import torch
@@ -215,32 +214,6 @@ def test_moe_dispatch_full_size(ref):
     for r in range(W):
         want = tok[r].view(T, 1, R).expand(T, k, R)
         assert torch.equal(out[r].view(T, k, R), want), f"round trip rank {r}"
-
-
-def test_embedding_key_exchange_full(ref):
-    """W=8, 26 tables, batch 8192, lengths min(Poisson(20), 100), int64 keys:
-    keys (8-byte rows) and lengths (4-byte rows) as two a2av calls."""
-    W = 8
-    g = I.rng(88)
-    ranks = [I.emb_keys_rank(g) for _ in range(W)]
-    # the owner-order layout comes from the oracle's bucketing here, so this
-    # test isolates the two exchanges
-    bk = [ref.keys_bucketize(W, 26, 8192, r.lengths, r.keys) for r in ranks]
-    assert all(b[0] == 0 for b in bk)
-    Sk = np.stack([b[3] for b in bk])
-    Sl = np.stack([b[4] for b in bk])
-    keys = [b[2].view(np.uint8).reshape(-1, 8) for b in bk]
-    lens = [b[1].view(np.uint8).reshape(-1, 4) for b in bk]
-    _say("emb keys per rank", [k.shape[0] for k in keys])
-    gk = gpu_a2av(8, keys, Sk)
-    gl = gpu_a2av(4, lens, Sl)
-    assert_same(gk, ref_a2av(ref, 8, keys, Sk), "keys")
-    assert_same(gl, ref_a2av(ref, 4, lens, Sl), "lengths")
-    # the two calls agree: each received lengths chunk sums to its keys chunk
-    for d in range(W):
-        lv = gl[4][d].reshape(-1).view(np.int32)
-        for s in range(W):
-            assert lv[gl[3][d, s]:gl[3][d, s + 1]].sum() == gk[1][d, s]
 
 
 @pytest.mark.parametrize("env", [

@@ -71,6 +71,8 @@ MUTANTS = {
     "combine_reverse_order": [
         ("for (int j = 0; j < k; j++) {\n                const int64_t row = perm[t * k + j];",
          "for (int j = k - 1; j >= 0; j--) {\n                const int64_t row = perm[t * k + j];", 0)],
+    "combine_keeps_nan_payload": [
+        ("if (isnan(f)) return 0x7FC0u;", "if (isnan(f)) return (uint16_t)((u >> 16) | 0x0040u);", 0)],
     "combine_truncates_to_bf16": [
         ("return (uint16_t)((u + 0x7FFFu + lsb) >> 16);", "(void)lsb; return (uint16_t)(u >> 16);", 0)],
     "bucketize_reads_keys_at_output_position": [
