@@ -253,19 +253,25 @@ def time_cpu(fn, budget_s=2.0, min_runs=2):
     return statistics.median(times)
 
 
-def fused_args(st, R, ins, in_rows, outs, caps):
+def _vp_array(tensors):
+    return (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+
+
+def _i64_array(vals):
+    return (ctypes.c_int64 * len(vals))(*[int(x) for x in vals])
+
+
+def fused_args(st, R, ins, in_rows, outs, caps, stream=None, status=None):
     """Pre-marshalled argument tuple of one a2av_all_to_all_vdev call, so that
     timing a small exchange measures the GPU rather than Python."""
     import torch
     W = len(ins)
     vp = ctypes.c_void_p
-    a_in = (ctypes.c_void_p * W)(*[t.data_ptr() for t in ins])
-    a_out = (ctypes.c_void_p * W)(*[t.data_ptr() for t in outs])
-    a_rows = (ctypes.c_int64 * W)(*[int(x) for x in in_rows])
-    a_caps = (ctypes.c_int64 * W)(*[int(x) for x in caps])
-    hs = vp(torch.cuda.current_stream().cuda_stream)
-    return (W, R, a_in, a_rows, a_out, a_caps, vp(st.S.data_ptr()), vp(st.O.data_ptr()),
-            vp(st.send_off.data_ptr()), vp(st.recv_off.data_ptr()), vp(st.status.data_ptr()), hs)
+    s = stream if stream is not None else torch.cuda.current_stream()
+    stat = status if status is not None else st.status
+    return (W, R, _vp_array(ins), _i64_array(in_rows), _vp_array(outs), _i64_array(caps),
+            vp(st.S.data_ptr()), vp(st.O.data_ptr()), vp(st.send_off.data_ptr()),
+            vp(st.recv_off.data_ptr()), vp(stat.data_ptr()), vp(s.cuda_stream))
 
 
 def row_entry(nbytes, ms, cpu_bytes=None, cpu_s=None, note=""):
@@ -278,26 +284,127 @@ def row_entry(nbytes, ms, cpu_bytes=None, cpu_s=None, note=""):
     return e
 
 
-def row_benchmarks(torch, B, I, with_cpu=True):
-    """The other steps of the path, each at its full size: the MoE dispatch
-    pack, the dispatch and return a2av, the un-pack, and the embedding-key
-    exchange (keys and lengths). GB/s counts algorithmic bytes (payload read
-    + written, index bytes for the pack and un-pack)."""
+def _check_status(B, named):
+    for name, st in named:
+        v = int(st.item())
+        if v != 0:
+            raise RuntimeError(f"{name}: status {v} ({B.a2av_strerror(v)})")
+
+
+class KeyChain:
+    """The embedding-key exchange of one batch as pre-marshalled C-ABI calls on
+    one stream: keys_bucketize (owner order + the two split matrices on the
+    device), then the keys a2av and the lengths a2av reading those splits."""
+
+    NT, BATCH = 26, 8192
+
+    def __init__(self, torch, B, I, W, seed, stream):
+        from embeddings_a2av_virtual_amd.vranks import A2av
+        self.W = W
+        g = I.rng(seed)
+        ranks = [I.emb_keys_rank(g) for _ in range(W)]
+        self.host = ranks
+        self.len_in = [torch.from_numpy(r.lengths.reshape(-1)).cuda() for r in ranks]
+        self.key_in = [torch.from_numpy(r.keys).cuda() for r in ranks]
+        self.n_keys = [int(r.keys.size) for r in ranks]
+        self.len_b = [torch.empty_like(x) for x in self.len_in]
+        self.key_b = [torch.empty_like(x) for x in self.key_in]
+        self.ka, self.la = A2av(W), A2av(W)
+        self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.ws = torch.empty(B.keys_bucketize_workspace_bytes(W, self.NT), dtype=torch.uint8,
+                              device="cuda")
+        vp = ctypes.c_void_p
+        hs = vp(stream.cuda_stream)
+        self.b_args = (W, self.NT, self.BATCH, _vp_array(self.len_in), _vp_array(self.key_in),
+                       _i64_array(self.n_keys), _vp_array(self.len_b), _vp_array(self.key_b),
+                       vp(self.ka.S.data_ptr()), vp(self.la.S.data_ptr()), vp(self.ws.data_ptr()),
+                       self.ws.numel(), vp(self.status.data_ptr()), hs)
+        self.L = B.lib()
+        # receive capacity from one bucketing pass (set-up, outside any timing)
+        assert self.L.keys_bucketize(*self.b_args) == 0
+        torch.cuda.synchronize()
+        _check_status(B, [("bucketize", self.status)])
+        self.Sk = self.ka.S.cpu().numpy().copy()
+        self.Sl = self.la.S.cpu().numpy().copy()
+        kc = [int(c) for c in self.Sk.sum(axis=0)]
+        lc = [int(c) for c in self.Sl.sum(axis=0)]
+        self.key_out = [torch.empty(c, dtype=torch.int64, device="cuda") for c in kc]
+        self.len_out = [torch.empty(c, dtype=torch.int32, device="cuda") for c in lc]
+        self.k_args = fused_args(self.ka, 8, self.key_b, self.n_keys, self.key_out, kc,
+                                 stream=stream, status=self.status)
+        self.l_args = fused_args(self.la, 4, self.len_b, [x.numel() for x in self.len_b],
+                                 self.len_out, lc, stream=stream, status=self.status)
+        self.bucket_bytes = sum(2 * (8 * n + 4 * self.NT * self.BATCH) for n in self.n_keys)
+        self.key_bytes = 2 * 8 * int(self.Sk.sum())
+        self.len_bytes = 2 * 4 * int(self.Sl.sum())
+
+    def bucketize(self):
+        assert self.L.keys_bucketize(*self.b_args) == 0
+
+    def keys(self):
+        assert self.L.a2av_all_to_all_vdev(*self.k_args) == 0
+
+    def lengths(self):
+        assert self.L.a2av_all_to_all_vdev(*self.l_args) == 0
+
+    def __call__(self):
+        self.bucketize()
+        self.keys()
+        self.lengths()
+
+
+def time_overlap(torch, fa, fb, sa, sb, reps=20):
+    """GPU time (ms) per repetition of a then b on stream sa, and of a on sa
+    alongside b on sb (b's stream waits for the repetition's start and sa for
+    b's end, so a repetition ends when both have)."""
+    def serial():
+        fa()
+        fb_s()
+
+    fb_s = fb["on_a"]
+    fb_b = fb["on_b"]
+    for _ in range(2):
+        fa()
+        fb_s()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(sa)
+    for _ in range(reps):
+        serial()
+    e1.record(sa)
+    torch.cuda.synchronize()
+    t_serial = e0.elapsed_time(e1) / reps
+    starts = [torch.cuda.Event() for _ in range(reps)]
+    ends = [torch.cuda.Event() for _ in range(reps)]
+    torch.cuda.synchronize()
+    e0.record(sa)
+    for i in range(reps):
+        starts[i].record(sa)
+        sb.wait_event(starts[i])
+        fa()
+        fb_b()
+        ends[i].record(sb)
+        sa.wait_event(ends[i])
+    e1.record(sa)
+    torch.cuda.synchronize()
+    t_over = e0.elapsed_time(e1) / reps
+    return t_serial, t_over
+
+
+def moe_rows(torch, B, I, o, out):
+    """MoE dispatch workload: W=8, 8192 tokens x 7168 bf16 per rank, top-8 of
+    256 Zipf(1.1) experts. pack -> dispatch a2av -> regroup to expert-major
+    and back -> return a2av -> combine (weighted) and un-pack."""
     import numpy as np
-    sys.path.insert(0, ROOT)
     from embeddings_a2av_virtual_amd.vranks import A2av
-    out = {}
-    o = None
-    if with_cpu:
-        from oracle.ref import Oracle
-        o = Oracle()
-    # ---- MoE dispatch: W=8, 8192 tokens x 7168 bf16, top-8 of 256 Zipf(1.1) experts
     W, T, k, E, hidden = 8, 8192, 8, 256, 7168
     R, Q = hidden * 2, T * k
     g = I.rng(900)
     ids_h = [I.topk_ids(g, T, k, E, 1.1) for _ in range(W)]
+    w_h = [I.gate_weights(g, T, k) for _ in range(W)]
     tok = [I.payload_bf16(T, hidden, 9000 + r, device="cuda") for r in range(W)]
     ids = [torch.from_numpy(i.reshape(-1)).cuda() for i in ids_h]
+    wts = [torch.from_numpy(w.reshape(-1)).cuda() for w in w_h]
     send = [torch.empty((Q, hidden), dtype=torch.bfloat16, device="cuda") for _ in range(W)]
     perm = [torch.empty(Q, dtype=torch.int64, device="cuda") for _ in range(W)]
     S = torch.empty((W, W), dtype=torch.int64, device="cuda")
@@ -328,25 +435,142 @@ def row_benchmarks(torch, B, I, with_cpu=True):
     moved = 2 * R * sum(cap)
     out["dispatch_a2av"] = row_entry(moved, ms)
     out["dispatch_a2av"]["rows_received_per_rank"] = cap
-    del send
+    # ---- regroup: (source, expert) -> (expert, source) and back
+    grp = [torch.empty_like(x) for x in recv]
+    eoff = torch.empty((W, E // W + 1), dtype=torch.int64, device="cuda")
+    rws = torch.empty(B.moe_regroup_workspace_bytes(W, E), dtype=torch.uint8, device="cuda")
+    rst = torch.zeros(1, dtype=torch.int32, device="cuda")
+    to_expert = lambda: B.moe_regroup(W, E, R, counts, recv, cap, grp, cap, eoff, 0, rws, rst)
+    to_source = lambda: B.moe_regroup(W, E, R, counts, grp, cap, recv, cap, eoff, 1, rws, rst)
+    ms0 = time_events(torch, to_expert, 5)
+    ms1 = time_events(torch, to_source, 5)
+    cpu = {}
+    if o is not None:
+        cnt_h = counts.cpu().numpy()
+        x7 = recv[W - 1].view(torch.uint8).cpu().numpy()
+        cs = time_cpu(lambda: o.moe_regroup(W, E, W - 1, R, cnt_h, x7, cap[W - 1], cap[W - 1], 0))
+        cpu = dict(cpu_bytes=2 * R * cap[W - 1], cpu_s=cs,
+                   note=f"rank {W - 1} whole ({cap[W - 1]} rows)")
+    out["moe_regroup_to_expert"] = row_entry(moved, ms0, **cpu)
+    out["moe_regroup_to_source"] = row_entry(moved, ms1)
+    del grp
+    # ---- return a2av: every row goes home
     bk = A2av(W)
     bk.S.copy_(fwd.O)
     back = [torch.empty((Q, hidden), dtype=torch.bfloat16, device="cuda") for _ in range(W)]
     ret = lambda: bk(R, recv, cap, back, [Q] * W, fused=True)
     ms = time_events(torch, ret, 5)
     out["return_a2av"] = row_entry(moved, ms)
-    del recv
+    # ---- weighted combine: read k rows per token, write one
+    comb = [torch.empty((T, hidden), dtype=torch.bfloat16, device="cuda") for _ in range(W)]
+    cst = torch.zeros(1, dtype=torch.int32, device="cuda")
+    combine = lambda: B.moe_combine(W, T, k, hidden, back, perm, wts, comb, cst)
+    ms = time_events(torch, combine, 5)
+    comb_bytes = W * (Q * R + T * R + Q * (8 + 4))
+    cpu = {}
+    if o is not None:
+        Ts = 128   # one rank, 128 tokens, their own rows
+        p0 = perm[0][:Ts * k].cpu().numpy()
+        b0 = back[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        sub = np.ascontiguousarray(b0[p0])
+        ident = np.arange(Ts * k, dtype=np.int64)
+        cs = time_cpu(lambda: o.moe_combine(Ts, k, hidden, sub, ident, w_h[0][:Ts]))
+        cpu = dict(cpu_bytes=Ts * k * R + Ts * R + Ts * k * 12, cpu_s=cs,
+                   note="one rank, 128 tokens (fp32 fma chain, single thread)")
+        del b0
+    out["moe_combine"] = row_entry(comb_bytes, ms, **cpu)
+    del comb
+    # ---- un-pack (no weights): every slot gets its row back
     outb = [torch.empty((Q, hidden), dtype=torch.bfloat16, device="cuda") for _ in range(W)]
     ust = torch.zeros(1, dtype=torch.int32, device="cuda")
     unpack = lambda: B.moe_unpack(W, T, k, R, back, perm, outb, ust)
     ms = time_events(torch, unpack, 5)
     out["moe_unpack"] = row_entry(W * (2 * Q * R + 8 * Q), ms)
     torch.cuda.synchronize()
-    for name, st in (("pack", status), ("dispatch", fwd.status), ("return", bk.status),
-                     ("unpack", ust)):
-        if int(st.item()) != 0:
-            raise RuntimeError(f"{name} status {int(st.item())}")
-    del back, outb, tok, perm
+    _check_status(B, [("pack", status), ("dispatch", fwd.status), ("regroup", rst),
+                      ("return", bk.status), ("combine", cst), ("unpack", ust)])
+    return dict(fwd=fwd, send=send, recv=recv, cap=cap, R=R, Q=Q, W=W)
+
+
+def key_rows(torch, B, I, o, out):
+    """Embedding keys: W=8, 26 tables, batch 8192, lengths min(Poisson(20), 100):
+    bucketing by owner, then the keys and lengths a2av."""
+    import numpy as np
+    stream = torch.cuda.current_stream()
+    kc = KeyChain(torch, B, I, 8, 901, stream)
+    res = {}
+    ms = time_events(torch, kc.bucketize, 50)
+    cpu = {}
+    if o is not None:
+        r0 = kc.host[0]
+        cs = time_cpu(lambda: o.keys_bucketize(8, kc.NT, kc.BATCH, r0.lengths, r0.keys))
+        cpu = dict(cpu_bytes=2 * (8 * r0.keys.size + 4 * r0.lengths.size), cpu_s=cs,
+                   note="one rank whole")
+    res["bucketize"] = row_entry(kc.bucket_bytes, ms, **cpu)
+    for name, fn, nb, R2 in (("keys", kc.keys, kc.key_bytes, 8),
+                             ("lengths", kc.lengths, kc.len_bytes, 4)):
+        ms = time_events(torch, fn, 50)
+        cpu = {}
+        if o is not None:
+            Sx = kc.Sk if name == "keys" else kc.Sl
+            src = kc.key_b if name == "keys" else kc.len_b
+            xh = [x.view(torch.uint8).cpu().numpy() for x in src]
+            capx = Sx.sum(axis=0)
+            yh = [np.empty(int(c) * R2, dtype=np.uint8) for c in capx]
+            rows_in = np.array([x.numel() for x in src], dtype=np.int64)
+            cs = time_cpu(lambda: o.a2av(R2, xh, rows_in, yh, capx, Sx))
+            cpu = dict(cpu_bytes=nb, cpu_s=cs, note="whole exchange")
+        res[name + "_a2av"] = row_entry(nb, ms, **cpu)
+    ms = time_events(torch, kc, 50)
+    res["chain"] = row_entry(kc.bucket_bytes + kc.key_bytes + kc.len_bytes, ms)
+    torch.cuda.synchronize()
+    _check_status(B, [("key chain", kc.status)])
+    out["emb_keys_exchange"] = res
+    return kc
+
+
+def overlap_rows(torch, B, I, moe, out):
+    """The next batch's key exchange on a stream of its own, next to the
+    current step's traffic on the main stream (both default priority):
+    per-repetition GPU time with both on one stream and side by side."""
+    sa = torch.cuda.current_stream()
+    sb = torch.cuda.Stream()
+    kb = KeyChain(torch, B, I, 8, 902, sb)
+    ka = KeyChain(torch, B, I, 8, 902, sa)
+    res = {}
+    t_keys = time_events(torch, ka, 20)
+    fwd, W, R, Q = moe["fwd"], moe["W"], moe["R"], moe["Q"]
+    disp_args = fused_args(fwd, R, moe["send"], [Q] * W, moe["recv"], moe["cap"], stream=sa)
+    L = B.lib()
+    disp = lambda: L.a2av_all_to_all_vdev(*disp_args)
+    small = VSet(torch, B, I, 4, 4096, 4096, seed=77, stream_handle=sa.cuda_stream)
+    a32 = lambda: L.a2av_all_to_all_vdev(*small.fused_args)
+    for name, fa in (("dispatch_a2av", disp), ("a2av_w4_32mib", a32)):
+        t_a = time_events(torch, fa, 10)
+        ts, to = time_overlap(torch, fa, {"on_a": ka, "on_b": kb}, sa, sb)
+        res[name] = {"a_us": round(t_a * 1e3, 2), "keys_us": round(t_keys * 1e3, 2),
+                     "serial_us": round(ts * 1e3, 2), "overlapped_us": round(to * 1e3, 2),
+                     "hidden_frac_of_keys": round((ts - to) / t_keys, 3)}
+    torch.cuda.synchronize()
+    _check_status(B, [("keys a", ka.status), ("keys b", kb.status), ("a2av", small.st.status),
+                      ("dispatch", fwd.status)])
+    out["key_exchange_overlap"] = res
+
+
+def row_benchmarks(torch, B, I, with_cpu=True):
+    """The other steps of the path, each at its full size. GB/s counts
+    algorithmic bytes (payload read + written, plus index and weight bytes
+    where a kernel reads them)."""
+    sys.path.insert(0, ROOT)
+    out = {}
+    o = None
+    if with_cpu:
+        from oracle.ref import Oracle
+        o = Oracle()
+    moe = moe_rows(torch, B, I, o, out)
+    key_rows(torch, B, I, o, out)
+    overlap_rows(torch, B, I, moe, out)
+    del moe
     torch.cuda.empty_cache()
     return out
 
