@@ -308,79 +308,72 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
 
 constexpr int kCombineGroup = 8;  // slots whose rows are loaded before their fmas
 
-template <int U>
-__global__ __launch_bounds__(256) void k_moe_combine(const CombineArgs a) {
+// One wave per (rank, token, chunk of 64 vectors = 512 elements). The wave
+// index is made uniform so that the token, its perm entries and weights (read
+// with scalar loads) and the row bases all live in scalar registers; each
+// row load is then a base in scalar registers plus one shared 32-bit lane
+// offset. Slots go in groups of 8: the group's 8 row loads are issued before
+// any of its fused multiply-adds (a scheduling barrier keeps the compiler from
+// interleaving them), and the adds run in slot order. Short-lived waves with
+// few registers keep many loads in flight per CU: in measurements this beat
+// looping waves, with or without software pipelining.
+template <bool SNT>
+__global__ __launch_bounds__(256) void k_moe_combine(const CombineArgs a, uint64_t nchunk) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint64_t wpb = blockDim.x / kWave;
     if (*(const const_i32 *)a.status) return;  // written only by earlier kernels
-    const uint64_t nwork = (uint64_t)a.W * (uint64_t)a.T;
+    const uint64_t nwork = (uint64_t)a.W * (uint64_t)a.T * nchunk;
     const int k = a.k;
     const uint64_t rowb = (uint64_t)a.H * 2;
     const uint64_t nv = (uint64_t)a.H / 8;  // 16-byte vectors per row
-    for (uint64_t wk = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave; wk < nwork;
+    const uint32_t wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    for (uint64_t wk = (uint64_t)blockIdx.x * wpb + wid; wk < nwork;
          wk += (uint64_t)gridDim.x * wpb) {
-        const int r = (int)(wk / (uint64_t)a.T);
-        const int64_t t = (int64_t)(wk - (uint64_t)r * (uint64_t)a.T);
-        const int64_t *pp = a.perm[r] + t * k;
-        const float *wp = a.w[r] + t * k;
+        const uint64_t tok = wk / nchunk;
+        const uint64_t c = wk - tok * nchunk;
+        const int r = (int)(tok / (uint64_t)a.T);
+        const int64_t t = (int64_t)(tok - (uint64_t)r * (uint64_t)a.T);
+        const const_i64 *pp = (const const_i64 *)(a.perm[r] + t * k);
+        const const_i32 *wp = (const const_i32 *)(a.w[r] + t * k);
         const unsigned char *bk = a.back[r];
-        u32x4 *dst = (u32x4 *)(a.out[r] + (uint64_t)t * rowb);
-        for (uint64_t base = 0; base < nv; base += (uint64_t)kWave * U) {
-            float acc[U][8];
+        uint64_t i = c * kWave + lane;
+        i = i < nv ? i : nv - 1;  // clamped lanes redo the last vector
+        const uint32_t off = (uint32_t)i * 16u;
+        float acc[8];
 #pragma unroll
-            for (int u = 0; u < U; u++)
+        for (int e = 0; e < 8; e++) acc[e] = 0.0f;
+        for (int j0 = 0; j0 < k; j0 += kCombineGroup) {
+            u32x4 v[kCombineGroup];
+            float wt[kCombineGroup];
 #pragma unroll
-                for (int e = 0; e < 8; e++) acc[u][e] = 0.0f;
-            uint64_t vi[U];
-#pragma unroll
-            for (int u = 0; u < U; u++) {
-                const uint64_t i = base + (uint64_t)u * kWave + lane;
-                vi[u] = i < nv ? i : nv - 1;  // clamped lanes redo the last vector
+            for (int g = 0; g < kCombineGroup; g++) {
+                // past the last slot the load repeats slot k-1; its fma is skipped
+                const int j = j0 + g < k ? j0 + g : k - 1;
+                const unsigned char *row = bk + (uint64_t)pp[j] * rowb;
+                v[g] = ld<true>((const u32x4 *)(row + off));
+                wt[g] = __int_as_float(wp[j]);
             }
-            for (int c0 = 0; c0 < k; c0 += kWave) {
-                const int nc = k - c0 < kWave ? k - c0 : kWave;
-                const int64_t pl = lane < nc ? pp[c0 + lane] : 0;
-                const float wl = lane < nc ? wp[c0 + lane] : 0.0f;
-                for (int j0 = 0; j0 < nc; j0 += kCombineGroup) {
-                    u32x4 v[kCombineGroup][U];
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int g = 0; g < kCombineGroup; g++) {
-                        // past the last slot the load repeats slot nc-1; its fma is skipped
-                        const int j = j0 + g < nc ? j0 + g : nc - 1;
-                        const u32x4 *row = (const u32x4 *)(bk + readlane_u64((uint64_t)pl, j) * rowb);
-#pragma unroll
-                        for (int u = 0; u < U; u++) v[g][u] = ld<true>(row + vi[u]);
-                    }
-#pragma unroll
-                    for (int g = 0; g < kCombineGroup; g++) {
-                        if (j0 + g < nc) {
-                            const float wt = __int_as_float(
-                                __builtin_amdgcn_readlane(__float_as_int(wl), j0 + g));
-#pragma unroll
-                            for (int u = 0; u < U; u++) {
-                                acc[u][0] = __builtin_fmaf(wt, bf16_lo(v[g][u].x), acc[u][0]);
-                                acc[u][1] = __builtin_fmaf(wt, bf16_hi(v[g][u].x), acc[u][1]);
-                                acc[u][2] = __builtin_fmaf(wt, bf16_lo(v[g][u].y), acc[u][2]);
-                                acc[u][3] = __builtin_fmaf(wt, bf16_hi(v[g][u].y), acc[u][3]);
-                                acc[u][4] = __builtin_fmaf(wt, bf16_lo(v[g][u].z), acc[u][4]);
-                                acc[u][5] = __builtin_fmaf(wt, bf16_hi(v[g][u].z), acc[u][5]);
-                                acc[u][6] = __builtin_fmaf(wt, bf16_lo(v[g][u].w), acc[u][6]);
-                                acc[u][7] = __builtin_fmaf(wt, bf16_hi(v[g][u].w), acc[u][7]);
-                            }
-                        }
-                    }
+            for (int g = 0; g < kCombineGroup; g++) {
+                if (j0 + g < k) {
+                    acc[0] = __builtin_fmaf(wt[g], bf16_lo(v[g].x), acc[0]);
+                    acc[1] = __builtin_fmaf(wt[g], bf16_hi(v[g].x), acc[1]);
+                    acc[2] = __builtin_fmaf(wt[g], bf16_lo(v[g].y), acc[2]);
+                    acc[3] = __builtin_fmaf(wt[g], bf16_hi(v[g].y), acc[3]);
+                    acc[4] = __builtin_fmaf(wt[g], bf16_lo(v[g].z), acc[4]);
+                    acc[5] = __builtin_fmaf(wt[g], bf16_hi(v[g].z), acc[5]);
+                    acc[6] = __builtin_fmaf(wt[g], bf16_lo(v[g].w), acc[6]);
+                    acc[7] = __builtin_fmaf(wt[g], bf16_hi(v[g].w), acc[7]);
                 }
             }
-#pragma unroll
-            for (int u = 0; u < U; u++) {
-                u32x4 o;
-                o.x = to_bf16(acc[u][0]) | (to_bf16(acc[u][1]) << 16);
-                o.y = to_bf16(acc[u][2]) | (to_bf16(acc[u][3]) << 16);
-                o.z = to_bf16(acc[u][4]) | (to_bf16(acc[u][5]) << 16);
-                o.w = to_bf16(acc[u][6]) | (to_bf16(acc[u][7]) << 16);
-                st<true>(dst + vi[u], o);
-            }
         }
+        u32x4 o;
+        o.x = to_bf16(acc[0]) | (to_bf16(acc[1]) << 16);
+        o.y = to_bf16(acc[2]) | (to_bf16(acc[3]) << 16);
+        o.z = to_bf16(acc[4]) | (to_bf16(acc[5]) << 16);
+        o.w = to_bf16(acc[6]) | (to_bf16(acc[7]) << 16);
+        st<SNT>((u32x4 *)(a.out[r] + (uint64_t)t * rowb + off), o);
     }
 }
 
@@ -570,14 +563,20 @@ A2AV_API int moe_combine(int W, int64_t T, int k, int64_t H, const void *const *
     const int64_t check_blocks = (c.Q + 255) / 256;
     if (check_blocks > INT32_MAX) return A2AV_EARG;
     hipLaunchKernelGGL(k_perm_check, dim3((unsigned)check_blocks, W), dim3(256), 0, stream, c);
-    uint64_t blocks = ((uint64_t)W * (uint64_t)T + 3) / 4;
-    if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
-    const int cu = (int)env_long("A2AV_COMBINE_UNROLL", 2, 1, 2);
-    if (!aligned)
+    // the fast path needs 16-byte vectors and rows under 4 GiB (32-bit lane offsets)
+    if (!aligned || (uint64_t)H * 2 >= (1ull << 32)) {
+        uint64_t blocks = ((uint64_t)W * (uint64_t)T + 3) / 4;
+        if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
         hipLaunchKernelGGL(k_moe_combine_any, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-    else if (cu == 1)
-        hipLaunchKernelGGL((k_moe_combine<1>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((k_moe_combine<2>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    } else {
+        const uint64_t nchunk = ((uint64_t)H / 8 + kWave - 1) / kWave;
+        uint64_t blocks = ((uint64_t)W * (uint64_t)T * nchunk + 3) / 4;
+        if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
+        // tuning knob: A2AV_COMBINE_STORE_NT (non-temporal stores, 0/1)
+        if (env_long("A2AV_COMBINE_STORE_NT", 1, 0, 1))
+            hipLaunchKernelGGL((k_moe_combine<true>), dim3((unsigned)blocks), dim3(256), 0, stream, a, nchunk);
+        else
+            hipLaunchKernelGGL((k_moe_combine<false>), dim3((unsigned)blocks), dim3(256), 0, stream, a, nchunk);
+    }
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
 }

@@ -225,11 +225,11 @@ int moe_unpack(int W, int64_t T, int k, size_t row_bytes,
  *   out[W]      device bf16 [T][H] per rank
  *   status      A2AV_ST_BAD_PERM if a perm entry is outside [0, T*k):
  *               nothing is written.
- * Two kernels: a range check of perm, then one wave per (rank, token) that
- * loads the token's k rows 8 slots at a time and accumulates in registers
- * (16-byte vectors when H % 8 == 0 and every base is 16-byte aligned, else
- * one element per lane). Tuning: A2AV_COMBINE_UNROLL (1 or 2 vectors per
- * lane per step).
+ * Two kernels: a range check of perm, then the sum. When H % 8 == 0 and
+ * every base is 16-byte aligned, one wave per (rank, token, 512 elements)
+ * loads the token's k rows 8 slots at a time (16 bytes per lane) and
+ * accumulates in registers; otherwise one wave per (rank, token) goes one
+ * element per lane. Tuning: A2AV_COMBINE_STORE_NT (0/1, non-temporal stores).
  */
 int moe_combine(int W, int64_t T, int k, int64_t H, const void *const *back,
                 const int64_t *const *perm, const float *const *weights,
