@@ -18,7 +18,8 @@ Also reported on the same JSON line:
                 from rocprofv3 counters when they were taken on this exact
                 kernel source (else null)
   cpu_baseline  the CPU oracle on the same workload on this host
-  headline      W in {4, 8} x {32 MiB, 1 GiB} per rank, payload kernel and step
+  headline      W in {4, 8} x {32 MiB, 1 GiB} per rank, and W in {16, 64} at
+                32 MiB, payload kernel and step
   ceilings      plain device copy of the same bytes (this library's copy loop
                 and torch's D2D copy)
 """
@@ -623,7 +624,7 @@ def main(argv=None):
     headline = {}
     if not args.no_headline:
         for W, mib, steps, nsets in ((4, 32, 200, 8), (8, 32, 200, 8), (4, 1024, 20, 2),
-                                     (8, 1024, 10, 2)):
+                                     (8, 1024, 10, 2), (16, 32, 50, 8), (64, 32, 20, 2)):
             for entry in ("fused", "3call"):
                 r = run_config(torch, B, I, W, mib, steps, 5, nsets, entry)
                 key = f"w{W}_{mib}mib" + ("" if entry == "fused" else "_3call")

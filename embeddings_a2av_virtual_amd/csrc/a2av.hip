@@ -474,6 +474,143 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- W > 8
+// More ranks than a wave holds (s, d) pairs: one workgroup prepares and
+// checks everything first, then waves copy pieces of the flat destination
+// space as above, looking the pieces up in the offsets the prep wrote.
+//
+// k_a2av_prep (one 1024-thread workgroup). Fused mode: checks the splits,
+// writes O, send_off and recv_off from S, and checks the totals against the
+// caller's rows and capacities. Given mode (a2av_copy): checks the given
+// offsets against S and the given totals against rows and capacities. It is
+// the only writer of the status word before the copy launch, and it reads
+// the word once, at entry.
+template <bool FUSED>
+__global__ __launch_bounds__(1024) void k_a2av_prep(const CopyArgs a) {
+    __shared__ int64_t sl[A2AV_MAX_W * A2AV_MAX_W];
+    __shared__ int poisoned, lbits;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    constexpr int NWV = 1024 / kWave;
+    const int W = a.W, W1 = W + 1;
+    if (tid == 0) {
+        poisoned = status_poisoned(a.status);
+        lbits = 0;
+    }
+    int bad = 0;
+    for (int i = tid; i < W * W; i += 1024) {
+        sl[i] = a.S[i];
+        bad |= (int)split_invalid(sl[i]);
+    }
+    __syncthreads();
+    if (poisoned) return;
+    if (FUSED && __syncthreads_or(bad)) {
+        // invalid splits stop the sequence at the exchange
+        if (tid == 0) atomicOr(a.status, A2AV_ST_BAD_SPLIT);
+        return;
+    }
+    int bits = 0;
+    if constexpr (FUSED) {
+        // rows r < W: send offsets of rank r; rows W + d: receive offsets of d
+        for (int r = wave; r < 2 * W; r += NWV) {
+            int64_t v = 0;
+            if (lane < W) v = r < W ? sl[r * W + lane] : sl[lane * W + (r - W)];
+            const int64_t incl = wave_incl_scan(v);
+            int64_t *dst = r < W ? a.send_off_out + r * W1 : a.recv_off_out + (r - W) * W1;
+            if (lane < W) dst[lane] = incl - v;
+            if (lane == W - 1) {
+                dst[W] = incl;
+                if (r < W && incl > a.in_rows[r]) bits |= A2AV_ST_SEND_OVERRUN;
+                if (r >= W && incl > a.cap[r - W]) bits |= A2AV_ST_RECV_OVERFLOW;
+            }
+        }
+        for (int i = tid; i < W * W; i += 1024) {
+            const int s = i / W, d = i - s * W;
+            a.O_out[d * W + s] = sl[i];
+        }
+    } else {
+        for (int i = tid; i < W * W; i += 1024) {
+            const int s = i / W, d = i - s * W;
+            bits |= pair_bits(sl[i], a.send_off[s * W1 + d], a.send_off[s * W1 + d + 1],
+                              a.recv_off[d * W1 + s], a.recv_off[d * W1 + s + 1], s, d);
+        }
+        for (int r = tid; r < W; r += 1024) {
+            if (a.send_off[r * W1 + W] > a.in_rows[r]) bits |= A2AV_ST_SEND_OVERRUN;
+            if (a.recv_off[r * W1 + W] > a.cap[r]) bits |= A2AV_ST_RECV_OVERFLOW;
+        }
+    }
+    if (bits) atomicOr(&lbits, bits);
+    __syncthreads();
+    if (tid == 0 && lbits) atomicOr(a.status, lbits);
+}
+
+// Lane l of a wave holds entry l of the rank-indexed vector v[0..W) (W <= 64).
+__device__ __forceinline__ int64_t lane_load(const int64_t *v, int W, int lane) {
+    return lane < W ? v[lane] : 0;
+}
+
+// The copy after k_a2av_prep, one piece per wave. Lane d holds the rows
+// destination d receives (recv_off[d][W]) and, while the wave works inside
+// destination d, lane s holds recv_off[d][s], S[s][d] and send_off[s][d].
+template <int U, bool ALIGNED>
+__global__ __launch_bounds__(256) void k_a2av_wave_any(const CopyArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t wpb = blockDim.x / kWave;
+    const uint64_t gw = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave;
+    const uint64_t TW = (uint64_t)gridDim.x * wpb;
+    const int W = a.W, W1 = W + 1;
+    if (*(const const_i32 *)a.status) return;  // final: the prep launch wrote it
+    const uint64_t R = a.R;
+    const uint64_t tot = lane < W ? (uint64_t)a.recv_off[lane * W1 + W] : 0;
+    const uint64_t incl = wave_incl_scan_u64(tot);
+    const uint64_t pre = incl - tot;  // rows of destinations before lane d
+    const uint64_t B = readlane_u64(incl, kWave - 1) * R;
+    const uint64_t piece = a.piece;
+    for (uint64_t p = gw; p * piece < B; p += TW) {
+        const uint64_t lo = p * piece;
+        const uint64_t hi = lo + piece < B ? lo + piece : B;
+        const uint64_t mask_d = __ballot(lane < W && pre * R <= lo);
+        if (mask_d == 0) break;  // cannot happen: pre[0] == 0
+        int d = 63 - __clzll(mask_d);
+        uint64_t dbase = readlane_u64(pre, d) * R;
+        uint64_t ro = (uint64_t)lane_load(a.recv_off + d * W1, W, lane);
+        uint64_t n = lane < W ? (uint64_t)a.S[lane * W + d] : 0;
+        uint64_t so = lane < W ? (uint64_t)a.send_off[lane * W1 + d] : 0;
+        const uint64_t mask_s = __ballot(lane < W && dbase + ro * R <= lo);
+        if (mask_s == 0) break;  // cannot happen: recv_off[d][0] == 0
+        int s = 63 - __clzll(mask_s);
+        uint64_t x = lo;
+        while (x < hi && d < W) {
+            const uint64_t nn = readlane_u64(n, s);
+            const uint64_t r0 = readlane_u64(ro, s);
+            const uint64_t F = dbase + r0 * R;
+            const uint64_t L = nn * R;
+            if (nn > 0 && x < F + L) {
+                const uint64_t e = hi < F + L ? hi : F + L;
+                const uint64_t off = x - F;
+                const uint64_t s0 = readlane_u64(so, s);
+                // checked offsets always pass; the check keeps every access
+                // inside the caller's buffers regardless
+                if ((int64_t)(r0 + nn) <= a.cap[d] && (int64_t)(s0 + nn) <= a.in_rows[s]) {
+                    unsigned char *dst = a.out[d] + r0 * R + off;
+                    const unsigned char *src = a.in[s] + s0 * R + off;
+                    if constexpr (ALIGNED) wave_copy16<U>(dst, src, e - x, lane);
+                    else wave_copy_any<U>(dst, src, e - x, lane);
+                }
+                x = e;
+            }
+            if (++s == W) {
+                s = 0;
+                if (++d < W && x < hi) {
+                    dbase = readlane_u64(pre, d) * R;
+                    ro = (uint64_t)lane_load(a.recv_off + d * W1, W, lane);
+                    n = lane < W ? (uint64_t)a.S[lane * W + d] : 0;
+                    so = lane < W ? (uint64_t)a.send_off[lane * W1 + d] : 0;
+                }
+            }
+        }
+    }
+}
+
 // Plain copy with the same one-piece-per-wave structure.
 template <int U, bool ALIGNED>
 __global__ __launch_bounds__(256) void k_device_copy_wave(unsigned char *dst, const unsigned char *src,
@@ -591,6 +728,25 @@ static void launch_wave(const CopyArgs &a, bool aligned, int unroll, int grid, h
     }
 }
 
+// W > kWaveMaxW: the prep workgroup, then the wave copy on the offsets it
+// checked (fused: the offsets it wrote).
+template <bool FUSED>
+static void launch_wave_any(CopyArgs a, bool aligned, const WaveTuning &wt, int grid,
+                            hipStream_t st) {
+    hipLaunchKernelGGL((k_a2av_prep<FUSED>), dim3(1), dim3(1024), 0, st, a);
+    if (FUSED) {
+        a.send_off = a.send_off_out;
+        a.recv_off = a.recv_off_out;
+    }
+    if (wt.unroll == 16) {
+        if (aligned) hipLaunchKernelGGL((k_a2av_wave_any<16, true>), dim3(grid), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((k_a2av_wave_any<16, false>), dim3(grid), dim3(256), 0, st, a);
+    } else {
+        if (aligned) hipLaunchKernelGGL((k_a2av_wave_any<8, true>), dim3(grid), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((k_a2av_wave_any<8, false>), dim3(grid), dim3(256), 0, st, a);
+    }
+}
+
 // Largest possible traffic in bytes (what either side can hold) and whether
 // every base and row allows the 16-byte path.
 static void traffic_bound(const CopyArgs &a, uint64_t *bmax, bool *aligned) {
@@ -692,13 +848,14 @@ A2AV_API int a2av_copy(int W, size_t row_bytes, const void *const *in, const int
     const CopyTuning t = copy_tuning();
     a.min_piece = (uint64_t)t.min_piece;
     a.piece = (uint64_t)t.piece;
-    if (W <= kWaveMaxW && !t.block_kernel) {
+    if (!t.block_kernel) {
         uint64_t bmax;
         bool aligned;
         traffic_bound(a, &bmax, &aligned);
         const WaveTuning wt = wave_tuning(bmax);
         a.piece = wt.piece;
-        launch_wave<kCopyGiven>(a, aligned, wt.unroll, wave_grid(bmax, wt.piece), stream);
+        if (W <= kWaveMaxW) launch_wave<kCopyGiven>(a, aligned, wt.unroll, wave_grid(bmax, wt.piece), stream);
+        else launch_wave_any<false>(a, aligned, wt, wave_grid(bmax, wt.piece), stream);
         return launch_status();
     }
     const int grid = payload_grid(t, stream);
@@ -718,6 +875,21 @@ A2AV_API int a2av_all_to_all_vdev(int W, size_t row_bytes, const void *const *in
     CopyArgs a;
     const int rc = fill_buffers(a, W, row_bytes, in, in_rows, out, out_cap_rows);
     if (rc != A2AV_OK) return rc;
+    const CopyTuning t = copy_tuning();
+    if (W > kWaveMaxW && !t.block_kernel) {
+        a.S = S;
+        a.O_out = O;
+        a.send_off_out = send_off;
+        a.recv_off_out = recv_off;
+        a.status = status;
+        uint64_t bmax;
+        bool aligned;
+        traffic_bound(a, &bmax, &aligned);
+        const WaveTuning wt = wave_tuning(bmax);
+        a.piece = wt.piece;
+        launch_wave_any<true>(a, aligned, wt, wave_grid(bmax, wt.piece), stream);
+        return launch_status();
+    }
     if (W > kMetaW) {
         // the three steps as separate launches, in stream order
         int r = a2av_exchange_splits(W, S, O, status, stream);
@@ -732,7 +904,6 @@ A2AV_API int a2av_all_to_all_vdev(int W, size_t row_bytes, const void *const *in
     a.send_off_out = send_off;
     a.recv_off_out = recv_off;
     a.status = status;
-    const CopyTuning t = copy_tuning();
     a.min_piece = (uint64_t)t.min_piece;
     a.piece = (uint64_t)t.piece;
     if (W <= kWaveMaxW && !t.block_kernel) {

@@ -118,17 +118,20 @@ int a2av_offsets(int W, const int64_t *S, const int64_t *O, int64_t *send_off,
  *                 (send_off[s][W] > in_rows[s]), A2AV_ST_RECV_OVERFLOW
  *                 (recv_off[d][W] > out_cap_rows[d]); any of them => no byte
  *                 of any out[d] is written.
- * One kernel. The destination byte space of all ranks (out[0]'s rows, then
- * out[1]'s, ...) is cut into equal pieces, so skewed or zero splits leave no
- * compute unit idle. For W <= 8 every wave reads S and the offsets through the
- * scalar cache, checks them, and copies one piece with 16-byte coalesced
- * non-temporal accesses (realigned in registers when source and destination
- * differ mod 16); the grid is sized to min(sum in_rows, sum out_cap_rows) *
- * row_bytes. For larger W each workgroup stages the matrices in LDS (W <= 16)
- * or reads them from global memory, then copies its piece.
+ * The destination byte space of all ranks (out[0]'s rows, then out[1]'s, ...)
+ * is cut into equal pieces, one per wave, so skewed or zero splits leave no
+ * compute unit idle; pieces are copied with 16-byte coalesced non-temporal
+ * accesses (realigned in registers when source and destination differ mod
+ * 16), and the grid is sized to min(sum in_rows, sum out_cap_rows) *
+ * row_bytes. For W <= 8 this is one kernel: every wave reads S and the
+ * offsets through the scalar cache and checks them itself. For larger W a
+ * single workgroup checks everything first and the copy kernel follows (two
+ * launches); each wave then reads, per destination it works in, one row of
+ * recv_off and the matching columns of S and send_off.
  * Tuning (read on every call; defaults are compiled in): A2AV_WAVE_PIECE,
- * A2AV_WAVE_UNROLL (wave kernel); A2AV_BLOCK_KERNEL=1 forces the workgroup
- * kernel; A2AV_BLOCKS_PER_CU, A2AV_UNROLL, A2AV_NT, A2AV_PIECE,
+ * A2AV_WAVE_UNROLL (wave kernels); A2AV_BLOCK_KERNEL=1 forces the older
+ * workgroup kernel (one workgroup per piece, matrices staged in LDS for
+ * W <= 16); A2AV_BLOCKS_PER_CU, A2AV_UNROLL, A2AV_NT, A2AV_PIECE,
  * A2AV_MIN_PIECE (workgroup kernel). Every setting gives identical bytes.
  */
 int a2av_copy(int W, size_t row_bytes, const void *const *in,
@@ -144,10 +147,12 @@ int a2av_copy(int W, size_t row_bytes, const void *const *in,
  * / RECV_OVERFLOW leave O and the offsets written and no payload byte).
  *   S                      device int64 [W][W] (input splits)
  *   O, send_off, recv_off  device outputs as in the separate calls
- * For W <= 16 this is ONE kernel launch: every wave (W <= 8) or workgroup
- * (W <= 16) reads S, computes O and both offset matrices itself (the first
- * one also writes them out), checks them, and copies its piece of the
- * destination space; larger W runs the three launches.
+ * For W <= 8 this is ONE kernel launch: every wave reads S, computes O and
+ * both offset matrices in registers (the first one also writes them out),
+ * checks them, and copies its piece of the destination space. For larger W,
+ * two launches: one workgroup computes, writes and checks O and the offsets,
+ * then the wave copy of a2av_copy runs on them. (With A2AV_BLOCK_KERNEL=1:
+ * one workgroup-kernel launch for W <= 16, the three calls above that.)
  */
 int a2av_all_to_all_vdev(int W, size_t row_bytes, const void *const *in,
                          const int64_t *in_rows, void *const *out,
