@@ -380,3 +380,80 @@ int ref_keys_bucketize(int W, int n_tables, int64_t batch, const int32_t *length
     free(tstart);
     return 0;
 }
+
+/*
+ * The whole embedding-key exchange of one batch, as the plain composition of
+ * its two steps: every rank buckets its keys by owner (ref_keys_bucketize),
+ * then keys and lengths go out as two all-to-all-v calls whose splits are the
+ * bucketing's split rows. Checks in the order the composition meets them:
+ * the bucketing of every source first (their bits are the result if any
+ * fails), then the receive capacities; payload only when all pass.
+ */
+int ref_keys_exchange(int W, int n_tables, int64_t batch, const int32_t *const *lengths,
+                      const int64_t *const *keys, const int64_t *n_keys,
+                      int32_t *const *lengths_out, const int64_t *lengths_cap,
+                      int64_t *const *keys_out, const int64_t *keys_cap, int64_t *split_keys,
+                      int64_t *split_lengths, int64_t *recv_off_keys) {
+    if (W < 1 || W > REF_MAX_W || n_tables < 0 || batch < 0 || !lengths || !keys || !n_keys ||
+        !lengths_out || !lengths_cap || !keys_out || !keys_cap || !split_keys ||
+        !split_lengths || !recv_off_keys)
+        return REF_EARG;
+    if (n_tables > 0 && batch > INT64_MAX / n_tables) return REF_EARG;
+    const int64_t nl = (int64_t)n_tables * batch;
+    int st = 0;
+    int32_t **lo = calloc((size_t)W, sizeof(int32_t *));
+    int64_t **ko = calloc((size_t)W, sizeof(int64_t *));
+    int64_t *Sk = calloc((size_t)W * W, sizeof(int64_t));
+    int64_t *Sl = calloc((size_t)W * W, sizeof(int64_t));
+    if (!lo || !ko || !Sk || !Sl) { st = REF_EARG; goto done; }
+    /* step 1: bucketing on every source rank */
+    for (int s = 0; s < W; s++) {
+        if (n_keys[s] < 0) { st = REF_EARG; goto done; }
+        lo[s] = malloc((size_t)(nl > 0 ? nl : 1) * sizeof(int32_t));
+        ko[s] = malloc((size_t)(n_keys[s] > 0 ? n_keys[s] : 1) * sizeof(int64_t));
+        if (!lo[s] || !ko[s]) { st = REF_EARG; goto done; }
+        st |= ref_keys_bucketize(W, n_tables, batch, lengths[s], keys[s], n_keys[s], lo[s], ko[s],
+                                 Sk + (size_t)s * W, Sl + (size_t)s * W);
+    }
+    if (st) goto done;
+    /* step 2: what each receiver gets against its capacities */
+    for (int d = 0; d < W; d++) {
+        int64_t rk = 0, rl = 0;
+        for (int s = 0; s < W; s++) { rk += Sk[s * W + d]; rl += Sl[s * W + d]; }
+        if (rk > keys_cap[d] || rl > lengths_cap[d]) { st |= REF_RECV_OVERFLOW; continue; }
+        /* this receiver's split columns and receive offsets */
+        int64_t run = 0;
+        for (int s = 0; s < W; s++) {
+            split_keys[s * W + d] = Sk[s * W + d];
+            split_lengths[s * W + d] = Sl[s * W + d];
+            recv_off_keys[d * (W + 1) + s] = run;
+            run += Sk[s * W + d];
+        }
+        recv_off_keys[d * (W + 1) + W] = run;
+    }
+    if (st) goto done;
+    /* step 3: the two exchanges */
+    {
+        int64_t *rows_k = malloc((size_t)W * sizeof(int64_t));
+        int64_t *rows_l = malloc((size_t)W * sizeof(int64_t));
+        int64_t *O = malloc((size_t)W * W * sizeof(int64_t));
+        int64_t *so = malloc((size_t)W * (W + 1) * sizeof(int64_t));
+        int64_t *ro = malloc((size_t)W * (W + 1) * sizeof(int64_t));
+        if (!rows_k || !rows_l || !O || !so || !ro) {
+            st = REF_EARG;
+        } else {
+            for (int s = 0; s < W; s++) { rows_k[s] = n_keys[s]; rows_l[s] = nl; }
+            st |= ref_a2av(W, 8, (const void *const *)ko, rows_k, (void *const *)keys_out, keys_cap,
+                           Sk, O, so, ro);
+            if (!st)
+                st |= ref_a2av(W, 4, (const void *const *)lo, rows_l, (void *const *)lengths_out,
+                               lengths_cap, Sl, O, so, ro);
+        }
+        free(rows_k); free(rows_l); free(O); free(so); free(ro);
+    }
+done:
+    if (lo) for (int s = 0; s < W; s++) free(lo[s]);
+    if (ko) for (int s = 0; s < W; s++) free(ko[s]);
+    free(lo); free(ko); free(Sk); free(Sl);
+    return st;
+}

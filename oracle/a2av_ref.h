@@ -119,6 +119,22 @@ int ref_keys_bucketize(int W, int n_tables, int64_t batch, const int32_t *length
                        const int64_t *keys, int64_t n_keys, int32_t *lengths_out,
                        int64_t *keys_out, int64_t *split_keys, int64_t *split_lengths);
 
+/* The whole key exchange of one batch for all W ranks: ref_keys_bucketize on
+ * every source, then keys (8-byte rows) and lengths (4-byte rows) as two
+ * ref_a2av calls with the bucketing's split rows. lengths_cap / keys_cap are
+ * the receivers' capacities (entries). Result: the OR of the sources'
+ * bucketing bits if any fails (nothing written); else REF_RECV_OVERFLOW if a
+ * receiver's totals exceed its capacities (split columns and receive offsets
+ * written for the receivers that fit; no payload); else 0 with everything
+ * written. split_keys / split_lengths are W x W (row s = source s);
+ * recv_off_keys[d][s] = keys before source s's chunk at receiver d, total at
+ * index W. */
+int ref_keys_exchange(int W, int n_tables, int64_t batch, const int32_t *const *lengths,
+                      const int64_t *const *keys, const int64_t *n_keys,
+                      int32_t *const *lengths_out, const int64_t *lengths_cap,
+                      int64_t *const *keys_out, const int64_t *keys_cap, int64_t *split_keys,
+                      int64_t *split_lengths, int64_t *recv_off_keys);
+
 #ifdef __cplusplus
 }
 #endif

@@ -62,9 +62,11 @@ def _bind(lib):
     lib.ref_keys_bucketize.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, i32p,
                                        ctypes.c_void_p, ctypes.c_int64, i32p, ctypes.c_void_p,
                                        i64p, i64p]
+    lib.ref_keys_exchange.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, vpp, vpp, i64p,
+                                      vpp, i64p, vpp, i64p, i64p, i64p, i64p]
     for name in ("ref_exchange_splits", "ref_offsets", "ref_copy", "ref_a2av", "ref_source_of",
                  "ref_moe_pack", "ref_moe_unpack", "ref_moe_regroup", "ref_moe_combine",
-                 "ref_keys_bucketize"):
+                 "ref_keys_bucketize", "ref_keys_exchange"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -207,3 +209,33 @@ class Oracle:
                                          lo.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                          ko.ctypes.data, _i64(sk), _i64(sl))
         return st, lo, ko, sk, sl
+
+    def keys_exchange(self, W, n_tables, batch, lengths, keys, lengths_cap=None, keys_cap=None):
+        """All W ranks at once. lengths: per-rank int32 [n_tables, batch]; keys:
+        per-rank int64. Capacities default to what each receiver gets. Returns
+        (status, [lengths_out], [keys_out], split_keys, split_lengths,
+        recv_off_keys); outputs start as zeros (-7 for the matrices)."""
+        lengths = [np.ascontiguousarray(l, dtype=np.int32).reshape(-1) for l in lengths]
+        keys = [np.ascontiguousarray(k, dtype=np.int64) for k in keys]
+        n_keys = np.array([k.size for k in keys], dtype=np.int64)
+        if lengths_cap is None or keys_cap is None:
+            owned = [len(range(d, n_tables, W)) for d in range(W)]
+            lcap = np.array([W * owned[d] * batch for d in range(W)], dtype=np.int64)
+            kcap = np.zeros(W, dtype=np.int64)
+            for s in range(W):
+                tk = lengths[s].reshape(n_tables, batch).sum(axis=1) if n_tables else np.zeros(0)
+                for t in range(n_tables):
+                    kcap[t % W] += int(tk[t])
+            lengths_cap = lcap if lengths_cap is None else lengths_cap
+            keys_cap = kcap if keys_cap is None else keys_cap
+        lengths_cap = np.ascontiguousarray(lengths_cap, dtype=np.int64)
+        keys_cap = np.ascontiguousarray(keys_cap, dtype=np.int64)
+        lo = [np.zeros(max(int(c), 0), dtype=np.int32) for c in lengths_cap]
+        ko = [np.zeros(max(int(c), 0), dtype=np.int64) for c in keys_cap]
+        sk = np.full((W, W), -7, dtype=np.int64)
+        sl = np.full((W, W), -7, dtype=np.int64)
+        ro = np.full((W, W + 1), -7, dtype=np.int64)
+        st = self.lib.ref_keys_exchange(W, n_tables, batch, _ptrs(lengths), _ptrs(keys),
+                                        _i64(n_keys), _ptrs(lo), _i64(lengths_cap), _ptrs(ko),
+                                        _i64(keys_cap), _i64(sk), _i64(sl), _i64(ro))
+        return st, lo, ko, sk, sl, ro

@@ -147,6 +147,43 @@ static void one_bucketize(int W, int n_tables, int64_t batch) {
     free(len); free(lo); free(keys); free(ko); free(sk); free(sl);
 }
 
+static void one_keys_exchange(int W, int n_tables, int64_t batch) {
+    const int64_t nl = (int64_t)n_tables * batch;
+    int32_t **len = malloc(sizeof(int32_t *) * W), **lo = malloc(sizeof(int32_t *) * W);
+    int64_t **keys = malloc(sizeof(int64_t *) * W), **ko = malloc(sizeof(int64_t *) * W);
+    int64_t *nk = malloc(sizeof(int64_t) * W), *kcap = calloc(W, sizeof(int64_t));
+    int64_t *lcap = calloc(W, sizeof(int64_t));
+    int64_t *sk = malloc(sizeof(int64_t) * W * W), *sl = malloc(sizeof(int64_t) * W * W);
+    int64_t *ro = malloc(sizeof(int64_t) * W * (W + 1));
+    for (int s = 0; s < W; s++) {
+        len[s] = malloc(sizeof(int32_t) * (nl + 1));
+        nk[s] = 0;
+        for (int64_t i = 0; i < nl; i++) {
+            len[s][i] = (int32_t)(next_u64() % 5);
+            nk[s] += len[s][i];
+            kcap[(i / (batch > 0 ? batch : 1)) % W] += len[s][i];
+        }
+        keys[s] = malloc(sizeof(int64_t) * (nk[s] + 1));
+        for (int64_t i = 0; i < nk[s]; i++) keys[s][i] = (int64_t)(next_u64() >> 2);
+    }
+    for (int d = 0; d < W; d++) {
+        for (int t = d; t < n_tables; t += W) lcap[d] += (int64_t)W * batch;
+        lo[d] = malloc(sizeof(int32_t) * (lcap[d] + 1));
+        ko[d] = malloc(sizeof(int64_t) * (kcap[d] + 1));
+    }
+    CHECK(ref_keys_exchange(W, n_tables, batch, (const int32_t *const *)len,
+                            (const int64_t *const *)keys, nk, lo, lcap, ko, kcap, sk, sl, ro) == 0);
+    if (kcap[0] > 0) {
+        kcap[0] -= 1;
+        CHECK(ref_keys_exchange(W, n_tables, batch, (const int32_t *const *)len,
+                                (const int64_t *const *)keys, nk, lo, lcap, ko, kcap, sk, sl, ro) ==
+              REF_RECV_OVERFLOW);
+    }
+    for (int s = 0; s < W; s++) { free(len[s]); free(keys[s]); free(lo[s]); free(ko[s]); }
+    free(len); free(lo); free(keys); free(ko); free(nk); free(kcap); free(lcap);
+    free(sk); free(sl); free(ro);
+}
+
 int main(void) {
     const size_t widths[] = {1, 3, 8, 16, 100};
     for (int W = 1; W <= 9; W++)
@@ -167,6 +204,10 @@ int main(void) {
     one_bucketize(8, 26, 64);
     one_bucketize(3, 2, 0);
     one_bucketize(5, 0, 10);
+    one_keys_exchange(8, 26, 32);
+    one_keys_exchange(3, 2, 5);
+    one_keys_exchange(1, 3, 4);
+    one_keys_exchange(4, 0, 7);
     printf("oracle sanitized: ok\n");
     return 0;
 }

@@ -392,6 +392,57 @@ def pin_emb_two_call_consistency(o):
     assert sum(int(r.keys.size) for r in ranks) == int(rok[:, W].sum())
 
 
+def pin_keys_exchange_closed_form(o):
+    """The fused exchange: receiver d holds, for s = 0..W-1 in order, source
+    s's keys and lengths of the tables d owns (ascending), written out from
+    the generator's table-order arrays with numpy slicing; the split
+    matrices, receive offsets and every failure case as the composition
+    defines them."""
+    from embeddings_a2av_virtual_amd.inputs import emb_keys_rank
+    g = np.random.default_rng(30)
+    for W, tables, batch in ((4, 7, 16), (3, 2, 5), (1, 4, 3), (5, 0, 4), (2, 3, 0), (8, 26, 9)):
+        ranks = [emb_keys_rank(g, tables=tables, batch=batch) for _ in range(W)]
+        L = [r.lengths for r in ranks]
+        K = [r.keys for r in ranks]
+        st, lo, ko, sk, sl, ro = o.keys_exchange(W, tables, batch, L, K)
+        assert st == 0
+        for d in range(W):
+            own = list(range(d, tables, W))
+            wl, wk, col = [], [], []
+            for s in range(W):
+                bounds = np.concatenate([[0], np.cumsum(L[s].sum(axis=1))]).astype(np.int64)
+                mine = [K[s][bounds[t]:bounds[t + 1]] for t in own]
+                wk += mine
+                wl += [L[s][t] for t in own]
+                col.append(sum(m.size for m in mine))
+            want_k = np.concatenate(wk) if wk else np.zeros(0, np.int64)
+            want_l = np.concatenate(wl) if wl else np.zeros(0, np.int32)
+            assert np.array_equal(ko[d], want_k) and np.array_equal(lo[d], want_l)
+            assert np.array_equal(sk[:, d], col)
+            assert np.array_equal(sl[:, d], [len(own) * batch] * W)
+            assert np.array_equal(ro[d], np.concatenate([[0], np.cumsum(col)]))
+    # failures: a negative length, keys short of the lengths, a receiver short of room
+    W, tables, batch = 3, 5, 6
+    ranks = [emb_keys_rank(g, tables=tables, batch=batch) for _ in range(W)]
+    L = [r.lengths.copy() for r in ranks]
+    K = [r.keys for r in ranks]
+    bad = [l.copy() for l in L]; bad[1][2, 3] = -1
+    st, lo, ko, sk, sl, ro = o.keys_exchange(W, tables, batch, bad, K)
+    assert st == R.BAD_SPLIT and (sk == -7).all() and (ro == -7).all()
+    assert not any(x.any() for x in ko) and not any(x.any() for x in lo)
+    short = [k.copy() for k in K]; short[2] = short[2][:-1]
+    assert o.keys_exchange(W, tables, batch, L, short)[0] == R.SEND_OVERRUN
+    st, lo, ko, sk, sl, ro = o.keys_exchange(W, tables, batch, L, K)
+    kcap = ro[:, W].copy()
+    lcap = np.array([x.size for x in lo], dtype=np.int64)
+    kcap[1] -= 1
+    st, lo2, ko2, sk2, sl2, ro2 = o.keys_exchange(W, tables, batch, L, K, lcap, kcap)
+    assert st == R.RECV_OVERFLOW
+    assert not any(x.any() for x in ko2)
+    assert (sk2[:, 1] == -7).all() and (ro2[1] == -7).all()
+    assert np.array_equal(sk2[:, 0], sk[:, 0]) and np.array_equal(ro2[2], ro[2])
+
+
 # ------------------------------------------------------------------ expert regroup
 def _regroup_by_sort(W, E, d, R, counts, inp):
     """Independent formulation: tag every source-major row with (source,

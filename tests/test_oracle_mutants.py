@@ -78,6 +78,12 @@ MUTANTS = {
     "bucketize_reads_keys_at_output_position": [
         ("memcpy(keys_out + kpos, keys + tstart[t], (size_t)tk[t] * 8);",
          "memcpy(keys_out + kpos, keys + kpos, (size_t)tk[t] * 8);", 0)],
+    "keys_exchange_offsets_inclusive": [
+        ("            recv_off_keys[d * (W + 1) + s] = run;\n            run += Sk[s * W + d];",
+         "            run += Sk[s * W + d];\n            recv_off_keys[d * (W + 1) + s] = run;", 0)],
+    "keys_exchange_lengths_use_key_splits": [
+        ("(void *const *)lengths_out,\n                               lengths_cap, Sl, O, so, ro);",
+         "(void *const *)lengths_out,\n                               lengths_cap, Sk, O, so, ro);", 0)],
     "bucketize_length_split_counts_keys": [
         ("split_lengths[d] += batch;", "split_lengths[d] += tk[t];", 0)],
 }
