@@ -338,6 +338,24 @@ class KeyChain:
         self.bucket_bytes = sum(2 * (8 * n + 4 * self.NT * self.BATCH) for n in self.n_keys)
         self.key_bytes = 2 * 8 * int(self.Sk.sum())
         self.len_bytes = 2 * 4 * int(self.Sl.sum())
+        # the fused exchange: same inputs, straight into receive buffers of its own
+        self.fkey_out = [torch.empty(c, dtype=torch.int64, device="cuda") for c in kc]
+        self.flen_out = [torch.empty(c, dtype=torch.int32, device="cuda") for c in lc]
+        self.fsk = torch.empty((W, W), dtype=torch.int64, device="cuda")
+        self.fsl = torch.empty((W, W), dtype=torch.int64, device="cuda")
+        self.fro = torch.empty((W, W + 1), dtype=torch.int64, device="cuda")
+        self.fws = torch.empty(B.keys_exchange_workspace_bytes(W, self.NT), dtype=torch.uint8,
+                               device="cuda")
+        self.fstatus = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.x_args = (W, self.NT, self.BATCH, _vp_array(self.len_in), _vp_array(self.key_in),
+                       _i64_array(self.n_keys), _vp_array(self.flen_out), _i64_array(lc),
+                       _vp_array(self.fkey_out), _i64_array(kc), vp(self.fsk.data_ptr()),
+                       vp(self.fsl.data_ptr()), vp(self.fro.data_ptr()), vp(self.fws.data_ptr()),
+                       self.fws.numel(), vp(self.fstatus.data_ptr()), hs)
+        # algorithmic bytes of the fused exchange: lengths read once for the
+        # counts, then keys and lengths read and written once each
+        self.fused_bytes = (sum(4 * self.NT * self.BATCH for _ in range(W)) + self.key_bytes +
+                            self.len_bytes)
 
     def bucketize(self):
         assert self.L.keys_bucketize(*self.b_args) == 0
@@ -347,6 +365,9 @@ class KeyChain:
 
     def lengths(self):
         assert self.L.a2av_all_to_all_vdev(*self.l_args) == 0
+
+    def fused(self):
+        assert self.L.keys_exchange(*self.x_args) == 0
 
     def __call__(self):
         self.bucketize()
@@ -524,8 +545,14 @@ def key_rows(torch, B, I, o, out):
         res[name + "_a2av"] = row_entry(nb, ms, **cpu)
     ms = time_events(torch, kc, 50)
     res["chain"] = row_entry(kc.bucket_bytes + kc.key_bytes + kc.len_bytes, ms)
+    ms = time_events(torch, kc.fused, 50)
+    res["fused_exchange"] = row_entry(kc.fused_bytes, ms)
     torch.cuda.synchronize()
-    _check_status(B, [("key chain", kc.status)])
+    _check_status(B, [("key chain", kc.status), ("fused exchange", kc.fstatus)])
+    # the fused exchange delivers the same bytes as the chain
+    for a, b in zip(kc.key_out + kc.len_out, kc.fkey_out + kc.flen_out):
+        if not torch.equal(a, b):
+            raise RuntimeError("fused key exchange differs from the chain")
     out["emb_keys_exchange"] = res
     return kc
 
@@ -539,7 +566,7 @@ def overlap_rows(torch, B, I, moe, out):
     kb = KeyChain(torch, B, I, 8, 902, sb)
     ka = KeyChain(torch, B, I, 8, 902, sa)
     res = {}
-    t_keys = time_events(torch, ka, 20)
+    t_keys = time_events(torch, ka.fused, 20)
     fwd, W, R, Q = moe["fwd"], moe["W"], moe["R"], moe["Q"]
     disp_args = fused_args(fwd, R, moe["send"], [Q] * W, moe["recv"], moe["cap"], stream=sa)
     L = B.lib()
@@ -548,12 +575,12 @@ def overlap_rows(torch, B, I, moe, out):
     a32 = lambda: L.a2av_all_to_all_vdev(*small.fused_args)
     for name, fa in (("dispatch_a2av", disp), ("a2av_w4_32mib", a32)):
         t_a = time_events(torch, fa, 10)
-        ts, to = time_overlap(torch, fa, {"on_a": ka, "on_b": kb}, sa, sb)
+        ts, to = time_overlap(torch, fa, {"on_a": ka.fused, "on_b": kb.fused}, sa, sb)
         res[name] = {"a_us": round(t_a * 1e3, 2), "keys_us": round(t_keys * 1e3, 2),
                      "serial_us": round(ts * 1e3, 2), "overlapped_us": round(to * 1e3, 2),
                      "hidden_frac_of_keys": round((ts - to) / t_keys, 3)}
     torch.cuda.synchronize()
-    _check_status(B, [("keys a", ka.status), ("keys b", kb.status), ("a2av", small.st.status),
+    _check_status(B, [("keys a", ka.fstatus), ("keys b", kb.fstatus), ("a2av", small.st.status),
                       ("dispatch", fwd.status)])
     out["key_exchange_overlap"] = res
 

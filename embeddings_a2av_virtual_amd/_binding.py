@@ -25,7 +25,8 @@ __all__ = [
     "a2av_all_to_all_vdev",
     "moe_pack_workspace_bytes", "moe_pack", "moe_unpack", "moe_combine",
     "moe_regroup_workspace_bytes", "moe_regroup", "keys_bucketize_workspace_bytes",
-    "keys_bucketize", "a2av_device_copy", "MAX_TABLES",
+    "keys_bucketize", "keys_exchange_workspace_bytes", "keys_exchange", "a2av_device_copy",
+    "MAX_TABLES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liba2av.so")
@@ -82,9 +83,13 @@ def lib():
         L.keys_bucketize_workspace_bytes.restype = sz
         L.keys_bucketize.argtypes = [i32, i32, i64, vpp, vpp, i64p, vpp, vpp, vp, vp, vp, sz, vp,
                                      vp]
+        L.keys_exchange_workspace_bytes.argtypes = [i32, i32]
+        L.keys_exchange_workspace_bytes.restype = sz
+        L.keys_exchange.argtypes = [i32, i32, i64, vpp, vpp, i64p, vpp, i64p, vpp, i64p, vp, vp, vp,
+                                    vp, sz, vp, vp]
         L.a2av_device_copy.argtypes = [vp, vp, sz, vp]
         for f in ("a2av_exchange_splits", "a2av_offsets", "a2av_copy", "a2av_all_to_all_vdev",
-                  "moe_pack", "moe_unpack", "moe_combine", "moe_regroup", "keys_bucketize",
+                  "moe_pack", "moe_unpack", "moe_combine", "moe_regroup", "keys_bucketize", "keys_exchange",
                   "a2av_device_copy"):
             getattr(L, f).restype = i32
         _lib = L
@@ -250,6 +255,28 @@ def keys_bucketize(W, n_tables, batch, lengths, keys, n_keys, lengths_out, keys_
                                 _dev(split_lengths, "split_lengths"), _dev(workspace, "workspace"),
                                 workspace.numel() * workspace.element_size(),
                                 _dev(status, "status"), _stream(stream, status)))
+
+
+def keys_exchange_workspace_bytes(W, n_tables) -> int:
+    return int(lib().keys_exchange_workspace_bytes(int(W), int(n_tables)))
+
+
+def keys_exchange(W, n_tables, batch, lengths, keys, n_keys, lengths_out, lengths_cap, keys_out,
+                  keys_cap, split_keys, split_lengths, recv_off_keys, workspace, status,
+                  stream=None):
+    """Bucketing and both exchanges of one batch's keys in one call."""
+    if any(len(x) != W for x in (lengths, keys, n_keys, lengths_out, lengths_cap, keys_out,
+                                 keys_cap)):
+        raise ValueError("every per-rank list needs W entries")
+    _check("keys_exchange",
+           lib().keys_exchange(int(W), int(n_tables), int(batch), _ptr_array(lengths, "lengths"),
+                               _ptr_array(keys, "keys"), _i64_array(n_keys),
+                               _ptr_array(lengths_out, "lengths_out"), _i64_array(lengths_cap),
+                               _ptr_array(keys_out, "keys_out"), _i64_array(keys_cap),
+                               _dev(split_keys, "split_keys"), _dev(split_lengths, "split_lengths"),
+                               _dev(recv_off_keys, "recv_off_keys"), _dev(workspace, "workspace"),
+                               workspace.numel() * workspace.element_size(),
+                               _dev(status, "status"), _stream(stream, status)))
 
 
 def a2av_device_copy(dst, src, nbytes, stream=None):

@@ -35,6 +35,7 @@ struct BlockArgs {
     int64_t cap[A2AV_MAX_W];
     const int64_t *dst_start;  // [W][B + 1]
     const int64_t *src_start;  // [W][B]
+    const int32_t *src_rank;   // [W][B] source rank of each block, or null: the rank itself
     const int32_t *bits;       // [W]
     int32_t *status;
     uint64_t R;
@@ -108,13 +109,14 @@ __global__ __launch_bounds__(256) void k_block_copy(const BlockArgs a) {
             if (b < 0) return;  // not a valid plan
             const uint64_t r0 = (uint64_t)ds[b], r1 = (uint64_t)ds[b + 1];
             const uint64_t s0 = (uint64_t)a.src_start[(uint64_t)d * B + b];
+            const int sr = a.src_rank ? a.src_rank[(uint64_t)d * B + b] : d;
             const uint64_t e = hr < r1 * R ? hr : r1 * R;
-            if (e <= xr) return;  // not a valid plan
+            if (e <= xr || sr < 0 || sr >= W) return;  // not a valid plan
             // a valid plan always passes; the check keeps every access inside
             // the caller's buffers regardless
-            if (r1 <= (uint64_t)a.cap[d] && s0 + (r1 - r0) <= (uint64_t)a.in_rows[d]) {
+            if (r1 <= (uint64_t)a.cap[d] && s0 + (r1 - r0) <= (uint64_t)a.in_rows[sr]) {
                 unsigned char *dst = a.out[d] + xr;
-                const unsigned char *src = a.in[d] + s0 * R + (xr - r0 * R);
+                const unsigned char *src = a.in[sr] + s0 * R + (xr - r0 * R);
                 if constexpr (ALIGNED) wave_copy16<U>(dst, src, e - xr, lane);
                 else wave_copy_any<U>(dst, src, e - xr, lane);
             }
@@ -370,6 +372,133 @@ __global__ __launch_bounds__(kPlanThreads) void k_bucket_plan(const BucketArgs a
     }
 }
 
+// ------------------------------------------------------------ fused key exchange
+// Bucketing and both exchanges in one plan: receiver d's blocks are the pairs
+// (source s, i-th table d owns), in that order, B = W * cmax of them per
+// receiver (cmax = tables of the owner with the most; blocks past a
+// receiver's own count are empty). Each block copies straight from source s's
+// table-order keys (or lengths) into d's output, so the bucketed arrays are
+// never written.
+constexpr int kKxPer = 5;  // blocks per planning thread: up to 5120 per receiver
+constexpr int kKxMaxB = A2AV_MAX_TABLES + A2AV_MAX_W;
+
+struct KeyxArgs {
+    int64_t n_keys[A2AV_MAX_W];
+    int64_t key_cap[A2AV_MAX_W];
+    int64_t len_cap[A2AV_MAX_W];
+    const int64_t *tk;       // [W][NT] keys per (source, table), -1 for a negative length
+    int64_t *kdst;           // [W][B + 1] keys plan, per receiver
+    int64_t *ksrc;           // [W][B]
+    int64_t *ldst;           // [W][B + 1] lengths plan
+    int64_t *lsrc;           // [W][B]
+    int32_t *rank;           // [W][B] source of each block
+    int32_t *bits;           // [W]
+    int64_t *split_keys;     // [W][W] outputs
+    int64_t *split_lengths;  // [W][W]
+    int64_t *recv_off;       // [W][W + 1]
+    const int32_t *status;
+    int64_t batch;
+    int W;
+    int NT;
+    int cmax;
+    int B;
+};
+
+__global__ __launch_bounds__(kPlanThreads) void k_keyx_plan(const KeyxArgs a) {
+    __shared__ ScanLds lds;
+    __shared__ int64_t tst[kKxMaxB];           // start of (s, i) in source s's keys
+    __shared__ int64_t sstart[A2AV_MAX_W + 1];  // first key of source s at this receiver
+    __shared__ int poisoned, sbits;
+    const int d = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    constexpr int NWV = kPlanThreads / kWave;
+    const int W = a.W, NT = a.NT, cmax = a.cmax, B = a.B;
+    if (tid == 0) {
+        poisoned = *a.status != 0;
+        sbits = 0;
+    }
+    __syncthreads();
+    if (poisoned) return;
+    // every source's table-order scan (one wave per source): where the tables
+    // d owns start, and the source's own checks (as its bucketing makes them)
+    for (int s = wave; s < W; s += NWV) {
+        int64_t run = 0;
+        bool neg = false;
+        for (int c0 = 0; c0 < NT; c0 += kWave) {
+            const int t = c0 + lane;
+            int64_t v = t < NT ? a.tk[(int64_t)s * NT + t] : 0;
+            neg = neg || __ballot(v < 0) != 0;
+            v = v < 0 ? 0 : v;
+            const int64_t incl = wave_incl_scan(v);
+            if (t < NT && t % W == d) tst[s * cmax + t / W] = run + incl - v;
+            run += (int64_t)readlane_u64((uint64_t)incl, kWave - 1);
+        }
+        if (lane == 0) {
+            const int b = neg ? A2AV_ST_BAD_SPLIT : run > a.n_keys[s] ? A2AV_ST_SEND_OVERRUN : 0;
+            if (b) atomicOr(&sbits, b);
+        }
+    }
+    __syncthreads();
+    if (sbits) {
+        if (tid == 0) a.bits[d] = sbits;
+        return;
+    }
+    const int cnt = (NT - d + W - 1) / W;  // tables d owns
+    int64_t nk[kKxPer], nl[kKxPer];
+    int64_t sk = 0, sl = 0;
+#pragma unroll
+    for (int u = 0; u < kKxPer; u++) {
+        const int b = tid * kKxPer + u;
+        nk[u] = nl[u] = 0;
+        if (b < B) {
+            const int s = b / cmax, i = b - (b / cmax) * cmax;
+            if (i < cnt) {
+                nk[u] = a.tk[(int64_t)s * NT + d + i * W];
+                nl[u] = a.batch;
+            }
+        }
+        sk += nk[u];
+        sl += nl[u];
+    }
+    int64_t ek, el, TK, TL;
+    block_excl_scan2(sk, sl, lds, &ek, &el, &TK, &TL);
+    const int32_t bits = TK > a.key_cap[d] || TL > a.len_cap[d] ? A2AV_ST_RECV_OVERFLOW : 0;
+    int64_t *kdst = a.kdst + (int64_t)d * (B + 1);
+    int64_t *ldst = a.ldst + (int64_t)d * (B + 1);
+#pragma unroll
+    for (int u = 0; u < kKxPer; u++) {
+        const int b = tid * kKxPer + u;
+        if (b < B) {
+            const int s = b / cmax, i = b - (b / cmax) * cmax;
+            const bool real = i < cnt;
+            kdst[b] = ek;
+            ldst[b] = el;
+            a.ksrc[(int64_t)d * B + b] = real ? tst[s * cmax + i] : 0;
+            a.lsrc[(int64_t)d * B + b] = real ? (int64_t)(d + i * W) * a.batch : 0;
+            a.rank[(int64_t)d * B + b] = s;
+            if (i == 0) sstart[s] = ek;
+        }
+        ek += nk[u];
+        el += nl[u];
+    }
+    if (tid == 0) {
+        kdst[B] = TK;
+        ldst[B] = TL;
+        sstart[W] = TK;
+        a.bits[d] = bits;
+    }
+    __syncthreads();
+    if (bits == 0 && tid < W) {
+        // with no tables (cmax == 0) every source starts at 0
+        const int64_t s0 = cmax > 0 ? sstart[tid] : 0;
+        const int64_t s1 = cmax > 0 ? sstart[tid + 1] : 0;
+        a.split_keys[(int64_t)tid * W + d] = s1 - s0;
+        a.split_lengths[(int64_t)tid * W + d] = (int64_t)cnt * a.batch;
+        a.recv_off[(int64_t)d * (W + 1) + tid] = s0;
+        if (tid == W - 1) a.recv_off[(int64_t)d * (W + 1) + W] = TK;
+    }
+}
+
 // ------------------------------------------------------------ host side
 static void piece_policy(uint64_t bmax, int *unroll, uint64_t *piece) {
     const bool small = bmax <= (512ull << 20);
@@ -550,5 +679,121 @@ A2AV_API int keys_bucketize(int W, int n_tables, int64_t batch, const int32_t *c
         // no tables: nothing to move, but the planning bits still go out
         launch_block_copy(ck, 0, kal, stream);
     }
+    return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
+}
+
+A2AV_API size_t keys_exchange_workspace_bytes(int W, int n_tables) {
+    if (W < 1 || W > A2AV_MAX_W || n_tables < 0 || n_tables > A2AV_MAX_TABLES) return 0;
+    const size_t cmax = ((size_t)n_tables + W - 1) / W;
+    const size_t B = (size_t)W * cmax;
+    const size_t i64s = (size_t)W * n_tables + 4 * (size_t)W * B + 2 * (size_t)W;
+    return round256(i64s * 8) + round256((size_t)W * B * 4) + round256((size_t)W * 4);
+}
+
+A2AV_API int keys_exchange(int W, int n_tables, int64_t batch, const int32_t *const *lengths,
+                           const int64_t *const *keys, const int64_t *n_keys,
+                           int32_t *const *lengths_out, const int64_t *lengths_cap,
+                           int64_t *const *keys_out, const int64_t *keys_cap, int64_t *split_keys,
+                           int64_t *split_lengths, int64_t *recv_off_keys, void *workspace,
+                           size_t workspace_bytes, int32_t *status, hipStream_t stream) {
+    if (W < 1 || W > A2AV_MAX_W || n_tables < 0 || n_tables > A2AV_MAX_TABLES || batch < 0 ||
+        !lengths || !keys || !n_keys || !lengths_out || !lengths_cap || !keys_out || !keys_cap ||
+        !split_keys || !split_lengths || !recv_off_keys || !status)
+        return A2AV_EARG;
+    if (!workspace || workspace_bytes < keys_exchange_workspace_bytes(W, n_tables)) return A2AV_EARG;
+    if (n_tables > 0 && batch > ((int64_t)1 << 40) / n_tables) return A2AV_EARG;
+    const int64_t nl = (int64_t)n_tables * batch;
+    const int cmax = (n_tables + W - 1) / W;
+    const int B = W * cmax;
+    BucketArgs b;
+    KeyxArgs x;
+    BlockArgs ck, cl;
+    std::memset(&b, 0, sizeof(b));
+    std::memset(&x, 0, sizeof(x));
+    std::memset(&ck, 0, sizeof(ck));
+    std::memset(&cl, 0, sizeof(cl));
+    uint64_t kin = 0, kout = 0, lout = 0;
+    bool lal = (batch % 4) == 0;  // 16-byte path: every block edge on a 16-byte boundary
+    for (int r = 0; r < W; r++) {
+        if (n_keys[r] < 0 || n_keys[r] > ((int64_t)1 << 59) || keys_cap[r] < 0 ||
+            keys_cap[r] > ((int64_t)1 << 59) || lengths_cap[r] < 0 ||
+            lengths_cap[r] > ((int64_t)1 << 59))
+            return A2AV_EARG;
+        if (nl > 0 && !lengths[r]) return A2AV_EARG;
+        if (n_keys[r] > 0 && !keys[r]) return A2AV_EARG;
+        if ((keys_cap[r] > 0 && !keys_out[r]) || (lengths_cap[r] > 0 && !lengths_out[r]))
+            return A2AV_EARG;
+        b.lengths[r] = lengths[r];
+        x.n_keys[r] = n_keys[r];
+        x.key_cap[r] = keys_cap[r];
+        x.len_cap[r] = lengths_cap[r];
+        ck.in[r] = (const unsigned char *)keys[r];
+        ck.out[r] = (unsigned char *)keys_out[r];
+        ck.in_rows[r] = n_keys[r];
+        ck.cap[r] = keys_cap[r];
+        cl.in[r] = (const unsigned char *)lengths[r];
+        cl.out[r] = (unsigned char *)lengths_out[r];
+        cl.in_rows[r] = nl;
+        cl.cap[r] = lengths_cap[r];
+        kin += (uint64_t)n_keys[r];
+        kout += (uint64_t)keys_cap[r];
+        lout += (uint64_t)lengths_cap[r];
+        lal = lal && ((uintptr_t)lengths[r] % 16 == 0) && ((uintptr_t)lengths_out[r] % 16 == 0);
+    }
+    // workspace: tk | kdst | ksrc | ldst | lsrc | src rank | bits
+    int64_t *ws = (int64_t *)workspace;
+    const size_t nt = (size_t)n_tables, BB = (size_t)B;
+    int64_t *tk = ws;
+    int64_t *kdst = tk + (size_t)W * nt;
+    int64_t *ksrc = kdst + (size_t)W * (BB + 1);
+    int64_t *ldst = ksrc + (size_t)W * BB;
+    int64_t *lsrc = ldst + (size_t)W * (BB + 1);
+    const size_t i64s = (size_t)W * nt + 4 * (size_t)W * BB + 2 * (size_t)W;
+    int32_t *rank = (int32_t *)((unsigned char *)workspace + round256(i64s * 8));
+    int32_t *bits = (int32_t *)((unsigned char *)rank + round256((size_t)W * BB * 4));
+    b.tk = tk;
+    b.batch = batch;
+    b.W = W;
+    b.n_tables = n_tables;
+    x.tk = tk;
+    x.kdst = kdst;
+    x.ksrc = ksrc;
+    x.ldst = ldst;
+    x.lsrc = lsrc;
+    x.rank = rank;
+    x.bits = bits;
+    x.split_keys = split_keys;
+    x.split_lengths = split_lengths;
+    x.recv_off = recv_off_keys;
+    x.status = status;
+    x.batch = batch;
+    x.W = W;
+    x.NT = n_tables;
+    x.cmax = cmax;
+    x.B = B;
+    if (n_tables > 0)
+        hipLaunchKernelGGL(k_bucket_sums, dim3(n_tables, W), dim3(256), 0, stream, b);
+    hipLaunchKernelGGL(k_keyx_plan, dim3(W), dim3(kPlanThreads), 0, stream, x);
+    ck.dst_start = kdst;
+    ck.src_start = ksrc;
+    ck.src_rank = rank;
+    ck.bits = bits;
+    ck.status = status;
+    ck.R = 8;
+    ck.W = W;
+    ck.B = B;
+    cl.dst_start = ldst;
+    cl.src_start = lsrc;
+    cl.src_rank = rank;
+    cl.bits = bits;
+    cl.status = status;
+    cl.R = 4;
+    cl.W = W;
+    cl.B = B;
+    const uint64_t kmax = (kin < kout ? kin : kout) * 8;
+    const uint64_t lin = (uint64_t)W * (uint64_t)nl;
+    const uint64_t lmax = (lin < lout ? lin : lout) * 4;
+    launch_block_copy(ck, kmax, false, stream);  // also reports the planning bits
+    if (lmax > 0) launch_block_copy(cl, lmax, lal, stream);
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
 }

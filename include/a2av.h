@@ -313,6 +313,48 @@ int keys_bucketize(int W, int n_tables, int64_t batch, const int32_t *const *len
                    size_t workspace_bytes, int32_t *status, hipStream_t stream);
 
 /*
+ * Workspace bytes keys_exchange needs (0 for invalid sizes).
+ */
+size_t keys_exchange_workspace_bytes(int W, int n_tables);
+
+/*
+ * The whole embedding-key exchange of one batch in one call: the result of
+ * keys_bucketize on every rank followed by the keys a2av (8-byte rows) and
+ * the lengths a2av (4-byte rows) on the bucketing's split matrices, without
+ * writing the bucketed arrays. This is the exchange the page "Different nccl
+ * stream within EmbeddingKey alltoall and EmbeddingValue..." (TorchRec,
+ * description) gives a stream of its own. Table t is owned by rank t mod W.
+ *   lengths[W], keys[W], n_keys[W]   as for keys_bucketize (table order)
+ *   lengths_out[W]  device int32 per receiver d: for s = 0..W-1, the lengths
+ *                   rows of the tables d owns (ascending) from source s;
+ *                   lengths_cap[d] (host) entries of room
+ *   keys_out[W]     device int64 per receiver d: the same order for the
+ *                   keys; keys_cap[d] (host) entries of room
+ *   split_keys, split_lengths  device int64 [W][W] (row s = source s), the
+ *                   splits of the two exchanges
+ *   recv_off_keys   device int64 [W][W+1]: keys before source s's chunk at
+ *                   receiver d, the total at index W
+ *   workspace       device scratch of >= keys_exchange_workspace_bytes()
+ *   status          checks in the order the composition meets them: if any
+ *                   source fails its bucketing checks (A2AV_ST_BAD_SPLIT for a
+ *                   negative length, else A2AV_ST_SEND_OVERRUN when its
+ *                   lengths add to more than n_keys), those bits and nothing
+ *                   written; else A2AV_ST_RECV_OVERFLOW if a receiver lacks
+ *                   room (its split columns and offsets are then not written,
+ *                   those of the others are) and no payload; else everything.
+ * Four kernels: per-(table, rank) key counts, a per-receiver plan (every
+ * source's table scan, then the receiver's blocks in (source, table) order),
+ * and a block copy each for keys and lengths that reads each source's arrays
+ * in place.
+ */
+int keys_exchange(int W, int n_tables, int64_t batch, const int32_t *const *lengths,
+                  const int64_t *const *keys, const int64_t *n_keys,
+                  int32_t *const *lengths_out, const int64_t *lengths_cap,
+                  int64_t *const *keys_out, const int64_t *keys_cap, int64_t *split_keys,
+                  int64_t *split_lengths, int64_t *recv_off_keys, void *workspace,
+                  size_t workspace_bytes, int32_t *status, hipStream_t stream);
+
+/*
  * Plain contiguous device copy of `bytes` bytes (dst and src device pointers,
  * not overlapping), with the same copy loop as a2av_copy. A bandwidth
  * ceiling for the payload kernel and the reference for counter scaling.

@@ -154,3 +154,106 @@ def test_embedding_key_exchange_full(ref):
         own = list(range(d, NT, W))
         want = np.concatenate([lengths[s][own].reshape(-1) for s in range(W)])
         assert np.array_equal(gl[4][d].reshape(-1).view(np.int32), want)
+
+
+# ------------------------------------------------------------------ fused exchange
+def gpu_keys_exchange(W, NT, batch, lengths, keys, lcap=None, kcap=None, status_init=0, pad=0,
+                      ref=None):
+    """keys_exchange on the GPU; capacities default to the oracle's (what each
+    receiver gets). Returns (status, [lengths_out], [keys_out], split_keys,
+    split_lengths, recv_off, guards)."""
+    if lcap is None or kcap is None:
+        _, lo, ko, _, _, _ = ref.keys_exchange(W, NT, batch, lengths, keys)
+        lcap = [x.size for x in lo] if lcap is None else lcap
+        kcap = [x.size for x in ko] if kcap is None else kcap
+    lin = [upload_rows(l.reshape(-1).view(np.uint8), pad=pad) for l in lengths]
+    kin = [upload_rows(k.view(np.uint8), pad=pad) for k in keys]
+    lout = [GuardedBuffer(int(c) * 4, pad=pad) for c in lcap]
+    kout = [GuardedBuffer(int(c) * 8, pad=pad) for c in kcap]
+    sk = torch.full((W, W), -7, dtype=torch.int64, device="cuda")
+    sl = torch.full((W, W), -7, dtype=torch.int64, device="cuda")
+    ro = torch.full((W, W + 1), -7, dtype=torch.int64, device="cuda")
+    ws = torch.empty(B.keys_exchange_workspace_bytes(W, NT), dtype=torch.uint8, device="cuda")
+    status = torch.full((1,), status_init, dtype=torch.int32, device="cuda")
+    B.keys_exchange(W, NT, batch, [b.view for b in lin], [b.view for b in kin],
+                    [k.size for k in keys], [b.view for b in lout], list(lcap),
+                    [b.view for b in kout], list(kcap), sk, sl, ro, ws, status)
+    torch.cuda.synchronize()
+    guards = all(b.guards_intact() for b in lin + kin + lout + kout)
+    return (int(status.item()), [b.host().view(np.int32) for b in lout],
+            [b.host().view(np.int64) for b in kout], sk.cpu().numpy(), sl.cpu().numpy(),
+            ro.cpu().numpy(), guards)
+
+
+def _compare_exchange(got, want, what=""):
+    st, lo, ko, sk, sl, ro, guards = got
+    rst, rlo, rko, rsk, rsl, rro = want
+    assert guards, what
+    assert st == rst, f"{what}: status {st} != oracle {rst}"
+    assert np.array_equal(sk, rsk) and np.array_equal(sl, rsl), f"{what}: splits"
+    assert np.array_equal(ro, rro), f"{what}: receive offsets"
+    for d in range(len(lo)):
+        if st == 0:
+            assert np.array_equal(lo[d], rlo[d]), f"{what}: lengths at {d}"
+            assert np.array_equal(ko[d], rko[d]), f"{what}: keys at {d}"
+        else:
+            assert (lo[d] == LSENT).all() and (ko[d] == KSENT).all(), f"{what}: written at {d}"
+
+
+@pytest.mark.parametrize("W,NT,batch,pad", [
+    (8, 26, 64, 0), (8, 26, 333, 0), (3, 7, 100, 4), (5, 2, 10, 0), (4, 0, 10, 0), (2, 3, 0, 0),
+    (1, 5, 33, 0), (16, 300, 7, 0), (64, 100, 3, 0), (3, 4096, 2, 0),
+])
+def test_keys_exchange_matches_oracle(ref, W, NT, batch, pad):
+    _say("keys_exchange", W, NT, batch, pad)
+    g = I.rng(W * 7 + NT + batch)
+    lengths, keys = _inputs(g, W, NT, batch, lam=3.0, cap=10)
+    want = ref.keys_exchange(W, NT, batch, lengths, keys)
+    assert want[0] == 0
+    got = gpu_keys_exchange(W, NT, batch, lengths, keys, pad=pad, ref=ref)
+    _compare_exchange(got, want, f"W={W} NT={NT} batch={batch}")
+
+
+@pytest.mark.parametrize("case", ["negative", "overrun", "keys_room", "lengths_room", "poisoned"])
+def test_keys_exchange_errors(ref, case):
+    W, NT, batch = 4, 9, 50
+    g = I.rng(13)
+    lengths, keys = _inputs(g, W, NT, batch)
+    _, lo, ko, _, _, _ = ref.keys_exchange(W, NT, batch, lengths, keys)
+    lcap = [x.size for x in lo]
+    kcap = [x.size for x in ko]
+    init = 0
+    if case == "negative":
+        lengths[3][1, 2] = -5
+    elif case == "overrun":
+        keys[0] = keys[0][:-3]
+    elif case == "keys_room":
+        kcap[2] -= 1
+    elif case == "lengths_room":
+        lcap[1] -= 1
+    else:
+        init = 8
+    got = gpu_keys_exchange(W, NT, batch, lengths, keys, lcap, kcap, status_init=init)
+    if case == "poisoned":
+        st, lo_, ko_, sk, sl, ro, guards = got
+        assert guards and st == init and (sk == -7).all() and (ro == -7).all()
+        assert all((l == LSENT).all() for l in lo_) and all((k == KSENT).all() for k in ko_)
+        return
+    want = ref.keys_exchange(W, NT, batch, lengths, keys, np.array(lcap), np.array(kcap))
+    assert want[0] != 0
+    _compare_exchange(got, want, case)
+
+
+def test_keys_exchange_full(ref):
+    """W=8, 26 tables, batch 8192, lengths min(Poisson(20), 100): the fused
+    exchange against the oracle's composition, every byte."""
+    W, NT, batch = 8, 26, 8192
+    g = I.rng(89)
+    ranks = [I.emb_keys_rank(g) for _ in range(W)]
+    lengths = [r.lengths for r in ranks]
+    keys = [r.keys for r in ranks]
+    want = ref.keys_exchange(W, NT, batch, lengths, keys)
+    assert want[0] == 0
+    got = gpu_keys_exchange(W, NT, batch, lengths, keys, ref=ref)
+    _compare_exchange(got, want, "full")
+    _say("keys_exchange full: keys received", [k.size for k in got[2]])
