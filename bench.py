@@ -547,8 +547,25 @@ def key_rows(torch, B, I, o, out):
     res["chain"] = row_entry(kc.bucket_bytes + kc.key_bytes + kc.len_bytes, ms)
     ms = time_events(torch, kc.fused, 50)
     res["fused_exchange"] = row_entry(kc.fused_bytes, ms)
+    # the fused exchange captured once into a HIP graph and replayed
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    kg = KeyChain(torch, B, I, 8, 901, side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        kg.fused()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            kg.fused()
     torch.cuda.synchronize()
-    _check_status(B, [("key chain", kc.status), ("fused exchange", kc.fstatus)])
+    ms = time_events(torch, graph.replay, 50)
+    res["fused_exchange_graph"] = row_entry(kg.fused_bytes, ms)
+    torch.cuda.synchronize()
+    _check_status(B, [("key chain", kc.status), ("fused exchange", kc.fstatus),
+                      ("graph replays", kg.fstatus)])
+    for a, b in zip(kc.fkey_out + kc.flen_out, kg.fkey_out + kg.flen_out):
+        if not torch.equal(a, b):
+            raise RuntimeError("graph replay of the key exchange differs from the eager call")
     # the fused exchange delivers the same bytes as the chain
     for a, b in zip(kc.key_out + kc.len_out, kc.fkey_out + kc.flen_out):
         if not torch.equal(a, b):
