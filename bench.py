@@ -21,7 +21,8 @@ Also reported on the same JSON line:
   headline      W in {4, 8} x {32 MiB, 1 GiB} per rank, and W in {16, 64} at
                 32 MiB, payload kernel and step
   ceilings      plain device copy of the same bytes (this library's copy loop
-                and torch's D2D copy)
+                and torch's D2D copy), and the exchange as W*W separate
+                device-to-device copies (the library-call baseline)
 """
 from __future__ import annotations
 
@@ -153,6 +154,20 @@ def run_config(torch, B, I, W, mib, steps, warmup, nsets, entry="fused"):
     if entry == "fused":
         res["kernel_ms_mean"] = gpu_ms / steps
         res["kernel_gbs"] = res["gpu_step_gbs"]
+        # per-launch distribution from an event pair around each call (the
+        # pair adds a little time of its own, so these read slightly high)
+        n = min(steps, 100)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            evs[i][0].record(stream)
+            step(sets[i % nsets])
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        per = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        res["per_launch_us"] = {"min": round(per[0], 2), "p50": round(per[len(per) // 2], 2),
+                                "p90": round(per[min(len(per) - 1, (9 * len(per)) // 10)], 2)}
     else:
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)]
@@ -170,6 +185,45 @@ def run_config(torch, B, I, W, mib, steps, warmup, nsets, entry="fused"):
     del sets
     torch.cuda.empty_cache()
     return res
+
+
+def naive_per_chunk(torch, I, W=4, mib=32, reps=50, nsets=8):
+    """The same exchange as W * W separate device-to-device copies (one
+    hipMemcpyAsync per (source, destination) chunk, offsets computed on the
+    host): the library-call baseline."""
+    cols = 4096
+    R = cols * 2
+    rows = I.rows_for_mib(mib, R)
+    sets = []
+    for k in range(nsets):
+        g = I.rng(100 + 17 * W + mib + k)
+        S = I.uniform_splits(g, W, rows)
+        ins = [torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda") for _ in range(W)]
+        cap = S.sum(axis=0)
+        outs = [torch.empty((int(c), cols), dtype=torch.bfloat16, device="cuda") for c in cap]
+        so = [[int(S[s, :d].sum()) for d in range(W)] for s in range(W)]
+        ro = [[int(S[:s, d].sum()) for s in range(W)] for d in range(W)]
+        pairs = [(outs[d][ro[d][s]:ro[d][s] + int(S[s, d])], ins[s][so[s][d]:so[s][d] + int(S[s, d])])
+                 for d in range(W) for s in range(W) if S[s, d] > 0]
+        sets.append((pairs, 2 * R * int(S.sum())))
+
+    def step(i):
+        for dst, src in sets[i % nsets][0]:
+            dst.copy_(src)
+
+    for i in range(3):
+        step(i)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(reps):
+        step(i)
+    b.record()
+    torch.cuda.synchronize()
+    moved = sum(sets[i % nsets][1] for i in range(reps))
+    del sets
+    torch.cuda.empty_cache()
+    return gbps(moved, a.elapsed_time(b) / 1e3)
 
 
 def ceilings(torch, B, nbytes, reps=50, nsets=8):
@@ -195,9 +249,23 @@ def ceilings(torch, B, nbytes, reps=50, nsets=8):
     return out
 
 
+def host_cpu():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
 def cpu_baseline(torch, I, W=4, mib=32, budget_s=10.0):
     """The CPU oracle on one full set of the workload, repeated for about
-    budget_s seconds (at least 3 runs); single-threaded C."""
+    budget_s seconds (at least 3 runs); single-threaded C, pinned to one core
+    while it runs."""
     import numpy as np
     sys.path.insert(0, ROOT)
     from oracle.ref import Oracle
@@ -214,17 +282,25 @@ def cpu_baseline(torch, I, W=4, mib=32, budget_s=10.0):
     Y = [np.empty(int(c) * R, dtype=np.uint8) for c in cap]
     in_rows = np.full(W, rows, dtype=np.int64)
     times = []
-    t_start = time.perf_counter()
-    while len(times) < 3 or (time.perf_counter() - t_start < budget_s and len(times) < 500):
-        t0 = time.perf_counter()
-        st = o.a2av(R, X, in_rows, Y, cap, S)[0]
-        times.append(time.perf_counter() - t0)
-        assert st == 0
+    old_aff = os.sched_getaffinity(0)
+    core = min(old_aff)
+    os.sched_setaffinity(0, {core})
+    try:
+        t_start = time.perf_counter()
+        while len(times) < 3 or (time.perf_counter() - t_start < budget_s and len(times) < 500):
+            t0 = time.perf_counter()
+            st = o.a2av(R, X, in_rows, Y, cap, S)[0]
+            times.append(time.perf_counter() - t0)
+            assert st == 0
+    finally:
+        os.sched_setaffinity(0, old_aff)
     moved = 2 * R * int(S.sum())
     med = statistics.median(times)
+    model, ncpu = host_cpu()
     return {"value": round(gbps(moved, med), 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"whole W={W} x {mib} MiB/rank a2av (exchange+offsets+copy), "
-                      f"{len(times)} runs, median {med * 1e3:.1f} ms"}
+                      f"{len(times)} runs, median {med * 1e3:.1f} ms, pinned to core {core} of "
+                      f"{ncpu} ({model})"}
 
 
 def time_events(torch, fn, reps, warmup=2):
@@ -679,8 +755,11 @@ def main(argv=None):
                     "step_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
                     "kernel_us": round(r["kernel_ms_mean"] * 1e3, 2),
                     "step_us": round(r["step_ms"] * 1e3, 2)}
+                if "per_launch_us" in r:
+                    headline[key]["per_launch_us"] = r["per_launch_us"]
                 log("bench: headline", key, json.dumps(headline[key]))
     ceil = ceilings(torch, B, int(main_res["bytes_per_step"]))
+    ceil["naive_w2_memcpy_gbs"] = naive_per_chunk(torch, I)
     log("bench: ceilings", json.dumps(ceil))
 
     rows = {}
@@ -715,7 +794,8 @@ def main(argv=None):
                    "frac_of_hbm_peak": round(main_res["step_gbs"] / HBM_PEAK_GBS, 4),
                    "three_call_step_gbs": round(three["step_gbs"], 1),
                    "three_call_copy_kernel_gbs": round(three["kernel_gbs"], 1),
-                   "three_call_copy_kernel_frac": round(three["kernel_gbs"] / HBM_PEAK_GBS, 4)},
+                   "three_call_copy_kernel_frac": round(three["kernel_gbs"] / HBM_PEAK_GBS, 4),
+                   "per_launch_us": main_res.get("per_launch_us")},
         "roofline": {"bound": "hbm", "kernel": "k_a2av_wave (one launch: exchange+offsets+copy)",
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
