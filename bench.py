@@ -63,11 +63,12 @@ class VSet:
     """One independent set of W virtual ranks: payload, outputs, device
     splits/offsets/status, and pre-marshalled C-ABI argument tuples."""
 
-    def __init__(self, torch, B, I, W, rows, cols, seed, stream_handle):
+    def __init__(self, torch, B, I, W, rows, cols, seed, stream_handle, splits="uniform"):
         from embeddings_a2av_virtual_amd.vranks import A2av
         self.W, self.rows, self.R = W, rows, cols * 2
         g = I.rng(seed)
-        self.S_host = I.uniform_splits(g, W, rows)
+        self.S_host = (I.uniform_splits(g, W, rows) if splits == "uniform"
+                       else I.half_zero_splits(g, W, rows))
         self.ins = [I.payload_bf16(rows, cols, seed * 1000 + r, device="cuda") for r in range(W)]
         cap = self.S_host.sum(axis=0)
         self.cap = [int(c) for c in cap]
@@ -94,7 +95,7 @@ class VSet:
                            vp(st.recv_off.data_ptr()), vp(st.status.data_ptr()), hs)
 
 
-def run_config(torch, B, I, W, mib, steps, warmup, nsets, entry="fused"):
+def run_config(torch, B, I, W, mib, steps, warmup, nsets, entry="fused", splits="uniform"):
     """Time `steps` whole a2av steps over `nsets` rotating buffer sets.
 
     entry="fused": one a2av_all_to_all_vdev call per step (one kernel that
@@ -113,8 +114,8 @@ def run_config(torch, B, I, W, mib, steps, warmup, nsets, entry="fused"):
     hs = stream.cuda_stream
     cols = 4096
     rows = I.rows_for_mib(mib, cols * 2)
-    sets = [VSet(torch, B, I, W, rows, cols, seed=100 + 17 * W + mib + s, stream_handle=hs)
-            for s in range(nsets)]
+    sets = [VSet(torch, B, I, W, rows, cols, seed=100 + 17 * W + mib + s, stream_handle=hs,
+                 splits=splits) for s in range(nsets)]
     torch.cuda.synchronize()
 
     def step(vs, ev=None):
@@ -716,6 +717,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the MoE pack / un-pack and key-exchange measurements")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time W=4 at 1..4096 MiB per rank, uniform and 50%%-zero splits")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -758,6 +761,18 @@ def main(argv=None):
                 if "per_launch_us" in r:
                     headline[key]["per_launch_us"] = r["per_launch_us"]
                 log("bench: headline", key, json.dumps(headline[key]))
+    sweep = {}
+    if args.sweep:
+        for splits in ("uniform", "half_zero"):
+            for mib in [1 << i for i in range(13)]:
+                per_step = 2 * 4 * mib << 20
+                nsets = max(1, min(8, (2 << 30) // per_step))
+                steps = max(5, min(200, (8 << 30) // per_step))
+                r = run_config(torch, B, I, 4, mib, steps, 3, nsets, "fused", splits)
+                sweep[f"{splits}_{mib}mib"] = {"kernel_gbs": round(r["kernel_gbs"], 1),
+                                               "kernel_us": round(r["kernel_ms_mean"] * 1e3, 2),
+                                               "step_gbs": round(r["step_gbs"], 1)}
+                log("bench: sweep", splits, mib, json.dumps(sweep[f"{splits}_{mib}mib"]))
     ceil = ceilings(torch, B, int(main_res["bytes_per_step"]))
     ceil["naive_w2_memcpy_gbs"] = naive_per_chunk(torch, I)
     log("bench: ceilings", json.dumps(ceil))
@@ -805,6 +820,7 @@ def main(argv=None):
                      "avg_launch_us": round(main_res["kernel_ms_mean"] * 1e3, 3)},
         "cpu_baseline": cpu,
         "headline": headline,
+        "sweep": sweep or None,
         "rows": rows,
         "ceilings": {k: round(v, 1) for k, v in ceil.items()},
     }
