@@ -722,9 +722,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} requested, but this build runs on ONE GPU: the "
-              "W ranks are virtual (partitions of one GPU's HBM) and there is no multi-GPU "
-              "path; run with --gpus 1.", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} requested, but this benchmark runs on ONE GPU: "
+              "the W ranks are virtual (partitions of one GPU's HBM) and there is no "
+              "multi-GPU path; run with --gpus 1.", file=sys.stderr)
         return 2
     if int(os.environ.get("RANK", "0")) != 0:
         return 0
