@@ -457,3 +457,64 @@ done:
     free(lo); free(ko); free(Sk); free(Sl);
     return st;
 }
+
+/*
+ * The MoE dispatch with its receive-side regroup in one step, and its
+ * inverse. Pack side: rank s's rows in pack order (expert ascending, the
+ * counts[s][e] rows of expert e at Σ_{e'<e} counts[s][e']). Expert side:
+ * rank d's rows in expert-major order (owned expert j outer, source s inner).
+ * Direction 0 moves pack side -> expert side (the dispatch a2av followed by
+ * the regroup); direction 1 moves expert side -> pack side (the inverse
+ * regroup followed by the return a2av).
+ */
+int ref_moe_dispatch_grouped(int W, int E, size_t R, const int64_t *counts,
+                             const void *const *in, const int64_t *in_rows,
+                             void *const *out, const int64_t *out_cap,
+                             int64_t *expert_offsets, int direction) {
+    if (W < 1 || W > REF_MAX_W || E < 1 || E % W != 0 || R == 0 || !counts || !in || !in_rows ||
+        !out || !out_cap || !expert_offsets || (direction != 0 && direction != 1))
+        return REF_EARG;
+    const int P = E / W;
+    for (int64_t i = 0; i < (int64_t)W * E; i++)
+        if (!split_is_valid(counts[i])) return REF_BAD_SPLIT;
+    /* the expert side: offsets of each owned expert at its owner */
+    for (int d = 0; d < W; d++) {
+        int64_t run = 0;
+        for (int j = 0; j < P; j++) {
+            expert_offsets[d * (P + 1) + j] = run;
+            for (int s = 0; s < W; s++) run += counts[s * E + d * P + j];
+        }
+        expert_offsets[d * (P + 1) + P] = run;
+    }
+    int st = 0;
+    for (int r = 0; r < W; r++) {
+        int64_t pack_total = 0;
+        for (int e = 0; e < E; e++) pack_total += counts[r * E + e];
+        const int64_t exp_total = expert_offsets[r * (P + 1) + P];
+        const int64_t sent = direction == 0 ? pack_total : exp_total;
+        const int64_t received = direction == 0 ? exp_total : pack_total;
+        if (sent > in_rows[r]) st |= REF_SEND_OVERRUN;
+        if (received > out_cap[r]) st |= REF_RECV_OVERFLOW;
+        if ((sent > 0 && !in[r]) || (received > 0 && !out[r])) return REF_EARG;
+    }
+    if (st) return st;
+    for (int s = 0; s < W; s++) {
+        int64_t pack_pos = 0;
+        for (int e = 0; e < E; e++) {
+            const int d = e / P, j = e % P;
+            const int64_t n = counts[s * E + e];
+            int64_t exp_pos = expert_offsets[d * (P + 1) + j];
+            for (int s2 = 0; s2 < s; s2++) exp_pos += counts[s2 * E + e];
+            if (n > 0) {
+                if (direction == 0)
+                    memcpy((unsigned char *)out[d] + (size_t)exp_pos * R,
+                           (const unsigned char *)in[s] + (size_t)pack_pos * R, (size_t)n * R);
+                else
+                    memcpy((unsigned char *)out[s] + (size_t)pack_pos * R,
+                           (const unsigned char *)in[d] + (size_t)exp_pos * R, (size_t)n * R);
+            }
+            pack_pos += n;
+        }
+    }
+    return 0;
+}

@@ -119,6 +119,22 @@ int ref_keys_bucketize(int W, int n_tables, int64_t batch, const int32_t *length
                        const int64_t *keys, int64_t n_keys, int32_t *lengths_out,
                        int64_t *keys_out, int64_t *split_keys, int64_t *split_lengths);
 
+/* MoE dispatch plus receive-side regroup in one step, for all W ranks.
+ * counts is the W x E matrix of moe_pack's expert counts (row s = source s).
+ * Pack side of rank s: its rows in pack order (expert ascending). Expert side
+ * of rank d: for each owned expert j (e = d*P + j, P = E/W), for each source
+ * s, counts[s][e] rows. direction 0: in = pack side (indexed by source),
+ * out = expert side (indexed by owner); direction 1: the reverse.
+ * expert_offsets [W][P+1] = rows before owned expert j on the expert side
+ * (total at P), written whenever the counts are valid. REF_BAD_SPLIT for a
+ * count outside [0, 2^40] (nothing written); else REF_SEND_OVERRUN /
+ * REF_RECV_OVERFLOW when a rank's sent / received total exceeds in_rows /
+ * out_cap (no payload). */
+int ref_moe_dispatch_grouped(int W, int E, size_t R, const int64_t *counts,
+                             const void *const *in, const int64_t *in_rows,
+                             void *const *out, const int64_t *out_cap,
+                             int64_t *expert_offsets, int direction);
+
 /* The whole key exchange of one batch for all W ranks: ref_keys_bucketize on
  * every source, then keys (8-byte rows) and lengths (4-byte rows) as two
  * ref_a2av calls with the bucketing's split rows. lengths_cap / keys_cap are

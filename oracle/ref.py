@@ -62,11 +62,13 @@ def _bind(lib):
     lib.ref_keys_bucketize.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, i32p,
                                        ctypes.c_void_p, ctypes.c_int64, i32p, ctypes.c_void_p,
                                        i64p, i64p]
+    lib.ref_moe_dispatch_grouped.argtypes = [ctypes.c_int, ctypes.c_int, sz, i64p, vpp, i64p, vpp,
+                                             i64p, i64p, ctypes.c_int]
     lib.ref_keys_exchange.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, vpp, vpp, i64p,
                                       vpp, i64p, vpp, i64p, i64p, i64p, i64p]
     for name in ("ref_exchange_splits", "ref_offsets", "ref_copy", "ref_a2av", "ref_source_of",
                  "ref_moe_pack", "ref_moe_unpack", "ref_moe_regroup", "ref_moe_combine",
-                 "ref_keys_bucketize", "ref_keys_exchange"):
+                 "ref_keys_bucketize", "ref_keys_exchange", "ref_moe_dispatch_grouped"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -239,3 +241,17 @@ class Oracle:
                                         _i64(n_keys), _ptrs(lo), _i64(lengths_cap), _ptrs(ko),
                                         _i64(keys_cap), _i64(sk), _i64(sl), _i64(ro))
         return st, lo, ko, sk, sl, ro
+
+    def moe_dispatch_grouped(self, W, E, R, counts, ins, in_rows, out_cap, direction=0):
+        """All W ranks. ins: per-rank uint8 arrays; returns (status, [out bytes,
+        out_cap[r] * R each, zero-filled], expert_offsets [W, E/W + 1] (-7 where
+        not written))."""
+        counts = np.ascontiguousarray(counts, dtype=np.int64)
+        ins = [np.ascontiguousarray(x).view(np.uint8).reshape(-1) for x in ins]
+        in_rows = np.ascontiguousarray(in_rows, dtype=np.int64)
+        out_cap = np.ascontiguousarray(out_cap, dtype=np.int64)
+        outs = [np.zeros(max(int(c), 0) * R, dtype=np.uint8) for c in out_cap]
+        eoff = np.full((W, E // W + 1), -7, dtype=np.int64)
+        st = self.lib.ref_moe_dispatch_grouped(W, E, R, _i64(counts), _ptrs(ins), _i64(in_rows),
+                                               _ptrs(outs), _i64(out_cap), _i64(eoff), direction)
+        return st, outs, eoff

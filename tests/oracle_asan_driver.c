@@ -184,6 +184,31 @@ static void one_keys_exchange(int W, int n_tables, int64_t batch) {
     free(sk); free(sl); free(ro);
 }
 
+static void one_grouped(int W, int E, size_t R) {
+    const int P = E / W;
+    int64_t *counts = malloc(sizeof(int64_t) * W * E);
+    int64_t *rows = calloc(W, sizeof(int64_t)), *cap = calloc(W, sizeof(int64_t));
+    int64_t *eoff = malloc(sizeof(int64_t) * W * (P + 1));
+    for (int i = 0; i < W * E; i++) counts[i] = (int64_t)(next_u64() % 4);
+    for (int s = 0; s < W; s++)
+        for (int e = 0; e < E; e++) { rows[s] += counts[s * E + e]; cap[e / P] += counts[s * E + e]; }
+    unsigned char **in = malloc(sizeof(void *) * W), **out = malloc(sizeof(void *) * W);
+    unsigned char **back = malloc(sizeof(void *) * W);
+    for (int r = 0; r < W; r++) {
+        in[r] = malloc(rows[r] * R + 1);
+        back[r] = malloc(rows[r] * R + 1);
+        out[r] = malloc(cap[r] * R + 1);
+        for (int64_t b = 0; b < rows[r] * (int64_t)R; b++) in[r][b] = (unsigned char)next_u64();
+    }
+    CHECK(ref_moe_dispatch_grouped(W, E, R, counts, (const void *const *)in, rows,
+                                   (void *const *)out, cap, eoff, 0) == 0);
+    CHECK(ref_moe_dispatch_grouped(W, E, R, counts, (const void *const *)out, cap,
+                                   (void *const *)back, rows, eoff, 1) == 0);
+    for (int r = 0; r < W; r++) CHECK(rows[r] == 0 || memcmp(in[r], back[r], rows[r] * R) == 0);
+    for (int r = 0; r < W; r++) { free(in[r]); free(out[r]); free(back[r]); }
+    free(in); free(out); free(back); free(counts); free(rows); free(cap); free(eoff);
+}
+
 int main(void) {
     const size_t widths[] = {1, 3, 8, 16, 100};
     for (int W = 1; W <= 9; W++)
@@ -204,6 +229,9 @@ int main(void) {
     one_bucketize(8, 26, 64);
     one_bucketize(3, 2, 0);
     one_bucketize(5, 0, 10);
+    one_grouped(8, 256, 16);
+    one_grouped(3, 12, 5);
+    one_grouped(1, 1, 1);
     one_keys_exchange(8, 26, 32);
     one_keys_exchange(3, 2, 5);
     one_keys_exchange(1, 3, 4);

@@ -514,6 +514,73 @@ def pin_moe_dispatch_regroup_closed_form(o):
             assert np.array_equal(got, np.array(want, np.uint8).reshape(-1, R_bytes))
 
 
+def pin_moe_dispatch_grouped(o):
+    """Dispatch with regroup in one step: equals the a2av (splits = counts
+    grouped by owner) followed by the per-rank regroup, two functions pinned
+    on their own; the inverse direction brings every pack-order row home; and
+    after a real pack each expert's rows are its tokens in (source, token)
+    order."""
+    g = np.random.default_rng(31)
+    for W, E, Rb in ((4, 16, 8), (8, 256, 3), (1, 4, 5), (3, 3, 2), (2, 8, 1)):
+        P = E // W
+        counts = g.integers(0, 5, size=(W, E)).astype(np.int64)
+        counts[g.random((W, E)) < 0.3] = 0
+        rows = counts.sum(axis=1)
+        ins = [g.integers(0, 256, size=(int(rows[s]) + 2) * Rb, dtype=np.uint8) for s in range(W)]
+        in_rows = rows + 2
+        exp_tot = np.array([int(counts[:, d * P:(d + 1) * P].sum()) for d in range(W)])
+        cap = exp_tot + 1
+        st, outs, eoff = o.moe_dispatch_grouped(W, E, Rb, counts, ins, in_rows, cap, 0)
+        assert st == 0
+        # the composition: a2av with owner-grouped splits, then regroup
+        S = np.stack([counts[s].reshape(W, P).sum(axis=1) for s in range(W)]).astype(np.int64)
+        st2, Y, _, _, _ = run_a2av(o, Rb, [x.reshape(-1, Rb) for x in ins], S)
+        assert st2 == 0
+        for d in range(W):
+            st3, want, weoff = o.moe_regroup(W, E, d, Rb, counts, Y[d], exp_tot[d], cap[d], 0)
+            assert st3 == 0
+            assert np.array_equal(outs[d][:exp_tot[d] * Rb], want[:exp_tot[d] * Rb])
+            assert not outs[d][exp_tot[d] * Rb:].any()
+            assert np.array_equal(eoff[d], weoff)
+        # inverse
+        st4, back, eoff2 = o.moe_dispatch_grouped(W, E, Rb, counts, outs, cap, in_rows, 1)
+        assert st4 == 0 and np.array_equal(eoff2, eoff)
+        for s in range(W):
+            n = int(rows[s]) * Rb
+            assert np.array_equal(back[s][:n], ins[s][:n]) and not back[s][n:].any()
+    # after a real pack: expert e's rows are the tokens routed to it, source by source
+    W, T, k, E, Rb = 4, 30, 3, 12, 6
+    P = E // W
+    toks, idss, sends, counts = [], [], [], []
+    for r in range(W):
+        tokens, ids = _moe_case(g, T, k, E, Rb, distinct=True)
+        st, send, perm, splits, cnt = o.moe_pack(T, k, E, W, Rb, tokens, ids)
+        assert st == 0
+        toks.append(tokens); idss.append(ids); sends.append(send); counts.append(cnt)
+    counts = np.stack(counts)
+    cap = [int(counts[:, d * P:(d + 1) * P].sum()) for d in range(W)]
+    st, outs, eoff = o.moe_dispatch_grouped(W, E, Rb, counts, sends, [T * k] * W, cap, 0)
+    assert st == 0
+    for d in range(W):
+        got_rows = outs[d].reshape(-1, Rb)
+        for j in range(P):
+            e = d * P + j
+            want = [toks[s][t] for s in range(W) for t in range(T) for jj in range(k)
+                    if idss[s][t, jj] == e]
+            got = got_rows[eoff[d, j]:eoff[d, j + 1]]
+            assert np.array_equal(got, np.array(want, np.uint8).reshape(-1, Rb))
+    # errors
+    c2 = counts.copy(); c2[1, 5] = -1
+    st, outs2, e2 = o.moe_dispatch_grouped(W, E, Rb, c2, sends, [T * k] * W, cap, 0)
+    assert st == R.BAD_SPLIT and (e2 == -7).all() and not any(x.any() for x in outs2)
+    st, outs2, e2 = o.moe_dispatch_grouped(W, E, Rb, counts, sends, [T * k - 1] * W, cap, 0)
+    assert st == R.SEND_OVERRUN and not any(x.any() for x in outs2)
+    assert np.array_equal(e2, eoff)
+    cap2 = list(cap); cap2[2] -= 1
+    st, outs2, _ = o.moe_dispatch_grouped(W, E, Rb, counts, sends, [T * k] * W, cap2, 0)
+    assert st == R.RECV_OVERFLOW and not any(x.any() for x in outs2)
+
+
 # ------------------------------------------------------------------ gate-weighted combine
 def _round_f32(x):
     """A Fraction rounded to the nearest binary32, ties to even (finite, in

@@ -78,6 +78,12 @@ MUTANTS = {
     "bucketize_reads_keys_at_output_position": [
         ("memcpy(keys_out + kpos, keys + tstart[t], (size_t)tk[t] * 8);",
          "memcpy(keys_out + kpos, keys + kpos, (size_t)tk[t] * 8);", 0)],
+    "grouped_drops_earlier_sources": [
+        ("            for (int s2 = 0; s2 < s; s2++) exp_pos += counts[s2 * E + e];",
+         "            (void)0;", 0)],
+    "grouped_pack_pos_not_advanced": [
+        ("            pack_pos += n;\n        }\n    }\n    return 0;\n}",
+         "            (void)n;\n        }\n    }\n    return 0;\n}", 0)],
     "keys_exchange_offsets_inclusive": [
         ("            recv_off_keys[d * (W + 1) + s] = run;\n            run += Sk[s * W + d];",
          "            run += Sk[s * W + d];\n            recv_off_keys[d * (W + 1) + s] = run;", 0)],
