@@ -552,6 +552,33 @@ def moe_rows(torch, B, I, o, out):
                    note=f"rank {W - 1} whole ({cap[W - 1]} rows)")
     out["moe_regroup_to_expert"] = row_entry(moved, ms0, **cpu)
     out["moe_regroup_to_source"] = row_entry(moved, ms1)
+    # ---- the dispatch and the regroup as one copy, and the inverse
+    gws = torch.empty(B.moe_dispatch_grouped_workspace_bytes(W, E), dtype=torch.uint8,
+                      device="cuda")
+    gst = torch.zeros(1, dtype=torch.int32, device="cuda")
+    home = [torch.empty((Q, hidden), dtype=torch.bfloat16, device="cuda") for _ in range(W)]
+    gdisp = lambda: B.moe_dispatch_grouped(W, E, R, counts, send, [Q] * W, grp, cap, eoff, 0,
+                                           gws, gst)
+    gret = lambda: B.moe_dispatch_grouped(W, E, R, counts, grp, cap, home, [Q] * W, eoff, 1,
+                                          gws, gst)
+    ms0 = time_events(torch, gdisp, 5)
+    ms1 = time_events(torch, gret, 5)
+    cpu = {}
+    if o is not None:
+        cnt_h = counts.cpu().numpy()
+        sh = [x.view(torch.uint8).cpu().numpy().reshape(-1) for x in send]
+        cs = time_cpu(lambda: o.moe_dispatch_grouped(W, E, R, cnt_h, sh, [Q] * W, cap, 0),
+                      budget_s=3.0, min_runs=1)
+        cpu = dict(cpu_bytes=moved, cpu_s=cs, note="all ranks whole (memcpy per block)")
+        del sh
+    out["moe_dispatch_grouped"] = row_entry(moved, ms0, **cpu)
+    out["moe_return_grouped"] = row_entry(moved, ms1)
+    torch.cuda.synchronize()
+    _check_status(B, [("grouped", gst)])
+    for r in range(W):
+        if not torch.equal(home[r].view(torch.int16), send[r].view(torch.int16)):
+            raise RuntimeError("grouped dispatch + return did not bring the rows home")
+    del home
     del grp
     # ---- return a2av: every row goes home
     bk = A2av(W)

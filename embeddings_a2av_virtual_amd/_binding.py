@@ -24,7 +24,8 @@ __all__ = [
     "a2av_abi_version", "a2av_strerror", "a2av_exchange_splits", "a2av_offsets", "a2av_copy",
     "a2av_all_to_all_vdev",
     "moe_pack_workspace_bytes", "moe_pack", "moe_unpack", "moe_combine",
-    "moe_regroup_workspace_bytes", "moe_regroup", "keys_bucketize_workspace_bytes",
+    "moe_regroup_workspace_bytes", "moe_regroup", "moe_dispatch_grouped_workspace_bytes",
+    "moe_dispatch_grouped", "keys_bucketize_workspace_bytes",
     "keys_bucketize", "keys_exchange_workspace_bytes", "keys_exchange", "a2av_device_copy",
     "MAX_TABLES",
 ]
@@ -79,6 +80,10 @@ def lib():
         L.moe_regroup_workspace_bytes.argtypes = [i32, i32]
         L.moe_regroup_workspace_bytes.restype = sz
         L.moe_regroup.argtypes = [i32, i32, sz, vp, vpp, i64p, vpp, i64p, vp, i32, vp, sz, vp, vp]
+        L.moe_dispatch_grouped_workspace_bytes.argtypes = [i32, i32]
+        L.moe_dispatch_grouped_workspace_bytes.restype = sz
+        L.moe_dispatch_grouped.argtypes = [i32, i32, sz, vp, vpp, i64p, vpp, i64p, vp, i32, vp, sz,
+                                           vp, vp]
         L.keys_bucketize_workspace_bytes.argtypes = [i32, i32]
         L.keys_bucketize_workspace_bytes.restype = sz
         L.keys_bucketize.argtypes = [i32, i32, i64, vpp, vpp, i64p, vpp, vpp, vp, vp, vp, sz, vp,
@@ -89,7 +94,8 @@ def lib():
                                     vp, sz, vp, vp]
         L.a2av_device_copy.argtypes = [vp, vp, sz, vp]
         for f in ("a2av_exchange_splits", "a2av_offsets", "a2av_copy", "a2av_all_to_all_vdev",
-                  "moe_pack", "moe_unpack", "moe_combine", "moe_regroup", "keys_bucketize", "keys_exchange",
+                  "moe_pack", "moe_unpack", "moe_combine", "moe_regroup", "moe_dispatch_grouped",
+                  "keys_bucketize", "keys_exchange",
                   "a2av_device_copy"):
             getattr(L, f).restype = i32
         _lib = L
@@ -236,6 +242,25 @@ def moe_regroup(W, E, row_bytes, counts, ins, in_rows, outs, out_cap_rows, exper
                              int(direction), _dev(workspace, "workspace"),
                              workspace.numel() * workspace.element_size(),
                              _dev(status, "status"), _stream(stream, status)))
+
+
+def moe_dispatch_grouped_workspace_bytes(W, E) -> int:
+    return int(lib().moe_dispatch_grouped_workspace_bytes(int(W), int(E)))
+
+
+def moe_dispatch_grouped(W, E, row_bytes, counts, ins, in_rows, outs, out_cap_rows,
+                         expert_offsets, direction, workspace, status, stream=None):
+    """Dispatch a2av + expert regroup in one copy (direction 0), or its inverse (1)."""
+    if len(ins) != W or len(outs) != W or len(in_rows) != W or len(out_cap_rows) != W:
+        raise ValueError("ins, outs, in_rows and out_cap_rows need W entries each")
+    _check("moe_dispatch_grouped",
+           lib().moe_dispatch_grouped(int(W), int(E), int(row_bytes), _dev(counts, "counts"),
+                                      _ptr_array(ins, "ins"), _i64_array(in_rows),
+                                      _ptr_array(outs, "outs"), _i64_array(out_cap_rows),
+                                      _dev(expert_offsets, "expert_offsets"), int(direction),
+                                      _dev(workspace, "workspace"),
+                                      workspace.numel() * workspace.element_size(),
+                                      _dev(status, "status"), _stream(stream, status)))
 
 
 def keys_bucketize_workspace_bytes(W, n_tables) -> int:

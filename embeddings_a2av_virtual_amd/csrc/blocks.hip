@@ -499,6 +499,167 @@ __global__ __launch_bounds__(kPlanThreads) void k_keyx_plan(const KeyxArgs a) {
     }
 }
 
+// ------------------------------------------------------------ grouped MoE dispatch
+// The dispatch a2av and the receive-side regroup as one block copy (and the
+// inverse). Pack side of rank s: its rows by expert, expert e's counts[s][e]
+// rows at Y_s(e) = sum of counts[s][e'] for e' < e. Expert side of rank d:
+// owned expert j (e = d*P + j) outer, source s inner. Forward plans run per
+// owner d (blocks (j, s) in expert-major order, read from source s's pack
+// side); backward plans run per source s (blocks e in pack order, read from
+// the owner's expert side).
+struct GroupedArgs {
+    int64_t in_rows[A2AV_MAX_W];
+    int64_t cap[A2AV_MAX_W];
+    const int64_t *counts;    // [W][E]
+    int64_t *dst;             // [W][E + 1]
+    int64_t *src;             // [W][E]
+    int32_t *rank;            // [W][E]
+    int32_t *bits;            // [W]
+    int64_t *expert_offsets;  // [W][P + 1]
+    const int32_t *status;
+    int W;
+    int E;
+};
+
+// Every count in range; the caller's workgroup decides together.
+__device__ __forceinline__ bool grouped_counts_bad(const GroupedArgs &a) {
+    int bad = 0;
+    for (int i = threadIdx.x; i < a.W * a.E; i += kPlanThreads) bad |= (int)split_invalid(a.counts[i]);
+    return __syncthreads_or(bad) != 0;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void k_grouped_plan_fwd(const GroupedArgs a) {
+    __shared__ ScanLds lds;
+    __shared__ int64_t ypre[A2AV_MAX_EXPERTS];  // Y_s(d*P + j) at j*W + s
+    __shared__ int poisoned, sbits;
+    const int d = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    constexpr int NWV = kPlanThreads / kWave;
+    const int W = a.W, E = a.E, P = E / W;
+    if (tid == 0) {
+        poisoned = *a.status != 0;
+        sbits = 0;
+    }
+    __syncthreads();
+    if (poisoned) return;
+    if (grouped_counts_bad(a)) {
+        if (tid == 0) a.bits[d] = A2AV_ST_BAD_SPLIT;
+        return;
+    }
+    // one wave per source: its pack-side prefix over experts, kept for the
+    // experts d owns, and its pack total against its rows
+    for (int s = wave; s < W; s += NWV) {
+        int64_t run = 0;
+        for (int c0 = 0; c0 < E; c0 += kWave) {
+            const int e = c0 + lane;
+            const int64_t v = e < E ? a.counts[(int64_t)s * E + e] : 0;
+            const int64_t incl = wave_incl_scan(v);
+            if (e >= d * P && e < d * P + P) ypre[(e - d * P) * W + s] = run + incl - v;
+            run += (int64_t)readlane_u64((uint64_t)incl, kWave - 1);
+        }
+        if (lane == 0 && run > a.in_rows[s]) atomicOr(&sbits, A2AV_ST_SEND_OVERRUN);
+    }
+    __syncthreads();
+    int64_t nb[kPlanPer];
+    int64_t sum = 0;
+#pragma unroll
+    for (int u = 0; u < kPlanPer; u++) {
+        const int b = tid * kPlanPer + u;  // b = j*W + s
+        nb[u] = b < E ? a.counts[(int64_t)(b - (b / W) * W) * E + d * P + b / W] : 0;
+        sum += nb[u];
+    }
+    int64_t ex, ex2, total, total2;
+    block_excl_scan2(sum, 0, lds, &ex, &ex2, &total, &total2);
+    int64_t *dst = a.dst + (int64_t)d * (E + 1);
+#pragma unroll
+    for (int u = 0; u < kPlanPer; u++) {
+        const int b = tid * kPlanPer + u;
+        if (b < E) {
+            dst[b] = ex;
+            a.src[(int64_t)d * E + b] = ypre[b];
+            a.rank[(int64_t)d * E + b] = b - (b / W) * W;
+            if (b % W == 0) a.expert_offsets[(int64_t)d * (P + 1) + b / W] = ex;
+        }
+        ex += nb[u];
+    }
+    if (tid == 0) {
+        dst[E] = total;
+        a.expert_offsets[(int64_t)d * (P + 1) + P] = total;
+        a.bits[d] = sbits | (total > a.cap[d] ? A2AV_ST_RECV_OVERFLOW : 0);
+    }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void k_grouped_plan_bwd(const GroupedArgs a) {
+    __shared__ ScanLds lds;
+    __shared__ int64_t gpre[A2AV_MAX_EXPERTS + 1];  // exclusive scan of column sums over e
+    __shared__ int poisoned, sbits;
+    const int s = blockIdx.x, tid = threadIdx.x;
+    const int W = a.W, E = a.E, P = E / W;
+    if (tid == 0) {
+        poisoned = *a.status != 0;
+        sbits = 0;
+    }
+    __syncthreads();
+    if (poisoned) return;
+    if (grouped_counts_bad(a)) {
+        if (tid == 0) a.bits[s] = A2AV_ST_BAD_SPLIT;
+        return;
+    }
+    // per expert: the column sum (rows at its owner) and the rows of the
+    // sources before s; per source s: its own counts (pack order)
+    int64_t col[kPlanPer], before[kPlanPer], mine[kPlanPer];
+    int64_t scol = 0, smine = 0;
+#pragma unroll
+    for (int u = 0; u < kPlanPer; u++) {
+        const int e = tid * kPlanPer + u;
+        col[u] = before[u] = mine[u] = 0;
+        if (e < E) {
+            for (int s2 = 0; s2 < W; s2++) {
+                const int64_t c = a.counts[(int64_t)s2 * E + e];
+                col[u] += c;
+                if (s2 < s) before[u] += c;
+            }
+            mine[u] = a.counts[(int64_t)s * E + e];
+        }
+        scol += col[u];
+        smine += mine[u];
+    }
+    int64_t gx, yx, gtot, ytot;
+    block_excl_scan2(scol, smine, lds, &gx, &yx, &gtot, &ytot);
+#pragma unroll
+    for (int u = 0; u < kPlanPer; u++) {
+        const int e = tid * kPlanPer + u;
+        if (e < E) gpre[e] = gx;
+        gx += col[u];
+    }
+    if (tid == 0) gpre[E] = gtot;
+    __syncthreads();
+    int64_t *dst = a.dst + (int64_t)s * (E + 1);
+#pragma unroll
+    for (int u = 0; u < kPlanPer; u++) {
+        const int e = tid * kPlanPer + u;
+        if (e < E) {
+            const int d = e / P;
+            const int64_t at_owner = gpre[e] - gpre[d * P];  // expert_offsets[d][e - d*P]
+            dst[e] = yx;
+            a.src[(int64_t)s * E + e] = at_owner + before[u];
+            a.rank[(int64_t)s * E + e] = d;
+            if (s == 0) a.expert_offsets[(int64_t)d * (P + 1) + (e - d * P)] = at_owner;
+        }
+        yx += mine[u];
+    }
+    if (tid < W) {
+        const int64_t owner_total = gpre[(tid + 1) * P] - gpre[tid * P];
+        if (s == 0) a.expert_offsets[(int64_t)tid * (P + 1) + P] = owner_total;
+        if (owner_total > a.in_rows[tid]) atomicOr(&sbits, A2AV_ST_SEND_OVERRUN);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        dst[E] = ytot;
+        a.bits[s] = sbits | (ytot > a.cap[s] ? A2AV_ST_RECV_OVERFLOW : 0);
+    }
+}
+
 // ------------------------------------------------------------ host side
 static void piece_policy(uint64_t bmax, int *unroll, uint64_t *piece) {
     const bool small = bmax <= (512ull << 20);
@@ -795,5 +956,73 @@ A2AV_API int keys_exchange(int W, int n_tables, int64_t batch, const int32_t *co
     const uint64_t lmax = (lin < lout ? lin : lout) * 4;
     launch_block_copy(ck, kmax, false, stream);  // also reports the planning bits
     if (lmax > 0) launch_block_copy(cl, lmax, lal, stream);
+    return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
+}
+
+A2AV_API size_t moe_dispatch_grouped_workspace_bytes(int W, int E) {
+    if (W < 1 || W > A2AV_MAX_W || E < 1 || E > A2AV_MAX_EXPERTS || E % W != 0) return 0;
+    return round256((size_t)W * (2 * (size_t)E + 1) * 8) + round256((size_t)W * E * 4) +
+           round256((size_t)W * 4);
+}
+
+A2AV_API int moe_dispatch_grouped(int W, int E, size_t row_bytes, const int64_t *counts,
+                                  const void *const *in, const int64_t *in_rows,
+                                  void *const *out, const int64_t *out_cap_rows,
+                                  int64_t *expert_offsets, int direction, void *workspace,
+                                  size_t workspace_bytes, int32_t *status, hipStream_t stream) {
+    if (W < 1 || W > A2AV_MAX_W || E < 1 || E > A2AV_MAX_EXPERTS || E % W != 0 || row_bytes == 0 ||
+        !counts || !in || !in_rows || !out || !out_cap_rows || !expert_offsets || !status ||
+        (direction != 0 && direction != 1))
+        return A2AV_EARG;
+    if (!workspace || workspace_bytes < moe_dispatch_grouped_workspace_bytes(W, E)) return A2AV_EARG;
+    GroupedArgs g;
+    BlockArgs c;
+    std::memset(&g, 0, sizeof(g));
+    std::memset(&c, 0, sizeof(c));
+    uint64_t in_total = 0, cap_total = 0;
+    bool aligned = (row_bytes % 16) == 0;
+    for (int r = 0; r < W; r++) {
+        if (in_rows[r] < 0 || out_cap_rows[r] < 0) return A2AV_EARG;
+        if ((uint64_t)in_rows[r] > (uint64_t)INT64_MAX / row_bytes ||
+            (uint64_t)out_cap_rows[r] > (uint64_t)INT64_MAX / row_bytes)
+            return A2AV_EARG;
+        if ((in_rows[r] > 0 && !in[r]) || (out_cap_rows[r] > 0 && !out[r])) return A2AV_EARG;
+        g.in_rows[r] = c.in_rows[r] = in_rows[r];
+        g.cap[r] = c.cap[r] = out_cap_rows[r];
+        c.in[r] = (const unsigned char *)in[r];
+        c.out[r] = (unsigned char *)out[r];
+        in_total += (uint64_t)in_rows[r];
+        cap_total += (uint64_t)out_cap_rows[r];
+        if (cap_total * row_bytes > ((uint64_t)1 << 62)) return A2AV_EARG;
+        aligned = aligned && ((uintptr_t)in[r] % 16 == 0) && ((uintptr_t)out[r] % 16 == 0);
+    }
+    unsigned char *ws = (unsigned char *)workspace;
+    int64_t *dst = (int64_t *)ws;
+    int64_t *src = dst + (size_t)W * (E + 1);
+    int32_t *rank = (int32_t *)(ws + round256((size_t)W * (2 * (size_t)E + 1) * 8));
+    int32_t *bits = (int32_t *)((unsigned char *)rank + round256((size_t)W * E * 4));
+    g.counts = counts;
+    g.dst = dst;
+    g.src = src;
+    g.rank = rank;
+    g.bits = bits;
+    g.expert_offsets = expert_offsets;
+    g.status = status;
+    g.W = W;
+    g.E = E;
+    if (direction == 0)
+        hipLaunchKernelGGL(k_grouped_plan_fwd, dim3(W), dim3(kPlanThreads), 0, stream, g);
+    else
+        hipLaunchKernelGGL(k_grouped_plan_bwd, dim3(W), dim3(kPlanThreads), 0, stream, g);
+    c.dst_start = dst;
+    c.src_start = src;
+    c.src_rank = rank;
+    c.bits = bits;
+    c.status = status;
+    c.R = row_bytes;
+    c.W = W;
+    c.B = E;
+    const uint64_t bmax = (in_total < cap_total ? in_total : cap_total) * row_bytes;
+    launch_block_copy(c, bmax, aligned, stream);
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
 }

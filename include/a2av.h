@@ -278,6 +278,47 @@ int moe_regroup(int W, int E, size_t row_bytes, const int64_t *counts,
                 hipStream_t stream);
 
 /*
+ * Workspace bytes moe_dispatch_grouped needs (0 for invalid sizes).
+ */
+size_t moe_dispatch_grouped_workspace_bytes(int W, int E);
+
+/*
+ * The MoE dispatch a2av and the receive-side regroup (moe_regroup) as one
+ * copy, and the inverse: the exchange of the MoE region on the page "[a2av]
+ * Improve tuning for 4 GPUs" (section "Change") delivered straight into the
+ * layout an expert GEMM reads. With counts[s][e] the rows source s routed to
+ * expert e (moe_pack's expert_counts) and P = E/W experts per rank:
+ *   pack side of rank s    its rows in expert order, as moe_pack wrote them
+ *                          (expert e's counts[s][e] rows after those of the
+ *                          experts before e)
+ *   expert side of rank d  for each owned expert j (e = d*P + j), for each
+ *                          source s, counts[s][e] rows
+ *   direction 0 (dispatch): in[s] = pack side, out[d] = expert side
+ *   direction 1 (return):   in[d] = expert side, out[s] = pack side
+ * The result equals a2av_all_to_all_vdev with the owner-grouped splits
+ * followed by moe_regroup (direction 0), or moe_regroup direction 1 followed
+ * by the return a2av (direction 1), without the intermediate buffers.
+ *   counts          device int64 [W][E]
+ *   in[W], out[W]   device [rows][row_bytes]; in_rows[W], out_cap_rows[W] host
+ *   expert_offsets  device int64 [W][P+1]: rows before owned expert j on the
+ *                   expert side of rank d, total at P; written whenever the
+ *                   counts are valid
+ *   workspace       device scratch of >= moe_dispatch_grouped_workspace_bytes()
+ *   status          A2AV_ST_BAD_SPLIT (a count outside [0, 2^40]; nothing
+ *                   written), else A2AV_ST_SEND_OVERRUN / A2AV_ST_RECV_OVERFLOW
+ *                   (a rank sends more than in_rows / receives more than
+ *                   out_cap_rows; no payload byte written).
+ * Two kernels: a plan (one workgroup per destination rank; its blocks and,
+ * for each, the source rank and row) and the block copy of moe_regroup, each
+ * wave reading its piece in place from the source rank's buffer.
+ */
+int moe_dispatch_grouped(int W, int E, size_t row_bytes, const int64_t *counts,
+                         const void *const *in, const int64_t *in_rows, void *const *out,
+                         const int64_t *out_cap_rows, int64_t *expert_offsets, int direction,
+                         void *workspace, size_t workspace_bytes, int32_t *status,
+                         hipStream_t stream);
+
+/*
  * Workspace bytes keys_bucketize needs (0 for invalid sizes).
  */
 size_t keys_bucketize_workspace_bytes(int W, int n_tables);

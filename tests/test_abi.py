@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     for must in ("a2av_exchange_splits", "a2av_offsets", "a2av_copy", "moe_pack", "moe_unpack",
                  "moe_pack_workspace_bytes", "a2av_abi_version", "a2av_strerror",
                  "moe_combine", "moe_regroup", "moe_regroup_workspace_bytes", "keys_bucketize",
-                 "keys_bucketize_workspace_bytes", "keys_exchange", "keys_exchange_workspace_bytes"):
+                 "keys_bucketize_workspace_bytes", "keys_exchange", "keys_exchange_workspace_bytes",
+                 "moe_dispatch_grouped", "moe_dispatch_grouped_workspace_bytes"):
         assert must in names
 
 
@@ -109,6 +110,13 @@ def test_host_argument_errors(L):
                             vp(8), None) == EARG
     assert L.keys_bucketize(2, 26, 8, ptrs, ptrs, negr, ptrs, ptrs, vp(8), vp(8), vp(8), wsb,
                             vp(8), None) == EARG
+    # grouped dispatch: E % W, bad direction, small workspace
+    wsg = L.moe_dispatch_grouped_workspace_bytes(2, 8)
+    assert wsg > 0 and L.moe_dispatch_grouped_workspace_bytes(3, 8) == 0
+    assert L.moe_dispatch_grouped(2, 8, 16, vp(8), ptrs, two, ptrs, two, vp(8), 3, vp(8), wsg,
+                                  vp(8), None) == EARG
+    assert L.moe_dispatch_grouped(2, 8, 16, vp(8), ptrs, two, ptrs, two, vp(8), 0, vp(8), wsg - 1,
+                                  vp(8), None) == EARG
     # fused exchange: small workspace, negative capacity, too many tables
     wsx = L.keys_exchange_workspace_bytes(2, 26)
     assert wsx > 0 and L.keys_exchange_workspace_bytes(2, 4097) == 0
