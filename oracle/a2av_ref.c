@@ -518,3 +518,66 @@ int ref_moe_dispatch_grouped(int W, int E, size_t R, const int64_t *counts,
     }
     return 0;
 }
+
+/*
+ * The gate-weighted combine read straight from the expert side: the grouped
+ * return (ref_moe_dispatch_grouped, direction 1) followed by ref_moe_combine,
+ * written as one step. Slot q = t*k + j of source s names its expert
+ * ids[s][q] and its pack-order row perm[s][q]; that row lies in expert e's
+ * pack block [Y_s(e), Y_s(e) + counts[s][e]) and sits on the expert side of
+ * owner e / P at expert_start(s, e) + (perm[s][q] - Y_s(e)).
+ */
+int ref_moe_combine_grouped(int W, int64_t T, int k, int E, int64_t H, const int64_t *counts,
+                            const int32_t *const *ids, const int64_t *const *perm,
+                            const uint16_t *const *expert_side, const int64_t *exp_rows,
+                            const float *const *w, uint16_t *const *out) {
+    if (W < 1 || W > REF_MAX_W || T < 0 || k < 1 || E < 1 || E % W != 0 || H < 1 || !counts ||
+        !ids || !perm || !expert_side || !exp_rows || !w || !out)
+        return REF_EARG;
+    if (T > INT64_MAX / k) return REF_EARG;
+    const int P = E / W;
+    const int64_t Q = T * k;
+    for (int64_t i = 0; i < (int64_t)W * E; i++)
+        if (!split_is_valid(counts[i])) return REF_BAD_SPLIT;
+    /* Y[s][e]: pack position of expert e at source s; X[s][e]: its start on the expert side */
+    int64_t *Y = malloc(sizeof(int64_t) * (size_t)W * E);
+    int64_t *X = malloc(sizeof(int64_t) * (size_t)W * E);
+    if (!Y || !X) { free(Y); free(X); return REF_EARG; }
+    int st = 0;
+    for (int d = 0; d < W; d++) {
+        int64_t run = 0;
+        for (int j = 0; j < P; j++)
+            for (int s = 0; s < W; s++) {
+                X[s * E + d * P + j] = run;
+                run += counts[s * E + d * P + j];
+            }
+        if (run > exp_rows[d]) st |= REF_SEND_OVERRUN;
+    }
+    for (int s = 0; s < W; s++) {
+        int64_t run = 0;
+        for (int e = 0; e < E; e++) { Y[s * E + e] = run; run += counts[s * E + e]; }
+    }
+    for (int s = 0; s < W; s++)
+        for (int64_t q = 0; q < Q; q++) {
+            const int32_t e = ids[s][q];
+            const int64_t p = perm[s][q];
+            if (e < 0 || e >= E) { st |= REF_BAD_EXPERT; continue; }
+            if (p < Y[s * E + e] || p >= Y[s * E + e] + counts[s * E + e]) st |= REF_BAD_PERM;
+        }
+    if (st) { free(Y); free(X); return st; }
+    for (int s = 0; s < W; s++)
+        for (int64_t t = 0; t < T; t++)
+            for (int64_t h = 0; h < H; h++) {
+                float acc = 0.0f;
+                for (int j = 0; j < k; j++) {
+                    const int64_t q = t * k + j;
+                    const int e = ids[s][q];
+                    const int64_t row = X[s * E + e] + (perm[s][q] - Y[s * E + e]);
+                    acc = fmaf(w[s][q], bf16_to_float(expert_side[e / P][row * H + h]), acc);
+                }
+                out[s][t * H + h] = float_to_bf16(acc);
+            }
+    free(Y);
+    free(X);
+    return 0;
+}

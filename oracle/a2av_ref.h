@@ -135,6 +135,20 @@ int ref_moe_dispatch_grouped(int W, int E, size_t R, const int64_t *counts,
                              void *const *out, const int64_t *out_cap,
                              int64_t *expert_offsets, int direction);
 
+/* The gate-weighted combine read straight from the expert side, for all W
+ * ranks: what ref_moe_dispatch_grouped (direction 1) followed by
+ * ref_moe_combine gives, as one step. ids[s] and perm[s] are moe_pack's
+ * inputs and output for source s (T*k slots); expert_side[d] holds
+ * exp_rows[d] rows of H bf16 in owner d's expert-major order; w[s] is
+ * [T][k] fp32; out[s] is [T][H] bf16. REF_BAD_SPLIT for a count outside
+ * [0, 2^40] (first); else the OR of REF_SEND_OVERRUN (an owner's rows exceed
+ * exp_rows), REF_BAD_EXPERT (an id outside [0, E)) and REF_BAD_PERM (a perm
+ * entry outside its expert's pack block). Nothing is written on failure. */
+int ref_moe_combine_grouped(int W, int64_t T, int k, int E, int64_t H, const int64_t *counts,
+                            const int32_t *const *ids, const int64_t *const *perm,
+                            const uint16_t *const *expert_side, const int64_t *exp_rows,
+                            const float *const *w, uint16_t *const *out);
+
 /* The whole key exchange of one batch for all W ranks: ref_keys_bucketize on
  * every source, then keys (8-byte rows) and lengths (4-byte rows) as two
  * ref_a2av calls with the bucketing's split rows. lengths_cap / keys_cap are

@@ -209,6 +209,39 @@ static void one_grouped(int W, int E, size_t R) {
     free(in); free(out); free(back); free(counts); free(rows); free(cap); free(eoff);
 }
 
+/* pack, grouped dispatch, then the combine read from the expert side */
+static void one_combine_grouped(int W, int64_t T, int k, int E, int64_t H) {
+    const int P = E / W;
+    const int64_t Q = T * k;
+    int64_t *counts = malloc(sizeof(int64_t) * W * E), *exp_rows = calloc(W, sizeof(int64_t));
+    int32_t **ids = malloc(sizeof(void *) * W);
+    int64_t **perm = malloc(sizeof(void *) * W);
+    float **w = malloc(sizeof(void *) * W);
+    uint16_t **out = malloc(sizeof(void *) * W), **xs = malloc(sizeof(void *) * W);
+    unsigned char *tok = calloc((size_t)T + 1, 1), *send = malloc((size_t)Q + 1);
+    int64_t *splits = malloc(sizeof(int64_t) * W);
+    for (int s = 0; s < W; s++) {
+        ids[s] = malloc(sizeof(int32_t) * (Q + 1));
+        perm[s] = malloc(sizeof(int64_t) * (Q + 1));
+        w[s] = malloc(sizeof(float) * (Q + 1));
+        out[s] = malloc(sizeof(uint16_t) * (T * H + 1));
+        for (int64_t q = 0; q < Q; q++) { ids[s][q] = (int32_t)(next_u64() % E); w[s][q] = 0.5f; }
+        CHECK(ref_moe_pack(T, k, E, W, 1, tok, ids[s], send, perm[s], splits, counts + (size_t)s * E) == 0);
+    }
+    for (int s = 0; s < W; s++)
+        for (int e = 0; e < E; e++) exp_rows[e / P] += counts[s * E + e];
+    for (int d = 0; d < W; d++) {
+        xs[d] = malloc(sizeof(uint16_t) * (exp_rows[d] * H + 1));
+        for (int64_t i = 0; i < exp_rows[d] * H; i++) xs[d][i] = (uint16_t)(next_u64() & 0x7F7F);
+    }
+    CHECK(ref_moe_combine_grouped(W, T, k, E, H, counts, (const int32_t *const *)ids,
+                                  (const int64_t *const *)perm, (const uint16_t *const *)xs,
+                                  exp_rows, (const float *const *)w, out) == 0);
+    for (int s = 0; s < W; s++) { free(ids[s]); free(perm[s]); free(w[s]); free(out[s]); free(xs[s]); }
+    free(ids); free(perm); free(w); free(out); free(xs); free(counts); free(exp_rows);
+    free(tok); free(send); free(splits);
+}
+
 int main(void) {
     const size_t widths[] = {1, 3, 8, 16, 100};
     for (int W = 1; W <= 9; W++)
@@ -229,6 +262,9 @@ int main(void) {
     one_bucketize(8, 26, 64);
     one_bucketize(3, 2, 0);
     one_bucketize(5, 0, 10);
+    one_combine_grouped(8, 100, 8, 256, 24);
+    one_combine_grouped(3, 17, 2, 6, 5);
+    one_combine_grouped(1, 1, 1, 1, 1);
     one_grouped(8, 256, 16);
     one_grouped(3, 12, 5);
     one_grouped(1, 1, 1);

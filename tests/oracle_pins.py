@@ -581,6 +581,63 @@ def pin_moe_dispatch_grouped(o):
     assert st == R.RECV_OVERFLOW and not any(x.any() for x in outs2)
 
 
+def pin_moe_combine_grouped(o):
+    """Combine read from the expert side: after a real pack and grouped
+    dispatch, equals the grouped return followed by the combine (pinned on
+    their own); bad ids, perm entries outside their expert's block, and short
+    expert sides are refused with nothing written."""
+    import torch
+    g = np.random.default_rng(32)
+    for W, T, k, E, H, distinct in ((4, 30, 3, 12, 8, True), (2, 17, 4, 8, 5, False),
+                                    (1, 9, 2, 3, 16, True), (3, 0, 2, 6, 4, False)):
+        P = E // W
+        ids, perms, sends, counts, ws = [], [], [], [], []
+        for r in range(W):
+            tok = torch.randn(T, H, generator=torch.Generator().manual_seed(100 + r))
+            tok = tok.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint8)
+            _, idr = _moe_case(g, T, k, E, 1, distinct)
+            st, send, perm, splits, cnt = o.moe_pack(T, k, E, W, 2 * H, tok, idr)
+            assert st == 0
+            ids.append(idr.reshape(-1)); perms.append(perm); sends.append(send)
+            counts.append(cnt)
+            ws.append((g.random((T, k)) * 2 - 0.5).astype(np.float32))
+        counts = np.stack(counts)
+        rows = [int(counts[:, d * P:(d + 1) * P].sum()) for d in range(W)]
+        st, exp, _ = o.moe_dispatch_grouped(W, E, 2 * H, counts, sends, [T * k] * W, rows, 0)
+        assert st == 0
+        exp16 = [x.view(np.uint16).reshape(-1, H) for x in exp]
+        st, got = o.moe_combine_grouped(W, T, k, E, H, counts, ids, perms, exp16, ws)
+        assert st == 0
+        st, back, _ = o.moe_dispatch_grouped(W, E, 2 * H, counts, exp, rows, [T * k] * W, 1)
+        assert st == 0
+        for r in range(W):
+            st, want = o.moe_combine(T, k, H, back[r].view(np.uint16).reshape(-1, H), perms[r], ws[r])
+            assert st == 0 and np.array_equal(got[r], want), r
+    # failures (the last shape above: W=3, T=0 has no slots; rebuild a small one)
+    W, T, k, E, H = 2, 6, 2, 4, 8
+    P = E // W
+    ids, perms, counts, ws = [], [], [], []
+    for r in range(W):
+        _, idr = _moe_case(g, T, k, E, 1, True)
+        st, send, perm, _, cnt = o.moe_pack(T, k, E, W, 1, np.zeros((T, 1), np.uint8), idr)
+        ids.append(idr.reshape(-1)); perms.append(perm); counts.append(cnt)
+        ws.append(np.ones((T, k), np.float32))
+    counts = np.stack(counts)
+    exp16 = [np.ones((int(counts[:, d * P:(d + 1) * P].sum()), H), np.uint16) for d in range(W)]
+    assert o.moe_combine_grouped(W, T, k, E, H, counts, ids, perms, exp16, ws)[0] == 0
+    bad_ids = [x.copy() for x in ids]; bad_ids[1][3] = E
+    st, out = o.moe_combine_grouped(W, T, k, E, H, counts, bad_ids, perms, exp16, ws)
+    assert st == R.BAD_EXPERT and not any(x.any() for x in out)
+    swapped = [x.copy() for x in ids]  # an id of another expert than the row's block
+    q = int(np.nonzero(swapped[0] != swapped[0][0])[0][0])
+    swapped[0][0], swapped[0][q] = swapped[0][q], swapped[0][0]
+    assert o.moe_combine_grouped(W, T, k, E, H, counts, swapped, perms, exp16, ws)[0] == R.BAD_PERM
+    short = [x[:-1] for x in exp16]
+    assert o.moe_combine_grouped(W, T, k, E, H, counts, ids, perms, short, ws)[0] == R.SEND_OVERRUN
+    c2 = counts.copy(); c2[0, 0] = -2
+    assert o.moe_combine_grouped(W, T, k, E, H, c2, ids, perms, exp16, ws)[0] == R.BAD_SPLIT
+
+
 # ------------------------------------------------------------------ gate-weighted combine
 def _round_f32(x):
     """A Fraction rounded to the nearest binary32, ties to even (finite, in

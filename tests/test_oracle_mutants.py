@@ -84,6 +84,12 @@ MUTANTS = {
     "grouped_pack_pos_not_advanced": [
         ("            pack_pos += n;\n        }\n    }\n    return 0;\n}",
          "            (void)n;\n        }\n    }\n    return 0;\n}", 0)],
+    "combine_grouped_ignores_block_offset": [
+        ("const int64_t row = X[s * E + e] + (perm[s][q] - Y[s * E + e]);",
+         "const int64_t row = X[s * E + e];", 0)],
+    "combine_grouped_skips_block_check": [
+        ("if (p < Y[s * E + e] || p >= Y[s * E + e] + counts[s * E + e]) st |= REF_BAD_PERM;",
+         "(void)p;", 0)],
     "keys_exchange_offsets_inclusive": [
         ("            recv_off_keys[d * (W + 1) + s] = run;\n            run += Sk[s * W + d];",
          "            run += Sk[s * W + d];\n            recv_off_keys[d * (W + 1) + s] = run;", 0)],
