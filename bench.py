@@ -579,6 +579,21 @@ def moe_rows(torch, B, I, o, out):
         if not torch.equal(home[r].view(torch.int16), send[r].view(torch.int16)):
             raise RuntimeError("grouped dispatch + return did not bring the rows home")
     del home
+    # ---- the return trip and the weighted combine in one pass, from the expert side
+    cgo = [torch.empty((T, hidden), dtype=torch.bfloat16, device="cuda") for _ in range(W)]
+    cgws = torch.empty(B.moe_combine_grouped_workspace_bytes(W, T, k, E), dtype=torch.uint8,
+                       device="cuda")
+    cgst = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cgrp = lambda: B.moe_combine_grouped(W, T, k, E, hidden, counts, ids, perm, grp, cap, wts,
+                                         cgo, cgws, cgst)
+    ms = time_events(torch, cgrp, 5)
+    out["moe_combine_grouped"] = row_entry(W * (Q * R + T * R + Q * (8 + 4 + 8)), ms)
+    # the whole fused MoE round trip after the pack: grouped dispatch + combine from the expert side
+    ms = time_events(torch, lambda: (gdisp(), cgrp()), 5)
+    out["moe_fused_round_trip"] = {"us": round(ms * 1e3, 2),
+                                   "note": "grouped dispatch + combine from the expert side"}
+    torch.cuda.synchronize()
+    _check_status(B, [("grouped combine", cgst), ("grouped", gst)])
     del grp
     # ---- return a2av: every row goes home
     bk = A2av(W)
@@ -615,6 +630,13 @@ def moe_rows(torch, B, I, o, out):
     torch.cuda.synchronize()
     _check_status(B, [("pack", status), ("dispatch", fwd.status), ("regroup", rst),
                       ("return", bk.status), ("combine", cst), ("unpack", ust)])
+    # the same round trip unfused: dispatch a2av, regroup to expert-major and
+    # back, return a2av, combine (sum of the rows above)
+    out["moe_chain_round_trip"] = {
+        "us": round(sum(out[x]["us"] for x in ("dispatch_a2av", "moe_regroup_to_expert",
+                                                 "moe_regroup_to_source", "return_a2av",
+                                                 "moe_combine")), 2),
+        "note": "sum of dispatch a2av, both regroups, return a2av and combine"}
     return dict(fwd=fwd, send=send, recv=recv, cap=cap, R=R, Q=Q, W=W)
 
 

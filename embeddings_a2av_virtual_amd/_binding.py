@@ -25,7 +25,8 @@ __all__ = [
     "a2av_all_to_all_vdev",
     "moe_pack_workspace_bytes", "moe_pack", "moe_unpack", "moe_combine",
     "moe_regroup_workspace_bytes", "moe_regroup", "moe_dispatch_grouped_workspace_bytes",
-    "moe_dispatch_grouped", "keys_bucketize_workspace_bytes",
+    "moe_dispatch_grouped", "moe_combine_grouped_workspace_bytes", "moe_combine_grouped",
+    "keys_bucketize_workspace_bytes",
     "keys_bucketize", "keys_exchange_workspace_bytes", "keys_exchange", "a2av_device_copy",
     "MAX_TABLES",
 ]
@@ -84,6 +85,10 @@ def lib():
         L.moe_dispatch_grouped_workspace_bytes.restype = sz
         L.moe_dispatch_grouped.argtypes = [i32, i32, sz, vp, vpp, i64p, vpp, i64p, vp, i32, vp, sz,
                                            vp, vp]
+        L.moe_combine_grouped_workspace_bytes.argtypes = [i32, i64, i32, i32]
+        L.moe_combine_grouped_workspace_bytes.restype = sz
+        L.moe_combine_grouped.argtypes = [i32, i64, i32, i32, i64, vp, vpp, vpp, vpp, i64p, vpp,
+                                          vpp, vp, sz, vp, vp]
         L.keys_bucketize_workspace_bytes.argtypes = [i32, i32]
         L.keys_bucketize_workspace_bytes.restype = sz
         L.keys_bucketize.argtypes = [i32, i32, i64, vpp, vpp, i64p, vpp, vpp, vp, vp, vp, sz, vp,
@@ -95,6 +100,7 @@ def lib():
         L.a2av_device_copy.argtypes = [vp, vp, sz, vp]
         for f in ("a2av_exchange_splits", "a2av_offsets", "a2av_copy", "a2av_all_to_all_vdev",
                   "moe_pack", "moe_unpack", "moe_combine", "moe_regroup", "moe_dispatch_grouped",
+                  "moe_combine_grouped",
                   "keys_bucketize", "keys_exchange",
                   "a2av_device_copy"):
             getattr(L, f).restype = i32
@@ -261,6 +267,25 @@ def moe_dispatch_grouped(W, E, row_bytes, counts, ins, in_rows, outs, out_cap_ro
                                       _dev(workspace, "workspace"),
                                       workspace.numel() * workspace.element_size(),
                                       _dev(status, "status"), _stream(stream, status)))
+
+
+def moe_combine_grouped_workspace_bytes(W, T, k, E) -> int:
+    return int(lib().moe_combine_grouped_workspace_bytes(int(W), int(T), int(k), int(E)))
+
+
+def moe_combine_grouped(W, T, k, E, H, counts, ids, perm, expert_side, exp_rows, weights, out,
+                        workspace, status, stream=None):
+    """The return trip and the weighted combine in one pass, reading every
+    slot's row on its owner's expert side."""
+    _check("moe_combine_grouped",
+           lib().moe_combine_grouped(int(W), int(T), int(k), int(E), int(H),
+                                     _dev(counts, "counts"), _ptr_array(ids, "ids"),
+                                     _ptr_array(perm, "perm"),
+                                     _ptr_array(expert_side, "expert_side"),
+                                     _i64_array(exp_rows), _ptr_array(weights, "weights"),
+                                     _ptr_array(out, "out"), _dev(workspace, "workspace"),
+                                     workspace.numel() * workspace.element_size(),
+                                     _dev(status, "status"), _stream(stream, status)))
 
 
 def keys_bucketize_workspace_bytes(W, n_tables) -> int:

@@ -233,6 +233,21 @@ __device__ __forceinline__ int32_t wave_or(int32_t v) {
     return v;
 }
 
+// ------------------------------------------------------------ bfloat16
+// The two bf16 halves of a 32-bit word as fp32 (bf16 is the top half of an
+// IEEE binary32).
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
+
+// float -> bfloat16 bits, round to nearest even; every NaN becomes 0x7FC0
+// (the sign and payload of a NaN result are not fixed by IEEE 754 and differ
+// between processors).
+__device__ __forceinline__ uint32_t to_bf16(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 // ------------------------------------------------------------ host helpers
 int device_cu_count(hipStream_t stream);
 long env_long(const char *name, long dflt, long lo, long hi);

@@ -319,6 +319,40 @@ int moe_dispatch_grouped(int W, int E, size_t row_bytes, const int64_t *counts,
                          hipStream_t stream);
 
 /*
+ * Workspace bytes moe_combine_grouped needs (0 for invalid sizes).
+ */
+size_t moe_combine_grouped_workspace_bytes(int W, int64_t T, int k, int E);
+
+/*
+ * The gate-weighted combine (as moe_combine) read straight from where
+ * moe_dispatch_grouped (direction 0) left every row: the return trip and the
+ * combine in one pass, for all W ranks at once. Equal to
+ * moe_dispatch_grouped(direction 1) into the pack side followed by
+ * moe_combine, without writing the pack side. Slot q = t*k + j of source s
+ * has expert ids[s][q] and pack row perm[s][q] (moe_pack's input and output);
+ * its row on the expert side of owner e / (E/W) is found from the counts.
+ *   counts            device int64 [W][E] (moe_pack's expert_counts)
+ *   ids[W], perm[W]   device int32 / int64 [T*k] per source
+ *   expert_side[W]    device bf16 [exp_rows[d]][H] per owner d (host exp_rows)
+ *   weights[W]        device fp32 [T][k];  out[W]  device bf16 [T][H]
+ *   workspace         device scratch of >= moe_combine_grouped_workspace_bytes()
+ *   status            A2AV_ST_BAD_SPLIT (a count outside [0, 2^40]); else the OR
+ *                     of A2AV_ST_SEND_OVERRUN (an owner's rows exceed exp_rows),
+ *                     A2AV_ST_BAD_EXPERT (an id outside [0, E)) and
+ *                     A2AV_ST_BAD_PERM (a perm entry outside its expert's block
+ *                     of the pack order). Nothing is written on failure.
+ * Three kernels: the backward plan of moe_dispatch_grouped, a check that also
+ * records every slot's row at its owner, and the combine (one wave per
+ * (source, token, 512 elements), as moe_combine, 16-byte vectors when H % 8
+ * == 0 and the bases are 16-byte aligned, else one element per lane).
+ */
+int moe_combine_grouped(int W, int64_t T, int k, int E, int64_t H, const int64_t *counts,
+                        const int32_t *const *ids, const int64_t *const *perm,
+                        const void *const *expert_side, const int64_t *exp_rows,
+                        const float *const *weights, void *const *out, void *workspace,
+                        size_t workspace_bytes, int32_t *status, hipStream_t stream);
+
+/*
  * Workspace bytes keys_bucketize needs (0 for invalid sizes).
  */
 size_t keys_bucketize_workspace_bytes(int W, int n_tables);

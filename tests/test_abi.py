@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
                  "moe_pack_workspace_bytes", "a2av_abi_version", "a2av_strerror",
                  "moe_combine", "moe_regroup", "moe_regroup_workspace_bytes", "keys_bucketize",
                  "keys_bucketize_workspace_bytes", "keys_exchange", "keys_exchange_workspace_bytes",
-                 "moe_dispatch_grouped", "moe_dispatch_grouped_workspace_bytes"):
+                 "moe_dispatch_grouped", "moe_dispatch_grouped_workspace_bytes",
+                 "moe_combine_grouped", "moe_combine_grouped_workspace_bytes"):
         assert must in names
 
 
@@ -117,6 +118,13 @@ def test_host_argument_errors(L):
                                   vp(8), None) == EARG
     assert L.moe_dispatch_grouped(2, 8, 16, vp(8), ptrs, two, ptrs, two, vp(8), 0, vp(8), wsg - 1,
                                   vp(8), None) == EARG
+    # grouped combine: small workspace, E % W, H = 0
+    wsc = L.moe_combine_grouped_workspace_bytes(2, 10, 2, 8)
+    assert wsc > 0 and L.moe_combine_grouped_workspace_bytes(3, 10, 2, 8) == 0
+    assert L.moe_combine_grouped(2, 10, 2, 8, 16, vp(8), ptrs, ptrs, ptrs, two, ptrs, ptrs, vp(8),
+                                 wsc - 1, vp(8), None) == EARG
+    assert L.moe_combine_grouped(2, 10, 2, 8, 0, vp(8), ptrs, ptrs, ptrs, two, ptrs, ptrs, vp(8),
+                                 wsc, vp(8), None) == EARG
     # fused exchange: small workspace, negative capacity, too many tables
     wsx = L.keys_exchange_workspace_bytes(2, 26)
     assert wsx > 0 and L.keys_exchange_workspace_bytes(2, 4097) == 0
