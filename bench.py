@@ -93,6 +93,9 @@ class VSet:
         self.fused_args = (W, self.R, ins, in_rows, outs, caps, vp(st.S.data_ptr()),
                            vp(st.O.data_ptr()), vp(st.send_off.data_ptr()),
                            vp(st.recv_off.data_ptr()), vp(st.status.data_ptr()), hs)
+        # inputs and the zeroed status were written on the current stream; the
+        # launch stream may be another one
+        torch.cuda.synchronize()
 
 
 def run_config(torch, B, I, W, mib, steps, warmup, nsets, entry="fused", splits="uniform"):
@@ -398,6 +401,9 @@ class KeyChain:
                        vp(self.ka.S.data_ptr()), vp(self.la.S.data_ptr()), vp(self.ws.data_ptr()),
                        self.ws.numel(), vp(self.status.data_ptr()), hs)
         self.L = B.lib()
+        # the buffers above were filled on the current stream; the calls below
+        # run on `stream`, which may be another one
+        torch.cuda.synchronize()
         # receive capacity from one bucketing pass (set-up, outside any timing)
         assert self.L.keys_bucketize(*self.b_args) == 0
         torch.cuda.synchronize()
@@ -433,6 +439,7 @@ class KeyChain:
         # counts, then keys and lengths read and written once each
         self.fused_bytes = (sum(4 * self.NT * self.BATCH for _ in range(W)) + self.key_bytes +
                             self.len_bytes)
+        torch.cuda.synchronize()   # status words zeroed before any call on `stream`
 
     def bucketize(self):
         assert self.L.keys_bucketize(*self.b_args) == 0
