@@ -581,3 +581,161 @@ int ref_moe_combine_grouped(int W, int64_t T, int k, int E, int64_t H, const int
     free(X);
     return 0;
 }
+
+/*
+ * The MoE pack and its dispatch in one step, for all W ranks: each routing
+ * slot's token row goes straight to the receive buffer of its expert's owner
+ * (e / P, P = E / W). Owner d's rows are its slots from every source, sorted
+ * by the key (source, expert, slot) for layout 0, the order the pack
+ * followed by the a2av leaves, or (expert, source, slot) for layout 1, the
+ * order the pack followed by the grouped dispatch leaves. Written here as
+ * that sort, with perm, the splits and the counts from the pack's own
+ * definition.
+ */
+typedef struct {
+    int64_t key[3];
+    int src;
+    int64_t tok;
+} ref_slot_key;
+
+static int cmp_slot_key(const void *a, const void *b) {
+    const ref_slot_key *x = a, *y = b;
+    for (int i = 0; i < 3; i++)
+        if (x->key[i] != y->key[i]) return x->key[i] < y->key[i] ? -1 : 1;
+    return 0;
+}
+
+int ref_moe_pack_dispatch(int W, int64_t T, int k, int E, size_t R,
+                          const void *const *tokens, const int32_t *const *ids,
+                          void *const *recv, const int64_t *recv_cap, int64_t *const *perm,
+                          int64_t *S, int64_t *expert_counts, int64_t *block_offsets,
+                          int layout) {
+    if (W < 1 || W > REF_MAX_W || T < 0 || k < 1 || E < 1 || E % W != 0 || R == 0 || !tokens ||
+        !ids || !recv || !recv_cap || !perm || !S || !expert_counts || !block_offsets ||
+        (layout != 0 && layout != 1))
+        return REF_EARG;
+    if (T > INT64_MAX / k) return REF_EARG;
+    const int P = E / W;
+    const int64_t Q = T * k;
+    for (int s = 0; s < W; s++) {
+        if (Q > 0 && (!tokens[s] || !ids[s] || !perm[s])) return REF_EARG;
+        for (int64_t q = 0; q < Q; q++)
+            if (ids[s][q] < 0 || ids[s][q] >= E) return REF_BAD_EXPERT;
+    }
+    /* the pack of every source: counts, perm, splits */
+    int64_t *next = malloc(sizeof(int64_t) * (size_t)E);
+    if (!next) return REF_EARG;
+    for (int s = 0; s < W; s++) {
+        int64_t *cnt = expert_counts + (size_t)s * E;
+        for (int e = 0; e < E; e++) cnt[e] = 0;
+        for (int64_t q = 0; q < Q; q++) cnt[ids[s][q]] += 1;
+        int64_t run = 0;
+        for (int e = 0; e < E; e++) { next[e] = run; run += cnt[e]; }
+        for (int64_t q = 0; q < Q; q++) perm[s][q] = next[ids[s][q]]++;
+        for (int d = 0; d < W; d++) {
+            S[s * W + d] = 0;
+            for (int j = 0; j < P; j++) S[s * W + d] += cnt[d * P + j];
+        }
+    }
+    free(next);
+    /* block starts at each receiver: sources (layout 0) or owned experts (layout 1) */
+    int st = 0;
+    const int G = layout == 0 ? W : P;
+    for (int d = 0; d < W; d++) {
+        int64_t run = 0;
+        for (int g = 0; g < G; g++) {
+            block_offsets[d * (G + 1) + g] = run;
+            if (layout == 0) run += S[g * W + d];
+            else for (int s = 0; s < W; s++) run += expert_counts[(size_t)s * E + d * P + g];
+        }
+        block_offsets[d * (G + 1) + G] = run;
+        if (run > recv_cap[d]) st |= REF_RECV_OVERFLOW;
+        if (run > 0 && !recv[d]) return REF_EARG;
+    }
+    if (st) return st;
+    ref_slot_key *keys = malloc(sizeof(ref_slot_key) * (size_t)(W * Q > 0 ? W * Q : 1));
+    if (!keys) return REF_EARG;
+    for (int d = 0; d < W; d++) {
+        int64_t n = 0;
+        for (int s = 0; s < W; s++)
+            for (int64_t q = 0; q < Q; q++) {
+                const int64_t e = ids[s][q];
+                if (e / P != d) continue;
+                ref_slot_key *x = &keys[n++];
+                x->key[0] = layout == 0 ? s : e;
+                x->key[1] = layout == 0 ? e : s;
+                x->key[2] = q;
+                x->src = s;
+                x->tok = q / k;
+            }
+        qsort(keys, (size_t)n, sizeof(ref_slot_key), cmp_slot_key);
+        for (int64_t i = 0; i < n; i++)
+            memcpy((unsigned char *)recv[d] + (size_t)i * R,
+                   (const unsigned char *)tokens[keys[i].src] + (size_t)keys[i].tok * R, R);
+    }
+    free(keys);
+    return 0;
+}
+
+/*
+ * The inverse of ref_moe_pack_dispatch: every slot's row read back from its
+ * owner's receive buffer (the return a2av followed by the un-pack, or the
+ * grouped return followed by the un-pack, as one step). Slot q of source s
+ * names expert e = ids[s][q] and pack row perm[s][q], which must lie in
+ * expert e's pack block [Y_s(e), Y_s(e) + counts[s][e]); the row sits at
+ * owner e / P at the start of the (s, e) block in the layout's order plus
+ * perm[s][q] - Y_s(e).
+ */
+int ref_moe_unpack_return(int W, int64_t T, int k, int E, size_t R, const int64_t *counts,
+                          const int32_t *const *ids, const int64_t *const *perm,
+                          const void *const *recv, const int64_t *recv_rows, void *const *out,
+                          int layout) {
+    if (W < 1 || W > REF_MAX_W || T < 0 || k < 1 || E < 1 || E % W != 0 || R == 0 || !counts ||
+        !ids || !perm || !recv || !recv_rows || !out || (layout != 0 && layout != 1))
+        return REF_EARG;
+    if (T > INT64_MAX / k) return REF_EARG;
+    const int P = E / W;
+    const int64_t Q = T * k;
+    for (int64_t i = 0; i < (int64_t)W * E; i++)
+        if (!split_is_valid(counts[i])) return REF_BAD_SPLIT;
+    /* Y[s][e]: pack position of expert e at source s; Z[s][e]: start of the (s, e) block at its owner */
+    int64_t *Y = malloc(sizeof(int64_t) * (size_t)W * E);
+    int64_t *Z = malloc(sizeof(int64_t) * (size_t)W * E);
+    if (!Y || !Z) { free(Y); free(Z); return REF_EARG; }
+    int st = 0;
+    for (int s = 0; s < W; s++) {
+        int64_t run = 0;
+        for (int e = 0; e < E; e++) { Y[s * E + e] = run; run += counts[s * E + e]; }
+    }
+    for (int d = 0; d < W; d++) {
+        int64_t run = 0;
+        if (layout == 0) {
+            for (int s = 0; s < W; s++)
+                for (int j = 0; j < P; j++) { Z[s * E + d * P + j] = run; run += counts[s * E + d * P + j]; }
+        } else {
+            for (int j = 0; j < P; j++)
+                for (int s = 0; s < W; s++) { Z[s * E + d * P + j] = run; run += counts[s * E + d * P + j]; }
+        }
+        if (run > recv_rows[d]) st |= REF_SEND_OVERRUN;
+    }
+    for (int s = 0; s < W; s++) {
+        if (Q > 0 && (!ids[s] || !perm[s] || !out[s])) { free(Y); free(Z); return REF_EARG; }
+        for (int64_t q = 0; q < Q; q++) {
+            const int32_t e = ids[s][q];
+            const int64_t p = perm[s][q];
+            if (e < 0 || e >= E) { st |= REF_BAD_EXPERT; continue; }
+            if (p < Y[s * E + e] || p >= Y[s * E + e] + counts[s * E + e]) st |= REF_BAD_PERM;
+        }
+    }
+    if (st) { free(Y); free(Z); return st; }
+    for (int s = 0; s < W; s++)
+        for (int64_t q = 0; q < Q; q++) {
+            const int e = ids[s][q];
+            const int64_t row = Z[s * E + e] + (perm[s][q] - Y[s * E + e]);
+            memcpy((unsigned char *)out[s] + (size_t)q * R,
+                   (const unsigned char *)recv[e / P] + (size_t)row * R, R);
+        }
+    free(Y);
+    free(Z);
+    return 0;
+}

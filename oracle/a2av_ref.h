@@ -149,6 +149,36 @@ int ref_moe_combine_grouped(int W, int64_t T, int k, int E, int64_t H, const int
                             const uint16_t *const *expert_side, const int64_t *exp_rows,
                             const float *const *w, uint16_t *const *out);
 
+/* The MoE pack and its dispatch in one step, for all W ranks: slot q of
+ * source s (expert e = ids[s][q]) sends token row q / k of tokens[s]
+ * straight to owner e / P (P = E / W). Owner d's receive rows are its slots
+ * from all sources sorted by (source, expert, slot) for layout 0 (what
+ * ref_moe_pack followed by ref_a2av leaves) or (expert, source, slot) for
+ * layout 1 (what ref_moe_pack followed by ref_moe_dispatch_grouped leaves).
+ * perm[s] ([T*k]), S (W x W, row s = source s) and expert_counts (W x E) are
+ * ref_moe_pack's outputs; block_offsets[d] ([G+1], G = W for layout 0, E/W
+ * for layout 1) = rows before block g (source g, or owned expert g) at
+ * receiver d, total at G. REF_BAD_EXPERT for an id outside [0, E) (nothing
+ * written); else REF_RECV_OVERFLOW when a receiver's total exceeds recv_cap
+ * (perm, S, counts and offsets written; no payload). */
+int ref_moe_pack_dispatch(int W, int64_t T, int k, int E, size_t R,
+                          const void *const *tokens, const int32_t *const *ids,
+                          void *const *recv, const int64_t *recv_cap, int64_t *const *perm,
+                          int64_t *S, int64_t *expert_counts, int64_t *block_offsets,
+                          int layout);
+
+/* The inverse: out[s][q] = the row of slot q of source s, read from its
+ * owner's receive buffer recv[d] (recv_rows[d] rows in the layout's order).
+ * counts is the W x E expert-count matrix; ids and perm are the pack's input
+ * and output per source. REF_BAD_SPLIT for a count outside [0, 2^40]
+ * (first); else the OR of REF_SEND_OVERRUN (an owner's rows exceed
+ * recv_rows), REF_BAD_EXPERT and REF_BAD_PERM (a perm entry outside its
+ * expert's pack block). Nothing is written on failure. */
+int ref_moe_unpack_return(int W, int64_t T, int k, int E, size_t R, const int64_t *counts,
+                          const int32_t *const *ids, const int64_t *const *perm,
+                          const void *const *recv, const int64_t *recv_rows, void *const *out,
+                          int layout);
+
 /* The whole key exchange of one batch for all W ranks: ref_keys_bucketize on
  * every source, then keys (8-byte rows) and lengths (4-byte rows) as two
  * ref_a2av calls with the bucketing's split rows. lengths_cap / keys_cap are

@@ -67,12 +67,17 @@ def _bind(lib):
     lib.ref_moe_combine_grouped.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                             ctypes.c_int, ctypes.c_int64, i64p, vpp, vpp, vpp,
                                             i64p, vpp, vpp]
+    lib.ref_moe_pack_dispatch.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                          sz, vpp, vpp, vpp, i64p, vpp, i64p, i64p, i64p,
+                                          ctypes.c_int]
+    lib.ref_moe_unpack_return.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                          sz, i64p, vpp, vpp, vpp, i64p, vpp, ctypes.c_int]
     lib.ref_keys_exchange.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, vpp, vpp, i64p,
                                       vpp, i64p, vpp, i64p, i64p, i64p, i64p]
     for name in ("ref_exchange_splits", "ref_offsets", "ref_copy", "ref_a2av", "ref_source_of",
                  "ref_moe_pack", "ref_moe_unpack", "ref_moe_regroup", "ref_moe_combine",
                  "ref_keys_bucketize", "ref_keys_exchange", "ref_moe_dispatch_grouped",
-                 "ref_moe_combine_grouped"):
+                 "ref_moe_combine_grouped", "ref_moe_pack_dispatch", "ref_moe_unpack_return"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -259,6 +264,38 @@ class Oracle:
         st = self.lib.ref_moe_dispatch_grouped(W, E, R, _i64(counts), _ptrs(ins), _i64(in_rows),
                                                _ptrs(outs), _i64(out_cap), _i64(eoff), direction)
         return st, outs, eoff
+
+    def moe_pack_dispatch(self, W, T, k, E, R, tokens, ids, recv_cap, layout=0):
+        """All W ranks. tokens: per-rank [T, R] bytes (any dtype); ids: per-rank
+        int32 [T*k]. Returns (status, [recv bytes, recv_cap[d] * R each,
+        zero-filled where not written], perm [W][T*k], S [W][W], counts [W][E],
+        block offsets [W][G+1]); the integer outputs start at -7."""
+        toks = [np.ascontiguousarray(x).view(np.uint8).reshape(-1) for x in tokens]
+        ids = [np.ascontiguousarray(i, dtype=np.int32).reshape(-1) for i in ids]
+        recv_cap = np.ascontiguousarray(recv_cap, dtype=np.int64)
+        recv = [np.zeros(max(int(c), 0) * R, dtype=np.uint8) for c in recv_cap]
+        perm = [np.full(T * k, -7, dtype=np.int64) for _ in range(W)]
+        S = np.full((W, W), -7, dtype=np.int64)
+        counts = np.full((W, E), -7, dtype=np.int64)
+        G = W if layout == 0 else E // W
+        boff = np.full((W, G + 1), -7, dtype=np.int64)
+        st = self.lib.ref_moe_pack_dispatch(W, T, k, E, R, _ptrs(toks), _ptrs(ids), _ptrs(recv),
+                                            _i64(recv_cap), _ptrs(perm), _i64(S), _i64(counts),
+                                            _i64(boff), layout)
+        return st, recv, perm, S, counts, boff
+
+    def moe_unpack_return(self, W, T, k, E, R, counts, ids, perms, recv, layout=0):
+        """All W ranks. recv: per-owner receive bytes (rows = size // R).
+        Returns (status, [out bytes [T*k*R], zero-filled where not written])."""
+        counts = np.ascontiguousarray(counts, dtype=np.int64)
+        ids = [np.ascontiguousarray(i, dtype=np.int32).reshape(-1) for i in ids]
+        perms = [np.ascontiguousarray(p, dtype=np.int64).reshape(-1) for p in perms]
+        rv = [np.ascontiguousarray(x).view(np.uint8).reshape(-1) for x in recv]
+        rows = np.array([x.size // R for x in rv], dtype=np.int64)
+        outs = [np.zeros(T * k * R, dtype=np.uint8) for _ in range(W)]
+        st = self.lib.ref_moe_unpack_return(W, T, k, E, R, _i64(counts), _ptrs(ids), _ptrs(perms),
+                                            _ptrs(rv), _i64(rows), _ptrs(outs), layout)
+        return st, outs
 
     def moe_combine_grouped(self, W, T, k, E, H, counts, ids, perms, expert_side, weights):
         """All W ranks. ids: per-rank int32 [T*k]; perms: int64 [T*k]; expert_side:

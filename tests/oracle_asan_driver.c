@@ -242,6 +242,47 @@ static void one_combine_grouped(int W, int64_t T, int k, int E, int64_t H) {
     free(tok); free(send); free(splits);
 }
 
+/* pack + dispatch in one step and its inverse, both layouts: every slot comes home */
+static void one_pack_dispatch(int W, int64_t T, int k, int E, size_t R, int layout) {
+    const int P = E / W;
+    const int64_t Q = T * k;
+    const int G = layout == 0 ? W : P;
+    void **tok = malloc(sizeof(void *) * W), **recv = malloc(sizeof(void *) * W);
+    void **out = malloc(sizeof(void *) * W);
+    int32_t **ids = malloc(sizeof(void *) * W);
+    int64_t **perm = malloc(sizeof(void *) * W);
+    int64_t *S = malloc(sizeof(int64_t) * W * W), *counts = malloc(sizeof(int64_t) * W * E);
+    int64_t *boff = malloc(sizeof(int64_t) * W * (G + 1)), *cap = malloc(sizeof(int64_t) * W);
+    int64_t *rows = malloc(sizeof(int64_t) * W);
+    for (int s = 0; s < W; s++) {
+        tok[s] = malloc((size_t)T * R + 1);
+        for (int64_t i = 0; i < T * (int64_t)R; i++) ((unsigned char *)tok[s])[i] = (unsigned char)next_u64();
+        ids[s] = malloc(sizeof(int32_t) * (Q + 1));
+        perm[s] = malloc(sizeof(int64_t) * (Q + 1));
+        out[s] = malloc((size_t)Q * R + 1);
+        for (int64_t q = 0; q < Q; q++) ids[s][q] = (int32_t)(next_u64() % E);
+    }
+    for (int d = 0; d < W; d++) {
+        rows[d] = 0;
+        for (int s = 0; s < W; s++)
+            for (int64_t q = 0; q < Q; q++) rows[d] += ids[s][q] / P == d;
+        cap[d] = rows[d];
+        recv[d] = malloc((size_t)rows[d] * R + 1);
+    }
+    CHECK(ref_moe_pack_dispatch(W, T, k, E, R, (const void *const *)tok,
+                                (const int32_t *const *)ids, recv, cap, perm, S, counts, boff,
+                                layout) == 0);
+    CHECK(ref_moe_unpack_return(W, T, k, E, R, counts, (const int32_t *const *)ids,
+                                (const int64_t *const *)perm, (const void *const *)recv, rows, out,
+                                layout) == 0);
+    for (int s = 0; s < W; s++)
+        for (int64_t q = 0; q < Q; q++)
+            CHECK(memcmp((unsigned char *)out[s] + q * R, (unsigned char *)tok[s] + (q / k) * R, R) == 0);
+    for (int s = 0; s < W; s++) { free(tok[s]); free(recv[s]); free(out[s]); free(ids[s]); free(perm[s]); }
+    free(tok); free(recv); free(out); free(ids); free(perm); free(S); free(counts); free(boff);
+    free(cap); free(rows);
+}
+
 int main(void) {
     const size_t widths[] = {1, 3, 8, 16, 100};
     for (int W = 1; W <= 9; W++)
@@ -268,6 +309,12 @@ int main(void) {
     one_grouped(8, 256, 16);
     one_grouped(3, 12, 5);
     one_grouped(1, 1, 1);
+    for (int layout = 0; layout < 2; layout++) {
+        one_pack_dispatch(8, 60, 8, 256, 16, layout);
+        one_pack_dispatch(3, 17, 2, 6, 5, layout);
+        one_pack_dispatch(1, 1, 1, 1, 1, layout);
+        one_pack_dispatch(4, 0, 2, 8, 3, layout);
+    }
     one_keys_exchange(8, 26, 32);
     one_keys_exchange(3, 2, 5);
     one_keys_exchange(1, 3, 4);

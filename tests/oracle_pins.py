@@ -638,6 +638,118 @@ def pin_moe_combine_grouped(o):
     assert o.moe_combine_grouped(W, T, k, E, H, c2, ids, perms, exp16, ws)[0] == R.BAD_SPLIT
 
 
+def _return_a2av_unpack(o, W, T, k, R_bytes, S, perms, recv):
+    """The unfused return trip of layout 0: the a2av with the transposed
+    splits brings every owner's block home, then the un-pack."""
+    Ot = np.ascontiguousarray(S.T)
+    back = [np.zeros(T * k * R_bytes, np.uint8) for _ in range(W)]
+    st, _, _, _ = o.a2av(R_bytes, recv, Ot.sum(axis=1), back, np.full(W, T * k), Ot)
+    assert st == 0
+    outs = []
+    for s in range(W):
+        st, out = o.moe_unpack(T, k, R_bytes, back[s], perms[s])
+        assert st == 0
+        outs.append(out)
+    return outs
+
+
+def pin_moe_pack_dispatch(o):
+    """Pack + dispatch in one step: for both layouts equal to the pack
+    followed by the a2av (layout 0) or by the grouped dispatch (layout 1),
+    both pinned on their own; its inverse brings every slot its token row
+    (closed form) and equals the unfused return trip on arbitrary receive
+    contents; bad ids, short receivers, bad counts, perm entries outside
+    their block are refused with nothing (or only the metadata) written."""
+    g = np.random.default_rng(41)
+    for W, T, k, E, Rb, distinct in ((4, 40, 3, 12, 6, True), (2, 17, 4, 8, 5, False),
+                                     (1, 9, 2, 3, 16, True), (3, 0, 2, 6, 4, False),
+                                     (8, 64, 8, 256, 16, True), (5, 23, 2, 5, 3, False)):
+        P = E // W
+        toks, ids, sends, perms, splits, counts = [], [], [], [], [], []
+        for r in range(W):
+            tok, idr = _moe_case(g, T, k, E, Rb, distinct)
+            st, send, perm, spl, cnt = o.moe_pack(T, k, E, W, Rb, tok, idr)
+            assert st == 0
+            toks.append(tok); ids.append(idr.reshape(-1)); sends.append(send)
+            perms.append(perm); splits.append(spl); counts.append(cnt)
+        S = np.stack(splits).reshape(W, W)
+        counts = np.stack(counts).reshape(W, E)
+        tot = S.sum(axis=0)
+        # layout 0 against pack + a2av
+        cap = tot + np.arange(W)          # spare rows stay untouched
+        st, recv, perm, S0, c0, boff = o.moe_pack_dispatch(W, T, k, E, Rb, toks, ids, cap, 0)
+        assert st == 0
+        assert np.array_equal(S0, S) and np.array_equal(c0, counts)
+        assert all(np.array_equal(a, b) for a, b in zip(perm, perms))
+        want = [np.zeros(int(c) * Rb, np.uint8) for c in cap]
+        st, _, _, rro = o.a2av(Rb, sends, np.full(W, T * k), want, cap, S)
+        assert st == 0 and np.array_equal(boff, rro)
+        assert all(np.array_equal(a, b) for a, b in zip(recv, want))
+        st, outs = o.moe_unpack_return(W, T, k, E, Rb, counts, ids, perms,
+                                       [x[:int(t) * Rb] for x, t in zip(recv, tot)], 0)
+        assert st == 0
+        for s in range(W):   # every slot gets its token row back
+            assert np.array_equal(outs[s].reshape(T * k, Rb), np.repeat(toks[s], k, axis=0))
+        # layout 1 against pack + grouped dispatch
+        st, recv1, perm1, S1, c1, boff1 = o.moe_pack_dispatch(W, T, k, E, Rb, toks, ids, cap, 1)
+        assert st == 0 and np.array_equal(S1, S) and np.array_equal(c1, counts)
+        assert all(np.array_equal(a, b) for a, b in zip(perm1, perms))
+        st, want1, eoff = o.moe_dispatch_grouped(W, E, Rb, counts, sends, [T * k] * W, cap, 0)
+        assert st == 0 and np.array_equal(boff1, eoff)
+        assert all(np.array_equal(a, b) for a, b in zip(recv1, want1))
+        st, outs1 = o.moe_unpack_return(W, T, k, E, Rb, counts, ids, perms, recv1, 1)
+        assert st == 0
+        for s in range(W):
+            assert np.array_equal(outs1[s].reshape(T * k, Rb), np.repeat(toks[s], k, axis=0))
+        # the inverse on arbitrary receive contents equals the unfused return trips
+        junk = [g.integers(0, 256, size=int(t) * Rb, dtype=np.uint8) for t in tot]
+        st, got0 = o.moe_unpack_return(W, T, k, E, Rb, counts, ids, perms, junk, 0)
+        assert st == 0
+        w0 = _return_a2av_unpack(o, W, T, k, Rb, S, perms, junk)
+        assert all(np.array_equal(a, b) for a, b in zip(got0, w0))
+        st, got1 = o.moe_unpack_return(W, T, k, E, Rb, counts, ids, perms, junk, 1)
+        assert st == 0
+        st, back, _ = o.moe_dispatch_grouped(W, E, Rb, counts, junk, tot, [T * k] * W, 1)
+        assert st == 0
+        for s in range(W):
+            st, w1 = o.moe_unpack(T, k, Rb, back[s], perms[s])
+            assert st == 0 and np.array_equal(got1[s], w1), s
+    # failures
+    W, T, k, E, Rb = 2, 6, 2, 4, 4
+    toks, ids = [], []
+    for r in range(W):
+        tok, idr = _moe_case(g, T, k, E, Rb, True)
+        toks.append(tok); ids.append(idr.reshape(-1))
+    st, recv, perm, S, counts, boff = o.moe_pack_dispatch(W, T, k, E, Rb, toks, ids, [99] * W, 0)
+    assert st == 0
+    tot = S.sum(axis=0)
+    bad = [x.copy() for x in ids]; bad[1][5] = -1
+    for layout in (0, 1):
+        st, rv, pm, S2, c2, b2 = o.moe_pack_dispatch(W, T, k, E, Rb, toks, bad, [99] * W, layout)
+        assert st == R.BAD_EXPERT and not any(x.any() for x in rv)
+        assert all((x == -7).all() for x in pm) and (S2 == -7).all() and (c2 == -7).all()
+        short = tot.copy(); short[1] -= 1
+        st, rv, pm, S2, c2, b2 = o.moe_pack_dispatch(W, T, k, E, Rb, toks, ids, short, layout)
+        assert st == R.RECV_OVERFLOW and not any(x.any() for x in rv)
+        assert np.array_equal(S2, S) and np.array_equal(c2, counts)
+        assert all(np.array_equal(a, b) for a, b in zip(pm, perm))
+        assert b2[1, -1] == tot[1]
+        full = [x[:int(t) * Rb] for x, t in zip(recv, tot)]
+        st, out = o.moe_unpack_return(W, T, k, E, Rb, counts, bad, perm, full, layout)
+        assert st == R.BAD_EXPERT and not any(x.any() for x in out)
+        swapped = [x.copy() for x in ids]
+        q = int(np.nonzero(swapped[0] != swapped[0][0])[0][0])
+        swapped[0][0], swapped[0][q] = swapped[0][q], swapped[0][0]
+        st, out = o.moe_unpack_return(W, T, k, E, Rb, counts, swapped, perm, full, layout)
+        assert st == R.BAD_PERM and not any(x.any() for x in out)
+        st, out = o.moe_unpack_return(W, T, k, E, Rb, counts, ids, perm,
+                                      [x[:-Rb] for x in full], layout)
+        assert st == R.SEND_OVERRUN and not any(x.any() for x in out)
+        c3 = counts.copy(); c3[1, 2] = -1
+        st, out = o.moe_unpack_return(W, T, k, E, Rb, c3, ids, perm, full, layout)
+        assert st == R.BAD_SPLIT and not any(x.any() for x in out)
+
+
 # ------------------------------------------------------------------ gate-weighted combine
 def _round_f32(x):
     """A Fraction rounded to the nearest binary32, ties to even (finite, in

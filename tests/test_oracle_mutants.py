@@ -90,6 +90,19 @@ MUTANTS = {
     "combine_grouped_skips_block_check": [
         ("if (p < Y[s * E + e] || p >= Y[s * E + e] + counts[s * E + e]) st |= REF_BAD_PERM;",
          "(void)p;", 0)],
+    "pack_dispatch_layout1_source_major": [
+        ("x->key[0] = layout == 0 ? s : e;\n                x->key[1] = layout == 0 ? e : s;",
+         "x->key[0] = s;\n                x->key[1] = e;", 0)],
+    "pack_dispatch_source_offsets_transposed": [
+        ("if (layout == 0) run += S[g * W + d];", "if (layout == 0) run += S[d * W + g];", 0)],
+    "pack_dispatch_wrong_token": [("x->tok = q / k;", "x->tok = q % T;", 0)],
+    "unpack_return_ignores_layout": [("        if (layout == 0) {\n", "        if (layout == 2) {\n", 0)],
+    "unpack_return_ignores_block_offset": [
+        ("const int64_t row = Z[s * E + e] + (perm[s][q] - Y[s * E + e]);",
+         "const int64_t row = Z[s * E + e];", 0)],
+    "unpack_return_overrun_off_by_one": [
+        ("if (run > recv_rows[d]) st |= REF_SEND_OVERRUN;",
+         "if (run >= recv_rows[d]) st |= REF_SEND_OVERRUN;", 0)],
     "keys_exchange_offsets_inclusive": [
         ("            recv_off_keys[d * (W + 1) + s] = run;\n            run += Sk[s * W + d];",
          "            run += Sk[s * W + d];\n            recv_off_keys[d * (W + 1) + s] = run;", 0)],
