@@ -601,7 +601,50 @@ def moe_rows(torch, B, I, o, out):
                                    "note": "grouped dispatch + combine from the expert side"}
     torch.cuda.synchronize()
     _check_status(B, [("grouped combine", cgst), ("grouped", gst)])
-    del grp
+    # ---- the pack and the dispatch in one step (no send buffer), both receive
+    # orders, and the inverse (return trip and un-pack in one step)
+    pdws = torch.empty(B.moe_pack_dispatch_workspace_bytes(W, T, k, E), dtype=torch.uint8,
+                       device="cuda")
+    pdst = torch.zeros(1, dtype=torch.int32, device="cuda")
+    S1, cnt1 = torch.empty_like(S), torch.empty_like(counts)
+    perm1 = [torch.empty_like(x) for x in perm]
+    boff0 = torch.empty((W, W + 1), dtype=torch.int64, device="cuda")
+    boff1 = torch.empty((W, E // W + 1), dtype=torch.int64, device="cuda")
+    pd0 = lambda: B.moe_pack_dispatch(W, T, k, E, R, tok, ids, recv, cap, perm1, S1, cnt1, boff0,
+                                      0, pdws, pdst)
+    pd1 = lambda: B.moe_pack_dispatch(W, T, k, E, R, tok, ids, grp, cap, perm1, S1, cnt1, boff1,
+                                      1, pdws, pdst)
+    out["moe_pack_dispatch"] = row_entry(pack_bytes, time_events(torch, pd0, 5))
+    out["moe_pack_dispatch_grouped"] = row_entry(pack_bytes, time_events(torch, pd1, 5))
+    urws = torch.empty(B.moe_unpack_return_workspace_bytes(W, E), dtype=torch.uint8,
+                       device="cuda")
+    urst = torch.zeros(1, dtype=torch.int32, device="cuda")
+    home = [torch.empty((Q, hidden), dtype=torch.bfloat16, device="cuda") for _ in range(W)]
+    ur0 = lambda: B.moe_unpack_return(W, T, k, E, R, cnt1, ids, perm1, recv, cap, home, 0, urws,
+                                      urst)
+    ur1 = lambda: B.moe_unpack_return(W, T, k, E, R, cnt1, ids, perm1, grp, cap, home, 1, urws,
+                                      urst)
+    unpack_bytes = W * (2 * Q * R + Q * (8 + 4))
+    out["moe_unpack_return"] = row_entry(unpack_bytes, time_events(torch, ur0, 5))
+    out["moe_unpack_return_grouped"] = row_entry(unpack_bytes, time_events(torch, ur1, 5))
+    # whole round trips from the tokens, each as one-step calls
+    cgrp1 = lambda: B.moe_combine_grouped(W, T, k, E, hidden, cnt1, ids, perm1, grp, cap, wts,
+                                          cgo, cgws, cgst)
+    ms = time_events(torch, lambda: (pd0(), ur0()), 5)
+    out["moe_tokens_unpack_round_trip"] = {
+        "us": round(ms * 1e3, 2), "note": "moe_pack_dispatch + moe_unpack_return (layout 0)"}
+    ms = time_events(torch, lambda: (pd1(), cgrp1()), 5)
+    out["moe_tokens_combine_round_trip"] = {
+        "us": round(ms * 1e3, 2),
+        "note": "moe_pack_dispatch (layout 1) + combine from the expert side"}
+    torch.cuda.synchronize()
+    _check_status(B, [("pack + dispatch", pdst), ("unpack + return", urst),
+                      ("grouped combine", cgst)])
+    for r in range(W):
+        if not torch.equal(home[r].view(torch.int16),
+                           tok[r].view(torch.int16).repeat_interleave(k, dim=0)):
+            raise RuntimeError("pack + dispatch and its inverse did not bring every slot home")
+    del grp, home
     # ---- return a2av: every row goes home
     bk = A2av(W)
     bk.S.copy_(fwd.O)
@@ -644,6 +687,15 @@ def moe_rows(torch, B, I, o, out):
                                                  "moe_regroup_to_source", "return_a2av",
                                                  "moe_combine")), 2),
         "note": "sum of dispatch a2av, both regroups, return a2av and combine"}
+    # from the tokens, unfused: pack, then those steps (weighted), or pack,
+    # dispatch a2av, return a2av and un-pack (unweighted)
+    out["moe_tokens_combine_round_trip_chain"] = {
+        "us": round(out["moe_pack"]["us"] + out["moe_chain_round_trip"]["us"], 2),
+        "note": "moe_pack + the chain above"}
+    out["moe_tokens_unpack_round_trip_chain"] = {
+        "us": round(sum(out[x]["us"] for x in ("moe_pack", "dispatch_a2av", "return_a2av",
+                                                 "moe_unpack")), 2),
+        "note": "sum of pack, dispatch a2av, return a2av and un-pack"}
     return dict(fwd=fwd, send=send, recv=recv, cap=cap, R=R, Q=Q, W=W)
 
 

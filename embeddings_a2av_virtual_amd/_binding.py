@@ -26,6 +26,8 @@ __all__ = [
     "moe_pack_workspace_bytes", "moe_pack", "moe_unpack", "moe_combine",
     "moe_regroup_workspace_bytes", "moe_regroup", "moe_dispatch_grouped_workspace_bytes",
     "moe_dispatch_grouped", "moe_combine_grouped_workspace_bytes", "moe_combine_grouped",
+    "moe_pack_dispatch_workspace_bytes", "moe_pack_dispatch", "moe_unpack_return_workspace_bytes",
+    "moe_unpack_return",
     "keys_bucketize_workspace_bytes",
     "keys_bucketize", "keys_exchange_workspace_bytes", "keys_exchange", "a2av_device_copy",
     "MAX_TABLES",
@@ -89,6 +91,14 @@ def lib():
         L.moe_combine_grouped_workspace_bytes.restype = sz
         L.moe_combine_grouped.argtypes = [i32, i64, i32, i32, i64, vp, vpp, vpp, vpp, i64p, vpp,
                                           vpp, vp, sz, vp, vp]
+        L.moe_pack_dispatch_workspace_bytes.argtypes = [i32, i64, i32, i32]
+        L.moe_pack_dispatch_workspace_bytes.restype = sz
+        L.moe_pack_dispatch.argtypes = [i32, i64, i32, i32, sz, vpp, vpp, vpp, i64p, vpp, vp, vp,
+                                        vp, i32, vp, sz, vp, vp]
+        L.moe_unpack_return_workspace_bytes.argtypes = [i32, i32]
+        L.moe_unpack_return_workspace_bytes.restype = sz
+        L.moe_unpack_return.argtypes = [i32, i64, i32, i32, sz, vp, vpp, vpp, vpp, i64p, vpp, i32,
+                                        vp, sz, vp, vp]
         L.keys_bucketize_workspace_bytes.argtypes = [i32, i32]
         L.keys_bucketize_workspace_bytes.restype = sz
         L.keys_bucketize.argtypes = [i32, i32, i64, vpp, vpp, i64p, vpp, vpp, vp, vp, vp, sz, vp,
@@ -100,7 +110,7 @@ def lib():
         L.a2av_device_copy.argtypes = [vp, vp, sz, vp]
         for f in ("a2av_exchange_splits", "a2av_offsets", "a2av_copy", "a2av_all_to_all_vdev",
                   "moe_pack", "moe_unpack", "moe_combine", "moe_regroup", "moe_dispatch_grouped",
-                  "moe_combine_grouped",
+                  "moe_combine_grouped", "moe_pack_dispatch", "moe_unpack_return",
                   "keys_bucketize", "keys_exchange",
                   "a2av_device_copy"):
             getattr(L, f).restype = i32
@@ -286,6 +296,50 @@ def moe_combine_grouped(W, T, k, E, H, counts, ids, perm, expert_side, exp_rows,
                                      _ptr_array(out, "out"), _dev(workspace, "workspace"),
                                      workspace.numel() * workspace.element_size(),
                                      _dev(status, "status"), _stream(stream, status)))
+
+
+def moe_pack_dispatch_workspace_bytes(W, T, k, E) -> int:
+    return int(lib().moe_pack_dispatch_workspace_bytes(int(W), int(T), int(k), int(E)))
+
+
+def moe_pack_dispatch(W, T, k, E, row_bytes, tokens, ids, recv, recv_cap_rows, perm, S,
+                      expert_counts, block_offsets, layout, workspace, status, stream=None):
+    """moe_pack and the dispatch in one step: every slot's token row written
+    straight into its owner's receive buffer (layout 0: source-major, as the
+    a2av delivers; 1: expert-major, as the grouped dispatch delivers)."""
+    if (len(tokens) != W or len(ids) != W or len(recv) != W or len(recv_cap_rows) != W
+            or len(perm) != W):
+        raise ValueError("tokens, ids, recv, recv_cap_rows and perm need W entries each")
+    _check("moe_pack_dispatch",
+           lib().moe_pack_dispatch(int(W), int(T), int(k), int(E), int(row_bytes),
+                                   _ptr_array(tokens, "tokens"), _ptr_array(ids, "ids"),
+                                   _ptr_array(recv, "recv"), _i64_array(recv_cap_rows),
+                                   _ptr_array(perm, "perm"), _dev(S, "S"),
+                                   _dev(expert_counts, "expert_counts"),
+                                   _dev(block_offsets, "block_offsets"), int(layout),
+                                   _dev(workspace, "workspace"),
+                                   workspace.numel() * workspace.element_size(),
+                                   _dev(status, "status"), _stream(stream, status)))
+
+
+def moe_unpack_return_workspace_bytes(W, E) -> int:
+    return int(lib().moe_unpack_return_workspace_bytes(int(W), int(E)))
+
+
+def moe_unpack_return(W, T, k, E, row_bytes, expert_counts, ids, perm, recv, recv_rows, out,
+                      layout, workspace, status, stream=None):
+    """The inverse of moe_pack_dispatch: every slot's row read back from its
+    owner's receive buffer."""
+    if len(ids) != W or len(perm) != W or len(recv) != W or len(recv_rows) != W or len(out) != W:
+        raise ValueError("ids, perm, recv, recv_rows and out need W entries each")
+    _check("moe_unpack_return",
+           lib().moe_unpack_return(int(W), int(T), int(k), int(E), int(row_bytes),
+                                   _dev(expert_counts, "expert_counts"), _ptr_array(ids, "ids"),
+                                   _ptr_array(perm, "perm"), _ptr_array(recv, "recv"),
+                                   _i64_array(recv_rows), _ptr_array(out, "out"), int(layout),
+                                   _dev(workspace, "workspace"),
+                                   workspace.numel() * workspace.element_size(),
+                                   _dev(status, "status"), _stream(stream, status)))
 
 
 def keys_bucketize_workspace_bytes(W, n_tables) -> int:

@@ -25,8 +25,6 @@
 
 namespace a2av {
 
-constexpr int kPlanThreads = 1024;
-constexpr int kPlanPer = 4;  // blocks per planning thread: up to 4096 per rank
 
 struct BlockArgs {
     const unsigned char *in[A2AV_MAX_W];
@@ -129,39 +127,6 @@ __global__ __launch_bounds__(256) void k_block_copy(const BlockArgs a) {
 // Exclusive scans of two sequences at once over a 1024-thread block: each
 // thread contributes its sums (va, vb) and gets the sums of the threads
 // before it; ta, tb receive the block totals.
-struct ScanLds {
-    int64_t a[kPlanThreads / kWave];
-    int64_t b[kPlanThreads / kWave];
-};
-
-__device__ __forceinline__ void block_excl_scan2(int64_t va, int64_t vb, ScanLds &l,
-                                                 int64_t *ea, int64_t *eb, int64_t *ta, int64_t *tb) {
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-    constexpr int NW = kPlanThreads / kWave;
-    const int64_t ia = wave_incl_scan(va), ib = wave_incl_scan(vb);
-    if (lane == kWave - 1) {
-        l.a[wv] = ia;
-        l.b[wv] = ib;
-    }
-    __syncthreads();
-    int64_t pa = 0, pb = 0, sa = 0, sb = 0;
-#pragma unroll
-    for (int w = 0; w < NW; w++) {
-        const int64_t xa = l.a[w], xb = l.b[w];
-        if (w < wv) {
-            pa += xa;
-            pb += xb;
-        }
-        sa += xa;
-        sb += xb;
-    }
-    __syncthreads();  // the arrays may be reused by the caller
-    *ea = pa + ia - va;
-    *eb = pb + ib - vb;
-    *ta = sa;
-    *tb = sb;
-}
-
 // ------------------------------------------------------------ expert regroup plan
 struct RegroupPlanArgs {
     const int64_t *counts;    // [W][E]

@@ -248,6 +248,77 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// ------------------------------------------------------------ block scans
+// Plans run one 1024-thread workgroup per rank, each thread owning up to
+// kPlanPer consecutive entries (4096 per rank at most).
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanPer = 4;
+
+// Two exclusive scans over the workgroup at once, with both totals.
+struct ScanLds {
+    int64_t a[kPlanThreads / kWave];
+    int64_t b[kPlanThreads / kWave];
+};
+
+__device__ __forceinline__ void block_excl_scan2(int64_t va, int64_t vb, ScanLds &l,
+                                                 int64_t *ea, int64_t *eb, int64_t *ta, int64_t *tb) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    constexpr int NW = kPlanThreads / kWave;
+    const int64_t ia = wave_incl_scan(va), ib = wave_incl_scan(vb);
+    if (lane == kWave - 1) {
+        l.a[wv] = ia;
+        l.b[wv] = ib;
+    }
+    __syncthreads();
+    int64_t pa = 0, pb = 0, sa = 0, sb = 0;
+#pragma unroll
+    for (int w = 0; w < NW; w++) {
+        const int64_t xa = l.a[w], xb = l.b[w];
+        if (w < wv) {
+            pa += xa;
+            pb += xb;
+        }
+        sa += xa;
+        sb += xb;
+    }
+    __syncthreads();  // the arrays may be reused by the caller
+    *ea = pa + ia - va;
+    *eb = pb + ib - vb;
+    *ta = sa;
+    *tb = sb;
+}
+
+// Three exclusive scans over the workgroup at once, with their totals.
+struct ScanLds3 {
+    int64_t v[3][kPlanThreads / kWave];
+};
+
+__device__ __forceinline__ void block_excl_scan3(const int64_t (&v)[3], ScanLds3 &l,
+                                                 int64_t (&ex)[3], int64_t (&tot)[3]) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    constexpr int NW = kPlanThreads / kWave;
+    int64_t inc[3];
+#pragma unroll
+    for (int i = 0; i < 3; i++) {
+        inc[i] = wave_incl_scan(v[i]);
+        if (lane == kWave - 1) l.v[i][wv] = inc[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 3; i++) {
+        int64_t pre = 0, sum = 0;
+#pragma unroll 4
+        for (int w = 0; w < NW; w++) {
+            const int64_t x = l.v[i][w];
+            pre += w < wv ? x : 0;
+            sum += x;
+        }
+        ex[i] = pre + inc[i] - v[i];
+        tot[i] = sum;
+    }
+    __syncthreads();  // the arrays may be reused by the caller
+}
+
 // ------------------------------------------------------------ host helpers
 int device_cu_count(hipStream_t stream);
 long env_long(const char *name, long dflt, long lo, long hi);

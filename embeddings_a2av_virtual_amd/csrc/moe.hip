@@ -34,6 +34,10 @@ struct MoeArgs {
     int64_t *S;
     int64_t *expert_counts;
     int32_t *hist;   // workspace: [W][E][nseg] int32
+    // pack + dispatch in one step: slot rows go to row_addr[s][e] + perm * R
+    // (an owner's receive buffer) instead of send[s] + perm * R
+    const uint64_t *row_addr;   // [W][E]
+    const int32_t *plan_bits;   // the plan's verdict
     int32_t *status;
     uint64_t R;
     int64_t T;
@@ -177,12 +181,23 @@ __global__ __launch_bounds__(256) void k_moe_rank(const MoeArgs a) {
 
 // ------------------------------------------------------------------ scatter
 // One wave per (rank, token): the token row is read once into registers (up
-// to 64 x 16 x U bytes per pass) and stored to the k packed rows of its
-// slots. Rows or bases that are not 16-byte aligned take k realigning wave
-// copies of the row instead (the re-reads hit in L2).
-template <int U, bool ALIGNED, bool SNT>
+// to 64 x 16 x U bytes per pass) and stored to the k rows of its slots. Lane
+// j < k holds the address of slot j's row: send[r] + perm * R for the pack,
+// or the owner's receive row row_addr[r][e] + perm * R when the pack and the
+// dispatch run as one step (DIRECT). Rows or bases that are not 16-byte
+// aligned take k realigning wave copies of the row instead (the re-reads hit
+// in L2).
+template <int U, bool ALIGNED, bool SNT, bool DIRECT>
 __global__ __launch_bounds__(256) void k_moe_scatter(const MoeArgs a) {
     if (status_poisoned(a.status)) return;
+    if constexpr (DIRECT) {
+        // a receiver too small: report once; no wave writes a row
+        const int32_t pb = *(const const_i32 *)a.plan_bits;
+        if (pb) {
+            if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.status, pb);
+            return;
+        }
+    }
     const int lane = threadIdx.x & (kWave - 1);
     const uint64_t wpb = blockDim.x / kWave;
     const uint64_t nwork = (uint64_t)a.W * (uint64_t)a.T;
@@ -192,11 +207,22 @@ __global__ __launch_bounds__(256) void k_moe_scatter(const MoeArgs a) {
         const int r = (int)(w / (uint64_t)a.T);
         const int64_t t = (int64_t)(w - (uint64_t)r * (uint64_t)a.T);
         const unsigned char *src = a.tokens[r] + (uint64_t)t * R;
-        const int64_t *perm = a.perm[r] + t * a.k;
-        unsigned char *send = a.send[r];
-        // the token's k packed rows, one per lane, fetched before any store
-        // (k <= 64 here; the host routes larger k to the unaligned form)
-        const int64_t pl = lane < a.k ? perm[lane] : -1;
+        // the token's k rows, one address per lane, fetched before any store
+        // (k <= 64 here; the host routes larger k to the pack's unaligned form)
+        uint64_t al = 0;
+        bool okl = false;
+        if (lane < a.k) {
+            const int64_t p = a.perm[r][t * a.k + lane];
+            okl = p >= 0 && p < a.Q;
+            if constexpr (DIRECT) {
+                const int e = a.ids[r][t * a.k + lane];
+                okl = okl && (unsigned)e < (unsigned)a.E;
+                al = okl ? a.row_addr[(int64_t)r * a.E + e] + (uint64_t)p * R : 0;
+            } else {
+                al = (uint64_t)(uintptr_t)a.send[r] + (uint64_t)p * R;
+            }
+        }
+        const uint64_t okm = __ballot(okl);
         if constexpr (ALIGNED) {
             const uint64_t nv = R / 16;
             const u32x4 *s16 = (const u32x4 *)src;
@@ -212,23 +238,234 @@ __global__ __launch_bounds__(256) void k_moe_scatter(const MoeArgs a) {
                     v[u] = ld<true>(s16 + idx[u]);
                 }
                 for (int j = 0; j < a.k; j++) {
-                    const int64_t p = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
-                                                     (int)((uint64_t)pl >> 32), j) << 32) |
-                                                 (uint32_t)__builtin_amdgcn_readlane((int)pl, j));
-                    if (p < 0 || p >= a.Q) continue;
-                    u32x4 *d16 = (u32x4 *)(send + (uint64_t)p * R);
+                    if (!((okm >> j) & 1)) continue;
+                    u32x4 *d16 = (u32x4 *)(uintptr_t)readlane_u64(al, j);
 #pragma unroll
                     for (int u = 0; u < U; u++) st<SNT>(d16 + idx[u], v[u]);
                 }
             }
-        } else {
-            (void)pl;
+        } else if constexpr (DIRECT) {
             for (int j = 0; j < a.k; j++) {
-                const int64_t p = perm[j];
+                if (!((okm >> j) & 1)) continue;
+                wave_copy_any<4>((unsigned char *)(uintptr_t)readlane_u64(al, j), src, R, lane);
+            }
+        } else {
+            // any k: slot j's row straight from perm
+            for (int j = 0; j < a.k; j++) {
+                const int64_t p = a.perm[r][t * a.k + j];
                 if (p < 0 || p >= a.Q) continue;
-                wave_copy_any<4>(send + (uint64_t)p * R, src, R, lane);
+                wave_copy_any<4>(a.send[r] + (uint64_t)p * R, src, R, lane);
             }
         }
+    }
+}
+
+// ------------------------------------------------------------------ row shifts
+// Where slot rows sit at their owners when the pack and the dispatch run as
+// one step. Owner d = e / P (P = E / W) keeps its rows in one of two orders:
+// layout 0 = (source, expert, slot), as the pack followed by the a2av leaves
+// them; layout 1 = (expert, source, slot), as the pack followed by the
+// grouped dispatch leaves them. Slot q of source s with expert e and pack row
+// p then sits at owner row p + shift(s, e):
+//   layout 0: shift = (rows d holds from sources before s) - Y_s(d*P)
+//   layout 1: shift = (rows d holds of its experts before e)
+//                     + (rows of expert e from sources before s) - Y_s(e)
+// where Y_s(e) = rows of source s's smaller experts (its pack position).
+struct ShiftArgs {
+    const unsigned char *base[A2AV_MAX_W];  // row 0 of each owner's receive buffer
+    int64_t limit[A2AV_MAX_W];              // rows each owner's buffer holds
+    const int64_t *counts;                  // [W][E]
+    uint64_t *row_addr;                     // [W][E] base[d] + shift * R (mod 2^64)
+    int64_t *ystart;                        // [W][E] Y_s(e), or null
+    int64_t *block_offsets;                 // [W][G + 1] (G = W or P), or null
+    int32_t *words;                         // [0] plan bits, [1] cleared for the slot check
+    const int32_t *status;
+    uint64_t R;
+    int W;
+    int E;
+    int layout;
+    int over_bit;      // raised when an owner's rows exceed its limit
+    int check_counts;  // counts come from the caller: range-check them
+};
+
+__global__ __launch_bounds__(kPlanThreads) void k_shift_plan(const ShiftArgs a) {
+    __shared__ ScanLds3 lds;
+    __shared__ int64_t gb[A2AV_MAX_W + 1];  // column sums over experts before d*P
+    __shared__ int64_t bb[A2AV_MAX_W + 1];  // rows of sources before s, experts before d*P
+    __shared__ int64_t yb[A2AV_MAX_W + 1];  // Y_s(d*P)
+    __shared__ uint64_t base[A2AV_MAX_W];
+    __shared__ int64_t limit[A2AV_MAX_W];
+    __shared__ int poisoned;
+    const int s = blockIdx.x, tid = threadIdx.x;
+    const int W = a.W, E = a.E, P = E / W;
+    if (tid == 0) {
+        poisoned = status_poisoned(a.status);
+        for (int d = 0; d < W; d++) {
+            base[d] = (uint64_t)(uintptr_t)a.base[d];
+            limit[d] = a.limit[d];
+        }
+    }
+    __syncthreads();
+    if (poisoned) return;
+    if (a.check_counts) {
+        int bad = 0;
+        for (int i = tid; i < W * E; i += kPlanThreads) bad |= (int)split_invalid(a.counts[i]);
+        if (__syncthreads_or(bad)) {
+            if (s == 0 && tid == 0) {
+                a.words[0] = A2AV_ST_BAD_SPLIT;
+                a.words[1] = 0;
+            }
+            return;
+        }
+    }
+    int64_t col[kPlanPer], before[kPlanPer], mine[kPlanPer];
+    int64_t scol = 0, sbef = 0, smine = 0;
+#pragma unroll
+    for (int u = 0; u < kPlanPer; u++) {
+        const int e = tid * kPlanPer + u;
+        col[u] = before[u] = mine[u] = 0;
+        if (e < E) {
+            for (int s2 = 0; s2 < W; s2++) {
+                const int64_t c = a.counts[(int64_t)s2 * E + e];
+                col[u] += c;
+                if (s2 < s) before[u] += c;
+            }
+            mine[u] = a.counts[(int64_t)s * E + e];
+        }
+        scol += col[u];
+        sbef += before[u];
+        smine += mine[u];
+    }
+    const int64_t sums[3] = {scol, sbef, smine};
+    int64_t ex[3], tot[3];
+    block_excl_scan3(sums, lds, ex, tot);
+    int64_t gx = ex[0], yx = ex[2];
+    const int64_t bx = ex[1], gt = tot[0], bt = tot[1], yt = tot[2];
+    // the prefixes at every owner's first expert
+    {
+        int64_t g = gx, b = bx, y = yx;
+#pragma unroll
+        for (int u = 0; u < kPlanPer; u++) {
+            const int e = tid * kPlanPer + u;
+            if (e < E && e % P == 0) {
+                gb[e / P] = g;
+                bb[e / P] = b;
+                yb[e / P] = y;
+            }
+            g += col[u];
+            b += before[u];
+            y += mine[u];
+        }
+    }
+    if (tid == 0) {
+        gb[W] = gt;
+        bb[W] = bt;
+        yb[W] = yt;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPlanPer; u++) {
+        const int e = tid * kPlanPer + u;
+        if (e < E) {
+            const int d = e / P;
+            const int64_t shift = a.layout == 0 ? (bb[d + 1] - bb[d]) - yb[d]
+                                                : (gx - gb[d]) + before[u] - yx;
+            a.row_addr[(int64_t)s * E + e] = base[d] + (uint64_t)shift * a.R;
+            if (a.ystart) a.ystart[(int64_t)s * E + e] = yx;
+            if (a.block_offsets && a.layout == 1 && s == 0)
+                a.block_offsets[(int64_t)d * (P + 1) + (e - d * P)] = gx - gb[d];
+        }
+        gx += col[u];
+        yx += mine[u];
+    }
+    if (tid < W && a.block_offsets) {
+        const int d = tid;
+        if (a.layout == 0) {
+            a.block_offsets[(int64_t)d * (W + 1) + s] = bb[d + 1] - bb[d];
+            if (s == 0) a.block_offsets[(int64_t)d * (W + 1) + W] = gb[d + 1] - gb[d];
+        } else if (s == 0) {
+            a.block_offsets[(int64_t)d * (P + 1) + P] = gb[d + 1] - gb[d];
+        }
+    }
+    if (s == 0) {
+        // every owner's rows against what its buffer holds
+        int over = 0;
+        if (tid < W) over = gb[tid + 1] - gb[tid] > limit[tid];
+        over = __syncthreads_or(over);
+        if (tid == 0) {
+            a.words[0] = over ? a.over_bit : 0;
+            a.words[1] = 0;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ return in one step
+// The inverse of the fused pack + dispatch: every slot's row read back from
+// its owner's receive buffer, out[s][q] = that row.
+struct ReturnArgs {
+    unsigned char *out[A2AV_MAX_W];
+    const int32_t *ids[A2AV_MAX_W];
+    const int64_t *perm[A2AV_MAX_W];
+    const int64_t *counts;     // [W][E]
+    const uint64_t *row_addr;  // [W][E] (plan)
+    const int64_t *ystart;     // [W][E] (plan)
+    int32_t *words;            // [0] plan bits, [1] slot bits
+    int32_t *status;
+    uint64_t R;
+    int64_t Q;
+    int E;
+    int W;
+};
+
+// One thread per (slot, source): its id in range and its pack row inside its
+// expert's block, so every row the gather reads lies in the owner's buffer.
+__global__ __launch_bounds__(256) void k_slot_check(const ReturnArgs a) {
+    if (status_poisoned(a.status)) return;
+    const int s = blockIdx.y;
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int bad = 0;
+    if (q < a.Q) {
+        const int32_t e = a.ids[s][q];
+        if (e < 0 || e >= a.E) {
+            bad = A2AV_ST_BAD_EXPERT;
+        } else {
+            const int64_t p = a.perm[s][q] - a.ystart[(int64_t)s * a.E + e];
+            if (p < 0 || p >= a.counts[(int64_t)s * a.E + e]) bad = A2AV_ST_BAD_PERM;
+        }
+    }
+    const int be = __ballot(bad & A2AV_ST_BAD_EXPERT) != 0, bp = __ballot(bad & A2AV_ST_BAD_PERM) != 0;
+    if ((be || bp) && (threadIdx.x & (kWave - 1)) == 0)
+        atomicOr(&a.words[1], (be ? A2AV_ST_BAD_EXPERT : 0) | (bp ? A2AV_ST_BAD_PERM : 0));
+}
+
+// One wave per (source, slot): the slot's row copied home. With a verdict
+// from the plan or the slot check, the first thread reports it (a bad count
+// alone, since the other checks read the counts) and no row moves.
+template <int U, bool ALIGNED>
+__global__ __launch_bounds__(256) void k_moe_gather_home(const ReturnArgs a) {
+    if (status_poisoned(a.status)) return;
+    const int32_t pb = *(const const_i32 *)&a.words[0];
+    const int32_t cw = *(const const_i32 *)&a.words[1];
+    if (pb | cw) {
+        if (blockIdx.x == 0 && threadIdx.x == 0)
+            atomicOr(a.status, (pb & A2AV_ST_BAD_SPLIT) ? A2AV_ST_BAD_SPLIT : (pb | cw));
+        return;
+    }
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t wpb = blockDim.x / kWave;
+    const uint64_t nwork = (uint64_t)a.W * (uint64_t)a.Q;
+    const uint64_t R = a.R;
+    const uint32_t wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    for (uint64_t w = (uint64_t)blockIdx.x * wpb + wid; w < nwork; w += (uint64_t)gridDim.x * wpb) {
+        const int r = (int)(w / (uint64_t)a.Q);
+        const int64_t q = (int64_t)(w - (uint64_t)r * (uint64_t)a.Q);
+        const int e = *(const const_i32 *)(a.ids[r] + q);
+        const int64_t p = *(const const_i64 *)(a.perm[r] + q);
+        const unsigned char *src =
+            (const unsigned char *)(uintptr_t)(a.row_addr[(int64_t)r * a.E + e] + (uint64_t)p * R);
+        unsigned char *dst = a.out[r] + (uint64_t)q * R;
+        if constexpr (ALIGNED) copy_elems<u32x4, kWave, U, true>((u32x4 *)dst, (const u32x4 *)src, R / 16, lane);
+        else wave_copy_any<U>(dst, src, R, lane);
     }
 }
 
@@ -402,6 +639,26 @@ static bool moe_sizes_ok(int W, int64_t T, int k, int E) {
     return T * k < ((int64_t)1 << 31);
 }
 
+// The counting sort of the pack for every rank: histograms, their scan (expert
+// counts and splits), then the stable rank of every slot (perm).
+static void launch_pack_sort(MoeArgs &a, hipStream_t stream) {
+    const int W = a.W, E = a.E;
+    a.nseg = (int)n_segments(a.Q);
+    const int nseg_grid = a.nseg > 0 ? a.nseg : 1;
+    if (a.nseg > 0) {
+        hipLaunchKernelGGL(k_moe_hist, dim3(a.nseg, W), dim3(256), E * sizeof(int32_t), stream, a);
+    } else {
+        a.nseg = 1;  // no slots: one empty segment so counts and splits come out zero
+        hipLaunchKernelGGL(k_moe_hist, dim3(1, W), dim3(256), E * sizeof(int32_t), stream, a);
+    }
+    hipLaunchKernelGGL(k_moe_scan, dim3(W), dim3(1024), 0, stream, a);
+    if (a.Q > 0)
+        hipLaunchKernelGGL(k_moe_rank, dim3(nseg_grid, W), dim3(kRankWaves * kWave),
+                           kRankWaves * E * sizeof(int32_t), stream, a);
+}
+
+static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
 }  // namespace a2av
 
 using namespace a2av;
@@ -443,18 +700,8 @@ A2AV_API int moe_pack(int W, int64_t T, int k, int E, size_t row_bytes,
     a.Q = T * k;
     a.E = E;
     a.W = W;
-    a.nseg = (int)n_segments(a.Q);
-    const int nseg_grid = a.nseg > 0 ? a.nseg : 1;
-    if (a.nseg > 0) {
-        hipLaunchKernelGGL(k_moe_hist, dim3(a.nseg, W), dim3(256), E * sizeof(int32_t), stream, a);
-    } else {
-        a.nseg = 1;  // no slots: one empty segment so counts and splits come out zero
-        hipLaunchKernelGGL(k_moe_hist, dim3(1, W), dim3(256), E * sizeof(int32_t), stream, a);
-    }
-    hipLaunchKernelGGL(k_moe_scan, dim3(W), dim3(1024), 0, stream, a);
+    launch_pack_sort(a, stream);
     if (a.Q > 0) {
-        hipLaunchKernelGGL(k_moe_rank, dim3(nseg_grid, W), dim3(kRankWaves * kWave),
-                           kRankWaves * E * sizeof(int32_t), stream, a);
         const uint64_t waves = (uint64_t)W * (uint64_t)T;
         uint64_t blocks = (waves + 3) / 4;
         if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
@@ -463,14 +710,168 @@ A2AV_API int moe_pack(int W, int64_t T, int k, int E, size_t row_bytes,
         const int mu = (int)env_long("A2AV_MOE_UNROLL", 16, 4, 16);
         const bool snt = env_long("A2AV_MOE_STORE_NT", 0, 0, 1) != 0;
 #define A2AV_SCATTER(UU, NT_) \
-    hipLaunchKernelGGL((k_moe_scatter<UU, true, NT_>), dim3((unsigned)blocks), dim3(256), 0, stream, a)
+    hipLaunchKernelGGL((k_moe_scatter<UU, true, NT_, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a)
         if (!aligned || k > kWave)
-            hipLaunchKernelGGL((k_moe_scatter<4, false, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((k_moe_scatter<4, false, true, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
         else if (mu <= 4) { if (snt) A2AV_SCATTER(4, true); else A2AV_SCATTER(4, false); }
         else if (mu <= 8) { if (snt) A2AV_SCATTER(8, true); else A2AV_SCATTER(8, false); }
         else { if (snt) A2AV_SCATTER(16, true); else A2AV_SCATTER(16, false); }
 #undef A2AV_SCATTER
     }
+    return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
+}
+
+A2AV_API size_t moe_pack_dispatch_workspace_bytes(int W, int64_t T, int k, int E) {
+    const size_t pack = moe_pack_workspace_bytes(W, T, k, E);
+    if (pack == 0) return 0;
+    return pack + round256((size_t)W * (size_t)E * 8) + 256;
+}
+
+A2AV_API int moe_pack_dispatch(int W, int64_t T, int k, int E, size_t row_bytes,
+                               const void *const *tokens, const int32_t *const *ids,
+                               void *const *recv, const int64_t *recv_cap_rows,
+                               int64_t *const *perm, int64_t *S, int64_t *expert_counts,
+                               int64_t *block_offsets, int layout, void *workspace,
+                               size_t workspace_bytes, int32_t *status, hipStream_t stream) {
+    if (!moe_sizes_ok(W, T, k, E) || k > kWave || row_bytes == 0 || !tokens || !ids || !recv ||
+        !recv_cap_rows || !perm || !S || !expert_counts || !block_offsets || !status ||
+        (layout != 0 && layout != 1))
+        return A2AV_EARG;
+    if (!workspace || workspace_bytes < moe_pack_dispatch_workspace_bytes(W, T, k, E))
+        return A2AV_EARG;
+    if ((uint64_t)T * (uint64_t)k > (uint64_t)INT64_MAX / row_bytes) return A2AV_EARG;
+    MoeArgs a;
+    ShiftArgs p;
+    std::memset(&a, 0, sizeof(a));
+    std::memset(&p, 0, sizeof(p));
+    bool aligned = (row_bytes % 16) == 0;
+    for (int r = 0; r < W; r++) {
+        if (T > 0 && (!tokens[r] || !ids[r] || !perm[r])) return A2AV_EARG;
+        const int64_t cap = recv_cap_rows[r];
+        if (cap < 0 || (uint64_t)cap > (uint64_t)INT64_MAX / row_bytes) return A2AV_EARG;
+        if (cap > 0 && !recv[r]) return A2AV_EARG;
+        a.tokens[r] = (const unsigned char *)tokens[r];
+        a.ids[r] = ids[r];
+        a.perm[r] = perm[r];
+        p.base[r] = (const unsigned char *)recv[r];
+        p.limit[r] = cap;
+        aligned = aligned && ((uintptr_t)tokens[r] % 16 == 0) && ((uintptr_t)recv[r] % 16 == 0);
+    }
+    unsigned char *ws = (unsigned char *)workspace;
+    const size_t pack_ws = moe_pack_workspace_bytes(W, T, k, E);
+    uint64_t *row_addr = (uint64_t *)(ws + pack_ws);
+    int32_t *words = (int32_t *)(ws + pack_ws + round256((size_t)W * (size_t)E * 8));
+    a.S = S;
+    a.expert_counts = expert_counts;
+    a.hist = (int32_t *)ws;
+    a.row_addr = row_addr;
+    a.plan_bits = words;
+    a.status = status;
+    a.R = row_bytes;
+    a.T = T;
+    a.k = k;
+    a.Q = T * k;
+    a.E = E;
+    a.W = W;
+    launch_pack_sort(a, stream);
+    p.counts = expert_counts;
+    p.row_addr = row_addr;
+    p.block_offsets = block_offsets;
+    p.words = words;
+    p.status = status;
+    p.R = row_bytes;
+    p.W = W;
+    p.E = E;
+    p.layout = layout;
+    p.over_bit = A2AV_ST_RECV_OVERFLOW;
+    hipLaunchKernelGGL(k_shift_plan, dim3(W), dim3(kPlanThreads), 0, stream, p);
+    if (a.Q > 0) {
+        uint64_t blocks = ((uint64_t)W * (uint64_t)T + 3) / 4;
+        if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
+        if (aligned)
+            hipLaunchKernelGGL((k_moe_scatter<16, true, false, true>), dim3((unsigned)blocks),
+                               dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_moe_scatter<4, false, false, true>), dim3((unsigned)blocks),
+                               dim3(256), 0, stream, a);
+    }
+    return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
+}
+
+A2AV_API size_t moe_unpack_return_workspace_bytes(int W, int E) {
+    if (W < 1 || W > A2AV_MAX_W || E < 1 || E > A2AV_MAX_EXPERTS || E % W != 0) return 0;
+    return 2 * round256((size_t)W * (size_t)E * 8) + 256;
+}
+
+A2AV_API int moe_unpack_return(int W, int64_t T, int k, int E, size_t row_bytes,
+                               const int64_t *expert_counts, const int32_t *const *ids,
+                               const int64_t *const *perm, const void *const *recv,
+                               const int64_t *recv_rows, void *const *out, int layout,
+                               void *workspace, size_t workspace_bytes, int32_t *status,
+                               hipStream_t stream) {
+    if (W < 1 || W > A2AV_MAX_W || E < 1 || E > A2AV_MAX_EXPERTS || E % W != 0 || T < 0 ||
+        k < 1 || row_bytes == 0 || !expert_counts || !ids || !perm || !recv || !recv_rows ||
+        !out || !status || (layout != 0 && layout != 1))
+        return A2AV_EARG;
+    if (!workspace || workspace_bytes < moe_unpack_return_workspace_bytes(W, E)) return A2AV_EARG;
+    if (T > ((int64_t)1 << 31) / k || (uint64_t)T * (uint64_t)k > (uint64_t)INT64_MAX / row_bytes)
+        return A2AV_EARG;
+    ShiftArgs p;
+    ReturnArgs c;
+    std::memset(&p, 0, sizeof(p));
+    std::memset(&c, 0, sizeof(c));
+    bool aligned = (row_bytes % 16) == 0;
+    for (int r = 0; r < W; r++) {
+        if (T > 0 && (!ids[r] || !perm[r] || !out[r])) return A2AV_EARG;
+        const int64_t rows = recv_rows[r];
+        if (rows < 0 || (uint64_t)rows > (uint64_t)INT64_MAX / row_bytes) return A2AV_EARG;
+        if (rows > 0 && !recv[r]) return A2AV_EARG;
+        p.base[r] = (const unsigned char *)recv[r];
+        p.limit[r] = rows;
+        c.out[r] = (unsigned char *)out[r];
+        c.ids[r] = ids[r];
+        c.perm[r] = perm[r];
+        aligned = aligned && ((uintptr_t)recv[r] % 16 == 0) && ((uintptr_t)out[r] % 16 == 0);
+    }
+    unsigned char *ws = (unsigned char *)workspace;
+    const size_t table = round256((size_t)W * (size_t)E * 8);
+    uint64_t *row_addr = (uint64_t *)ws;
+    int64_t *ystart = (int64_t *)(ws + table);
+    int32_t *words = (int32_t *)(ws + 2 * table);
+    p.counts = expert_counts;
+    p.row_addr = row_addr;
+    p.ystart = ystart;
+    p.words = words;
+    p.status = status;
+    p.R = row_bytes;
+    p.W = W;
+    p.E = E;
+    p.layout = layout;
+    p.over_bit = A2AV_ST_SEND_OVERRUN;
+    p.check_counts = 1;
+    c.counts = expert_counts;
+    c.row_addr = row_addr;
+    c.ystart = ystart;
+    c.words = words;
+    c.status = status;
+    c.R = row_bytes;
+    c.Q = T * k;
+    c.E = E;
+    c.W = W;
+    hipLaunchKernelGGL(k_shift_plan, dim3(W), dim3(kPlanThreads), 0, stream, p);
+    if (c.Q > 0)
+        hipLaunchKernelGGL(k_slot_check, dim3((unsigned)((c.Q + 255) / 256), W), dim3(256), 0,
+                           stream, c);
+    // at least one wave, so that a verdict of the plan is reported
+    uint64_t blocks = ((uint64_t)W * (uint64_t)c.Q + 3) / 4;
+    if (blocks < 1) blocks = 1;
+    if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
+    if (aligned)
+        hipLaunchKernelGGL((k_moe_gather_home<16, true>), dim3((unsigned)blocks), dim3(256), 0,
+                           stream, c);
+    else
+        hipLaunchKernelGGL((k_moe_gather_home<8, false>), dim3((unsigned)blocks), dim3(256), 0,
+                           stream, c);
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
 }
 

@@ -197,6 +197,82 @@ int moe_pack(int W, int64_t T, int k, int E, size_t row_bytes,
              int32_t *status, hipStream_t stream);
 
 /*
+ * Workspace bytes moe_pack_dispatch needs (0 for invalid sizes).
+ */
+size_t moe_pack_dispatch_workspace_bytes(int W, int64_t T, int k, int E);
+
+/*
+ * moe_pack and the dispatch a2av of its rows as one step, for all W ranks:
+ * the MoE region on the page "[a2av] Improve tuning for 4 GPUs" (section
+ * "Change") packs tokens by destination rank and expert and then exchanges
+ * them; here every slot's token row is written once, straight into the
+ * receive buffer of its expert's owner (rank e / (E/W)), and no send buffer
+ * exists. Owner d's rows come in one of two orders:
+ *   layout 0  (source, expert, token, slot): what moe_pack followed by
+ *             a2av_all_to_all_vdev with its splits delivers
+ *   layout 1  (expert, source, token, slot): what moe_pack followed by
+ *             moe_dispatch_grouped (direction 0) delivers
+ *   tokens[W], ids[W]   as moe_pack (k <= 64)
+ *   recv[W]             device [recv_cap_rows[d]][row_bytes] per owner (host
+ *                       recv_cap_rows); rows past the owner's total untouched
+ *   perm[W], S, expert_counts   written as moe_pack writes them (perm = each
+ *                       slot's row in the pack order, which the inverse and
+ *                       moe_combine_grouped read)
+ *   block_offsets       device int64 [W][G+1], written: rows before block g at
+ *                       owner d, total at G; blocks are sources (G = W, the
+ *                       a2av's receive offsets) for layout 0 and owned experts
+ *                       (G = E/W, moe_dispatch_grouped's expert_offsets) for
+ *                       layout 1
+ *   workspace           device scratch of >= moe_pack_dispatch_workspace_bytes()
+ *   status              A2AV_ST_BAD_EXPERT for an id outside [0, E): nothing
+ *                       but the workspace is written; A2AV_ST_RECV_OVERFLOW
+ *                       when an owner's rows exceed recv_cap_rows: perm, S,
+ *                       expert_counts and block_offsets are written (so the
+ *                       caller can size the buffers), no payload byte.
+ * Five kernels: the three of moe_pack's counting sort, a plan (one workgroup
+ * per source; for every (source, expert) the shift from a slot's pack row to
+ * its row at the owner) and moe_pack's token-major row scatter with those
+ * destinations.
+ */
+int moe_pack_dispatch(int W, int64_t T, int k, int E, size_t row_bytes,
+                      const void *const *tokens, const int32_t *const *ids,
+                      void *const *recv, const int64_t *recv_cap_rows, int64_t *const *perm,
+                      int64_t *S, int64_t *expert_counts, int64_t *block_offsets, int layout,
+                      void *workspace, size_t workspace_bytes, int32_t *status,
+                      hipStream_t stream);
+
+/*
+ * Workspace bytes moe_unpack_return needs (0 for invalid sizes).
+ */
+size_t moe_unpack_return_workspace_bytes(int W, int E);
+
+/*
+ * The inverse of moe_pack_dispatch: the return trip and the un-pack as one
+ * step, out[s][q] = the row of slot q of source s, read from the receive
+ * buffer of its owner in the given layout. Equal to the return a2av (splits
+ * O) followed by moe_unpack for layout 0, and to moe_dispatch_grouped
+ * (direction 1) followed by moe_unpack for layout 1, without the returned
+ * buffer.
+ *   expert_counts    device int64 [W][E] (moe_pack's)
+ *   ids[W], perm[W]  device int32 / int64 [T*k] per source
+ *   recv[W]          device [recv_rows[d]][row_bytes] per owner (host recv_rows)
+ *   out[W]           device [T*k][row_bytes] per source
+ *   workspace        device scratch of >= moe_unpack_return_workspace_bytes()
+ *   status           A2AV_ST_BAD_SPLIT (a count outside [0, 2^40]); else the
+ *                    OR of A2AV_ST_SEND_OVERRUN (an owner's rows exceed
+ *                    recv_rows), A2AV_ST_BAD_EXPERT and A2AV_ST_BAD_PERM (a
+ *                    perm entry outside its expert's block of the pack order).
+ *                    Nothing is written on failure.
+ * Three kernels: the plan of moe_pack_dispatch, a check of every slot, and a
+ * row gather (one wave per slot row, as moe_unpack).
+ */
+int moe_unpack_return(int W, int64_t T, int k, int E, size_t row_bytes,
+                      const int64_t *expert_counts, const int32_t *const *ids,
+                      const int64_t *const *perm, const void *const *recv,
+                      const int64_t *recv_rows, void *const *out, int layout, void *workspace,
+                      size_t workspace_bytes, int32_t *status, hipStream_t stream);
+
+/*
  * MoE un-pack after the return trip ("inverse combine" without weights):
  * out[r][q] = back[r][perm[r][q]] for q < T*k, i.e. every slot gets back the
  * row it was packed to. back is what the return a2av (splits O, the

@@ -31,7 +31,9 @@ def test_header_declares_the_boundary():
                  "moe_combine", "moe_regroup", "moe_regroup_workspace_bytes", "keys_bucketize",
                  "keys_bucketize_workspace_bytes", "keys_exchange", "keys_exchange_workspace_bytes",
                  "moe_dispatch_grouped", "moe_dispatch_grouped_workspace_bytes",
-                 "moe_combine_grouped", "moe_combine_grouped_workspace_bytes"):
+                 "moe_combine_grouped", "moe_combine_grouped_workspace_bytes",
+                 "moe_pack_dispatch", "moe_pack_dispatch_workspace_bytes", "moe_unpack_return",
+                 "moe_unpack_return_workspace_bytes"):
         assert must in names
 
 
@@ -125,6 +127,30 @@ def test_host_argument_errors(L):
                                  wsc - 1, vp(8), None) == EARG
     assert L.moe_combine_grouped(2, 10, 2, 8, 0, vp(8), ptrs, ptrs, ptrs, two, ptrs, ptrs, vp(8),
                                  wsc, vp(8), None) == EARG
+    # pack + dispatch: bad layout, k above 64, small workspace, negative capacity
+    wsp = L.moe_pack_dispatch_workspace_bytes(2, 10, 2, 8)
+    assert wsp > L.moe_pack_workspace_bytes(2, 10, 2, 8)
+    assert L.moe_pack_dispatch_workspace_bytes(3, 10, 2, 8) == 0
+    assert L.moe_pack_dispatch(2, 10, 2, 8, 16, ptrs, ptrs, ptrs, two, ptrs, vp(8), vp(8), vp(8),
+                               2, vp(8), wsp, vp(8), None) == EARG
+    assert L.moe_pack_dispatch(2, 10, 65, 8, 16, ptrs, ptrs, ptrs, two, ptrs, vp(8), vp(8), vp(8),
+                               0, vp(8), L.moe_pack_dispatch_workspace_bytes(2, 10, 65, 8),
+                               vp(8), None) == EARG
+    assert L.moe_pack_dispatch(2, 10, 2, 8, 16, ptrs, ptrs, ptrs, two, ptrs, vp(8), vp(8), vp(8),
+                               0, vp(8), wsp - 1, vp(8), None) == EARG
+    assert L.moe_pack_dispatch(2, 10, 2, 8, 16, ptrs, ptrs, ptrs, negr, ptrs, vp(8), vp(8), vp(8),
+                               0, vp(8), wsp, vp(8), None) == EARG
+    # its inverse: bad layout, small workspace, negative receive rows, E % W
+    wsu = L.moe_unpack_return_workspace_bytes(2, 8)
+    assert wsu > 0 and L.moe_unpack_return_workspace_bytes(3, 8) == 0
+    assert L.moe_unpack_return(2, 10, 2, 8, 16, vp(8), ptrs, ptrs, ptrs, two, ptrs, 5, vp(8), wsu,
+                               vp(8), None) == EARG
+    assert L.moe_unpack_return(2, 10, 2, 8, 16, vp(8), ptrs, ptrs, ptrs, two, ptrs, 1, vp(8),
+                               wsu - 1, vp(8), None) == EARG
+    assert L.moe_unpack_return(2, 10, 2, 8, 16, vp(8), ptrs, ptrs, ptrs, negr, ptrs, 0, vp(8), wsu,
+                               vp(8), None) == EARG
+    assert L.moe_unpack_return(3, 10, 2, 8, 16, vp(8), ptrs, ptrs, ptrs, two, ptrs, 0, vp(8), wsu,
+                               vp(8), None) == EARG
     # fused exchange: small workspace, negative capacity, too many tables
     wsx = L.keys_exchange_workspace_bytes(2, 26)
     assert wsx > 0 and L.keys_exchange_workspace_bytes(2, 4097) == 0
