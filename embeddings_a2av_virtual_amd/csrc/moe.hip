@@ -180,15 +180,18 @@ __global__ __launch_bounds__(256) void k_moe_rank(const MoeArgs a) {
 }
 
 // ------------------------------------------------------------------ scatter
-// One wave per (rank, token): the token row is read once into registers (up
-// to 64 x 16 x U bytes per pass) and stored to the k rows of its slots. Lane
-// j < k holds the address of slot j's row: send[r] + perm * R for the pack,
-// or the owner's receive row row_addr[r][e] + perm * R when the pack and the
-// dispatch run as one step (DIRECT). Rows or bases that are not 16-byte
-// aligned take k realigning wave copies of the row instead (the re-reads hit
-// in L2).
-template <int U, bool ALIGNED, bool SNT, bool DIRECT>
-__global__ __launch_bounds__(256) void k_moe_scatter(const MoeArgs a) {
+// One wave per (rank, token, chunk of 64 x U vectors): the chunk of the token
+// row is read once into registers and stored to the k rows of its slots. The
+// host picks the chunk count and U (1..8) so that the chunks tile the row
+// with as few idle lanes as it can (a 14 KiB row: two chunks of 7 vectors per
+// lane); short waves with few registers keep more stores in flight per CU
+// than one wave per row did. Lane j < k holds the address of slot j's row:
+// send[r] + perm * R for the pack, or the owner's receive row
+// row_addr[r][e] + perm * R when the pack and the dispatch run as one step
+// (DIRECT). Rows or bases that are not 16-byte aligned take one wave per
+// token and k realigning wave copies of the row (the re-reads hit in L2).
+template <int U, bool ALIGNED, bool DIRECT>
+__global__ __launch_bounds__(256) void k_moe_scatter(const MoeArgs a, uint64_t nch) {
     if (status_poisoned(a.status)) return;
     if constexpr (DIRECT) {
         // a receiver too small: report once; no wave writes a row
@@ -200,12 +203,14 @@ __global__ __launch_bounds__(256) void k_moe_scatter(const MoeArgs a) {
     }
     const int lane = threadIdx.x & (kWave - 1);
     const uint64_t wpb = blockDim.x / kWave;
-    const uint64_t nwork = (uint64_t)a.W * (uint64_t)a.T;
+    const uint64_t nwork = (uint64_t)a.W * (uint64_t)a.T * nch;
     const uint64_t R = a.R;
-    for (uint64_t w = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave; w < nwork;
-         w += (uint64_t)gridDim.x * wpb) {
-        const int r = (int)(w / (uint64_t)a.T);
-        const int64_t t = (int64_t)(w - (uint64_t)r * (uint64_t)a.T);
+    const uint32_t wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    for (uint64_t w = (uint64_t)blockIdx.x * wpb + wid; w < nwork; w += (uint64_t)gridDim.x * wpb) {
+        const uint64_t tok = w / nch;
+        const uint64_t c = w - tok * nch;
+        const int r = (int)(tok / (uint64_t)a.T);
+        const int64_t t = (int64_t)(tok - (uint64_t)r * (uint64_t)a.T);
         const unsigned char *src = a.tokens[r] + (uint64_t)t * R;
         // the token's k rows, one address per lane, fetched before any store
         // (k <= 64 here; the host routes larger k to the pack's unaligned form)
@@ -226,23 +231,22 @@ __global__ __launch_bounds__(256) void k_moe_scatter(const MoeArgs a) {
         if constexpr (ALIGNED) {
             const uint64_t nv = R / 16;
             const u32x4 *s16 = (const u32x4 *)src;
+            const uint64_t base = c * (uint64_t)kWave * U;
             // indices past the row end are clamped to its last vector (no
             // per-lane branch; the clamped lanes store identical bytes)
-            for (uint64_t base = 0; base < nv; base += (uint64_t)kWave * U) {
-                u32x4 v[U];
-                uint64_t idx[U];
+            u32x4 v[U];
+            uint64_t idx[U];
 #pragma unroll
-                for (int u = 0; u < U; u++) {
-                    const uint64_t i = base + (uint64_t)u * kWave + lane;
-                    idx[u] = i < nv ? i : nv - 1;
-                    v[u] = ld<true>(s16 + idx[u]);
-                }
-                for (int j = 0; j < a.k; j++) {
-                    if (!((okm >> j) & 1)) continue;
-                    u32x4 *d16 = (u32x4 *)(uintptr_t)readlane_u64(al, j);
+            for (int u = 0; u < U; u++) {
+                const uint64_t i = base + (uint64_t)u * kWave + lane;
+                idx[u] = i < nv ? i : nv - 1;
+                v[u] = ld<true>(s16 + idx[u]);
+            }
+            for (int j = 0; j < a.k; j++) {
+                if (!((okm >> j) & 1)) continue;
+                u32x4 *d16 = (u32x4 *)(uintptr_t)readlane_u64(al, j);
 #pragma unroll
-                    for (int u = 0; u < U; u++) st<SNT>(d16 + idx[u], v[u]);
-                }
+                for (int u = 0; u < U; u++) st<false>(d16 + idx[u], v[u]);
             }
         } else if constexpr (DIRECT) {
             for (int j = 0; j < a.k; j++) {
@@ -659,6 +663,36 @@ static void launch_pack_sort(MoeArgs &a, hipStream_t stream) {
 
 static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// The row scatter: chunks of at most 512 vectors (8 per lane), as few as
+// tile the row, and U = the vectors per lane that cover one chunk.
+template <bool DIRECT>
+static void launch_scatter(const MoeArgs &a, bool aligned, hipStream_t stream) {
+    const uint64_t ntok = (uint64_t)a.W * (uint64_t)a.T;
+    if (!aligned || a.k > kWave) {
+        uint64_t blocks = (ntok + 3) / 4;
+        if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
+        hipLaunchKernelGGL((k_moe_scatter<4, false, DIRECT>), dim3((unsigned)blocks), dim3(256), 0,
+                           stream, a, (uint64_t)1);
+        return;
+    }
+    const uint64_t nv = a.R / 16;
+    const uint64_t nch = (nv + 8 * kWave - 1) / (8 * kWave);
+    const int U = (int)((nv + nch * kWave - 1) / (nch * kWave));
+    uint64_t blocks = (ntok * nch + 3) / 4;
+    if (blocks > (1u << 22)) blocks = 1u << 22;
+    const dim3 g((unsigned)blocks), b(256);
+    switch (U) {
+    case 1: hipLaunchKernelGGL((k_moe_scatter<1, true, DIRECT>), g, b, 0, stream, a, nch); break;
+    case 2: hipLaunchKernelGGL((k_moe_scatter<2, true, DIRECT>), g, b, 0, stream, a, nch); break;
+    case 3: hipLaunchKernelGGL((k_moe_scatter<3, true, DIRECT>), g, b, 0, stream, a, nch); break;
+    case 4: hipLaunchKernelGGL((k_moe_scatter<4, true, DIRECT>), g, b, 0, stream, a, nch); break;
+    case 5: hipLaunchKernelGGL((k_moe_scatter<5, true, DIRECT>), g, b, 0, stream, a, nch); break;
+    case 6: hipLaunchKernelGGL((k_moe_scatter<6, true, DIRECT>), g, b, 0, stream, a, nch); break;
+    case 7: hipLaunchKernelGGL((k_moe_scatter<7, true, DIRECT>), g, b, 0, stream, a, nch); break;
+    default: hipLaunchKernelGGL((k_moe_scatter<8, true, DIRECT>), g, b, 0, stream, a, nch); break;
+    }
+}
+
 }  // namespace a2av
 
 using namespace a2av;
@@ -701,23 +735,7 @@ A2AV_API int moe_pack(int W, int64_t T, int k, int E, size_t row_bytes,
     a.E = E;
     a.W = W;
     launch_pack_sort(a, stream);
-    if (a.Q > 0) {
-        const uint64_t waves = (uint64_t)W * (uint64_t)T;
-        uint64_t blocks = (waves + 3) / 4;
-        if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
-        // tuning knobs: A2AV_MOE_UNROLL (vectors per lane per pass, 4/8/16) and
-        // A2AV_MOE_STORE_NT (non-temporal stores, 0/1)
-        const int mu = (int)env_long("A2AV_MOE_UNROLL", 16, 4, 16);
-        const bool snt = env_long("A2AV_MOE_STORE_NT", 0, 0, 1) != 0;
-#define A2AV_SCATTER(UU, NT_) \
-    hipLaunchKernelGGL((k_moe_scatter<UU, true, NT_, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a)
-        if (!aligned || k > kWave)
-            hipLaunchKernelGGL((k_moe_scatter<4, false, true, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-        else if (mu <= 4) { if (snt) A2AV_SCATTER(4, true); else A2AV_SCATTER(4, false); }
-        else if (mu <= 8) { if (snt) A2AV_SCATTER(8, true); else A2AV_SCATTER(8, false); }
-        else { if (snt) A2AV_SCATTER(16, true); else A2AV_SCATTER(16, false); }
-#undef A2AV_SCATTER
-    }
+    if (a.Q > 0) launch_scatter<false>(a, aligned, stream);
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
 }
 
@@ -785,16 +803,7 @@ A2AV_API int moe_pack_dispatch(int W, int64_t T, int k, int E, size_t row_bytes,
     p.layout = layout;
     p.over_bit = A2AV_ST_RECV_OVERFLOW;
     hipLaunchKernelGGL(k_shift_plan, dim3(W), dim3(kPlanThreads), 0, stream, p);
-    if (a.Q > 0) {
-        uint64_t blocks = ((uint64_t)W * (uint64_t)T + 3) / 4;
-        if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
-        if (aligned)
-            hipLaunchKernelGGL((k_moe_scatter<16, true, false, true>), dim3((unsigned)blocks),
-                               dim3(256), 0, stream, a);
-        else
-            hipLaunchKernelGGL((k_moe_scatter<4, false, false, true>), dim3((unsigned)blocks),
-                               dim3(256), 0, stream, a);
-    }
+    if (a.Q > 0) launch_scatter<true>(a, aligned, stream);
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
 }
 

@@ -187,8 +187,8 @@ size_t moe_pack_workspace_bytes(int W, int64_t T, int k, int E);
  *                 the workspace is written.
  * Four kernels: an LDS histogram per slot segment, an expert-major scan of the
  * histograms, a stable in-segment rank (wave ballots), and a token-major row
- * scatter (one wave per token) that reads each token once and writes it k
- * times. Tuning: A2AV_MOE_UNROLL, A2AV_MOE_STORE_NT.
+ * scatter that reads each token once and writes it k times (one wave per
+ * token and chunk of at most 8 KiB; the chunks tile the row).
  */
 int moe_pack(int W, int64_t T, int k, int E, size_t row_bytes,
              const void *const *tokens, const int32_t *const *ids,

@@ -216,12 +216,14 @@ def test_moe_dispatch_full_size(ref):
         assert torch.equal(out[r].view(T, k, R), want), f"round trip rank {r}"
 
 
-@pytest.mark.parametrize("env", [
-    {"A2AV_MOE_UNROLL": "4"}, {"A2AV_MOE_UNROLL": "8", "A2AV_MOE_STORE_NT": "1"},
-    {"A2AV_MOE_GATHER_UNROLL": "4"}, {"A2AV_MOE_GATHER_UNROLL": "8"},
+@pytest.mark.parametrize("env,R", [
+    # the scatter's vectors per lane follow the row width: 1, 2, 3, 4, 5 (two
+    # chunks), 6, 7 (two chunks), 8
+    ({}, 16), ({}, 1040), ({}, 2064), ({}, 3088), ({}, 8208), ({}, 6144), ({}, 14336), ({}, 8192),
+    ({"A2AV_MOE_GATHER_UNROLL": "4"}, 1040), ({"A2AV_MOE_GATHER_UNROLL": "8"}, 1040),
 ])
-def test_moe_launch_shapes_give_identical_bytes(ref, monkeypatch, env):
-    W, T, k, E, R = 4, 300, 4, 16, 1040
+def test_moe_launch_shapes_give_identical_bytes(ref, monkeypatch, env, R):
+    W, T, k, E = 4, 300, 4, 16
     g = I.rng(31)
     tokens, ids = _moe_inputs(g, W, T, k, E, R, "zipf")
     for key, val in env.items():
