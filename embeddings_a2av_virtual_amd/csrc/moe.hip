@@ -89,8 +89,20 @@ __global__ __launch_bounds__(1024) void k_moe_scan(const MoeArgs a) {
     const int64_t per = (N + nthr - 1) / nthr;
     const int64_t b0 = (int64_t)threadIdx.x * per;
     const int64_t b1 = b0 + per < N ? b0 + per : N;
+    // a run of up to kScanRegs counters is read once into registers, all
+    // loads in flight together; longer runs are walked twice
+    constexpr int kScanRegs = 32;
+    const bool in_regs = per <= kScanRegs;
+    int32_t vals[kScanRegs];
     int32_t sum = 0;
-    for (int64_t i = b0; i < b1; i++) sum += H[i];
+    if (in_regs) {
+#pragma unroll
+        for (int u = 0; u < kScanRegs; u++) vals[u] = b0 + u < b1 ? H[b0 + u] : 0;
+#pragma unroll
+        for (int u = 0; u < kScanRegs; u++) sum += vals[u];
+    } else {
+        for (int64_t i = b0; i < b1; i++) sum += H[i];
+    }
     // block exclusive scan of `sum`
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int32_t incl = wave_incl_scan32(sum);
@@ -104,10 +116,18 @@ __global__ __launch_bounds__(1024) void k_moe_scan(const MoeArgs a) {
     }
     __syncthreads();
     int32_t run = wave_tot[wave] + incl - sum;
-    for (int64_t i = b0; i < b1; i++) {
-        const int32_t c = H[i];
-        H[i] = run;
-        run += c;
+    if (in_regs) {
+#pragma unroll
+        for (int u = 0; u < kScanRegs; u++) {
+            if (b0 + u < b1) H[b0 + u] = run;
+            run += vals[u];
+        }
+    } else {
+        for (int64_t i = b0; i < b1; i++) {
+            const int32_t c = H[i];
+            H[i] = run;
+            run += c;
+        }
     }
     __syncthreads();
     // base of expert e = H[e][0]; the count is the gap to the next base

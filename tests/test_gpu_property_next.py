@@ -1,7 +1,8 @@
-"""Property-based GPU parity of the expert regroup, the weighted combine and
-the fused key exchange: random rank counts, expert counts, row widths, base
-offsets, slot counts and table layouts, each compared bit-exactly with the CPU
-oracle. Derandomized, so every run draws the same examples."""
+"""Property-based GPU parity of the expert regroup, the weighted combine, the
+fused key exchange and the one-step MoE pack + dispatch with its inverse:
+random rank counts, expert counts, row widths, base offsets, slot counts,
+routings and table layouts, each compared bit-exactly with the CPU oracle.
+Derandomized, so every run draws the same examples."""
 import numpy as np
 import pytest
 from hypothesis import HealthCheck, given, settings
@@ -9,6 +10,7 @@ from hypothesis import strategies as st
 
 from test_gpu_combine import gpu_combine
 from test_gpu_keys import _compare_exchange, gpu_keys_exchange
+from test_gpu_pack_dispatch import gpu_pack_dispatch, gpu_unpack_return
 from test_gpu_regroup import _owned_total, gpu_regroup, ref_regroup
 from gpu_util import SENT
 
@@ -104,3 +106,51 @@ def test_random_keys_exchange_matches_oracle(ref, case):
     assert want[0] == 0
     got = gpu_keys_exchange(W, NT, batch, lengths, keys, pad=pad, ref=ref)
     _compare_exchange(got, want, f"W={W} NT={NT} batch={batch}")
+
+
+@st.composite
+def pack_dispatch_cases(draw):
+    W = draw(st.integers(1, 12))
+    P = draw(st.integers(1, 24))
+    T = draw(st.integers(0, 60))
+    k = draw(st.sampled_from([1, 2, 3, 8, 13, 64]))
+    R = draw(st.sampled_from([1, 4, 16, 48, 100, 1040, 2064, 8208]))
+    seed = draw(st.integers(0, 2 ** 31 - 1))
+    skew = draw(st.sampled_from([0.0, 1.1, 3.0]))
+    pad = draw(st.integers(0, 15))
+    layout = draw(st.integers(0, 1))
+    return W, T, k, W * P, R, seed, skew, pad, layout
+
+
+@settings(**SETTINGS)
+@given(pack_dispatch_cases())
+def test_random_pack_dispatch_matches_oracle(ref, case):
+    W, T, k, E, R, seed, skew, pad, layout = case
+    g = np.random.default_rng(seed)
+    if skew > 0:   # ids from a Zipf-like law, repeats within a token allowed
+        p = 1.0 / np.arange(1, E + 1) ** skew
+        ids = [g.choice(E, size=T * k, p=p / p.sum()).astype(np.int32) for _ in range(W)]
+    else:
+        ids = [g.integers(0, E, size=T * k).astype(np.int32) for _ in range(W)]
+    toks = [g.integers(0, 256, size=(T, R), dtype=np.uint8) for _ in range(W)]
+    tot = np.zeros(W, dtype=np.int64)
+    for x in ids:
+        tot += np.bincount(x.astype(np.int64) // (E // W), minlength=W)[:W]
+    cap = tot + g.integers(0, 3, size=W)
+    gst, recv, perm, S, cnt, boff, guards = gpu_pack_dispatch(W, T, k, E, R, toks, ids, cap,
+                                                               layout, pad=pad)
+    rst, rrecv, rperm, rS, rcnt, rboff = ref.moe_pack_dispatch(W, T, k, E, R, toks, ids, cap,
+                                                               layout)
+    assert guards and gst == rst == 0
+    assert np.array_equal(S, rS) and np.array_equal(cnt, rcnt) and np.array_equal(boff, rboff)
+    for s in range(W):
+        assert np.array_equal(perm[s], rperm[s]), s
+    for d in range(W):
+        t = int(tot[d])
+        assert np.array_equal(recv[d][:t], rrecv[d].reshape(-1, R)[:t]), d
+        assert (recv[d][t:] == SENT).all()
+    rows = [recv[d][:int(tot[d])] for d in range(W)]
+    gst, out, guards = gpu_unpack_return(W, T, k, E, R, cnt, ids, perm, rows, layout, pad=pad)
+    assert guards and gst == 0
+    for s in range(W):
+        assert np.array_equal(out[s], np.repeat(toks[s], k, axis=0)), s
