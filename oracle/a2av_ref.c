@@ -739,3 +739,37 @@ int ref_moe_unpack_return(int W, int64_t T, int k, int E, size_t R, const int64_
     free(Z);
     return 0;
 }
+
+/*
+ * The gate-weighted combine read at the owners: ref_moe_unpack_return (the
+ * return trip in one step, either layout) followed by ref_moe_combine over
+ * the rows it brings home, slot q = t*k + j of token t being row q there.
+ * Written as that composition; its status is the inverse's, and nothing is
+ * written when it fails.
+ */
+int ref_moe_combine_return(int W, int64_t T, int k, int E, int64_t H, const int64_t *counts,
+                           const int32_t *const *ids, const int64_t *const *perm,
+                           const uint16_t *const *recv, const int64_t *recv_rows,
+                           const float *const *w, uint16_t *const *out, int layout) {
+    if (W < 1 || W > REF_MAX_W || T < 0 || k < 1 || H < 1 || !w || !out) return REF_EARG;
+    if (T > INT64_MAX / k) return REF_EARG;
+    const int64_t Q = T * k;
+    void **home = calloc((size_t)W, sizeof(void *));
+    int64_t *ident = malloc(sizeof(int64_t) * (size_t)(Q > 0 ? Q : 1));
+    if (!home || !ident) { free(home); free(ident); return REF_EARG; }
+    int st = 0;
+    for (int s = 0; s < W && !st; s++) {
+        home[s] = malloc((size_t)(Q > 0 ? Q : 1) * (size_t)H * 2);
+        if (!home[s]) st = REF_EARG;
+    }
+    if (!st)
+        st = ref_moe_unpack_return(W, T, k, E, (size_t)H * 2, counts, ids, perm,
+                                   (const void *const *)recv, recv_rows, home, layout);
+    for (int64_t q = 0; q < Q; q++) ident[q] = q;
+    for (int s = 0; s < W && !st; s++)
+        st = ref_moe_combine(T, k, H, (const uint16_t *)home[s], ident, w[s], out[s]);
+    for (int s = 0; s < W; s++) free(home[s]);
+    free(home);
+    free(ident);
+    return st;
+}

@@ -179,6 +179,16 @@ int ref_moe_unpack_return(int W, int64_t T, int k, int E, size_t R, const int64_
                           const void *const *recv, const int64_t *recv_rows, void *const *out,
                           int layout);
 
+/* The gate-weighted combine read at the owners, for all W ranks:
+ * ref_moe_unpack_return (layout 0 or 1) followed by ref_moe_combine over the
+ * rows it brings home (slot t*k + j of token t). recv[d] holds recv_rows[d]
+ * bf16 rows of H; w[s] is [T][k] fp32; out[s] is [T][H] bf16. Status and
+ * what is written on failure: those of ref_moe_unpack_return. */
+int ref_moe_combine_return(int W, int64_t T, int k, int E, int64_t H, const int64_t *counts,
+                           const int32_t *const *ids, const int64_t *const *perm,
+                           const uint16_t *const *recv, const int64_t *recv_rows,
+                           const float *const *w, uint16_t *const *out, int layout);
+
 /* The whole key exchange of one batch for all W ranks: ref_keys_bucketize on
  * every source, then keys (8-byte rows) and lengths (4-byte rows) as two
  * ref_a2av calls with the bucketing's split rows. lengths_cap / keys_cap are

@@ -72,12 +72,16 @@ def _bind(lib):
                                           ctypes.c_int]
     lib.ref_moe_unpack_return.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                           sz, i64p, vpp, vpp, vpp, i64p, vpp, ctypes.c_int]
+    lib.ref_moe_combine_return.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int64, i64p, vpp, vpp, vpp, i64p,
+                                           vpp, vpp, ctypes.c_int]
     lib.ref_keys_exchange.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, vpp, vpp, i64p,
                                       vpp, i64p, vpp, i64p, i64p, i64p, i64p]
     for name in ("ref_exchange_splits", "ref_offsets", "ref_copy", "ref_a2av", "ref_source_of",
                  "ref_moe_pack", "ref_moe_unpack", "ref_moe_regroup", "ref_moe_combine",
                  "ref_keys_bucketize", "ref_keys_exchange", "ref_moe_dispatch_grouped",
-                 "ref_moe_combine_grouped", "ref_moe_pack_dispatch", "ref_moe_unpack_return"):
+                 "ref_moe_combine_grouped", "ref_moe_pack_dispatch", "ref_moe_unpack_return",
+                 "ref_moe_combine_return"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -295,6 +299,21 @@ class Oracle:
         outs = [np.zeros(T * k * R, dtype=np.uint8) for _ in range(W)]
         st = self.lib.ref_moe_unpack_return(W, T, k, E, R, _i64(counts), _ptrs(ids), _ptrs(perms),
                                             _ptrs(rv), _i64(rows), _ptrs(outs), layout)
+        return st, outs
+
+    def moe_combine_return(self, W, T, k, E, H, counts, ids, perms, recv, weights, layout=0):
+        """All W ranks. recv: per-owner uint16 [rows, H] in the layout's order;
+        weights: float32 [T, k]. Returns (status, [out uint16 [T, H]],
+        zero-filled where not written)."""
+        counts = np.ascontiguousarray(counts, dtype=np.int64)
+        ids = [np.ascontiguousarray(i, dtype=np.int32).reshape(-1) for i in ids]
+        perms = [np.ascontiguousarray(p, dtype=np.int64).reshape(-1) for p in perms]
+        xs = [np.ascontiguousarray(x, dtype=np.uint16).reshape(-1) for x in recv]
+        rows = np.array([x.size // H for x in xs], dtype=np.int64)
+        ws = [np.ascontiguousarray(x, dtype=np.float32).reshape(-1) for x in weights]
+        outs = [np.zeros((T, H), dtype=np.uint16) for _ in range(W)]
+        st = self.lib.ref_moe_combine_return(W, T, k, E, H, _i64(counts), _ptrs(ids), _ptrs(perms),
+                                             _ptrs(xs), _i64(rows), _ptrs(ws), _ptrs(outs), layout)
         return st, outs
 
     def moe_combine_grouped(self, W, T, k, E, H, counts, ids, perms, expert_side, weights):

@@ -275,6 +275,21 @@ static void one_pack_dispatch(int W, int64_t T, int k, int E, size_t R, int layo
     CHECK(ref_moe_unpack_return(W, T, k, E, R, counts, (const int32_t *const *)ids,
                                 (const int64_t *const *)perm, (const void *const *)recv, rows, out,
                                 layout) == 0);
+    if (R % 2 == 0) {  /* the same rows as bf16: the weighted combine at the owners */
+        const int64_t H = (int64_t)R / 2;
+        float **w = malloc(sizeof(void *) * W);
+        uint16_t **cout = malloc(sizeof(void *) * W);
+        for (int s = 0; s < W; s++) {
+            w[s] = malloc(sizeof(float) * (Q + 1));
+            for (int64_t q = 0; q < Q; q++) w[s][q] = 0.25f;
+            cout[s] = malloc(sizeof(uint16_t) * (T * H + 1));
+        }
+        CHECK(ref_moe_combine_return(W, T, k, E, H, counts, (const int32_t *const *)ids,
+                                     (const int64_t *const *)perm, (const uint16_t *const *)recv,
+                                     rows, (const float *const *)w, cout, layout) == 0);
+        for (int s = 0; s < W; s++) { free(w[s]); free(cout[s]); }
+        free(w); free(cout);
+    }
     for (int s = 0; s < W; s++)
         for (int64_t q = 0; q < Q; q++)
             CHECK(memcmp((unsigned char *)out[s] + q * R, (unsigned char *)tok[s] + (q / k) * R, R) == 0);

@@ -750,6 +750,86 @@ def pin_moe_pack_dispatch(o):
         assert st == R.BAD_SPLIT and not any(x.any() for x in out)
 
 
+def pin_moe_combine_return(o):
+    """Combine read at the owners, both layouts: for layout 1 equal to the
+    combine from the expert side (written directly, pinned on its own); for
+    layout 0 equal to the return a2av with the transposed splits followed by
+    the combine over the pack's perm; after the one-step dispatch of real
+    tokens, equal to combining the tokens themselves; failures as the
+    inverse's."""
+    import torch
+    g = np.random.default_rng(52)
+    for W, T, k, E, H, distinct in ((4, 30, 3, 12, 8, True), (2, 17, 4, 8, 5, False),
+                                    (1, 9, 2, 3, 16, True), (3, 0, 2, 6, 4, False)):
+        toks, ids = [], []
+        for r in range(W):
+            tok = torch.randn(T, H, generator=torch.Generator().manual_seed(300 + r))
+            toks.append(tok.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+            ids.append(_moe_case(g, T, k, E, 1, distinct)[1].reshape(-1))
+        ws = [(g.random((T, k)) * 2 - 0.5).astype(np.float32) for _ in range(W)]
+        st, _, perms, S, counts, _ = o.moe_pack_dispatch(W, T, k, E, 2 * H,
+                                                         [t.view(np.uint8) for t in toks], ids,
+                                                         [10 ** 6] * W, 0)
+        assert st == 0
+        tot = S.sum(axis=0)
+        junk = [g.integers(0, 1 << 16, size=(int(t), H), dtype=np.uint16) for t in tot]
+        junk = [np.where((x & 0x7F80) == 0x7F80, x & 0xBFFF, x).astype(np.uint16) for x in junk]
+        # layout 1 against the direct combine from the expert side
+        st, got = o.moe_combine_return(W, T, k, E, H, counts, ids, perms, junk, ws, 1)
+        st2, want = o.moe_combine_grouped(W, T, k, E, H, counts, ids, perms, junk, ws)
+        assert st == st2 == 0 and all(np.array_equal(a, b) for a, b in zip(got, want))
+        # layout 0 against the return a2av and the combine over perm
+        st, got = o.moe_combine_return(W, T, k, E, H, counts, ids, perms, junk, ws, 0)
+        assert st == 0
+        back = _return_a2av_unpack_back(o, W, T, k, 2 * H, S, junk)
+        for s in range(W):
+            st, want = o.moe_combine(T, k, H, back[s].view(np.uint16).reshape(-1, H), perms[s],
+                                     ws[s])
+            assert st == 0 and np.array_equal(got[s], want), s
+        # after the one-step dispatch of the tokens: the tokens' own combine
+        for layout in (0, 1):
+            st, recv, _, _, _, _ = o.moe_pack_dispatch(W, T, k, E, 2 * H,
+                                                       [t.view(np.uint8) for t in toks], ids,
+                                                       tot, layout)
+            assert st == 0
+            st, got = o.moe_combine_return(W, T, k, E, H, counts, ids, perms,
+                                           [x.view(np.uint16).reshape(-1, H) for x in recv], ws,
+                                           layout)
+            assert st == 0
+            for s in range(W):
+                rep = np.ascontiguousarray(np.repeat(toks[s], k, axis=0))
+                st, want = o.moe_combine(T, k, H, rep, np.arange(T * k, dtype=np.int64), ws[s])
+                assert st == 0 and np.array_equal(got[s], want), (layout, s)
+    # failures: the inverse's
+    W, T, k, E, H = 2, 6, 2, 4, 8
+    ids = [_moe_case(g, T, k, E, 1, True)[1].reshape(-1) for _ in range(W)]
+    toks = [np.zeros((T, 2 * H), np.uint8) for _ in range(W)]
+    st, _, perms, S, counts, _ = o.moe_pack_dispatch(W, T, k, E, 2 * H, toks, ids, [99] * W, 0)
+    ws = [np.ones((T, k), np.float32)] * W
+    full = [np.ones((int(t), H), np.uint16) for t in S.sum(axis=0)]
+    for layout in (0, 1):
+        assert o.moe_combine_return(W, T, k, E, H, counts, ids, perms, full, ws, layout)[0] == 0
+        bad = [x.copy() for x in ids]; bad[0][1] = E
+        st, out = o.moe_combine_return(W, T, k, E, H, counts, bad, perms, full, ws, layout)
+        assert st == R.BAD_EXPERT and not any(x.any() for x in out)
+        st, out = o.moe_combine_return(W, T, k, E, H, counts, ids, perms,
+                                       [x[:-1] for x in full], ws, layout)
+        assert st == R.SEND_OVERRUN and not any(x.any() for x in out)
+        c2 = counts.copy(); c2[1, 1] = -4
+        assert o.moe_combine_return(W, T, k, E, H, c2, ids, perms, full, ws, layout)[0] == R.BAD_SPLIT
+
+
+def _return_a2av_unpack_back(o, W, T, k, R_bytes, S, recv):
+    """The return a2av of layout 0 alone: every owner's blocks back at their
+    sources, in pack order."""
+    Ot = np.ascontiguousarray(S.T)
+    back = [np.zeros(T * k * R_bytes, np.uint8) for _ in range(W)]
+    st, _, _, _ = o.a2av(R_bytes, [np.ascontiguousarray(x).view(np.uint8).reshape(-1) for x in recv],
+                         Ot.sum(axis=1), back, np.full(W, T * k), Ot)
+    assert st == 0
+    return back
+
+
 # ------------------------------------------------------------------ gate-weighted combine
 def _round_f32(x):
     """A Fraction rounded to the nearest binary32, ties to even (finite, in

@@ -103,6 +103,10 @@ MUTANTS = {
     "unpack_return_overrun_off_by_one": [
         ("if (run > recv_rows[d]) st |= REF_SEND_OVERRUN;",
          "if (run >= recv_rows[d]) st |= REF_SEND_OVERRUN;", 0)],
+    "combine_return_ignores_layout": [("recv_rows, home, layout);", "recv_rows, home, 0);", 0)],
+    "combine_return_uses_pack_perm": [
+        ("(const uint16_t *)home[s], ident, w[s], out[s]);",
+         "(const uint16_t *)home[s], perm[s], w[s], out[s]);", 0)],
     "keys_exchange_offsets_inclusive": [
         ("            recv_off_keys[d * (W + 1) + s] = run;\n            run += Sk[s * W + d];",
          "            run += Sk[s * W + d];\n            recv_off_keys[d * (W + 1) + s] = run;", 0)],
