@@ -637,9 +637,24 @@ def moe_rows(torch, B, I, o, out):
     out["moe_tokens_combine_round_trip"] = {
         "us": round(ms * 1e3, 2),
         "note": "moe_pack_dispatch (layout 1) + combine from the expert side"}
+    # the weighted combine read at the owners, either receive order
+    crws = torch.empty(B.moe_combine_return_workspace_bytes(W, T, k, E), dtype=torch.uint8,
+                       device="cuda")
+    crst = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cr0 = lambda: B.moe_combine_return(W, T, k, E, hidden, cnt1, ids, perm1, recv, cap, wts, cgo,
+                                       0, crws, crst)
+    cr1 = lambda: B.moe_combine_return(W, T, k, E, hidden, cnt1, ids, perm1, grp, cap, wts, cgo,
+                                       1, crws, crst)
+    home_comb_bytes = W * (Q * R + T * R + Q * (8 + 4 + 8))
+    out["moe_combine_return"] = row_entry(home_comb_bytes, time_events(torch, cr0, 5))
+    out["moe_combine_return_grouped"] = row_entry(home_comb_bytes, time_events(torch, cr1, 5))
+    ms = time_events(torch, lambda: (pd0(), cr0()), 5)
+    out["moe_tokens_combine_round_trip_source_major"] = {
+        "us": round(ms * 1e3, 2),
+        "note": "moe_pack_dispatch (layout 0) + moe_combine_return (layout 0)"}
     torch.cuda.synchronize()
     _check_status(B, [("pack + dispatch", pdst), ("unpack + return", urst),
-                      ("grouped combine", cgst)])
+                      ("grouped combine", cgst), ("combine at the owners", crst)])
     for r in range(W):
         if not torch.equal(home[r].view(torch.int16),
                            tok[r].view(torch.int16).repeat_interleave(k, dim=0)):

@@ -27,7 +27,7 @@ __all__ = [
     "moe_regroup_workspace_bytes", "moe_regroup", "moe_dispatch_grouped_workspace_bytes",
     "moe_dispatch_grouped", "moe_combine_grouped_workspace_bytes", "moe_combine_grouped",
     "moe_pack_dispatch_workspace_bytes", "moe_pack_dispatch", "moe_unpack_return_workspace_bytes",
-    "moe_unpack_return",
+    "moe_unpack_return", "moe_combine_return_workspace_bytes", "moe_combine_return",
     "keys_bucketize_workspace_bytes",
     "keys_bucketize", "keys_exchange_workspace_bytes", "keys_exchange", "a2av_device_copy",
     "MAX_TABLES",
@@ -99,6 +99,10 @@ def lib():
         L.moe_unpack_return_workspace_bytes.restype = sz
         L.moe_unpack_return.argtypes = [i32, i64, i32, i32, sz, vp, vpp, vpp, vpp, i64p, vpp, i32,
                                         vp, sz, vp, vp]
+        L.moe_combine_return_workspace_bytes.argtypes = [i32, i64, i32, i32]
+        L.moe_combine_return_workspace_bytes.restype = sz
+        L.moe_combine_return.argtypes = [i32, i64, i32, i32, i64, vp, vpp, vpp, vpp, i64p, vpp, vpp,
+                                         i32, vp, sz, vp, vp]
         L.keys_bucketize_workspace_bytes.argtypes = [i32, i32]
         L.keys_bucketize_workspace_bytes.restype = sz
         L.keys_bucketize.argtypes = [i32, i32, i64, vpp, vpp, i64p, vpp, vpp, vp, vp, vp, sz, vp,
@@ -111,6 +115,7 @@ def lib():
         for f in ("a2av_exchange_splits", "a2av_offsets", "a2av_copy", "a2av_all_to_all_vdev",
                   "moe_pack", "moe_unpack", "moe_combine", "moe_regroup", "moe_dispatch_grouped",
                   "moe_combine_grouped", "moe_pack_dispatch", "moe_unpack_return",
+                  "moe_combine_return",
                   "keys_bucketize", "keys_exchange",
                   "a2av_device_copy"):
             getattr(L, f).restype = i32
@@ -340,6 +345,28 @@ def moe_unpack_return(W, T, k, E, row_bytes, expert_counts, ids, perm, recv, rec
                                    _dev(workspace, "workspace"),
                                    workspace.numel() * workspace.element_size(),
                                    _dev(status, "status"), _stream(stream, status)))
+
+
+def moe_combine_return_workspace_bytes(W, T, k, E) -> int:
+    return int(lib().moe_combine_return_workspace_bytes(int(W), int(T), int(k), int(E)))
+
+
+def moe_combine_return(W, T, k, E, H, expert_counts, ids, perm, recv, recv_rows, weights, out,
+                       layout, workspace, status, stream=None):
+    """The return trip and the gate-weighted combine in one pass, reading
+    every slot's row where moe_pack_dispatch left it."""
+    if (len(ids) != W or len(perm) != W or len(recv) != W or len(recv_rows) != W
+            or len(weights) != W or len(out) != W):
+        raise ValueError("ids, perm, recv, recv_rows, weights and out need W entries each")
+    _check("moe_combine_return",
+           lib().moe_combine_return(int(W), int(T), int(k), int(E), int(H),
+                                    _dev(expert_counts, "expert_counts"), _ptr_array(ids, "ids"),
+                                    _ptr_array(perm, "perm"), _ptr_array(recv, "recv"),
+                                    _i64_array(recv_rows), _ptr_array(weights, "weights"),
+                                    _ptr_array(out, "out"), int(layout),
+                                    _dev(workspace, "workspace"),
+                                    workspace.numel() * workspace.element_size(),
+                                    _dev(status, "status"), _stream(stream, status)))
 
 
 def keys_bucketize_workspace_bytes(W, n_tables) -> int:

@@ -433,6 +433,7 @@ struct ReturnArgs {
     const int64_t *counts;     // [W][E]
     const uint64_t *row_addr;  // [W][E] (plan)
     const int64_t *ystart;     // [W][E] (plan)
+    uint64_t *xaddr;           // [W][T*k] each slot's row address, or null
     int32_t *words;            // [0] plan bits, [1] slot bits
     int32_t *status;
     uint64_t R;
@@ -442,7 +443,8 @@ struct ReturnArgs {
 };
 
 // One thread per (slot, source): its id in range and its pack row inside its
-// expert's block, so every row the gather reads lies in the owner's buffer.
+// expert's block, so every row the gather reads lies in the owner's buffer;
+// for the combine, also the address of the slot's row.
 __global__ __launch_bounds__(256) void k_slot_check(const ReturnArgs a) {
     if (status_poisoned(a.status)) return;
     const int s = blockIdx.y;
@@ -455,6 +457,9 @@ __global__ __launch_bounds__(256) void k_slot_check(const ReturnArgs a) {
         } else {
             const int64_t p = a.perm[s][q] - a.ystart[(int64_t)s * a.E + e];
             if (p < 0 || p >= a.counts[(int64_t)s * a.E + e]) bad = A2AV_ST_BAD_PERM;
+            else if (a.xaddr)
+                a.xaddr[(int64_t)s * a.Q + q] =
+                    a.row_addr[(int64_t)s * a.E + e] + (uint64_t)a.perm[s][q] * a.R;
         }
     }
     const int be = __ballot(bad & A2AV_ST_BAD_EXPERT) != 0, bp = __ballot(bad & A2AV_ST_BAD_PERM) != 0;
@@ -548,12 +553,28 @@ struct CombineArgs {
     const int64_t *perm[A2AV_MAX_W];
     const float *w[A2AV_MAX_W];
     unsigned char *out[A2AV_MAX_W];
+    // read at the owners (HOME): slot rows at xaddr[r][t*k + j], after the
+    // verdict in words[0] (plan) and words[1] (slot check)
+    const uint64_t *xaddr;
+    const int32_t *words;
     int32_t *status;
     int64_t T;
     int64_t H;
     int k;
     int W;
 };
+
+// The verdict of the plan and the slot check of a combine read at the owners:
+// the first thread reports it (a bad count alone, since the other checks read
+// the counts); then no wave writes.
+__device__ __forceinline__ bool home_verdict(const CombineArgs &a) {
+    const int32_t pb = *(const const_i32 *)&a.words[0];
+    const int32_t cw = *(const const_i32 *)&a.words[1];
+    if ((pb | cw) == 0) return false;
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        atomicOr(a.status, (pb & A2AV_ST_BAD_SPLIT) ? A2AV_ST_BAD_SPLIT : (pb | cw));
+    return true;
+}
 
 
 constexpr int kCombineGroup = 8;  // slots whose rows are loaded before their fmas
@@ -567,11 +588,14 @@ constexpr int kCombineGroup = 8;  // slots whose rows are loaded before their fm
 // interleaving them), and the adds run in slot order. Short-lived waves with
 // few registers keep many loads in flight per CU: in measurements this beat
 // looping waves, with or without software pipelining.
-template <bool SNT>
+template <bool SNT, bool HOME>
 __global__ __launch_bounds__(256) void k_moe_combine(const CombineArgs a, uint64_t nchunk) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint64_t wpb = blockDim.x / kWave;
     if (*(const const_i32 *)a.status) return;  // written only by earlier kernels
+    if constexpr (HOME) {
+        if (home_verdict(a)) return;
+    }
     const uint64_t nwork = (uint64_t)a.W * (uint64_t)a.T * nchunk;
     const int k = a.k;
     const uint64_t rowb = (uint64_t)a.H * 2;
@@ -583,7 +607,8 @@ __global__ __launch_bounds__(256) void k_moe_combine(const CombineArgs a, uint64
         const uint64_t c = wk - tok * nchunk;
         const int r = (int)(tok / (uint64_t)a.T);
         const int64_t t = (int64_t)(tok - (uint64_t)r * (uint64_t)a.T);
-        const const_i64 *pp = (const const_i64 *)(a.perm[r] + t * k);
+        const const_i64 *pp = HOME ? (const const_i64 *)(a.xaddr + (uint64_t)r * a.T * k + t * k)
+                                   : (const const_i64 *)(a.perm[r] + t * k);
         const const_i32 *wp = (const const_i32 *)(a.w[r] + t * k);
         const unsigned char *bk = a.back[r];
         uint64_t i = c * kWave + lane;
@@ -599,7 +624,8 @@ __global__ __launch_bounds__(256) void k_moe_combine(const CombineArgs a, uint64
             for (int g = 0; g < kCombineGroup; g++) {
                 // past the last slot the load repeats slot k-1; its fma is skipped
                 const int j = j0 + g < k ? j0 + g : k - 1;
-                const unsigned char *row = bk + (uint64_t)pp[j] * rowb;
+                const unsigned char *row = HOME ? (const unsigned char *)(uintptr_t)(uint64_t)pp[j]
+                                                : bk + (uint64_t)pp[j] * rowb;
                 v[g] = ld<true>((const u32x4 *)(row + off));
                 wt[g] = __int_as_float(wp[j]);
             }
@@ -628,10 +654,14 @@ __global__ __launch_bounds__(256) void k_moe_combine(const CombineArgs a, uint64
 }
 
 // Any row width or alignment: one element per lane per step.
+template <bool HOME>
 __global__ __launch_bounds__(256) void k_moe_combine_any(const CombineArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint64_t wpb = blockDim.x / kWave;
     if (*(const const_i32 *)a.status) return;
+    if constexpr (HOME) {
+        if (home_verdict(a)) return;
+    }
     const uint64_t nwork = (uint64_t)a.W * (uint64_t)a.T;
     const int k = a.k;
     const uint64_t H = (uint64_t)a.H;
@@ -643,11 +673,13 @@ __global__ __launch_bounds__(256) void k_moe_combine_any(const CombineArgs a) {
         const float *wp = a.w[r] + t * k;
         const uint16_t *bk = (const uint16_t *)a.back[r];
         uint16_t *dst = (uint16_t *)a.out[r] + (uint64_t)t * H;
+        const uint64_t *xa = HOME ? a.xaddr + (uint64_t)r * a.T * k + t * k : nullptr;
         for (uint64_t h = lane; h < H; h += kWave) {
             float acc = 0.0f;
             for (int j = 0; j < k; j++) {
-                const uint64_t row = (uint64_t)pp[j];
-                acc = __builtin_fmaf(wp[j], __uint_as_float((uint32_t)bk[row * H + h] << 16), acc);
+                const uint16_t *row = HOME ? (const uint16_t *)(uintptr_t)xa[j]
+                                           : bk + (uint64_t)pp[j] * H;
+                acc = __builtin_fmaf(wp[j], __uint_as_float((uint32_t)row[h] << 16), acc);
             }
             dst[h] = (uint16_t)to_bf16(acc);
         }
@@ -904,6 +936,105 @@ A2AV_API int moe_unpack_return(int W, int64_t T, int k, int E, size_t row_bytes,
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
 }
 
+A2AV_API size_t moe_combine_return_workspace_bytes(int W, int64_t T, int k, int E) {
+    if (W < 1 || W > A2AV_MAX_W || E < 1 || E > A2AV_MAX_EXPERTS || E % W != 0 || T < 0 || k < 1)
+        return 0;
+    if (T > ((int64_t)1 << 31) / k) return 0;
+    return 2 * round256((size_t)W * (size_t)E * 8) + 256 +
+           round256((size_t)W * (size_t)(T * k) * 8);
+}
+
+A2AV_API int moe_combine_return(int W, int64_t T, int k, int E, int64_t H,
+                                const int64_t *expert_counts, const int32_t *const *ids,
+                                const int64_t *const *perm, const void *const *recv,
+                                const int64_t *recv_rows, const float *const *weights,
+                                void *const *out, int layout, void *workspace,
+                                size_t workspace_bytes, int32_t *status, hipStream_t stream) {
+    if (W < 1 || W > A2AV_MAX_W || E < 1 || E > A2AV_MAX_EXPERTS || E % W != 0 || T < 0 ||
+        k < 1 || H < 1 || !expert_counts || !ids || !perm || !recv || !recv_rows || !weights ||
+        !out || !status || (layout != 0 && layout != 1))
+        return A2AV_EARG;
+    if (T > ((int64_t)1 << 31) / k || (uint64_t)H > (uint64_t)INT64_MAX / 2) return A2AV_EARG;
+    const uint64_t row_bytes = 2 * (uint64_t)H;
+    if ((uint64_t)T * (uint64_t)k > (uint64_t)INT64_MAX / row_bytes) return A2AV_EARG;
+    if (!workspace || workspace_bytes < moe_combine_return_workspace_bytes(W, T, k, E))
+        return A2AV_EARG;
+    ShiftArgs p;
+    ReturnArgs c;
+    CombineArgs m;
+    std::memset(&p, 0, sizeof(p));
+    std::memset(&c, 0, sizeof(c));
+    std::memset(&m, 0, sizeof(m));
+    bool aligned = (H % 8) == 0;
+    for (int r = 0; r < W; r++) {
+        if (T > 0 && (!ids[r] || !perm[r] || !weights[r] || !out[r])) return A2AV_EARG;
+        const int64_t rows = recv_rows[r];
+        if (rows < 0 || (uint64_t)rows > (uint64_t)INT64_MAX / row_bytes) return A2AV_EARG;
+        if (rows > 0 && !recv[r]) return A2AV_EARG;
+        p.base[r] = (const unsigned char *)recv[r];
+        p.limit[r] = rows;
+        c.ids[r] = ids[r];
+        c.perm[r] = perm[r];
+        m.w[r] = weights[r];
+        m.out[r] = (unsigned char *)out[r];
+        aligned = aligned && ((uintptr_t)recv[r] % 16 == 0) && ((uintptr_t)out[r] % 16 == 0);
+    }
+    unsigned char *ws = (unsigned char *)workspace;
+    const size_t table = round256((size_t)W * (size_t)E * 8);
+    uint64_t *row_addr = (uint64_t *)ws;
+    int64_t *ystart = (int64_t *)(ws + table);
+    int32_t *words = (int32_t *)(ws + 2 * table);
+    uint64_t *xaddr = (uint64_t *)(ws + 2 * table + 256);
+    p.counts = expert_counts;
+    p.row_addr = row_addr;
+    p.ystart = ystart;
+    p.words = words;
+    p.status = status;
+    p.R = row_bytes;
+    p.W = W;
+    p.E = E;
+    p.layout = layout;
+    p.over_bit = A2AV_ST_SEND_OVERRUN;
+    p.check_counts = 1;
+    c.counts = expert_counts;
+    c.row_addr = row_addr;
+    c.ystart = ystart;
+    c.xaddr = xaddr;
+    c.words = words;
+    c.status = status;
+    c.R = row_bytes;
+    c.Q = T * k;
+    c.E = E;
+    c.W = W;
+    m.xaddr = xaddr;
+    m.words = words;
+    m.status = status;
+    m.T = T;
+    m.H = H;
+    m.k = k;
+    m.W = W;
+    hipLaunchKernelGGL(k_shift_plan, dim3(W), dim3(kPlanThreads), 0, stream, p);
+    if (c.Q > 0)
+        hipLaunchKernelGGL(k_slot_check, dim3((unsigned)((c.Q + 255) / 256), W), dim3(256), 0,
+                           stream, c);
+    // at least one wave, so that a verdict of the plan is reported; the fast
+    // path needs 16-byte vectors and rows under 4 GiB (32-bit lane offsets)
+    if (!aligned || row_bytes >= (1ull << 32)) {
+        uint64_t blocks = ((uint64_t)W * (uint64_t)T + 3) / 4;
+        if (blocks < 1) blocks = 1;
+        if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
+        hipLaunchKernelGGL(k_moe_combine_any<true>, dim3((unsigned)blocks), dim3(256), 0, stream, m);
+    } else {
+        const uint64_t nchunk = ((uint64_t)H / 8 + kWave - 1) / kWave;
+        uint64_t blocks = ((uint64_t)W * (uint64_t)T * nchunk + 3) / 4;
+        if (blocks < 1) blocks = 1;
+        if (blocks > (1u << 22)) blocks = 1u << 22;
+        hipLaunchKernelGGL((k_moe_combine<true, true>), dim3((unsigned)blocks), dim3(256), 0,
+                           stream, m, nchunk);
+    }
+    return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
+}
+
 A2AV_API int moe_unpack(int W, int64_t T, int k, size_t row_bytes, const void *const *back,
                         const int64_t *const *perm, void *const *out, int32_t *status,
                         hipStream_t stream) {
@@ -986,16 +1117,16 @@ A2AV_API int moe_combine(int W, int64_t T, int k, int64_t H, const void *const *
     if (!aligned || (uint64_t)H * 2 >= (1ull << 32)) {
         uint64_t blocks = ((uint64_t)W * (uint64_t)T + 3) / 4;
         if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
-        hipLaunchKernelGGL(k_moe_combine_any, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(k_moe_combine_any<false>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     } else {
         const uint64_t nchunk = ((uint64_t)H / 8 + kWave - 1) / kWave;
         uint64_t blocks = ((uint64_t)W * (uint64_t)T * nchunk + 3) / 4;
         if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
         // tuning knob: A2AV_COMBINE_STORE_NT (non-temporal stores, 0/1)
         if (env_long("A2AV_COMBINE_STORE_NT", 1, 0, 1))
-            hipLaunchKernelGGL((k_moe_combine<true>), dim3((unsigned)blocks), dim3(256), 0, stream, a, nchunk);
+            hipLaunchKernelGGL((k_moe_combine<true, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a, nchunk);
         else
-            hipLaunchKernelGGL((k_moe_combine<false>), dim3((unsigned)blocks), dim3(256), 0, stream, a, nchunk);
+            hipLaunchKernelGGL((k_moe_combine<false, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a, nchunk);
     }
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
 }

@@ -273,6 +273,34 @@ int moe_unpack_return(int W, int64_t T, int k, int E, size_t row_bytes,
                       size_t workspace_bytes, int32_t *status, hipStream_t stream);
 
 /*
+ * Workspace bytes moe_combine_return needs (0 for invalid sizes).
+ */
+size_t moe_combine_return_workspace_bytes(int W, int64_t T, int k, int E);
+
+/*
+ * The gate-weighted combine (as moe_combine) read at the owners: the return
+ * trip and the combine in one pass, for rows left by moe_pack_dispatch in
+ * either layout. Equal to moe_unpack_return followed by moe_combine over the
+ * rows it brings home (slot t*k + j of token t), without writing them; for
+ * layout 1 equal to moe_combine_grouped.
+ *   expert_counts    device int64 [W][E] (moe_pack's)
+ *   ids[W], perm[W]  device int32 / int64 [T*k] per source
+ *   recv[W]          device bf16 [recv_rows[d]][H] per owner (host recv_rows)
+ *   weights[W]       device fp32 [T][k];  out[W]  device bf16 [T][H]
+ *   workspace        device scratch of >= moe_combine_return_workspace_bytes()
+ *   status           as moe_unpack_return; nothing is written on failure.
+ * Three kernels: the plan of moe_pack_dispatch, a check of every slot that
+ * also records its row's address, and the combine of moe_combine reading
+ * those rows in place.
+ */
+int moe_combine_return(int W, int64_t T, int k, int E, int64_t H, const int64_t *expert_counts,
+                       const int32_t *const *ids, const int64_t *const *perm,
+                       const void *const *recv, const int64_t *recv_rows,
+                       const float *const *weights, void *const *out, int layout,
+                       void *workspace, size_t workspace_bytes, int32_t *status,
+                       hipStream_t stream);
+
+/*
  * MoE un-pack after the return trip ("inverse combine" without weights):
  * out[r][q] = back[r][perm[r][q]] for q < T*k, i.e. every slot gets back the
  * row it was packed to. back is what the return a2av (splits O, the

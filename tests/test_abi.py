@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
                  "moe_dispatch_grouped", "moe_dispatch_grouped_workspace_bytes",
                  "moe_combine_grouped", "moe_combine_grouped_workspace_bytes",
                  "moe_pack_dispatch", "moe_pack_dispatch_workspace_bytes", "moe_unpack_return",
-                 "moe_unpack_return_workspace_bytes"):
+                 "moe_unpack_return_workspace_bytes", "moe_combine_return",
+                 "moe_combine_return_workspace_bytes"):
         assert must in names
 
 
@@ -151,6 +152,17 @@ def test_host_argument_errors(L):
                                vp(8), None) == EARG
     assert L.moe_unpack_return(3, 10, 2, 8, 16, vp(8), ptrs, ptrs, ptrs, two, ptrs, 0, vp(8), wsu,
                                vp(8), None) == EARG
+    # combine at the owners: bad layout, H = 0, small workspace, negative rows
+    wcr = L.moe_combine_return_workspace_bytes(2, 10, 2, 8)
+    assert wcr > 0 and L.moe_combine_return_workspace_bytes(3, 10, 2, 8) == 0
+    assert L.moe_combine_return(2, 10, 2, 8, 16, vp(8), ptrs, ptrs, ptrs, two, ptrs, ptrs, 2,
+                                vp(8), wcr, vp(8), None) == EARG
+    assert L.moe_combine_return(2, 10, 2, 8, 0, vp(8), ptrs, ptrs, ptrs, two, ptrs, ptrs, 0,
+                                vp(8), wcr, vp(8), None) == EARG
+    assert L.moe_combine_return(2, 10, 2, 8, 16, vp(8), ptrs, ptrs, ptrs, two, ptrs, ptrs, 1,
+                                vp(8), wcr - 1, vp(8), None) == EARG
+    assert L.moe_combine_return(2, 10, 2, 8, 16, vp(8), ptrs, ptrs, ptrs, negr, ptrs, ptrs, 0,
+                                vp(8), wcr, vp(8), None) == EARG
     # fused exchange: small workspace, negative capacity, too many tables
     wsx = L.keys_exchange_workspace_bytes(2, 26)
     assert wsx > 0 and L.keys_exchange_workspace_bytes(2, 4097) == 0

@@ -1,6 +1,7 @@
-"""GPU parity of the MoE pack and dispatch in one step (moe_pack_dispatch)
-and its inverse (moe_unpack_return) against the CPU oracle: bit-exact
-receive rows, perm, splits, counts, block offsets and status, in both
+"""GPU parity of the MoE pack and dispatch in one step (moe_pack_dispatch),
+its inverse (moe_unpack_return) and the gate-weighted combine read at the
+owners (moe_combine_return) against the CPU oracle: bit-exact receive rows,
+perm, splits, counts, block offsets, combined rows and status, in both
 receive layouts, at small ragged shapes, on error paths, and at the full
 dispatch size."""
 import numpy as np
@@ -67,6 +68,37 @@ def gpu_unpack_return(W, T, k, E, R, counts, ids, perms, recv, layout, recv_rows
     torch.cuda.synchronize()
     guards = all(b.guards_intact() for b in out + rin)
     return int(status.item()), [b.host().reshape(-1, R) for b in out], guards
+
+
+def gpu_combine_return(W, T, k, E, H, counts, ids, perms, recv, weights, layout, recv_rows=None,
+                       pad=0, status_init=0):
+    """recv: per-owner host uint16 [rows, H]; weights: per-source float32
+    [T, k]. Returns (status, [out host uint16 [T, H]], guards)."""
+    rin = [upload_rows(np.ascontiguousarray(x).view(np.uint8), pad=pad) for x in recv]
+    rows = [x.shape[0] for x in recv] if recv_rows is None else list(recv_rows)
+    out = [GuardedBuffer(T * H * 2, pad=pad) for _ in range(W)]
+    cnt = torch.from_numpy(np.ascontiguousarray(counts, dtype=np.int64)).cuda()
+    idd = [_dev_array(i, np.int32) for i in ids]
+    pd = [_dev_array(p, np.int64) for p in perms]
+    wd = [_dev_array(w, np.float32) for w in weights]
+    ws = torch.empty(B.moe_combine_return_workspace_bytes(W, T, k, E), dtype=torch.uint8,
+                     device="cuda")
+    status = torch.full((1,), status_init, dtype=torch.int32, device="cuda")
+    B.moe_combine_return(W, T, k, E, H, cnt, idd, pd, [b.view for b in rin], rows, wd,
+                         [b.view for b in out], layout, ws, status)
+    torch.cuda.synchronize()
+    guards = all(b.guards_intact() for b in out + rin)
+    return (int(status.item()), [b.host().view(np.uint16).reshape(T, H) for b in out], guards)
+
+
+def _bf16_junk(g, rows, H):
+    """Random bf16 bit patterns, specials included (the two sides must agree
+    on every bit, NaN included)."""
+    x = g.integers(0, 1 << 16, size=(rows, H), dtype=np.uint16)
+    sp = np.array([0x7F80, 0xFF80, 0x7FC1, 0x0001, 0x8000, 0x7F7F], dtype=np.uint16)
+    m = g.random((rows, H)) < 0.01
+    x[m] = sp[g.integers(0, sp.size, size=int(m.sum()))]
+    return x
 
 
 def _case(g, W, T, k, E, R, distinct):
@@ -305,4 +337,117 @@ def test_pack_dispatch_full(ref, layout):
     for s in range(W):
         want = tok[s].view(torch.int16).repeat_interleave(k, dim=0)
         assert torch.equal(out[s].view(torch.int16), want), s
+    # the combine at the owners equals the combine over those home rows, and
+    # the oracle's on 32 sampled tokens per rank
+    w_h = [I.gate_weights(g, T, k) for _ in range(W)]
+    wts = [torch.from_numpy(x.reshape(-1)).cuda() for x in w_h]
+    cret = [torch.empty((T, hidden), dtype=torch.bfloat16, device="cuda") for _ in range(W)]
+    cws = torch.empty(B.moe_combine_return_workspace_bytes(W, T, k, E), dtype=torch.uint8,
+                      device="cuda")
+    B.moe_combine_return(W, T, k, E, hidden, cnt, ids, perm, recv, tot, wts, cret, layout, cws,
+                         status)
+    ident = [torch.arange(Q, dtype=torch.int64, device="cuda") for _ in range(W)]
+    cref = [torch.empty_like(x) for x in cret]
+    cst = torch.zeros(1, dtype=torch.int32, device="cuda")
+    B.moe_combine(W, T, k, hidden, out, ident, wts, cref, cst)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0 and int(cst.item()) == 0
+    for s in range(W):
+        assert torch.equal(cret[s].view(torch.int16), cref[s].view(torch.int16)), s
+        ts = np.sort(g.choice(T, size=32, replace=False))
+        rows = tok[s][torch.from_numpy(ts).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+        st_, want = ref.moe_combine(32, k, hidden, np.repeat(rows, k, axis=0),
+                                    np.arange(32 * k, dtype=np.int64), w_h[s][ts])
+        assert st_ == 0
+        got = cret[s][torch.from_numpy(ts).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, want), s
     _say("pack_dispatch full: ok, layout", layout, "rows per owner", tot.tolist())
+
+
+COMBINE_SHAPES = [
+    (8, 64, 8, 256, 512, True, 0),     # the dispatch layout, 1 KiB rows
+    (4, 50, 3, 12, 24, False, 0),      # repeated experts, three vectors per row
+    (3, 40, 2, 6, 13, False, 0),       # odd width: the element path
+    (3, 40, 2, 6, 64, True, 4),        # misaligned bases: the element path
+    (1, 20, 4, 5, 1000, False, 0),     # a clamped last chunk
+    (5, 30, 12, 10, 8, False, 0),      # k = 12: two slot groups
+    (2, 0, 2, 8, 16, False, 0),        # no tokens
+]
+
+
+@pytest.mark.parametrize("W,T,k,E,H,distinct,pad", COMBINE_SHAPES)
+@pytest.mark.parametrize("layout", [0, 1])
+def test_combine_return_matches_oracle(ref, W, T, k, E, H, distinct, pad, layout):
+    _say("combine_return", W, T, k, E, H, distinct, pad, layout)
+    g = I.rng(W * 131 + T * 7 + k + E + H + layout)
+    toks, ids = _case(g, W, T, k, E, 2 * H, distinct)
+    tot = _totals(ids, W, E)
+    st, recv, perm, S, cnt, boff, _ = gpu_pack_dispatch(W, T, k, E, 2 * H, toks, ids, tot, layout)
+    assert st == 0
+    wts = [I.gate_weights(g, T, k) for _ in range(W)]
+    # on the rows the dispatch left
+    rows16 = [x.view(np.uint16).reshape(-1, H) for x in recv]
+    gst, out, guards = gpu_combine_return(W, T, k, E, H, cnt, ids, perm, rows16, wts, layout,
+                                          pad=pad)
+    rst, rout = ref.moe_combine_return(W, T, k, E, H, cnt, ids, perm, rows16, wts, layout)
+    assert gst == rst == 0 and guards
+    for s in range(W):
+        assert np.array_equal(out[s], rout[s]), s
+    # on arbitrary bf16 patterns, specials included
+    junk = [_bf16_junk(g, int(t), H) for t in tot]
+    gst, out, guards = gpu_combine_return(W, T, k, E, H, cnt, ids, perm, junk, wts, layout,
+                                          pad=pad)
+    rst, rout = ref.moe_combine_return(W, T, k, E, H, cnt, ids, perm, junk, wts, layout)
+    assert gst == rst == 0 and guards
+    for s in range(W):
+        assert np.array_equal(out[s], rout[s]), s
+
+
+@pytest.mark.parametrize("case", ["bad_split", "bad_expert", "bad_perm", "overrun", "poisoned",
+                                  "empty_bad_split"])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_combine_return_errors(ref, case, layout):
+    _say("combine_return error", case, layout)
+    W, T, k, E, H = 3, 30, 2, 6, 16
+    g = I.rng(191 + layout)
+    toks, ids = _case(g, W, T, k, E, 2 * H, True)
+    st, recv, perm, S, cnt, boff, _ = gpu_pack_dispatch(W, T, k, E, 2 * H, toks, ids,
+                                                         _totals(ids, W, E), layout)
+    assert st == 0
+    rows16 = [x.view(np.uint16).reshape(-1, H) for x in recv]
+    wts = [I.gate_weights(g, T, k) for _ in range(W)]
+    ids = [x.copy() for x in ids]
+    nrows, init = None, 0
+    if case == "bad_split":
+        cnt = cnt.copy()
+        cnt[2, 1] = -5
+    elif case == "bad_expert":
+        ids[1][3] = E + 2
+    elif case == "bad_perm":
+        q = int(np.nonzero(ids[0] != ids[0][0])[0][0])
+        ids[0][0], ids[0][q] = ids[0][q], ids[0][0]
+    elif case == "overrun":
+        nrows = [x.shape[0] for x in rows16]
+        nrows[0] -= 1
+    elif case == "poisoned":
+        init = B.ST_BAD_OFFSETS
+    if case == "empty_bad_split":
+        cz = np.zeros((W, E), dtype=np.int64)
+        cz[1, 0] = -1
+        gst, out, guards = gpu_combine_return(W, 0, k, E, H, cz, [np.zeros(0, np.int32)] * W,
+                                              [np.zeros(0, np.int64)] * W,
+                                              [np.zeros((0, H), np.uint16)] * W,
+                                              [np.zeros((0, k), np.float32)] * W, layout)
+        assert gst == B.ST_BAD_SPLIT and guards
+        return
+    gst, out, guards = gpu_combine_return(W, T, k, E, H, cnt, ids, perm, rows16, wts, layout,
+                                          recv_rows=nrows, status_init=init)
+    assert guards and all((x.view(np.uint8) == SENT).all() for x in out)
+    if case == "poisoned":
+        assert gst == B.ST_BAD_OFFSETS
+        return
+    rrows = rows16 if nrows is None else [x[:n] for x, n in zip(rows16, nrows)]
+    rst, _ = ref.moe_combine_return(W, T, k, E, H, cnt, ids, perm, rrows, wts, layout)
+    want = {"bad_split": B.ST_BAD_SPLIT, "bad_expert": B.ST_BAD_EXPERT,
+            "bad_perm": B.ST_BAD_PERM, "overrun": B.ST_SEND_OVERRUN}[case]
+    assert gst == rst == want
