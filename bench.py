@@ -707,6 +707,10 @@ def moe_rows(torch, B, I, o, out):
     out["moe_tokens_combine_round_trip_chain"] = {
         "us": round(out["moe_pack"]["us"] + out["moe_chain_round_trip"]["us"], 2),
         "note": "moe_pack + the chain above"}
+    out["moe_tokens_combine_round_trip_source_major_chain"] = {
+        "us": round(sum(out[x]["us"] for x in ("moe_pack", "dispatch_a2av", "return_a2av",
+                                                 "moe_combine")), 2),
+        "note": "sum of pack, dispatch a2av, return a2av and combine"}
     out["moe_tokens_unpack_round_trip_chain"] = {
         "us": round(sum(out[x]["us"] for x in ("moe_pack", "dispatch_a2av", "return_a2av",
                                                  "moe_unpack")), 2),
