@@ -1,7 +1,9 @@
 """The entry points under HIP graph capture: a captured one-call a2av, MoE
-pack + dispatch and fused key exchange, each replayed several times with
-eager work and synchronisations between replays, and every replay compared
-with the eager result (which is itself checked against the oracle)."""
+pack + dispatch, fused key exchange and the one-step MoE trip (pack and
+dispatch in one step, the combine at the owners and the one-step inverse),
+each replayed several times with eager work and synchronisations between
+replays, and every replay compared with the eager result (which is itself
+checked against the oracle)."""
 import numpy as np
 import pytest
 import torch
@@ -156,4 +158,75 @@ def test_graph_fused_key_exchange(ref):
         status.zero_()
 
     _replay_and_check(graph, lambda: lo + ko + [sk, sl, ro], want, reset, _noise)
+    assert int(status.item()) == 0
+
+
+def test_graph_one_step_moe_trip(ref):
+    W, T, k, E, H = 4, 256, 4, 16, 256
+    R, Q = 2 * H, T * k
+    g = I.rng(61)
+    ids_h = [I.topk_ids(g, T, k, E, 1.1).reshape(-1) for _ in range(W)]
+    w_h = [I.gate_weights(g, T, k) for _ in range(W)]
+    tok = [I.payload_bf16(T, H, 70 + r, device="cuda") for r in range(W)]
+    ids = [torch.from_numpy(x).cuda() for x in ids_h]
+    wts = [torch.from_numpy(x.reshape(-1)).cuda() for x in w_h]
+    P = E // W
+    tot = np.zeros(W, dtype=np.int64)
+    for x in ids_h:
+        tot += np.bincount(x.astype(np.int64) // P, minlength=W)[:W]
+    tot = [int(t) for t in tot]
+    recv = [torch.zeros((t, H), dtype=torch.bfloat16, device="cuda") for t in tot]
+    perm = [torch.zeros(Q, dtype=torch.int64, device="cuda") for _ in range(W)]
+    S = torch.zeros((W, W), dtype=torch.int64, device="cuda")
+    cnt = torch.zeros((W, E), dtype=torch.int64, device="cuda")
+    boff = torch.zeros((W, P + 1), dtype=torch.int64, device="cuda")
+    comb = [torch.zeros((T, H), dtype=torch.bfloat16, device="cuda") for _ in range(W)]
+    home = [torch.zeros((Q, H), dtype=torch.bfloat16, device="cuda") for _ in range(W)]
+    pws = torch.empty(B.moe_pack_dispatch_workspace_bytes(W, T, k, E), dtype=torch.uint8,
+                      device="cuda")
+    cws = torch.empty(B.moe_combine_return_workspace_bytes(W, T, k, E), dtype=torch.uint8,
+                      device="cuda")
+    uws = torch.empty(B.moe_unpack_return_workspace_bytes(W, E), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def trip():
+        B.moe_pack_dispatch(W, T, k, E, R, tok, ids, recv, tot, perm, S, cnt, boff, 1, pws, status)
+        B.moe_combine_return(W, T, k, E, H, cnt, ids, perm, recv, tot, wts, comb, 1, cws, status)
+        B.moe_unpack_return(W, T, k, E, R, cnt, ids, perm, recv, tot, home, 1, uws, status)
+
+    trip()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    toks_h = [t.view(torch.uint8).cpu().numpy() for t in tok]
+    rst, rrecv, _, _, _, rboff = ref.moe_pack_dispatch(W, T, k, E, R, toks_h, ids_h, tot, 1)
+    assert rst == 0 and np.array_equal(boff.cpu().numpy(), rboff)
+    for d in range(W):
+        assert np.array_equal(recv[d].view(torch.uint8).cpu().numpy().reshape(-1), rrecv[d])
+    rst, rcomb = ref.moe_combine_return(W, T, k, E, H, cnt.cpu().numpy(), ids_h,
+                                        [p.cpu().numpy() for p in perm],
+                                        [x.view(torch.int16).cpu().numpy().view(np.uint16)
+                                         for x in recv], w_h, 1)
+    assert rst == 0
+    for s in range(W):
+        assert np.array_equal(comb[s].view(torch.int16).cpu().numpy().view(np.uint16), rcomb[s])
+        assert torch.equal(home[s].view(torch.int16),
+                           tok[s].view(torch.int16).repeat_interleave(k, dim=0))
+    outs = recv + perm + comb + home + [S, cnt, boff]
+    want = [x.clone() for x in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        trip()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            trip()
+    torch.cuda.synchronize()
+
+    def reset():
+        for x in outs:
+            x.zero_()
+        status.zero_()
+
+    _replay_and_check(graph, lambda: outs, want, reset, _noise)
     assert int(status.item()) == 0
