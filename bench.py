@@ -926,12 +926,14 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        # the path copies the payload bit for bit and computes only int64
+        # offsets: its arithmetic is on bytes; the payload itself is bf16
+        "dtype": "u8",
         "data": "synthetic",
         "config": {"workload": "a2av W=4 virtual ranks x 32 MiB/rank (4096 rows x 4096 bf16), "
                                "uniform multinomial splits; step = splits exchange + offsets + "
                                "copy in one a2av_all_to_all_vdev call",
-                   "W": 4, "rows_per_rank": 4096, "row_bytes": 8192,
+                   "W": 4, "rows_per_rank": 4096, "row_bytes": 8192, "payload": "bf16",
                    "rotating_sets": args.sets,
                    "frac_of_hbm_peak": round(main_res["step_gbs"] / HBM_PEAK_GBS, 4),
                    "three_call_step_gbs": round(three["step_gbs"], 1),
