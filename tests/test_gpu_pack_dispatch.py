@@ -128,6 +128,7 @@ SHAPES = [
     (2, 20, 64, 128, 16, True, 0),     # k = 64, the most a wave holds
     (64, 8, 2, 128, 16, False, 0),     # 64 ranks
     (4, 0, 2, 8, 16, False, 0),        # no tokens
+    (2, 40, 8, 4096, 32, False, 0),    # the most experts a plan holds
 ]
 
 
@@ -372,6 +373,7 @@ COMBINE_SHAPES = [
     (1, 20, 4, 5, 1000, False, 0),     # a clamped last chunk
     (5, 30, 12, 10, 8, False, 0),      # k = 12: two slot groups
     (2, 0, 2, 8, 16, False, 0),        # no tokens
+    (2, 30, 8, 4096, 64, False, 0),    # the most experts a plan holds
 ]
 
 
