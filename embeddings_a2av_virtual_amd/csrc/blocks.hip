@@ -1,9 +1,11 @@
 // blocks.hip — block-permutation copies next to the a2av (gfx950): the
-// receive-side expert regroup after the MoE dispatch, and the bucketing of
-// jagged embedding keys by owning rank before the key exchange.
+// receive-side expert regroup after the MoE dispatch, the dispatch and the
+// regroup as one copy (grouped dispatch), the bucketing of jagged embedding
+// keys by owning rank, and the bucketing with both key exchanges in one call.
 //
-// Both reorder whole runs of rows ("blocks") inside each virtual rank. A
-// planning kernel writes, per rank, the blocks in destination order:
+// All of them move whole runs of rows ("blocks"): inside each virtual rank,
+// or, with a source rank recorded per block, across ranks. A planning kernel
+// writes, per destination rank, the blocks in destination order:
 //   dst_start[r][b]  first destination row of block b (exclusive scan, the
 //                    rank's total at b = B)
 //   src_start[r][b]  first source row of block b
@@ -24,7 +26,6 @@
 #include "common.hpp"
 
 namespace a2av {
-
 
 struct BlockArgs {
     const unsigned char *in[A2AV_MAX_W];
@@ -123,10 +124,6 @@ __global__ __launch_bounds__(256) void k_block_copy(const BlockArgs a) {
     }
 }
 
-// ------------------------------------------------------------ block scans
-// Exclusive scans of two sequences at once over a 1024-thread block: each
-// thread contributes its sums (va, vb) and gets the sums of the threads
-// before it; ta, tb receive the block totals.
 // ------------------------------------------------------------ expert regroup plan
 struct RegroupPlanArgs {
     const int64_t *counts;    // [W][E]
@@ -481,7 +478,6 @@ struct GroupedArgs {
     int32_t *rank;            // [W][E]
     int32_t *bits;            // [W]
     int64_t *expert_offsets;  // [W][P + 1]
-    int32_t *check_word;      // cleared by the backward plan when set (combine)
     const int32_t *status;
     int W;
     int E;
@@ -623,159 +619,6 @@ __global__ __launch_bounds__(kPlanThreads) void k_grouped_plan_bwd(const Grouped
     if (tid == 0) {
         dst[E] = ytot;
         a.bits[s] = sbits | (ytot > a.cap[s] ? A2AV_ST_RECV_OVERFLOW : 0);
-        if (s == 0 && a.check_word) *a.check_word = 0;
-    }
-}
-
-// ------------------------------------------------------------ combine from the expert side
-// The gate-weighted combine (as moe_combine) reading every slot's row where
-// the grouped dispatch left it, on the expert side of the slot's owner. The
-// backward plan gives, per (source s, expert e), the pack position Y_s(e)
-// (its dst table) and the expert-side start (its src table).
-struct CombineGArgs {
-    const unsigned char *xs[A2AV_MAX_W];  // expert side of each owner
-    int64_t exp_rows[A2AV_MAX_W];
-    const int32_t *ids[A2AV_MAX_W];
-    const int64_t *perm[A2AV_MAX_W];
-    const float *w[A2AV_MAX_W];
-    unsigned char *out[A2AV_MAX_W];
-    const int64_t *counts;  // [W][E]
-    const int64_t *dst;     // [W][E + 1] pack positions (plan)
-    const int64_t *src;     // [W][E] expert-side starts (plan)
-    const int32_t *bits;    // [W] plan bits
-    int32_t *check_word;
-    int64_t *xrow;          // [W][T*k] each slot's row at its owner
-    int32_t *status;
-    int64_t T;
-    int64_t H;
-    int k;
-    int E;
-    int W;
-};
-
-// One thread per (slot, source): the slot's id in range, its pack row inside
-// its expert's block, and the row it occupies at the owner.
-__global__ __launch_bounds__(256) void k_combine_grouped_check(const CombineGArgs a) {
-    const int s = blockIdx.y;
-    const int64_t Q = a.T * a.k;
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    int bad = 0;
-    if (q < Q) {
-        const int32_t e = a.ids[s][q];
-        if (e < 0 || e >= a.E) {
-            bad = A2AV_ST_BAD_EXPERT;
-        } else {
-            const int64_t p = a.perm[s][q];
-            const int64_t y = a.dst[(int64_t)s * (a.E + 1) + e];
-            const int64_t n = a.counts[(int64_t)s * a.E + e];
-            if (p < y || p - y >= n) bad = A2AV_ST_BAD_PERM;
-            else a.xrow[(int64_t)s * Q + q] = a.src[(int64_t)s * a.E + e] + (p - y);
-        }
-    }
-    const int b = wave_or(bad);
-    if (b && (threadIdx.x & (kWave - 1)) == 0) atomicOr(a.check_word, b);
-}
-
-// One wave per (source, token, 512 elements), as k_moe_combine: scalar loads
-// of the slots' ids and rows, each row base in scalar registers.
-template <bool SNT>
-__global__ __launch_bounds__(256) void k_moe_combine_grouped(const CombineGArgs a, uint64_t nchunk) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const uint64_t wpb = blockDim.x / kWave;
-    const uint32_t wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const uint64_t gw = (uint64_t)blockIdx.x * wpb + wid;
-    const int W = a.W, k = a.k, P = a.E / a.W;
-    if (*(const const_i32 *)a.status) return;  // this op's earlier kernels never write it
-    const int32_t pb = wave_or(lane < W ? a.bits[lane] : 0);
-    const int32_t cw = *(const const_i32 *)a.check_word;
-    if (pb || cw) {
-        // bad counts stop everything; otherwise every failing check is reported
-        if (gw == 0 && lane == 0) atomicOr(a.status, (pb & A2AV_ST_BAD_SPLIT) ? A2AV_ST_BAD_SPLIT : (pb | cw));
-        return;
-    }
-    const uint64_t nwork = (uint64_t)W * (uint64_t)a.T * nchunk;
-    const uint64_t rowb = (uint64_t)a.H * 2;
-    const uint64_t nv = (uint64_t)a.H / 8;
-    const int64_t Q = a.T * k;
-    for (uint64_t wk = gw; wk < nwork; wk += (uint64_t)gridDim.x * wpb) {
-        const uint64_t tok = wk / nchunk;
-        const uint64_t c = wk - tok * nchunk;
-        const int s = (int)(tok / (uint64_t)a.T);
-        const int64_t t = (int64_t)(tok - (uint64_t)s * (uint64_t)a.T);
-        const const_i64 *xr = (const const_i64 *)(a.xrow + (int64_t)s * Q + t * k);
-        const const_i32 *ip = (const const_i32 *)(a.ids[s] + t * k);
-        const const_i32 *wp = (const const_i32 *)(a.w[s] + t * k);
-        uint64_t i = c * kWave + lane;
-        i = i < nv ? i : nv - 1;  // clamped lanes redo the last vector
-        const uint32_t off = (uint32_t)i * 16u;
-        float acc[8];
-#pragma unroll
-        for (int e = 0; e < 8; e++) acc[e] = 0.0f;
-        for (int j0 = 0; j0 < k; j0 += 8) {
-            u32x4 v[8];
-            float wt[8];
-#pragma unroll
-            for (int g = 0; g < 8; g++) {
-                const int j = j0 + g < k ? j0 + g : k - 1;
-                const int d = ip[j] / P;
-                const unsigned char *row = a.xs[d] + (uint64_t)xr[j] * rowb;
-                v[g] = ld<true>((const u32x4 *)(row + off));
-                wt[g] = __int_as_float(wp[j]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int g = 0; g < 8; g++) {
-                if (j0 + g < k) {
-                    acc[0] = __builtin_fmaf(wt[g], bf16_lo(v[g].x), acc[0]);
-                    acc[1] = __builtin_fmaf(wt[g], bf16_hi(v[g].x), acc[1]);
-                    acc[2] = __builtin_fmaf(wt[g], bf16_lo(v[g].y), acc[2]);
-                    acc[3] = __builtin_fmaf(wt[g], bf16_hi(v[g].y), acc[3]);
-                    acc[4] = __builtin_fmaf(wt[g], bf16_lo(v[g].z), acc[4]);
-                    acc[5] = __builtin_fmaf(wt[g], bf16_hi(v[g].z), acc[5]);
-                    acc[6] = __builtin_fmaf(wt[g], bf16_lo(v[g].w), acc[6]);
-                    acc[7] = __builtin_fmaf(wt[g], bf16_hi(v[g].w), acc[7]);
-                }
-            }
-        }
-        u32x4 o;
-        o.x = to_bf16(acc[0]) | (to_bf16(acc[1]) << 16);
-        o.y = to_bf16(acc[2]) | (to_bf16(acc[3]) << 16);
-        o.z = to_bf16(acc[4]) | (to_bf16(acc[5]) << 16);
-        o.w = to_bf16(acc[6]) | (to_bf16(acc[7]) << 16);
-        st<SNT>((u32x4 *)(a.out[s] + (uint64_t)t * rowb + off), o);
-    }
-}
-
-// Any row width or alignment: one wave per (source, token), one element per lane.
-__global__ __launch_bounds__(256) void k_moe_combine_grouped_any(const CombineGArgs a) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const uint64_t wpb = blockDim.x / kWave;
-    const uint32_t wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const uint64_t gw = (uint64_t)blockIdx.x * wpb + wid;
-    const int W = a.W, k = a.k, P = a.E / a.W;
-    if (*(const const_i32 *)a.status) return;
-    const int32_t pb = wave_or(lane < W ? a.bits[lane] : 0);
-    const int32_t cw = *(const const_i32 *)a.check_word;
-    if (pb || cw) {
-        if (gw == 0 && lane == 0) atomicOr(a.status, (pb & A2AV_ST_BAD_SPLIT) ? A2AV_ST_BAD_SPLIT : (pb | cw));
-        return;
-    }
-    const uint64_t H = (uint64_t)a.H;
-    const int64_t Q = a.T * k;
-    for (uint64_t wk = gw; wk < (uint64_t)W * (uint64_t)a.T; wk += (uint64_t)gridDim.x * wpb) {
-        const int s = (int)(wk / (uint64_t)a.T);
-        const int64_t t = (int64_t)(wk - (uint64_t)s * (uint64_t)a.T);
-        uint16_t *dst = (uint16_t *)a.out[s] + (uint64_t)t * H;
-        for (uint64_t h = lane; h < H; h += kWave) {
-            float acc = 0.0f;
-            for (int j = 0; j < k; j++) {
-                const int64_t q = t * k + j;
-                const uint16_t *row = (const uint16_t *)a.xs[a.ids[s][q] / P] +
-                                      (uint64_t)a.xrow[(int64_t)s * Q + q] * H;
-                acc = __builtin_fmaf(a.w[s][q], __uint_as_float((uint32_t)row[h] << 16), acc);
-            }
-            dst[h] = (uint16_t)to_bf16(acc);
-        }
     }
 }
 
@@ -1126,7 +969,6 @@ A2AV_API int moe_dispatch_grouped(int W, int E, size_t row_bytes, const int64_t 
     g.rank = rank;
     g.bits = bits;
     g.expert_offsets = expert_offsets;
-    g.check_word = nullptr;
     g.status = status;
     g.W = W;
     g.E = E;
@@ -1169,88 +1011,8 @@ A2AV_API int moe_combine_grouped(int W, int64_t T, int k, int E, int64_t H, cons
     const size_t need = moe_combine_grouped_workspace_bytes(W, T, k, E);
     if (need == 0 || !workspace || workspace_bytes < need) return A2AV_EARG;
     if ((uint64_t)H * 2 >= (1ull << 32)) return A2AV_EARG;  // 32-bit lane offsets in a row
-    GroupedArgs g;
-    CombineGArgs c;
-    std::memset(&g, 0, sizeof(g));
-    std::memset(&c, 0, sizeof(c));
-    bool aligned = (H % 8) == 0;
-    for (int r = 0; r < W; r++) {
-        if (exp_rows[r] < 0 || (uint64_t)exp_rows[r] > (uint64_t)INT64_MAX / (2 * (uint64_t)H))
-            return A2AV_EARG;
-        if (exp_rows[r] > 0 && !expert_side[r]) return A2AV_EARG;
-        if (T > 0 && (!ids[r] || !perm[r] || !weights[r] || !out[r])) return A2AV_EARG;
-        g.in_rows[r] = exp_rows[r];
-        g.cap[r] = INT64_MAX;  // the pack side is only read through perm
-        c.xs[r] = (const unsigned char *)expert_side[r];
-        c.exp_rows[r] = exp_rows[r];
-        c.ids[r] = ids[r];
-        c.perm[r] = perm[r];
-        c.w[r] = weights[r];
-        c.out[r] = (unsigned char *)out[r];
-        aligned = aligned && ((uintptr_t)expert_side[r] % 16 == 0) && ((uintptr_t)out[r] % 16 == 0);
-    }
-    // with no tokens the checks of the counts still run and report
-    // workspace: plan dst | src | rank | bits | expert offsets | check word | slot rows
-    unsigned char *ws = (unsigned char *)workspace;
-    const size_t P = (size_t)E / W;
-    size_t o = 0;
-    int64_t *dst = (int64_t *)(ws + o);
-    int64_t *src = dst + (size_t)W * (E + 1);
-    o += round256((size_t)W * (2 * (size_t)E + 1) * 8);
-    int32_t *rank = (int32_t *)(ws + o);
-    o += round256((size_t)W * E * 4);
-    int32_t *bits = (int32_t *)(ws + o);
-    o += round256((size_t)W * 4);
-    int64_t *eoff = (int64_t *)(ws + o);
-    o += round256((size_t)W * (P + 1) * 8);
-    int32_t *check = (int32_t *)(ws + o);
-    o += 256;
-    int64_t *xrow = (int64_t *)(ws + o);
-    g.counts = counts;
-    g.dst = dst;
-    g.src = src;
-    g.rank = rank;
-    g.bits = bits;
-    g.expert_offsets = eoff;
-    g.check_word = check;
-    g.status = status;
-    g.W = W;
-    g.E = E;
-    hipLaunchKernelGGL(k_grouped_plan_bwd, dim3(W), dim3(kPlanThreads), 0, stream, g);
-    c.counts = counts;
-    c.dst = dst;
-    c.src = src;
-    c.bits = bits;
-    c.check_word = check;
-    c.xrow = xrow;
-    c.status = status;
-    c.T = T;
-    c.H = H;
-    c.k = k;
-    c.E = E;
-    c.W = W;
-    const int64_t Q = T * k;
-    const int64_t cb = (Q + 255) / 256;
-    if (cb > INT32_MAX) return A2AV_EARG;
-    if (cb > 0)
-        hipLaunchKernelGGL(k_combine_grouped_check, dim3((unsigned)cb, W), dim3(256), 0, stream, c);
-    if (aligned) {
-        const uint64_t nchunk = ((uint64_t)H / 8 + kWave - 1) / kWave;
-        uint64_t blocks = ((uint64_t)W * (uint64_t)T * nchunk + 3) / 4;
-        if (blocks < 1) blocks = 1;  // one wave always runs, to report the checks
-        if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
-        // tuning knob: A2AV_COMBINE_STORE_NT (non-temporal stores, 0/1)
-        if (env_long("A2AV_COMBINE_STORE_NT", 1, 0, 1))
-            hipLaunchKernelGGL((k_moe_combine_grouped<true>), dim3((unsigned)blocks), dim3(256), 0,
-                               stream, c, nchunk);
-        else
-            hipLaunchKernelGGL((k_moe_combine_grouped<false>), dim3((unsigned)blocks), dim3(256), 0,
-                               stream, c, nchunk);
-    } else {
-        uint64_t blocks = ((uint64_t)W * (uint64_t)T + 3) / 4;
-        if (blocks < 1) blocks = 1;
-        if (blocks > (1u << 22)) blocks = 1u << 22;
-        hipLaunchKernelGGL(k_moe_combine_grouped_any, dim3((unsigned)blocks), dim3(256), 0, stream, c);
-    }
-    return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
+    // the expert side is moe_pack_dispatch's layout 1: the combine read at the
+    // owners in that order (its workspace never exceeds this one's)
+    return moe_combine_return(W, T, k, E, H, counts, ids, perm, expert_side, exp_rows, weights,
+                              out, 1, workspace, workspace_bytes, status, stream);
 }

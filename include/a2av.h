@@ -445,10 +445,11 @@ size_t moe_combine_grouped_workspace_bytes(int W, int64_t T, int k, int E);
  *                     A2AV_ST_BAD_EXPERT (an id outside [0, E)) and
  *                     A2AV_ST_BAD_PERM (a perm entry outside its expert's block
  *                     of the pack order). Nothing is written on failure.
- * Three kernels: the backward plan of moe_dispatch_grouped, a check that also
- * records every slot's row at its owner, and the combine (one wave per
- * (source, token, 512 elements), as moe_combine, 16-byte vectors when H % 8
- * == 0 and the bases are 16-byte aligned, else one element per lane).
+ * The expert side is moe_pack_dispatch's layout 1, so this runs as
+ * moe_combine_return with layout 1: a plan, a check that also records every
+ * slot's row address, and the combine (one wave per (source, token, 512
+ * elements), as moe_combine, 16-byte vectors when H % 8 == 0 and the bases
+ * are 16-byte aligned, else one element per lane).
  */
 int moe_combine_grouped(int W, int64_t T, int k, int E, int64_t H, const int64_t *counts,
                         const int32_t *const *ids, const int64_t *const *perm,
