@@ -129,6 +129,7 @@ SHAPES = [
     (64, 8, 2, 128, 16, False, 0),     # 64 ranks
     (4, 0, 2, 8, 16, False, 0),        # no tokens
     (2, 40, 8, 4096, 32, False, 0),    # the most experts a plan holds
+    (64, 6, 8, 4096, 16, True, 0),     # the most ranks and experts at once
 ]
 
 
@@ -374,6 +375,7 @@ COMBINE_SHAPES = [
     (5, 30, 12, 10, 8, False, 0),      # k = 12: two slot groups
     (2, 0, 2, 8, 16, False, 0),        # no tokens
     (2, 30, 8, 4096, 64, False, 0),    # the most experts a plan holds
+    (64, 5, 3, 4096, 8, False, 0),     # the most ranks and experts at once
 ]
 
 
