@@ -32,8 +32,10 @@
  *   - Device-side failures are reported through `status`, a caller-zeroed
  *     device int32. Kernels OR status bits into it. An op that finds the word
  *     nonzero on entry writes nothing, and an op that detects a failure writes
- *     no output byte (all-or-nothing), so a failed op poisons the rest of a
- *     sequence that shares the word. Read it after synchronising the stream.
+ *     no payload byte (all-or-nothing); on a capacity failure some ops still
+ *     write their splits, counts or offsets, as each call below states. A
+ *     failed op poisons the rest of a sequence that shares the word. Read it
+ *     after synchronising the stream.
  *   - Calls that overlap in time on buffers they share race; calls on
  *     disjoint buffers may run concurrently on different streams.
  */
@@ -247,9 +249,10 @@ int moe_pack_dispatch(int W, int64_t T, int k, int E, size_t row_bytes,
 size_t moe_unpack_return_workspace_bytes(int W, int E);
 
 /*
- * The inverse of moe_pack_dispatch: the return trip and the un-pack as one
- * step, out[s][q] = the row of slot q of source s, read from the receive
- * buffer of its owner in the given layout. Equal to the return a2av (splits
+ * The inverse of moe_pack_dispatch: the return trip of the MoE exchange on
+ * the page "[a2av] Improve tuning for 4 GPUs" (section "Change") and the
+ * un-pack as one step, out[s][q] = the row of slot q of source s, read from
+ * the receive buffer of its owner in the given layout. Equal to the return a2av (splits
  * O) followed by moe_unpack for layout 0, and to moe_dispatch_grouped
  * (direction 1) followed by moe_unpack for layout 1, without the returned
  * buffer.
@@ -279,8 +282,9 @@ size_t moe_combine_return_workspace_bytes(int W, int64_t T, int k, int E);
 
 /*
  * The gate-weighted combine (as moe_combine) read at the owners: the return
- * trip and the combine in one pass, for rows left by moe_pack_dispatch in
- * either layout. Equal to moe_unpack_return followed by moe_combine over the
+ * trip of the MoE exchange on the page "[a2av] Improve tuning for 4 GPUs"
+ * (section "Change") and the combine in one pass, for rows left by
+ * moe_pack_dispatch in either layout. Equal to moe_unpack_return followed by moe_combine over the
  * rows it brings home (slot t*k + j of token t), without writing them; for
  * layout 1 equal to moe_combine_grouped.
  *   expert_counts    device int64 [W][E] (moe_pack's)
@@ -301,9 +305,10 @@ int moe_combine_return(int W, int64_t T, int k, int E, int64_t H, const int64_t 
                        hipStream_t stream);
 
 /*
- * MoE un-pack after the return trip ("inverse combine" without weights):
- * out[r][q] = back[r][perm[r][q]] for q < T*k, i.e. every slot gets back the
- * row it was packed to. back is what the return a2av (splits O, the
+ * MoE un-pack after the return trip of the MoE exchange on the page "[a2av]
+ * Improve tuning for 4 GPUs" (section "Change"), the "inverse combine"
+ * without weights: out[r][q] = back[r][perm[r][q]] for q < T*k, i.e. every
+ * slot gets back the row it was packed to. back is what the return a2av (splits O, the
  * transpose of the dispatch splits) delivered to rank r.
  *   back[W], out[W]  device [T*k][row_bytes] per rank
  *   perm[W]          device int64 [T*k] per rank, from moe_pack
