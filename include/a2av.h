@@ -77,9 +77,10 @@ int a2av_abi_version(void);
 const char *a2av_strerror(int code);
 
 /*
- * Splits exchange: O[d][s] = S[s][d] (the output split matrix is the
- * transpose of the input splits; row d of O is what rank d receives from
- * each source).
+ * Splits exchange, the first step of the exchange timed on the page "[a2av]
+ * Improve tuning for 4 GPUs" (section "Problem"), as read above:
+ * O[d][s] = S[s][d] (the output split matrix is the transpose of the input
+ * splits; row d of O is what rank d receives from each source).
  *   W      1..A2AV_MAX_W
  *   S      device int64 [W][W], row s = rank s's split vector (rows per peer)
  *   O      device int64 [W][W], written
@@ -91,7 +92,8 @@ int a2av_exchange_splits(int W, const int64_t *S, int64_t *O, int32_t *status,
                          hipStream_t stream);
 
 /*
- * Offsets: send_off[s][d] = sum_{d'<d} S[s][d'] and recv_off[d][s] =
+ * Offsets, the second step of that exchange (same page and section, as read
+ * above): send_off[s][d] = sum_{d'<d} S[s][d'] and recv_off[d][s] =
  * sum_{s'<s} O[d][s'] (exclusive scans), with the row totals at index W.
  *   S, O      device int64 [W][W]
  *   send_off  device int64 [W][W+1], written
@@ -103,8 +105,9 @@ int a2av_offsets(int W, const int64_t *S, const int64_t *O, int64_t *send_off,
                  int64_t *recv_off, int32_t *status, hipStream_t stream);
 
 /*
- * Payload: for every (s, d), rows [send_off[s][d], +S[s][d]) of in[s] are
- * copied to out[d] at row recv_off[d][s]; rows are row_bytes wide and copied
+ * Payload, the third step of that exchange (same page, sections "Problem" and
+ * "Change", as read above): for every (s, d), rows [send_off[s][d],
+ * +S[s][d]) of in[s] are copied to out[d] at row recv_off[d][s]; rows are row_bytes wide and copied
  * bit-for-bit. Output bytes past recv_off[d][W] rows are not touched; input
  * rows past send_off[s][W] are not sent.
  *   row_bytes     >= 1, same for every rank; any alignment is accepted, the
@@ -143,8 +146,9 @@ int a2av_copy(int W, size_t row_bytes, const void *const *in,
               int32_t *status, hipStream_t stream);
 
 /*
- * The whole a2av in one call: a2av_exchange_splits, a2av_offsets and
- * a2av_copy with the same arguments, same outputs and same status bits
+ * The whole a2av in one call, nvshmem_all_to_all_vdev of the page "[a2av]
+ * Improve tuning for 4 GPUs" (section "Problem") as read above:
+ * a2av_exchange_splits, a2av_offsets and a2av_copy with the same arguments, same outputs and same status bits
  * (BAD_SPLIT alone stops it before O and the offsets are written; SEND_OVERRUN
  * / RECV_OVERFLOW leave O and the offsets written and no payload byte).
  *   S                      device int64 [W][W] (input splits)
