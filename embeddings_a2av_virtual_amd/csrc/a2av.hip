@@ -346,23 +346,14 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
     }
     uint64_t gso = 0, gro = 0, gso_t = 0, gro_t = 0;  // given send_off[s][d], recv_off[d][s], totals
     if constexpr (MODE == kCopyGiven) {
-        const const_i64 *soc = (const const_i64 *)a.send_off;
-        const const_i64 *roc = (const const_i64 *)a.recv_off;
-        // one row of each matrix per iteration keeps the scalar registers in budget
-#pragma unroll 1
-        for (int r = 0; r < W; r++) {
-#pragma unroll
-            for (int c = 0; c <= W; c++) {
-                const uint64_t x = (uint64_t)soc[r * (W + 1) + c];  // send_off[s=r][d=c]
-                const uint64_t y = (uint64_t)roc[r * (W + 1) + c];  // recv_off[d=r][s=c]
-                if (c < W) {
-                    gso = lane == r * W + c ? x : gso;
-                    gro = lane == c * W + r ? y : gro;
-                } else {
-                    gso_t = lane == r * W + W - 1 ? x : gso_t;
-                    gro_t = lane == (W - 1) * W + r ? y : gro_t;
-                }
-            }
+        // lane s*W + d fetches its own entries: four vector loads in flight
+        // together, one round trip for the whole wave
+        if (lane < N) {
+            const int s = lane / W, d = lane - (lane / W) * W;
+            gso = (uint64_t)a.send_off[s * (W + 1) + d];
+            gro = (uint64_t)a.recv_off[d * (W + 1) + s];
+            if (d == W - 1) gso_t = (uint64_t)a.send_off[s * (W + 1) + W];
+            if (s == W - 1) gro_t = (uint64_t)a.recv_off[d * (W + 1) + W];
         }
     }
     if (st0) return;
