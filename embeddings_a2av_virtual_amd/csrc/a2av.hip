@@ -424,8 +424,17 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
     const uint64_t B = total * R;
     const uint64_t piece = a.piece;
     for (uint64_t p = gw; p * piece < B; p += TW) {
-        const uint64_t lo = p * piece;
-        const uint64_t hi = lo + piece < B ? lo + piece : B;
+        uint64_t lo = p * piece;
+        uint64_t hi = lo + piece < B ? lo + piece : B;
+        if constexpr (!ALIGNED) {
+            // rows that are not 16-byte multiples: cut where the destination
+            // address is 128-byte aligned, so no cache line is split between
+            // two waves' partial writes (neighbouring pieces move the same
+            // boundary, so the pieces still tile the space)
+            lo = snap_to_line(lo, B, pre * R, lane, W, a.out);
+            hi = snap_to_line(hi, B, pre * R, lane, W, a.out);
+            if (lo >= hi) continue;
+        }
         // last destination starting at or before lo (lanes 0..W-1 hold pre[d]),
         // then the last source chunk inside it starting at or before lo
         const uint64_t mask_d = __ballot(lane < W && pre * R <= lo);

@@ -93,7 +93,14 @@ __global__ __launch_bounds__(256) void k_block_copy(const BlockArgs a) {
     const uint64_t piece = a.piece;
     for (uint64_t p = gw; p * piece < total; p += TW) {
         uint64_t x = p * piece;
-        const uint64_t hi = x + piece < total ? x + piece : total;
+        uint64_t hi = x + piece < total ? x + piece : total;
+        if constexpr (!ALIGNED) {
+            // cut where the destination address is 128-byte aligned, so no
+            // cache line is split between two waves' partial writes
+            x = snap_to_line(x, total, base, lane, W, a.out);
+            hi = snap_to_line(hi, total, base, lane, W, a.out);
+            if (x >= hi) continue;
+        }
         while (x < hi) {
             // last rank starting at or before x: empty ranks share the base of
             // the next one, so the highest match is the one holding x

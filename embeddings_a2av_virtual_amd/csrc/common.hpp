@@ -248,6 +248,22 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// ------------------------------------------------------------ piece boundaries
+// A flat position of the destination space (destination d's bytes start at
+// start_d, held by lane d) moved up to the next 128-byte boundary of its
+// destination's address, or to that destination's end; 0 and B stay put.
+__device__ __forceinline__ uint64_t snap_to_line(uint64_t x, uint64_t B, uint64_t start_d,
+                                                 int lane, int W, unsigned char *const *out) {
+    if (x == 0 || x >= B) return x < B ? x : B;
+    const uint64_t md = __ballot(lane < W && start_d <= x);
+    const int d = 63 - __clzll(md);
+    const uint64_t db = readlane_u64(start_d, d);
+    const uint64_t de = d + 1 < W ? readlane_u64(start_d, d + 1) : B;
+    const uint64_t addr = (uint64_t)(uintptr_t)out[d] + (x - db);
+    const uint64_t up = ((addr + 127) & ~(uint64_t)127) - addr;
+    return x + up < de ? x + up : de;
+}
+
 // ------------------------------------------------------------ block scans
 // Plans run one 1024-thread workgroup per rank, each thread owning up to
 // kPlanPer consecutive entries (4096 per rank at most).
