@@ -237,10 +237,22 @@ __global__ __launch_bounds__(256) void k_bucket_sums(const BucketArgs a) {
     const int32_t *L = a.lengths[r] + (int64_t)t * a.batch;
     int64_t s = 0;
     int n = 0;
-    for (int64_t i = tid; i < a.batch; i += 256) {
-        const int32_t v = L[i];
-        s += v;
-        n |= v < 0;
+    if ((a.batch & 3) == 0 && ((uintptr_t)L & 15) == 0) {
+        // four lengths per load, several loads in flight per thread
+        const u32x4 *L4 = (const u32x4 *)L;
+        const int64_t n4 = a.batch / 4;
+#pragma unroll 4
+        for (int64_t i = tid; i < n4; i += 256) {
+            const u32x4 v = L4[i];
+            s += (int64_t)(int32_t)v.x + (int32_t)v.y + (int32_t)v.z + (int32_t)v.w;
+            n |= (int32_t)(v.x | v.y | v.z | v.w) < 0;
+        }
+    } else {
+        for (int64_t i = tid; i < a.batch; i += 256) {
+            const int32_t v = L[i];
+            s += v;
+            n |= v < 0;
+        }
     }
     s = wave_incl_scan(s);
     n = __ballot(n) != 0;
