@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
         v = lane == i ? x : v;
     }
     uint64_t gso = 0, gro = 0, gso_t = 0, gro_t = 0;  // given send_off[s][d], recv_off[d][s], totals
-    if constexpr (MODE == kCopyGiven) {
+    auto load_given = [&]() {
         // lane s*W + d fetches its own entries: four vector loads in flight
         // together, one round trip for the whole wave
         if (lane < N) {
@@ -355,7 +355,10 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
             if (d == W - 1) gso_t = (uint64_t)a.send_off[s * (W + 1) + W];
             if (s == W - 1) gro_t = (uint64_t)a.recv_off[d * (W + 1) + W];
         }
-    }
+    };
+    // copy mode with aligned rows: loaded behind the wave's first payload
+    // loads (see the gate below)
+    if constexpr (MODE == kCopyGiven && !ALIGNED) load_given();
     if (st0) return;
 
     // ---- offsets from S, in registers (wrapping arithmetic, as the checks
@@ -387,15 +390,35 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
 
     // ---- checks, identical in every wave
     int bits = __ballot(act && split_invalid((int64_t)v)) ? A2AV_ST_BAD_SPLIT : 0;
-    if constexpr (MODE == kCopyGiven) {
+    // copy mode: the given offsets and totals against S and the buffers. With
+    // aligned rows the offsets are loaded and checked once the wave's first
+    // payload loads are in flight (a gate before its first store), so the
+    // check costs no round trip of its own; otherwise it runs here.
+    auto given_bits = [&]() -> int {
+        int b = bits;
         const bool bad_off = act && (gso != so || gro != ro || (d_ == W - 1 && gso_t != inc) ||
                                      (s_ == W - 1 && gro_t != inc2));
-        if (__ballot(bad_off)) bits |= A2AV_ST_BAD_OFFSETS;
+        if (__ballot(bad_off)) b |= A2AV_ST_BAD_OFFSETS;
 #pragma unroll
         for (int r = 0; r < W; r++) {
-            if ((int64_t)readlane_u64(gso_t, r * W + W - 1) > a.in_rows[r]) bits |= A2AV_ST_SEND_OVERRUN;
-            if ((int64_t)readlane_u64(gro_t, (W - 1) * W + r) > a.cap[r]) bits |= A2AV_ST_RECV_OVERFLOW;
+            if ((int64_t)readlane_u64(gso_t, r * W + W - 1) > a.in_rows[r]) b |= A2AV_ST_SEND_OVERRUN;
+            if ((int64_t)readlane_u64(gro_t, (W - 1) * W + r) > a.cap[r]) b |= A2AV_ST_RECV_OVERFLOW;
         }
+        return b;
+    };
+    constexpr bool kDeferred = MODE == kCopyGiven && ALIGNED;
+    bool pending = kDeferred;  // the gate has not run yet
+    auto gate = [&]() -> bool {
+        if (!pending) return true;
+        pending = false;
+        load_given();
+        const int b = given_bits();
+        if (b && gw == 0 && lane == 0) atomicOr(a.status, b);
+        return b == 0;
+    };
+    if constexpr (MODE == kCopyGiven) {
+        if (kDeferred && bits) load_given();
+        if (!kDeferred || bits) bits = given_bits();
     } else {
 #pragma unroll
         for (int r = 0; r < W; r++) {
@@ -455,13 +478,23 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
                 const uint64_t e = hi < F + L ? hi : F + L;
                 const uint64_t off = x - F;
                 const uint64_t s0 = readlane_u64(so, li);
+                // d and s are wave-uniform; saying so keeps the argument
+                // reads below scalar (a vector read would wait behind the
+                // payload traffic of older waves on the CU)
+                const int du = __builtin_amdgcn_readfirstlane(d);
+                const int su = __builtin_amdgcn_readfirstlane(s);
                 // validated offsets always pass; the check keeps every access
                 // inside the caller's buffers regardless
-                if ((int64_t)(r0 + n) <= a.cap[d] && (int64_t)(s0 + n) <= a.in_rows[s]) {
-                    unsigned char *dst = a.out[d] + r0 * R + off;
-                    const unsigned char *src = a.in[s] + s0 * R + off;
-                    if constexpr (ALIGNED) wave_copy16<U>(dst, src, e - x, lane);
-                    else wave_copy_any<U>(dst, src, e - x, lane);
+                if ((int64_t)(r0 + n) <= a.cap[du] && (int64_t)(s0 + n) <= a.in_rows[su]) {
+                    unsigned char *dst = a.out[du] + r0 * R + off;
+                    const unsigned char *src = a.in[su] + s0 * R + off;
+                    if constexpr (kDeferred) {
+                        if (!wave_copy16<U>(dst, src, e - x, lane, gate)) return;
+                    } else if constexpr (ALIGNED) {
+                        wave_copy16<U>(dst, src, e - x, lane);
+                    } else {
+                        wave_copy_any<U>(dst, src, e - x, lane);
+                    }
                 }
                 x = e;
             }
@@ -471,6 +504,10 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
                 if (d < W) dbase = readlane_u64(pre, d) * R;
             }
         }
+    }
+    // a wave that copied nothing still reports the verdict from wave 0
+    if constexpr (kDeferred) {
+        if (pending && gw == 0) gate();
     }
 }
 

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/a2av.h"
 
 #define A2AV_API extern "C" __attribute__((visibility("default")))
@@ -63,6 +65,12 @@ __device__ __forceinline__ void st(V *p, V v) {
     else *p = v;
 }
 
+// A check run once by copy_elems between the loads and the stores of its
+// first step (see below); the default lets every store through.
+struct NoGate {
+    __device__ __forceinline__ bool operator()() const { return true; }
+};
+
 // Cooperative copy of nv elements of V by BS threads: thread `tid` moves
 // elements tid, tid + BS, ...; each step issues U loads before their U
 // stores, so every lane keeps U accesses in flight. Full steps carry no
@@ -70,15 +78,29 @@ __device__ __forceinline__ void st(V *p, V v) {
 // of branching: a lane past the end re-copies the last element, and every
 // such lane writes the same bytes to the same place. (Guards in this loop
 // make the compiler wait for each load before the next one.)
-template <typename V, int BS, int U, bool NT>
-__device__ __forceinline__ void copy_elems(V *__restrict__ d, const V *__restrict__ s,
-                                           uint64_t nv, int tid) {
+//
+// With a gate, the first step's loads are issued before the gate runs and
+// nothing is stored unless it returns true (then the copy returns false);
+// a check that waits on loads of its own thus overlaps the first payload
+// loads. Every thread must get the same verdict.
+template <typename V, int BS, int U, bool NT, typename Gate = NoGate>
+__device__ __forceinline__ bool copy_elems(V *__restrict__ d, const V *__restrict__ s,
+                                           uint64_t nv, int tid, Gate gate = Gate()) {
+    constexpr bool kGated = !std::is_same<Gate, NoGate>::value;
     constexpr uint64_t step = (uint64_t)BS * U;
+    bool first = kGated;
     uint64_t base = 0;
     for (; base + step <= nv; base += step) {
         V r[U];
 #pragma unroll
         for (int u = 0; u < U; u++) r[u] = ld<NT>(s + base + (uint64_t)u * BS + tid);
+        if constexpr (kGated) {
+            if (first) {
+                __builtin_amdgcn_sched_barrier(0);
+                first = false;
+                if (!gate()) return false;
+            }
+        }
 #pragma unroll
         for (int u = 0; u < U; u++) st<NT>(d + base + (uint64_t)u * BS + tid, r[u]);
     }
@@ -89,12 +111,23 @@ __device__ __forceinline__ void copy_elems(V *__restrict__ d, const V *__restric
             const uint64_t i = base + (uint64_t)u * BS + tid;
             r[u] = ld<NT>(s + (i < nv ? i : nv - 1));
         }
+        if constexpr (kGated) {
+            if (first) {
+                __builtin_amdgcn_sched_barrier(0);
+                first = false;
+                if (!gate()) return false;
+            }
+        }
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const uint64_t i = base + (uint64_t)u * BS + tid;
             st<NT>(d + (i < nv ? i : nv - 1), r[u]);
         }
     }
+    if constexpr (kGated) {
+        if (first) return gate();  // nothing to copy: the verdict still counts
+    }
+    return true;
 }
 
 // Block-cooperative copy of n bytes between non-overlapping device ranges.
@@ -231,10 +264,11 @@ __device__ __forceinline__ void wave_copy_any(unsigned char *dst, const unsigned
 }
 
 // Wave-cooperative copy of n bytes, n a multiple of 16, both ends 16-aligned.
-template <int U>
-__device__ __forceinline__ void wave_copy16(unsigned char *dst, const unsigned char *src,
-                                            uint64_t n, int lane) {
-    copy_elems<u32x4, kWave, U, true>((u32x4 *)dst, (const u32x4 *)src, n / 16, lane);
+// With a gate, as copy_elems: false (and nothing stored) when it refuses.
+template <int U, typename Gate = NoGate>
+__device__ __forceinline__ bool wave_copy16(unsigned char *dst, const unsigned char *src,
+                                            uint64_t n, int lane, Gate gate = Gate()) {
+    return copy_elems<u32x4, kWave, U, true>((u32x4 *)dst, (const u32x4 *)src, n / 16, lane, gate);
 }
 
 // ------------------------------------------------------------ wave-uniform values
