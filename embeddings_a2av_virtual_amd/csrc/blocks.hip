@@ -41,6 +41,7 @@ struct BlockArgs {
     uint64_t piece;
     int W;
     int B;
+    uint32_t Rr[A2AV_MAX_W];   // row bytes per rank (k_block_copy<.., true> only)
 };
 
 // Largest i in [0, n) with v[i] <= key, for v non-decreasing with v[0] <= key
@@ -63,14 +64,17 @@ __device__ __forceinline__ int find_last_le(const int64_t *v, int n, uint64_t ke
     return lo + 63 - __clzll(m);
 }
 
-template <int U, bool ALIGNED>
+// MIXED: every rank has its own row size (Rr), so two exchanges with
+// different rows (keys and lengths) run as one launch over 2W ranks.
+template <int U, bool ALIGNED, bool MIXED = false>
 __global__ __launch_bounds__(256) void k_block_copy(const BlockArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint64_t wpb = blockDim.x / kWave;
     const uint64_t gw = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave;
     const uint64_t TW = (uint64_t)gridDim.x * wpb;
     const int W = a.W, B = a.B;
-    const uint64_t R = a.R;
+    // lane r: rank r's row bytes
+    const uint64_t Rl = MIXED ? (lane < W ? (uint64_t)a.Rr[lane] : 1) : a.R;
 
     const int32_t st0 = *(const const_i32 *)a.status;
     int32_t rb = 0;
@@ -86,7 +90,7 @@ __global__ __launch_bounds__(256) void k_block_copy(const BlockArgs a) {
         return;
     }
     // lane r: bytes of rank r and where they start in the flat space
-    const uint64_t bytes = rows * R;
+    const uint64_t bytes = rows * Rl;
     const uint64_t incl = wave_incl_scan_u64(bytes);
     const uint64_t base = incl - bytes;
     const uint64_t total = readlane_u64(incl, kWave - 1);
@@ -110,6 +114,7 @@ __global__ __launch_bounds__(256) void k_block_copy(const BlockArgs a) {
             const uint64_t rend = rbase + readlane_u64(bytes, d);
             const uint64_t xr = x - rbase;
             const uint64_t hr = (hi < rend ? hi : rend) - rbase;
+            const uint64_t R = MIXED ? readlane_u64(Rl, d) : a.R;
             const int64_t *ds = a.dst_start + (uint64_t)d * (B + 1);
             const int b = find_last_le(ds, B, xr / R, lane);
             if (b < 0) return;  // not a valid plan
@@ -372,8 +377,8 @@ struct KeyxArgs {
     int64_t *ksrc;           // [W][B]
     int64_t *ldst;           // [W][B + 1] lengths plan
     int64_t *lsrc;           // [W][B]
-    int32_t *rank;           // [W][B] source of each block
-    int32_t *bits;           // [W]
+    int32_t *rank;           // [W][B] source of each block ([2W][B] when merged)
+    int32_t *bits;           // [W] ([2W] when merged)
     int64_t *split_keys;     // [W][W] outputs
     int64_t *split_lengths;  // [W][W]
     int64_t *recv_off;       // [W][W + 1]
@@ -383,6 +388,8 @@ struct KeyxArgs {
     int NT;
     int cmax;
     int B;
+    int merged;  // 1: the plan also serves one block copy over 2W ranks,
+                 // receiver d's lengths being rank W + d (source s: W + s)
 };
 
 __global__ __launch_bounds__(kPlanThreads) void k_keyx_plan(const KeyxArgs a) {
@@ -400,6 +407,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_keyx_plan(const KeyxArgs a) {
     }
     __syncthreads();
     if (poisoned) return;
+    if (a.merged && tid == 0) a.bits[W + d] = 0;  // the plan's verdict sits in bits[d]
     // every source's table-order scan (one wave per source): where the tables
     // d owns start, and the source's own checks (as its bucketing makes them)
     for (int s = wave; s < W; s += NWV) {
@@ -457,6 +465,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_keyx_plan(const KeyxArgs a) {
             a.ksrc[(int64_t)d * B + b] = real ? tst[s * cmax + i] : 0;
             a.lsrc[(int64_t)d * B + b] = real ? (int64_t)(d + i * W) * a.batch : 0;
             a.rank[(int64_t)d * B + b] = s;
+            if (a.merged) a.rank[(int64_t)(W + d) * B + b] = W + s;
             if (i == 0) sstart[s] = ek;
         }
         ek += nk[u];
@@ -672,6 +681,18 @@ static void launch_block_copy(const BlockArgs &a, uint64_t bmax, bool aligned, h
     }
 }
 
+// The same with a row size per rank (a.Rr), any alignment.
+static void launch_block_copy_mixed(const BlockArgs &a, uint64_t bmax, hipStream_t st) {
+    int unroll;
+    uint64_t piece;
+    piece_policy(bmax, &unroll, &piece);
+    BlockArgs b = a;
+    b.piece = piece;
+    const int grid = copy_grid(bmax, piece);
+    if (unroll == 16) hipLaunchKernelGGL((k_block_copy<16, false, true>), dim3(grid), dim3(256), 0, st, b);
+    else hipLaunchKernelGGL((k_block_copy<8, false, true>), dim3(grid), dim3(256), 0, st, b);
+}
+
 static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 }  // namespace a2av
@@ -829,7 +850,7 @@ A2AV_API size_t keys_exchange_workspace_bytes(int W, int n_tables) {
     const size_t cmax = ((size_t)n_tables + W - 1) / W;
     const size_t B = (size_t)W * cmax;
     const size_t i64s = (size_t)W * n_tables + 4 * (size_t)W * B + 2 * (size_t)W;
-    return round256(i64s * 8) + round256((size_t)W * B * 4) + round256((size_t)W * 4);
+    return round256(i64s * 8) + round256(2 * (size_t)W * B * 4) + round256(2 * (size_t)W * 4);
 }
 
 A2AV_API int keys_exchange(int W, int n_tables, int64_t batch, const int32_t *const *lengths,
@@ -882,17 +903,20 @@ A2AV_API int keys_exchange(int W, int n_tables, int64_t batch, const int32_t *co
         lout += (uint64_t)lengths_cap[r];
         lal = lal && ((uintptr_t)lengths[r] % 16 == 0) && ((uintptr_t)lengths_out[r] % 16 == 0);
     }
-    // workspace: tk | kdst | ksrc | ldst | lsrc | src rank | bits
+    // workspace: tk | kdst | ldst | ksrc | lsrc | src rank [2W][B] | bits [2W].
+    // The keys and lengths plans sit back to back, so that with 2W ranks at
+    // most one block copy moves both: receiver d's lengths are rank W + d.
     int64_t *ws = (int64_t *)workspace;
     const size_t nt = (size_t)n_tables, BB = (size_t)B;
     int64_t *tk = ws;
     int64_t *kdst = tk + (size_t)W * nt;
-    int64_t *ksrc = kdst + (size_t)W * (BB + 1);
-    int64_t *ldst = ksrc + (size_t)W * BB;
-    int64_t *lsrc = ldst + (size_t)W * (BB + 1);
+    int64_t *ldst = kdst + (size_t)W * (BB + 1);
+    int64_t *ksrc = ldst + (size_t)W * (BB + 1);
+    int64_t *lsrc = ksrc + (size_t)W * BB;
     const size_t i64s = (size_t)W * nt + 4 * (size_t)W * BB + 2 * (size_t)W;
     int32_t *rank = (int32_t *)((unsigned char *)workspace + round256(i64s * 8));
-    int32_t *bits = (int32_t *)((unsigned char *)rank + round256((size_t)W * BB * 4));
+    int32_t *bits = (int32_t *)((unsigned char *)rank + round256(2 * (size_t)W * BB * 4));
+    const bool merged = 2 * W <= A2AV_MAX_W;
     b.tk = tk;
     b.batch = batch;
     b.W = W;
@@ -913,6 +937,7 @@ A2AV_API int keys_exchange(int W, int n_tables, int64_t batch, const int32_t *co
     x.NT = n_tables;
     x.cmax = cmax;
     x.B = B;
+    x.merged = merged ? 1 : 0;
     if (n_tables > 0)
         hipLaunchKernelGGL(k_bucket_sums, dim3(n_tables, W), dim3(256), 0, stream, b);
     hipLaunchKernelGGL(k_keyx_plan, dim3(W), dim3(kPlanThreads), 0, stream, x);
@@ -935,8 +960,24 @@ A2AV_API int keys_exchange(int W, int n_tables, int64_t batch, const int32_t *co
     const uint64_t kmax = (kin < kout ? kin : kout) * 8;
     const uint64_t lin = (uint64_t)W * (uint64_t)nl;
     const uint64_t lmax = (lin < lout ? lin : lout) * 4;
-    launch_block_copy(ck, kmax, false, stream);  // also reports the planning bits
-    if (lmax > 0) launch_block_copy(cl, lmax, lal, stream);
+    if (merged) {
+        // one launch: ranks 0..W-1 move keys (8-byte rows), ranks W..2W-1
+        // lengths (4-byte rows); it also reports the planning bits
+        BlockArgs c = ck;
+        c.W = 2 * W;
+        for (int r = 0; r < W; r++) {
+            c.in[W + r] = cl.in[r];
+            c.out[W + r] = cl.out[r];
+            c.in_rows[W + r] = cl.in_rows[r];
+            c.cap[W + r] = cl.cap[r];
+            c.Rr[r] = 8;
+            c.Rr[W + r] = 4;
+        }
+        launch_block_copy_mixed(c, kmax + lmax, stream);
+    } else {
+        launch_block_copy(ck, kmax, false, stream);  // also reports the planning bits
+        if (lmax > 0) launch_block_copy(cl, lmax, lal, stream);
+    }
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
 }
 

@@ -531,10 +531,11 @@ size_t keys_exchange_workspace_bytes(int W, int n_tables);
  *                   written; else A2AV_ST_RECV_OVERFLOW if a receiver lacks
  *                   room (its split columns and offsets are then not written,
  *                   those of the others are) and no payload; else everything.
- * Four kernels: per-(table, rank) key counts, a per-receiver plan (every
- * source's table scan, then the receiver's blocks in (source, table) order),
- * and a block copy each for keys and lengths that reads each source's arrays
- * in place.
+ * Three kernels up to W = 32: per-(table, rank) key counts, a per-receiver
+ * plan (every source's table scan, then the receiver's blocks in (source,
+ * table) order), and one block copy of keys and lengths together that reads
+ * each source's arrays in place. Above 32 ranks the keys and the lengths are
+ * two block copies.
  */
 int keys_exchange(int W, int n_tables, int64_t batch, const int32_t *const *lengths,
                   const int64_t *const *keys, const int64_t *n_keys,

@@ -203,6 +203,8 @@ def _compare_exchange(got, want, what=""):
 @pytest.mark.parametrize("W,NT,batch,pad", [
     (8, 26, 64, 0), (8, 26, 333, 0), (3, 7, 100, 4), (5, 2, 10, 0), (4, 0, 10, 0), (2, 3, 0, 0),
     (1, 5, 33, 0), (16, 300, 7, 0), (64, 100, 3, 0), (3, 4096, 2, 0),
+    # keys and lengths in one block copy over 2W ranks up to W = 32, two above
+    (32, 40, 5, 4), (33, 50, 4, 0),
 ])
 def test_keys_exchange_matches_oracle(ref, W, NT, batch, pad):
     _say("keys_exchange", W, NT, batch, pad)
