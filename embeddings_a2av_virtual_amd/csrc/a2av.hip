@@ -356,9 +356,13 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
             if (s == W - 1) gro_t = (uint64_t)a.recv_off[d * (W + 1) + W];
         }
     };
-    // copy mode with aligned rows: loaded behind the wave's first payload
-    // loads (see the gate below)
-    if constexpr (MODE == kCopyGiven && !ALIGNED) load_given();
+    // copy mode: with aligned rows and 8 vectors in flight per lane the
+    // offsets are loaded behind the wave's first payload loads (see the gate
+    // below); otherwise here. (With 16 in flight the gate's wait for all of
+    // them before the first store cost more than it saved: copies of 1 GiB
+    // per rank took 4 % longer.)
+    constexpr bool kDeferred = MODE == kCopyGiven && ALIGNED && U <= 8;
+    if constexpr (MODE == kCopyGiven && !kDeferred) load_given();
     if (st0) return;
 
     // ---- offsets from S, in registers (wrapping arithmetic, as the checks
@@ -390,8 +394,8 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
 
     // ---- checks, identical in every wave
     int bits = __ballot(act && split_invalid((int64_t)v)) ? A2AV_ST_BAD_SPLIT : 0;
-    // copy mode: the given offsets and totals against S and the buffers. With
-    // aligned rows the offsets are loaded and checked once the wave's first
+    // copy mode: the given offsets and totals against S and the buffers. When
+    // deferred, the offsets are loaded and checked once the wave's first
     // payload loads are in flight (a gate before its first store), so the
     // check costs no round trip of its own; otherwise it runs here.
     auto given_bits = [&]() -> int {
@@ -406,7 +410,6 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
         }
         return b;
     };
-    constexpr bool kDeferred = MODE == kCopyGiven && ALIGNED;
     bool pending = kDeferred;  // the gate has not run yet
     auto gate = [&]() -> bool {
         if (!pending) return true;
