@@ -224,13 +224,15 @@ struct BucketArgs {
     int64_t *ksrc;          // [W][n_tables]
     int64_t *ldst;          // [W][n_tables + 1] plan of the lengths
     int64_t *lsrc;          // [W][n_tables]
-    int32_t *bits;          // [W]
+    int32_t *bits;          // [W] ([2W] when merged)
     int64_t *split_keys;    // [W][W]
     int64_t *split_lengths; // [W][W]
     const int32_t *status;
     int64_t batch;
     int W;
     int n_tables;
+    int merged;  // 1: one block copy over 2W ranks moves keys and lengths,
+                 // rank r's lengths being rank W + r
 };
 
 // One block per (table, rank): the table's key count, or -1 when a length is
@@ -290,6 +292,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_bucket_plan(const BucketArgs a
     if (tid < A2AV_MAX_W) owner_keys[tid] = 0;
     __syncthreads();
     if (poisoned) return;
+    if (a.merged && tid == 0) a.bits[W + r] = 0;  // the plan's verdict sits in bits[r]
     const int64_t *tk = a.tk + (int64_t)r * NT;
     // by position in destination order: the table there, its key count
     int64_t nd[kPlanPer], nt[kPlanPer];
@@ -764,7 +767,7 @@ A2AV_API int moe_regroup(int W, int E, size_t row_bytes, const int64_t *counts,
 A2AV_API size_t keys_bucketize_workspace_bytes(int W, int n_tables) {
     if (W < 1 || W > A2AV_MAX_W || n_tables < 0 || n_tables > A2AV_MAX_TABLES) return 0;
     const size_t nt = (size_t)n_tables;
-    return round256((size_t)W * (5 * nt + 2) * 8) + round256((size_t)W * 4);
+    return round256((size_t)W * (5 * nt + 2) * 8) + round256(2 * (size_t)W * 4);
 }
 
 A2AV_API int keys_bucketize(int W, int n_tables, int64_t batch, const int32_t *const *lengths,
@@ -804,14 +807,18 @@ A2AV_API int keys_bucketize(int W, int n_tables, int64_t batch, const int32_t *c
         kmax += (uint64_t)n_keys[r] * 8;
         lal = lal && ((uintptr_t)lengths[r] % 16 == 0) && ((uintptr_t)lengths_out[r] % 16 == 0);
     }
+    // workspace: tk | kdst | ldst | ksrc | lsrc | bits [2W]. The two plans sit
+    // back to back, so that with 2W ranks at most one block copy moves both.
     const size_t nt = (size_t)n_tables;
+    const bool merged = 2 * W <= A2AV_MAX_W;
     int64_t *ws = (int64_t *)workspace;
     b.tk = ws;
     b.kdst = b.tk + (size_t)W * nt;
-    b.ksrc = b.kdst + (size_t)W * (nt + 1);
-    b.ldst = b.ksrc + (size_t)W * nt;
-    b.lsrc = b.ldst + (size_t)W * (nt + 1);
+    b.ldst = b.kdst + (size_t)W * (nt + 1);
+    b.ksrc = b.ldst + (size_t)W * (nt + 1);
+    b.lsrc = b.ksrc + (size_t)W * nt;
     b.bits = (int32_t *)((unsigned char *)workspace + round256((size_t)W * (5 * nt + 2) * 8));
+    b.merged = merged ? 1 : 0;
     b.split_keys = split_keys;
     b.split_lengths = split_lengths;
     b.status = status;
@@ -835,7 +842,21 @@ A2AV_API int keys_bucketize(int W, int n_tables, int64_t batch, const int32_t *c
     cl.R = 4;
     cl.W = W;
     cl.B = n_tables;
-    if (n_tables > 0) {
+    if (merged) {
+        // one launch: ranks 0..W-1 move keys (8-byte rows), ranks W..2W-1
+        // lengths (4-byte rows); it also reports the planning bits
+        BlockArgs c = ck;
+        c.W = 2 * W;
+        for (int r = 0; r < W; r++) {
+            c.in[W + r] = cl.in[r];
+            c.out[W + r] = cl.out[r];
+            c.in_rows[W + r] = cl.in_rows[r];
+            c.cap[W + r] = cl.cap[r];
+            c.Rr[r] = 8;
+            c.Rr[W + r] = 4;
+        }
+        launch_block_copy_mixed(c, kmax + (uint64_t)W * (uint64_t)nl * 4, stream);
+    } else if (n_tables > 0) {
         launch_block_copy(ck, kmax, kal, stream);
         launch_block_copy(cl, (uint64_t)W * (uint64_t)nl * 4, lal, stream);
     } else {

@@ -492,8 +492,9 @@ size_t keys_bucketize_workspace_bytes(int W, int n_tables);
  *                   n_keys[r]): nothing but the workspace is written, except
  *                   the splits of ranks that passed.
  * Keys past the lengths' total are not read and not written.
- * Four kernels: per-(table, rank) key counts, a per-rank plan, and a block
- * copy each for keys and lengths.
+ * Three kernels up to W = 32: per-(table, rank) key counts, a per-rank plan,
+ * and one block copy of keys and lengths together; above 32 ranks the keys
+ * and the lengths are two block copies.
  */
 int keys_bucketize(int W, int n_tables, int64_t batch, const int32_t *const *lengths,
                    const int64_t *const *keys, const int64_t *n_keys,

@@ -83,6 +83,8 @@ def _compare(ref, W, NT, batch, lengths, keys, got, n_keys=None):
     (2, 3, 0, 0, 0),       # empty batch
     (1, 5, 33, 1, 0),      # one rank
     (16, 300, 7, 0, 0),    # many tables: search over 300 blocks
+    (32, 50, 5, 0, 4),     # keys and lengths in one block copy over 2W = 64 ranks
+    (33, 40, 3, 0, 0),     # above 32 ranks: two block copies
 ])
 def test_bucketize_matches_oracle(ref, W, NT, batch, extra, pad):
     _say("bucketize", W, NT, batch, extra, pad)
