@@ -32,8 +32,7 @@ def _sample_rows(g, S, d, n_random=512):
     return sorted(js)
 
 
-def run_large(ref, W, mib, kind, seed, fused=True):
-    R = 8192
+def run_large(ref, W, mib, kind, seed, fused=True, R=8192):
     n = I.rows_for_mib(mib, R)
     g = I.rng(seed)
     S = I.uniform_splits(g, W, n) if kind == "uniform" else I.half_zero_splits(g, W, n)
@@ -62,7 +61,7 @@ def run_large(ref, W, mib, kind, seed, fused=True):
             rows = torch.tensor([src[k][1] for k in pick], dtype=torch.int64, device="cuda")
             want = X[s][rows]
             assert torch.equal(got[torch.tensor(pick, device="cuda")], want), \
-                f"W={W} {mib} MiB {kind}: rank {d} rows from {s}"
+                f"W={W} {mib} MiB {kind} R={R}: rank {d} rows from {s}"
     # round trip with the transposed splits, compared whole on the device
     back = [torch.empty((n, R), dtype=torch.uint8, device="cuda") for _ in range(W)]
     st2 = A2av(W)
@@ -88,3 +87,16 @@ def test_one_gib_half_zero(ref):
 def test_four_gib_per_rank(ref):
     _say("large 4 4 GiB")
     run_large(ref, 4, 4096, "uniform", 70)
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "3call"])
+@pytest.mark.parametrize("W,mib,R", [
+    (4, 160, 8196),  # rows 4 bytes past a multiple of 16: every source phase 0, 4, 8, 12
+    (8, 80, 8),      # 8-byte rows (keys): source phases 0 and 8
+])
+def test_misaligned_rows_past_512_mib(ref, W, mib, R, fused):
+    """More than 512 MiB on each side, so the copy runs 16 vectors per lane in
+    flight, with rows that are not 16-byte multiples: chunks start at every
+    4-byte phase of the 16-byte grid and take the one-load misaligned path."""
+    _say("large misaligned", W, mib, R, fused)
+    run_large(ref, W, mib, "uniform", 90 + W + R % 7, fused=fused, R=R)
