@@ -202,7 +202,9 @@ __device__ __forceinline__ void copy_elems_dw(u32x4 *__restrict__ d, const u32x4
         for (int u = 0; u < U; u++) {
             uint64_t i = base + (uint64_t)u * kWave + lane;
             i = i < nv ? i : nv - 1;
-            r[u] = ld<true>(s + i);
+            // the builtin on the 4-byte-aligned type itself: through ld<>
+            // the type would decay to the 16-byte-aligned vector
+            r[u] = __builtin_nontemporal_load(s + i);
         }
 #pragma unroll
         for (int u = 0; u < U; u++) {
