@@ -1,5 +1,5 @@
 """The entry points under HIP graph capture: a captured one-call a2av, MoE
-pack + dispatch, fused key exchange and the one-step MoE trip (pack and
+pack + dispatch, fused key exchange, key bucketing and the one-step MoE trip (pack and
 dispatch in one step, the combine at the owners and the one-step inverse),
 each replayed several times with eager work and synchronisations between
 replays, and every replay compared with the eager result (which is itself
@@ -158,6 +158,55 @@ def test_graph_fused_key_exchange(ref):
         status.zero_()
 
     _replay_and_check(graph, lambda: lo + ko + [sk, sl, ro], want, reset, _noise)
+    assert int(status.item()) == 0
+
+
+def test_graph_key_bucketing(ref):
+    """keys_bucketize captured (counts, plan, and the one block copy of keys
+    and lengths over 2W ranks), replays against the eager result and the
+    oracle's per-rank bucketing."""
+    W, NT, batch = 8, 26, 200
+    g = I.rng(23)
+    ranks = [I.emb_keys_rank(g, tables=NT, batch=batch) for _ in range(W)]
+    want_o = [ref.keys_bucketize(W, NT, batch, r.lengths, r.keys) for r in ranks]
+    assert all(w[0] == 0 for w in want_o)
+    lin = [torch.from_numpy(r.lengths.reshape(-1)).cuda() for r in ranks]
+    kin = [torch.from_numpy(r.keys).cuda() for r in ranks]
+    lo = [torch.zeros(NT * batch, dtype=torch.int32, device="cuda") for _ in range(W)]
+    ko = [torch.zeros(r.keys.size, dtype=torch.int64, device="cuda") for r in ranks]
+    sk = torch.zeros((W, W), dtype=torch.int64, device="cuda")
+    sl = torch.zeros((W, W), dtype=torch.int64, device="cuda")
+    ws = torch.empty(B.keys_bucketize_workspace_bytes(W, NT), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def call():
+        B.keys_bucketize(W, NT, batch, lin, kin, [r.keys.size for r in ranks], lo, ko, sk, sl, ws,
+                         status)
+
+    call()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for r in range(W):
+        _, rlo, rko, rsk, rsl = want_o[r]
+        assert np.array_equal(lo[r].cpu().numpy(), rlo) and np.array_equal(ko[r].cpu().numpy(), rko)
+        assert np.array_equal(sk[r].cpu().numpy(), rsk) and np.array_equal(sl[r].cpu().numpy(), rsl)
+    want = [x.clone() for x in lo + ko] + [sk.clone(), sl.clone()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        call()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            call()
+    torch.cuda.synchronize()
+
+    def reset():
+        for x in lo + ko + [sk, sl]:
+            x.zero_()
+        status.zero_()
+
+    _replay_and_check(graph, lambda: lo + ko + [sk, sl], want, reset, _noise)
     assert int(status.item()) == 0
 
 
