@@ -718,21 +718,44 @@ static void launch_dcopy_u(unsigned char *d, const unsigned char *s, uint64_t n,
 
 // Wave kernel: traffic up to kSmallTraffic moves in 8 KiB pieces with 8
 // loads in flight per lane; larger traffic in 32 KiB pieces with 16.
+//
+// W <= 8 with 16-byte rows from kShortTraffic up: 4 KiB pieces with 4 loads
+// in flight per lane, and for the one-call kernel (and the plain copy) at most
+// a few workgroups per CU, enforced with 32 KiB of LDS per workgroup that the
+// kernel does not use. Fewer, shorter-lived waves per CU stream HBM better
+// here: at W = 4 / 8 x 32 MiB per rank the one-call kernel went 46.6 -> 45.2 /
+// 89.7 -> 85.8 us and the copy-only kernel 47.3 -> 44.8 / 91.1 -> 87.4 us;
+// at 1 GiB per rank 1434 -> 1409 / 2887 -> 2826 us and 1451 -> 1414 /
+// 2990 -> 2867 us. The copy-only kernel's own registers already keep it to
+// five waves per SIMD there; the LDS cap made it slower. Below 64 MiB per
+// side, and for rows that are not 16-byte multiples, the shapes above stay.
 constexpr uint64_t kSmallTraffic = 512ull << 20;
+constexpr uint64_t kShortTraffic = 64ull << 20;
+constexpr unsigned kCapLds = 32768;
 
 struct WaveTuning {
     int unroll;
     uint64_t piece;
+    unsigned lds;  // dynamic LDS per workgroup (occupancy cap), 0: none
 };
 
-static WaveTuning wave_tuning(uint64_t bmax) {
+static WaveTuning wave_tuning(uint64_t bmax, bool short_pieces = false, bool cap = false) {
     WaveTuning t;
     const bool small = bmax <= kSmallTraffic;
-    t.unroll = (int)env_long("A2AV_WAVE_UNROLL", small ? 8 : 16, 8, 16);
-    if (t.unroll != 8 && t.unroll != 16) t.unroll = 8;
-    t.piece = (uint64_t)env_long("A2AV_WAVE_PIECE", small ? 8192 : 32768, 4096, 1L << 30);
+    const int u0 = short_pieces ? 4 : small ? 8 : 16;
+    const long p0 = short_pieces ? 4096 : small ? 8192 : 32768;
+    t.unroll = (int)env_long("A2AV_WAVE_UNROLL", u0, 4, 16);
+    if (t.unroll != 4 && t.unroll != 8 && t.unroll != 16) t.unroll = 8;
+    t.piece = (uint64_t)env_long("A2AV_WAVE_PIECE", p0, 4096, 1L << 30);
     t.piece = (t.piece + 4095) & ~(uint64_t)4095;
+    t.lds = (unsigned)env_long("A2AV_WAVE_LDS", short_pieces && cap ? kCapLds : 0, 0, 65536);
     return t;
+}
+
+// The tuning of the W <= 8 wave kernel (fused: the one-call kernel).
+static WaveTuning wave_tuning_w8(uint64_t bmax, bool aligned, bool fused) {
+    const bool short_pieces = aligned && bmax >= kShortTraffic;
+    return wave_tuning(bmax, short_pieces, fused);
 }
 
 static int wave_grid(uint64_t bmax, uint64_t piece) {
@@ -744,27 +767,33 @@ static int wave_grid(uint64_t bmax, uint64_t piece) {
 }
 
 template <int W, int MODE>
-static void launch_wave_w(const CopyArgs &a, bool aligned, int unroll, int grid, hipStream_t st) {
-    if (unroll == 16) {
-        if (aligned) hipLaunchKernelGGL((k_a2av_wave<W, 16, true, MODE>), dim3(grid), dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((k_a2av_wave<W, 16, false, MODE>), dim3(grid), dim3(256), 0, st, a);
+static void launch_wave_w(const CopyArgs &a, bool aligned, const WaveTuning &wt, int grid,
+                          hipStream_t st) {
+    const unsigned lds = wt.lds;
+    if (wt.unroll == 16) {
+        if (aligned) hipLaunchKernelGGL((k_a2av_wave<W, 16, true, MODE>), dim3(grid), dim3(256), lds, st, a);
+        else hipLaunchKernelGGL((k_a2av_wave<W, 16, false, MODE>), dim3(grid), dim3(256), lds, st, a);
+    } else if (wt.unroll == 4) {
+        if (aligned) hipLaunchKernelGGL((k_a2av_wave<W, 4, true, MODE>), dim3(grid), dim3(256), lds, st, a);
+        else hipLaunchKernelGGL((k_a2av_wave<W, 4, false, MODE>), dim3(grid), dim3(256), lds, st, a);
     } else {
-        if (aligned) hipLaunchKernelGGL((k_a2av_wave<W, 8, true, MODE>), dim3(grid), dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((k_a2av_wave<W, 8, false, MODE>), dim3(grid), dim3(256), 0, st, a);
+        if (aligned) hipLaunchKernelGGL((k_a2av_wave<W, 8, true, MODE>), dim3(grid), dim3(256), lds, st, a);
+        else hipLaunchKernelGGL((k_a2av_wave<W, 8, false, MODE>), dim3(grid), dim3(256), lds, st, a);
     }
 }
 
 template <int MODE>
-static void launch_wave(const CopyArgs &a, bool aligned, int unroll, int grid, hipStream_t st) {
+static void launch_wave(const CopyArgs &a, bool aligned, const WaveTuning &wt, int grid,
+                        hipStream_t st) {
     switch (a.W) {
-    case 1: launch_wave_w<1, MODE>(a, aligned, unroll, grid, st); break;
-    case 2: launch_wave_w<2, MODE>(a, aligned, unroll, grid, st); break;
-    case 3: launch_wave_w<3, MODE>(a, aligned, unroll, grid, st); break;
-    case 4: launch_wave_w<4, MODE>(a, aligned, unroll, grid, st); break;
-    case 5: launch_wave_w<5, MODE>(a, aligned, unroll, grid, st); break;
-    case 6: launch_wave_w<6, MODE>(a, aligned, unroll, grid, st); break;
-    case 7: launch_wave_w<7, MODE>(a, aligned, unroll, grid, st); break;
-    default: launch_wave_w<8, MODE>(a, aligned, unroll, grid, st); break;
+    case 1: launch_wave_w<1, MODE>(a, aligned, wt, grid, st); break;
+    case 2: launch_wave_w<2, MODE>(a, aligned, wt, grid, st); break;
+    case 3: launch_wave_w<3, MODE>(a, aligned, wt, grid, st); break;
+    case 4: launch_wave_w<4, MODE>(a, aligned, wt, grid, st); break;
+    case 5: launch_wave_w<5, MODE>(a, aligned, wt, grid, st); break;
+    case 6: launch_wave_w<6, MODE>(a, aligned, wt, grid, st); break;
+    case 7: launch_wave_w<7, MODE>(a, aligned, wt, grid, st); break;
+    default: launch_wave_w<8, MODE>(a, aligned, wt, grid, st); break;
     }
 }
 
@@ -892,9 +921,9 @@ A2AV_API int a2av_copy(int W, size_t row_bytes, const void *const *in, const int
         uint64_t bmax;
         bool aligned;
         traffic_bound(a, &bmax, &aligned);
-        const WaveTuning wt = wave_tuning(bmax);
+        const WaveTuning wt = W <= kWaveMaxW ? wave_tuning_w8(bmax, aligned, false) : wave_tuning(bmax);
         a.piece = wt.piece;
-        if (W <= kWaveMaxW) launch_wave<kCopyGiven>(a, aligned, wt.unroll, wave_grid(bmax, wt.piece), stream);
+        if (W <= kWaveMaxW) launch_wave<kCopyGiven>(a, aligned, wt, wave_grid(bmax, wt.piece), stream);
         else launch_wave_any<false>(a, aligned, wt, wave_grid(bmax, wt.piece), stream);
         return launch_status();
     }
@@ -950,9 +979,9 @@ A2AV_API int a2av_all_to_all_vdev(int W, size_t row_bytes, const void *const *in
         uint64_t bmax;
         bool aligned;
         traffic_bound(a, &bmax, &aligned);
-        const WaveTuning wt = wave_tuning(bmax);
+        const WaveTuning wt = wave_tuning_w8(bmax, aligned, true);
         a.piece = wt.piece;
-        launch_wave<kFused>(a, aligned, wt.unroll, wave_grid(bmax, wt.piece), stream);
+        launch_wave<kFused>(a, aligned, wt, wave_grid(bmax, wt.piece), stream);
         return launch_status();
     }
     launch_payload<kFused>(a, payload_grid(t, stream), t, stream);
@@ -964,20 +993,24 @@ A2AV_API int a2av_device_copy(void *dst, const void *src, size_t bytes, hipStrea
     if (!dst || !src) return A2AV_EARG;
     const CopyTuning t = copy_tuning();
     if (!t.block_kernel) {
-        const WaveTuning wt = wave_tuning(2 * (uint64_t)bytes);
-        const int grid = wave_grid(bytes, wt.piece);
         const bool aligned = ((uintptr_t)dst % 16 == 0) && ((uintptr_t)src % 16 == 0) && bytes % 16 == 0;
+        // the same shapes as the one-call a2av moving as many bytes
+        const WaveTuning wt = wave_tuning(2 * (uint64_t)bytes, aligned && bytes >= kShortTraffic, true);
+        const int grid = wave_grid(bytes, wt.piece);
         unsigned char *d = (unsigned char *)dst;
         const unsigned char *s = (const unsigned char *)src;
         if (!aligned)
             hipLaunchKernelGGL((k_device_copy_wave<8, false>), dim3(grid), dim3(256), 0, stream, d, s,
                                (uint64_t)bytes, wt.piece);
         else if (wt.unroll == 16)
-            hipLaunchKernelGGL((k_device_copy_wave<16, true>), dim3(grid), dim3(256), 0, stream, d, s,
-                               (uint64_t)bytes, wt.piece);
+            hipLaunchKernelGGL((k_device_copy_wave<16, true>), dim3(grid), dim3(256), wt.lds, stream,
+                               d, s, (uint64_t)bytes, wt.piece);
+        else if (wt.unroll == 4)
+            hipLaunchKernelGGL((k_device_copy_wave<4, true>), dim3(grid), dim3(256), wt.lds, stream,
+                               d, s, (uint64_t)bytes, wt.piece);
         else
-            hipLaunchKernelGGL((k_device_copy_wave<8, true>), dim3(grid), dim3(256), 0, stream, d, s,
-                               (uint64_t)bytes, wt.piece);
+            hipLaunchKernelGGL((k_device_copy_wave<8, true>), dim3(grid), dim3(256), wt.lds, stream,
+                               d, s, (uint64_t)bytes, wt.piece);
         return launch_status();
     }
     const int grid = payload_grid(t, stream);
