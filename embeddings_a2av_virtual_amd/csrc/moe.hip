@@ -579,6 +579,14 @@ __device__ __forceinline__ bool home_verdict(const CombineArgs &a) {
 
 constexpr int kCombineGroup = 8;  // slots whose rows are loaded before their fmas
 
+// Occupancy caps of the combine, as LDS per workgroup that the kernel does not
+// use: its 51 registers would allow eight waves per SIMD, and fewer streamed
+// HBM better (dispatch workload, same box: 1502 -> 1402 us with 32 KiB for the
+// combine over a returned buffer; 1529 -> 1427 us with 52 KiB for the combine
+// read at the owners, whose best cap differs).
+constexpr unsigned kCombineLds = 32768;
+constexpr unsigned kCombineHomeLds = 53248;
+
 // One wave per (rank, token, chunk of 64 vectors = 512 elements). The wave
 // index is made uniform so that the token, its perm entries and weights (read
 // with scalar loads) and the row bases all live in scalar registers; each
@@ -1029,7 +1037,8 @@ A2AV_API int moe_combine_return(int W, int64_t T, int k, int E, int64_t H,
         uint64_t blocks = ((uint64_t)W * (uint64_t)T * nchunk + 3) / 4;
         if (blocks < 1) blocks = 1;
         if (blocks > (1u << 22)) blocks = 1u << 22;
-        hipLaunchKernelGGL((k_moe_combine<true, true>), dim3((unsigned)blocks), dim3(256), 0,
+        hipLaunchKernelGGL((k_moe_combine<true, true>), dim3((unsigned)blocks), dim3(256),
+                           (unsigned)env_long("A2AV_COMBINE_LDS", kCombineHomeLds, 0, 65536),
                            stream, m, nchunk);
     }
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
@@ -1124,9 +1133,13 @@ A2AV_API int moe_combine(int W, int64_t T, int k, int64_t H, const void *const *
         if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
         // tuning knob: A2AV_COMBINE_STORE_NT (non-temporal stores, 0/1)
         if (env_long("A2AV_COMBINE_STORE_NT", 1, 0, 1))
-            hipLaunchKernelGGL((k_moe_combine<true, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a, nchunk);
+            hipLaunchKernelGGL((k_moe_combine<true, false>), dim3((unsigned)blocks), dim3(256),
+                               (unsigned)env_long("A2AV_COMBINE_LDS", kCombineLds, 0, 65536), stream, a,
+                               nchunk);
         else
-            hipLaunchKernelGGL((k_moe_combine<false, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a, nchunk);
+            hipLaunchKernelGGL((k_moe_combine<false, false>), dim3((unsigned)blocks), dim3(256),
+                               (unsigned)env_long("A2AV_COMBINE_LDS", kCombineLds, 0, 65536), stream, a,
+                               nchunk);
     }
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
 }
