@@ -654,10 +654,25 @@ __global__ __launch_bounds__(kPlanThreads) void k_grouped_plan_bwd(const Grouped
 }
 
 // ------------------------------------------------------------ host side
-static void piece_policy(uint64_t bmax, int *unroll, uint64_t *piece) {
+// Pieces of the block copy. From 64 MiB of traffic up: 4 KiB pieces with 4
+// loads in flight per lane, and with 16-byte rows at most a few workgroups per
+// CU (32 KiB of LDS per workgroup that the kernel does not use), as for the
+// a2av: dispatch workload regroup 2614 -> 2552 us, grouped dispatch 2579 ->
+// 2545 us; key workload (8-byte rows, no cap: with it they were slower) fused
+// exchange 108.4 -> 106.8 us. Below that, 8 KiB pieces with 8 loads in flight
+// (16 with 32 KiB pieces above 512 MiB).
+static void piece_policy(uint64_t bmax, bool aligned, int *unroll, uint64_t *piece,
+                         unsigned *lds) {
+    if (bmax >= (64ull << 20)) {
+        *unroll = 4;
+        *piece = 4096;
+        *lds = aligned ? 32768u : 0u;
+        return;
+    }
     const bool small = bmax <= (512ull << 20);
     *unroll = small ? 8 : 16;
     *piece = small ? 8192 : 32768;
+    *lds = 0;
 }
 
 static int copy_grid(uint64_t bmax, uint64_t piece) {
@@ -671,16 +686,20 @@ static int copy_grid(uint64_t bmax, uint64_t piece) {
 static void launch_block_copy(const BlockArgs &a, uint64_t bmax, bool aligned, hipStream_t st) {
     int unroll;
     uint64_t piece;
-    piece_policy(bmax, &unroll, &piece);
+    unsigned lds;
+    piece_policy(bmax, aligned, &unroll, &piece, &lds);
     BlockArgs b = a;
     b.piece = piece;
     const int grid = copy_grid(bmax, piece);
     if (unroll == 16) {
-        if (aligned) hipLaunchKernelGGL((k_block_copy<16, true>), dim3(grid), dim3(256), 0, st, b);
-        else hipLaunchKernelGGL((k_block_copy<16, false>), dim3(grid), dim3(256), 0, st, b);
+        if (aligned) hipLaunchKernelGGL((k_block_copy<16, true>), dim3(grid), dim3(256), lds, st, b);
+        else hipLaunchKernelGGL((k_block_copy<16, false>), dim3(grid), dim3(256), lds, st, b);
+    } else if (unroll == 4) {
+        if (aligned) hipLaunchKernelGGL((k_block_copy<4, true>), dim3(grid), dim3(256), lds, st, b);
+        else hipLaunchKernelGGL((k_block_copy<4, false>), dim3(grid), dim3(256), lds, st, b);
     } else {
-        if (aligned) hipLaunchKernelGGL((k_block_copy<8, true>), dim3(grid), dim3(256), 0, st, b);
-        else hipLaunchKernelGGL((k_block_copy<8, false>), dim3(grid), dim3(256), 0, st, b);
+        if (aligned) hipLaunchKernelGGL((k_block_copy<8, true>), dim3(grid), dim3(256), lds, st, b);
+        else hipLaunchKernelGGL((k_block_copy<8, false>), dim3(grid), dim3(256), lds, st, b);
     }
 }
 
@@ -688,12 +707,14 @@ static void launch_block_copy(const BlockArgs &a, uint64_t bmax, bool aligned, h
 static void launch_block_copy_mixed(const BlockArgs &a, uint64_t bmax, hipStream_t st) {
     int unroll;
     uint64_t piece;
-    piece_policy(bmax, &unroll, &piece);
+    unsigned lds;
+    piece_policy(bmax, false, &unroll, &piece, &lds);
     BlockArgs b = a;
     b.piece = piece;
     const int grid = copy_grid(bmax, piece);
-    if (unroll == 16) hipLaunchKernelGGL((k_block_copy<16, false, true>), dim3(grid), dim3(256), 0, st, b);
-    else hipLaunchKernelGGL((k_block_copy<8, false, true>), dim3(grid), dim3(256), 0, st, b);
+    if (unroll == 16) hipLaunchKernelGGL((k_block_copy<16, false, true>), dim3(grid), dim3(256), lds, st, b);
+    else if (unroll == 4) hipLaunchKernelGGL((k_block_copy<4, false, true>), dim3(grid), dim3(256), lds, st, b);
+    else hipLaunchKernelGGL((k_block_copy<8, false, true>), dim3(grid), dim3(256), lds, st, b);
 }
 
 static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
