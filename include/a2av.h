@@ -134,7 +134,9 @@ int a2av_offsets(int W, const int64_t *S, const int64_t *O, int64_t *send_off,
  * launches); each wave then reads, per destination it works in, one row of
  * recv_off and the matching columns of S and send_off.
  * Tuning (read on every call; defaults are compiled in): A2AV_WAVE_PIECE,
- * A2AV_WAVE_UNROLL (wave kernels); A2AV_BLOCK_KERNEL=1 forces the older
+ * A2AV_WAVE_UNROLL (4, 8 or 16), A2AV_WAVE_LDS (bytes of LDS per workgroup
+ * the kernel does not use, which limits workgroups per CU) for the wave
+ * kernels; A2AV_BLOCK_KERNEL=1 forces the older
  * workgroup kernel (one workgroup per piece, matrices staged in LDS for
  * W <= 16); A2AV_BLOCKS_PER_CU, A2AV_UNROLL, A2AV_NT, A2AV_PIECE,
  * A2AV_MIN_PIECE (workgroup kernel). Every setting gives identical bytes.
