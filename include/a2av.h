@@ -133,10 +133,10 @@ int a2av_offsets(int W, const int64_t *S, const int64_t *O, int64_t *send_off,
  * single workgroup checks everything first and the copy kernel follows (two
  * launches); each wave then reads, per destination it works in, one row of
  * recv_off and the matching columns of S and send_off.
- * From 64 MiB per side with 16-byte rows the one-call kernel (and the plain
- * copy, the block copies and the weighted combine) reserve LDS they do not
- * use, to run fewer workgroups per CU; a kernel on another stream then finds
- * less LDS free on the CUs they occupy.
+ * The one-call kernel, the plain copy and the block copies (from 64 MiB per
+ * side, with 16-byte rows) and the weighted combine (always) reserve LDS
+ * they do not use, to run fewer workgroups per CU; a kernel on another stream
+ * then finds less LDS free on the CUs they occupy.
  * Tuning (read on every call; defaults are compiled in): A2AV_WAVE_PIECE,
  * A2AV_WAVE_UNROLL (4, 8 or 16), A2AV_WAVE_LDS (bytes of LDS per workgroup
  * the kernel does not use, which limits workgroups per CU) for the wave
