@@ -93,6 +93,7 @@ def test_four_gib_per_rank(ref):
 @pytest.mark.parametrize("W,mib,R", [
     (4, 160, 8196),  # rows 4 bytes past a multiple of 16: every source phase 0, 4, 8, 12
     (8, 80, 8),      # 8-byte rows (keys): source phases 0 and 8
+    (12, 48, 8196),  # more than 8 ranks: the prep workgroup, then the wave copy
 ])
 def test_misaligned_rows_past_512_mib(ref, W, mib, R, fused):
     """More than 512 MiB on each side, so the copy runs 16 vectors per lane in
