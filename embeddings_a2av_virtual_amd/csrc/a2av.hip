@@ -280,8 +280,10 @@ __global__ __launch_bounds__(BS) void k_a2av_payload(const CopyArgs a) {
                 const uint64_t off = x - F;
                 const int64_t so = sop[s * W1 + d];
                 // validated metadata always passes; the check keeps every
-                // access inside the caller's buffers regardless
-                if (r0 >= 0 && so >= 0 && r0 + n <= a.cap[d] && so + n <= a.in_rows[s])
+                // access inside the caller's buffers regardless (no sum that
+                // can wrap: a negative value reads as 2^63 or more and fails)
+                if (span_fits((uint64_t)r0, (uint64_t)n, (uint64_t)a.cap[d]) &&
+                    span_fits((uint64_t)so, (uint64_t)n, (uint64_t)a.in_rows[s]))
                     copy_segment<BS, U, NT>(a.out[d] + (uint64_t)r0 * R + off,
                                             a.in[s] + (uint64_t)so * R + off, e - x, tid);
                 x = e;
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
     const uint64_t TW = (uint64_t)gridDim.x * wpb;
 
     // ---- scalar loads: status word, S, and in copy mode the given offsets
-    const int32_t st0 = *(const const_i32 *)a.status;
+    const int32_t st0 = status_at_entry(a.status);
     const const_i64 *Sc = (const const_i64 *)a.S;
     uint64_t v = 0;
 #pragma unroll
@@ -487,8 +489,9 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
                 const int du = __builtin_amdgcn_readfirstlane(d);
                 const int su = __builtin_amdgcn_readfirstlane(s);
                 // validated offsets always pass; the check keeps every access
-                // inside the caller's buffers regardless
-                if ((int64_t)(r0 + n) <= a.cap[du] && (int64_t)(s0 + n) <= a.in_rows[su]) {
+                // inside the caller's buffers regardless (no sum that can wrap)
+                if (span_fits(r0, n, (uint64_t)a.cap[du]) &&
+                    span_fits(s0, n, (uint64_t)a.in_rows[su])) {
                     unsigned char *dst = a.out[du] + r0 * R + off;
                     const unsigned char *src = a.in[su] + s0 * R + off;
                     if constexpr (kDeferred) {
@@ -598,7 +601,7 @@ __global__ __launch_bounds__(256) void k_a2av_wave_any(const CopyArgs a) {
     const uint64_t gw = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave;
     const uint64_t TW = (uint64_t)gridDim.x * wpb;
     const int W = a.W, W1 = W + 1;
-    if (*(const const_i32 *)a.status) return;  // final: the prep launch wrote it
+    if (status_at_entry(a.status)) return;  // final: the prep launch wrote it
     const uint64_t R = a.R;
     const uint64_t tot = lane < W ? (uint64_t)a.recv_off[lane * W1 + W] : 0;
     const uint64_t incl = wave_incl_scan_u64(tot);
@@ -629,8 +632,10 @@ __global__ __launch_bounds__(256) void k_a2av_wave_any(const CopyArgs a) {
                 const uint64_t off = x - F;
                 const uint64_t s0 = readlane_u64(so, s);
                 // checked offsets always pass; the check keeps every access
-                // inside the caller's buffers regardless
-                if ((int64_t)(r0 + nn) <= a.cap[d] && (int64_t)(s0 + nn) <= a.in_rows[s]) {
+                // inside the caller's buffers regardless (no sum that can
+                // wrap; the offsets are re-read from the caller's memory)
+                if (span_fits(r0, nn, (uint64_t)a.cap[d]) &&
+                    span_fits(s0, nn, (uint64_t)a.in_rows[s])) {
                     unsigned char *dst = a.out[d] + r0 * R + off;
                     const unsigned char *src = a.in[s] + s0 * R + off;
                     if constexpr (ALIGNED) wave_copy16<U>(dst, src, e - x, lane);

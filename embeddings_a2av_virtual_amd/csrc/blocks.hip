@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void k_block_copy(const BlockArgs a) {
     // lane r: rank r's row bytes
     const uint64_t Rl = MIXED ? (lane < W ? (uint64_t)a.Rr[lane] : 1) : a.R;
 
-    const int32_t st0 = *(const const_i32 *)a.status;
+    const int32_t st0 = status_at_entry(a.status);
     int32_t rb = 0;
     uint64_t rows = 0;
     if (lane < W) {
@@ -124,8 +124,11 @@ __global__ __launch_bounds__(256) void k_block_copy(const BlockArgs a) {
             const uint64_t e = hr < r1 * R ? hr : r1 * R;
             if (e <= xr || sr < 0 || sr >= W) return;  // not a valid plan
             // a valid plan always passes; the check keeps every access inside
-            // the caller's buffers regardless
-            if (r1 <= (uint64_t)a.cap[d] && s0 + (r1 - r0) <= (uint64_t)a.in_rows[sr]) {
+            // the caller's buffers regardless (rows [r0, r1) of the
+            // destination and [s0, s0 + r1 - r0) of the source, with no sum
+            // that can wrap)
+            if (r0 <= r1 && span_fits(r0, r1 - r0, (uint64_t)a.cap[d]) &&
+                span_fits(s0, r1 - r0, (uint64_t)a.in_rows[sr])) {
                 unsigned char *dst = a.out[d] + xr;
                 const unsigned char *src = a.in[sr] + s0 * R + (xr - r0 * R);
                 if constexpr (ALIGNED) wave_copy16<U>(dst, src, e - xr, lane);

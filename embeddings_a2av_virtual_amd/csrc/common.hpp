@@ -11,6 +11,7 @@
 #include <type_traits>
 
 #include "../../include/a2av.h"
+#include "bounds.h"
 
 #define A2AV_API extern "C" __attribute__((visibility("default")))
 
@@ -279,6 +280,22 @@ __device__ __forceinline__ bool wave_copy16(unsigned char *dst, const unsigned c
 // the wave's vector memory traffic.
 typedef __attribute__((address_space(4))) const int64_t const_i64;
 typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+// The status word as a wave finds it at entry, read once through the scalar
+// cache (a uniform load that does not queue behind the vector traffic older
+// waves keep in flight on the CU). The constant address space tells the
+// compiler the word does not change during the kernel, which is not so:
+// waves of the same launch may OR failure bits into it. The read is still
+// exact for its one use, an early return before the wave writes anything:
+// whatever the compiler does with a single-use load, the value it yields is
+// what earlier kernels left (their writes are visible at kernel start),
+// possibly with bits a wave of this launch has set since. The kernels that
+// call this have every wave make those checks itself and reach the same
+// verdict, so returning early on such bits changes nothing. A kernel whose
+// waves could disagree reads the word with status_poisoned instead.
+__device__ __forceinline__ int32_t status_at_entry(const int32_t *status) {
+    return *(const const_i32 *)status;
+}
 
 __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);

@@ -600,7 +600,9 @@ template <bool SNT, bool HOME>
 __global__ __launch_bounds__(256) void k_moe_combine(const CombineArgs a, uint64_t nchunk) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint64_t wpb = blockDim.x / kWave;
-    if (*(const const_i32 *)a.status) return;  // written only by earlier kernels
+    // earlier kernels' verdict; HOME waves also OR bits in (home_verdict), and
+    // every wave of this launch reads the same words and reaches the same one
+    if (status_at_entry(a.status)) return;
     if constexpr (HOME) {
         if (home_verdict(a)) return;
     }
@@ -666,7 +668,7 @@ template <bool HOME>
 __global__ __launch_bounds__(256) void k_moe_combine_any(const CombineArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint64_t wpb = blockDim.x / kWave;
-    if (*(const const_i32 *)a.status) return;
+    if (status_at_entry(a.status)) return;
     if constexpr (HOME) {
         if (home_verdict(a)) return;
     }

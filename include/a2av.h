@@ -173,12 +173,19 @@ int a2av_all_to_all_vdev(int W, size_t row_bytes, const void *const *in,
                          hipStream_t stream);
 
 /*
- * Workspace bytes moe_pack needs for these sizes (0 for invalid sizes).
+ * Workspace bytes moe_pack needs for these sizes (0 for invalid sizes): the
+ * scratch of the pack below, the step before the dispatch exchange of the MoE
+ * region on the page "[a2av] Improve tuning for 4 GPUs" (section "Change",
+ * the sentence under its timing table).
  */
 size_t moe_pack_workspace_bytes(int W, int64_t T, int k, int E);
 
 /*
- * MoE dispatch pack, for every rank r at once: the T*k routing slots
+ * MoE dispatch pack: the page "[a2av] Improve tuning for 4 GPUs" (section
+ * "Change", the sentence under its timing table) singles out the MoE region
+ * of message sizes, where each rank's message is its tokens grouped by
+ * destination rank; the pack builds that message. Read here as: for every
+ * rank r at once, the T*k routing slots
  * (slot q = t*k + j routes token t to expert ids[r][q]) are ordered by a
  * stable counting sort on the expert id. Experts are owned in contiguous
  * blocks of E/W per rank, so the order is (destination rank, expert, token,
