@@ -106,47 +106,72 @@ def test_degenerate_cases(ref, fused):
 
 
 # ------------------------------------------------------------------ error paths
+# Every payload kernel refuses: the one-call and copy-only wave kernels for
+# W <= 8 (aligned rows with the deferred gate, misaligned rows and 16 loads in
+# flight with the checks up front), the prep + wave copy for more ranks, and
+# the workgroup kernel (LDS metadata up to 16 ranks, global above).
+ERROR_ENVS = {"wave": {}, "wave_u16": {"A2AV_WAVE_UNROLL": "16"},
+              "block_kernel": {"A2AV_BLOCK_KERNEL": "1"}}
+
+
+@pytest.mark.parametrize("env", list(ERROR_ENVS), ids=list(ERROR_ENVS))
+@pytest.mark.parametrize("R", [16, 24])
+@pytest.mark.parametrize("W", [4, 12, 20])
 @pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
-def test_error_paths_match_oracle(ref, fused):
-    g = I.rng(10)
-    W, R, n = 4, 32, 40
+def test_error_paths_match_oracle(ref, monkeypatch, fused, W, R, env):
+    for k, v in ERROR_ENVS[env].items():
+        monkeypatch.setenv(k, v)
+    g = I.rng(10 + W + R)
+    per = 3
+    n = W * per
     X = [random_rows(g, n, R) for _ in range(W)]
-    good = np.full((W, W), n // W, dtype=np.int64)
+    good = np.full((W, W), per, dtype=np.int64)
     roomy = np.full(W, 1000)
 
     neg = good.copy(); neg[2, 1] = -3
-    big = good.copy(); big[0, 3] = B.MAX_SPLIT + 1
+    big = good.copy(); big[0, W - 1] = B.MAX_SPLIT + 1
     over = good.copy(); over[1, 0] += 1
     tight = good.sum(axis=0); tight[2] -= 1
     both = good.copy(); both[3, 2] += 2
     both_cap = both.sum(axis=0); both_cap[2] -= 1
+    last = good.copy(); last[W - 1, W - 1] += 1  # the last pair overruns and overflows
+    last_cap = good.sum(axis=0)
     cases = [("negative", neg, roomy), ("too_large", big, roomy), ("overrun", over, roomy),
              ("overflow", good, tight), ("overrun+overflow", both, both_cap),
-             ("exact_fit", good, good.sum(axis=0))]
+             ("last_pair", last, last_cap), ("exact_fit", good, good.sum(axis=0))]
     for name, S, cap in cases:
-        _say("error case", name)
+        _say("error case", name, "W", W, "R", R, env)
         gpu = gpu_a2av(R, X, S, cap=cap, fused=fused)
         want = ref_a2av(ref, R, X, S, cap=cap)
         assert_same(gpu, want, name)
         if want[0]:
             assert all(np.all(y == SENT) for y in gpu[4]), f"{name}: payload written on failure"
+        else:
+            assert name == "exact_fit"
 
 
-def test_copy_rejects_foreign_offsets(ref):
-    """Offsets that are not the scans of S: every workgroup refuses to copy."""
+@pytest.mark.parametrize("env", list(ERROR_ENVS), ids=list(ERROR_ENVS))
+@pytest.mark.parametrize("R", [16, 24])
+@pytest.mark.parametrize("W", [4, 12, 20])
+def test_copy_rejects_foreign_offsets(ref, monkeypatch, W, R, env):
+    """Offsets that are not the scans of S: the copy refuses and writes nothing."""
     from embeddings_a2av_virtual_amd.vranks import A2av
     from gpu_util import GuardedBuffer, upload_rows
-    g = I.rng(11)
-    W, R, n = 4, 16, 40
+    g = I.rng(11 + W + R)
+    per = 3
+    n = W * per
     X = [random_rows(g, n, R) for _ in range(W)]
-    S = np.full((W, W), n // W, dtype=np.int64)
+    S = np.full((W, W), per, dtype=np.int64)
     st = A2av(W)
     st.set_splits(S)
     st.exchange_and_offsets()
     torch.cuda.synchronize()
+    for k, v in ERROR_ENVS[env].items():
+        monkeypatch.setenv(k, v)
     so0, ro0 = st.send_off.clone(), st.recv_off.clone()
     for which, idx, delta in (("send", (1, 2), 1), ("recv", (0, 1), -1), ("send", (3, 0), 2),
-                              ("recv", (2, 4), 1)):
+                              ("recv", (2, W), 1), ("send", (W - 1, W - 1), -1),
+                              ("recv", (W - 1, W // 2), 1), ("send", (0, W), -1)):
         st.send_off.copy_(so0); st.recv_off.copy_(ro0); st.status.zero_()
         (st.send_off if which == "send" else st.recv_off)[idx] += delta
         ins = [upload_rows(x) for x in X]
@@ -158,9 +183,10 @@ def test_copy_rejects_foreign_offsets(ref):
         rst = ref.copy(R, [x.reshape(-1) for x in X], np.full(W, n), Y, caps, S,
                        st.send_off.cpu().numpy(), st.recv_off.cpu().numpy())
         gst = int(st.status.item())
-        _say("foreign offsets", which, idx, gst, rst)
+        _say("foreign offsets", which, idx, "W", W, "R", R, env, gst, rst)
         assert gst == rst and gst & B.ST_BAD_OFFSETS
         assert all(bool((b.view == SENT).all().item()) and b.guards_intact() for b in outs)
+        assert all(b.guards_intact() for b in ins)
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
