@@ -29,7 +29,8 @@ __all__ = [
     "moe_pack_dispatch_workspace_bytes", "moe_pack_dispatch", "moe_unpack_return_workspace_bytes",
     "moe_unpack_return", "moe_combine_return_workspace_bytes", "moe_combine_return",
     "keys_bucketize_workspace_bytes",
-    "keys_bucketize", "keys_exchange_workspace_bytes", "keys_exchange", "a2av_device_copy",
+    "keys_bucketize", "keys_exchange_workspace_bytes", "keys_exchange",
+    "keys_exchange_noalloc", "NOALLOC_SCRATCH_BYTES", "a2av_device_copy",
     "MAX_TABLES",
 ]
 
@@ -40,6 +41,7 @@ MAX_W = 64
 MAX_SPLIT = 1 << 40
 MAX_EXPERTS = 4096
 MAX_TABLES = 4096
+NOALLOC_SCRATCH_BYTES = 1 << 20
 ST_BAD_SPLIT = 1
 ST_SEND_OVERRUN = 2
 ST_RECV_OVERFLOW = 4
@@ -111,12 +113,14 @@ def lib():
         L.keys_exchange_workspace_bytes.restype = sz
         L.keys_exchange.argtypes = [i32, i32, i64, vpp, vpp, i64p, vpp, i64p, vpp, i64p, vp, vp, vp,
                                     vp, sz, vp, vp]
+        L.keys_exchange_noalloc.argtypes = [i32, i32, i64, vpp, vpp, i64p, vpp, i64p, vpp, i64p,
+                                            vp, vp, vp, vp, vp]
         L.a2av_device_copy.argtypes = [vp, vp, sz, vp]
         for f in ("a2av_exchange_splits", "a2av_offsets", "a2av_copy", "a2av_all_to_all_vdev",
                   "moe_pack", "moe_unpack", "moe_combine", "moe_regroup", "moe_dispatch_grouped",
                   "moe_combine_grouped", "moe_pack_dispatch", "moe_unpack_return",
                   "moe_combine_return",
-                  "keys_bucketize", "keys_exchange",
+                  "keys_bucketize", "keys_exchange", "keys_exchange_noalloc",
                   "a2av_device_copy"):
             getattr(L, f).restype = i32
         _lib = L
@@ -410,8 +414,28 @@ def keys_exchange(W, n_tables, batch, lengths, keys, n_keys, lengths_out, length
                                _dev(status, "status"), _stream(stream, status)))
 
 
+def keys_exchange_noalloc(W, n_tables, batch, lengths, keys, n_keys, lengths_out, lengths_cap,
+                          keys_out, keys_cap, split_keys, split_lengths, recv_off_keys, status,
+                          stream=None):
+    """keys_exchange with the library's fixed per-GPU scratch instead of a
+    workspace (allocates nothing)."""
+    if any(len(x) != W for x in (lengths, keys, n_keys, lengths_out, lengths_cap, keys_out,
+                                 keys_cap)):
+        raise ValueError("every per-rank list needs W entries")
+    _check("keys_exchange_noalloc",
+           lib().keys_exchange_noalloc(int(W), int(n_tables), int(batch),
+                                       _ptr_array(lengths, "lengths"), _ptr_array(keys, "keys"),
+                                       _i64_array(n_keys), _ptr_array(lengths_out, "lengths_out"),
+                                       _i64_array(lengths_cap), _ptr_array(keys_out, "keys_out"),
+                                       _i64_array(keys_cap), _dev(split_keys, "split_keys"),
+                                       _dev(split_lengths, "split_lengths"),
+                                       _dev(recv_off_keys, "recv_off_keys"),
+                                       _dev(status, "status"), _stream(stream, status)))
+
+
 def a2av_device_copy(dst, src, nbytes, stream=None):
     """Plain contiguous copy of nbytes from src to dst (bandwidth ceiling)."""
     _check("a2av_device_copy",
            lib().a2av_device_copy(_dev(dst, "dst"), _dev(src, "src"), int(nbytes),
                                   _stream(stream, dst)))
+

@@ -22,6 +22,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -898,17 +899,55 @@ A2AV_API size_t keys_exchange_workspace_bytes(int W, int n_tables) {
     return round256(i64s * 8) + round256(2 * (size_t)W * B * 4) + round256(2 * (size_t)W * 4);
 }
 
-A2AV_API int keys_exchange(int W, int n_tables, int64_t batch, const int32_t *const *lengths,
-                           const int64_t *const *keys, const int64_t *n_keys,
-                           int32_t *const *lengths_out, const int64_t *lengths_cap,
-                           int64_t *const *keys_out, const int64_t *keys_cap, int64_t *split_keys,
-                           int64_t *split_lengths, int64_t *recv_off_keys, void *workspace,
-                           size_t workspace_bytes, int32_t *status, hipStream_t stream) {
+// ------------------------------------------------------------ fixed scratch
+// The scratch of keys_exchange_noalloc: one array in the library's device
+// code, which every GPU the library runs on holds a copy of until the process
+// ends, so a call allocates nothing. In host code `scratch` names a host-side
+// stand-in, not a device address: host code never passes it to a kernel or a
+// copy, only the address hipGetSymbolAddress gives on the stream's GPU,
+// looked up once per GPU with that GPU current and kept.
+static __device__ __align__(256) unsigned char scratch[A2AV_NOALLOC_SCRATCH_BYTES];
+
+namespace a2av {
+
+constexpr int kMaxDevices = 256;
+
+static void *noalloc_scratch(hipStream_t stream) {
+    static std::mutex mu;
+    static void *ptr[kMaxDevices] = {};
+    int dev = 0;
+    if (stream == nullptr || hipStreamGetDevice(stream, &dev) != hipSuccess) {
+        if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptr[dev] == nullptr) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || p == nullptr) return nullptr;
+        ptr[dev] = p;
+    }
+    return ptr[dev];
+}
+
+// The body of keys_exchange on a workspace of at least
+// keys_exchange_workspace_bytes(W, n_tables) bytes, which the callers check;
+// a null workspace means the fixed scratch of the stream's GPU, looked up
+// once every argument has passed.
+static int keys_exchange_run(int W, int n_tables, int64_t batch, const int32_t *const *lengths,
+                             const int64_t *const *keys, const int64_t *n_keys,
+                             int32_t *const *lengths_out, const int64_t *lengths_cap,
+                             int64_t *const *keys_out, const int64_t *keys_cap,
+                             int64_t *split_keys, int64_t *split_lengths, int64_t *recv_off_keys,
+                             void *workspace, int32_t *status, hipStream_t stream) {
     if (W < 1 || W > A2AV_MAX_W || n_tables < 0 || n_tables > A2AV_MAX_TABLES || batch < 0 ||
         !lengths || !keys || !n_keys || !lengths_out || !lengths_cap || !keys_out || !keys_cap ||
         !split_keys || !split_lengths || !recv_off_keys || !status)
         return A2AV_EARG;
-    if (!workspace || workspace_bytes < keys_exchange_workspace_bytes(W, n_tables)) return A2AV_EARG;
     if (n_tables > 0 && batch > ((int64_t)1 << 40) / n_tables) return A2AV_EARG;
     const int64_t nl = (int64_t)n_tables * batch;
     const int cmax = (n_tables + W - 1) / W;
@@ -947,6 +986,10 @@ A2AV_API int keys_exchange(int W, int n_tables, int64_t batch, const int32_t *co
         kout += (uint64_t)keys_cap[r];
         lout += (uint64_t)lengths_cap[r];
         lal = lal && ((uintptr_t)lengths[r] % 16 == 0) && ((uintptr_t)lengths_out[r] % 16 == 0);
+    }
+    if (workspace == nullptr) {
+        workspace = noalloc_scratch(stream);
+        if (workspace == nullptr) return A2AV_EHIP;
     }
     // workspace: tk | kdst | ldst | ksrc | lsrc | src rank [2W][B] | bits [2W].
     // The keys and lengths plans sit back to back, so that with 2W ranks at
@@ -1024,6 +1067,35 @@ A2AV_API int keys_exchange(int W, int n_tables, int64_t batch, const int32_t *co
         if (lmax > 0) launch_block_copy(cl, lmax, lal, stream);
     }
     return hipGetLastError() == hipSuccess ? A2AV_OK : A2AV_EHIP;
+}
+
+}  // namespace a2av
+
+A2AV_API int keys_exchange(int W, int n_tables, int64_t batch, const int32_t *const *lengths,
+                           const int64_t *const *keys, const int64_t *n_keys,
+                           int32_t *const *lengths_out, const int64_t *lengths_cap,
+                           int64_t *const *keys_out, const int64_t *keys_cap, int64_t *split_keys,
+                           int64_t *split_lengths, int64_t *recv_off_keys, void *workspace,
+                           size_t workspace_bytes, int32_t *status, hipStream_t stream) {
+    const size_t need = keys_exchange_workspace_bytes(W, n_tables);
+    if (need == 0 || !workspace || workspace_bytes < need) return A2AV_EARG;
+    return keys_exchange_run(W, n_tables, batch, lengths, keys, n_keys, lengths_out, lengths_cap,
+                             keys_out, keys_cap, split_keys, split_lengths, recv_off_keys,
+                             workspace, status, stream);
+}
+
+A2AV_API int keys_exchange_noalloc(int W, int n_tables, int64_t batch,
+                                   const int32_t *const *lengths, const int64_t *const *keys,
+                                   const int64_t *n_keys, int32_t *const *lengths_out,
+                                   const int64_t *lengths_cap, int64_t *const *keys_out,
+                                   const int64_t *keys_cap, int64_t *split_keys,
+                                   int64_t *split_lengths, int64_t *recv_off_keys,
+                                   int32_t *status, hipStream_t stream) {
+    const size_t need = keys_exchange_workspace_bytes(W, n_tables);
+    if (need == 0 || need > A2AV_NOALLOC_SCRATCH_BYTES) return A2AV_EARG;
+    return keys_exchange_run(W, n_tables, batch, lengths, keys, n_keys, lengths_out, lengths_cap,
+                             keys_out, keys_cap, split_keys, split_lengths, recv_off_keys,
+                             nullptr, status, stream);
 }
 
 A2AV_API size_t moe_dispatch_grouped_workspace_bytes(int W, int E) {

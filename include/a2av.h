@@ -559,6 +559,39 @@ int keys_exchange(int W, int n_tables, int64_t batch, const int32_t *const *leng
                   size_t workspace_bytes, int32_t *status, hipStream_t stream);
 
 /*
+ * Scratch bytes per GPU behind keys_exchange_noalloc (1 MiB): room for
+ * keys_exchange_workspace_bytes(W, n_tables) up to about 2700 tables at
+ * W = 8, or 280 tables at W = 64.
+ */
+#define A2AV_NOALLOC_SCRATCH_BYTES ((size_t)1 << 20)
+
+/*
+ * keys_exchange for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same arguments without the workspace; the same kernels, outputs and
+ * status bits. Its scratch is one fixed array of A2AV_NOALLOC_SCRATCH_BYTES
+ * in the library's device code: each GPU the library runs on holds its own
+ * copy until the process ends, and its address on a GPU is looked up (with
+ * that GPU made current for the lookup) on the first call whose stream runs
+ * there, then kept. A call allocates nothing: no hipMalloc, no hipFree, no
+ * library routine that allocates.
+ *   returns A2AV_EARG (nothing enqueued) for every argument keys_exchange
+ *           rejects and when keys_exchange_workspace_bytes(W, n_tables)
+ *           exceeds A2AV_NOALLOC_SCRATCH_BYTES; A2AV_EHIP when the array's
+ *           address cannot be found on the stream's GPU.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (no call needs any of it cleared: each writes what it reads before
+ * reading it). Calls that overlap in time on one GPU, from different streams
+ * or host threads, therefore race: the caller serialises them.
+ */
+int keys_exchange_noalloc(int W, int n_tables, int64_t batch, const int32_t *const *lengths,
+                          const int64_t *const *keys, const int64_t *n_keys,
+                          int32_t *const *lengths_out, const int64_t *lengths_cap,
+                          int64_t *const *keys_out, const int64_t *keys_cap,
+                          int64_t *split_keys, int64_t *split_lengths, int64_t *recv_off_keys,
+                          int32_t *status, hipStream_t stream);
+
+/*
  * Plain contiguous device copy of `bytes` bytes (dst and src device pointers,
  * not overlapping), with the same copy loop as a2av_copy. A bandwidth
  * ceiling for the payload kernel and the reference for counter scaling.

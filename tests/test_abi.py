@@ -170,6 +170,23 @@ def test_host_argument_errors(L):
                            vp(8), wsx - 1, vp(8), None) == EARG
     assert L.keys_exchange(2, 26, 8, ptrs, ptrs, two, ptrs, negr, ptrs, two, vp(8), vp(8), vp(8),
                            vp(8), wsx, vp(8), None) == EARG
+    # the no-allocation exchange: sizes whose scratch exceeds its fixed array,
+    # then the exchange's own checks, all before any device call
+    from embeddings_a2av_virtual_amd import _binding as B
+    p64 = (ctypes.c_void_p * 64)(*([8] * 64))
+    z64 = (ctypes.c_int64 * 64)(*([0] * 64))
+    assert L.keys_exchange_workspace_bytes(64, 4096) > B.NOALLOC_SCRATCH_BYTES
+    assert L.keys_exchange_workspace_bytes(8, 26) <= B.NOALLOC_SCRATCH_BYTES
+    assert L.keys_exchange_noalloc(64, 4096, 1, p64, p64, z64, p64, z64, p64, z64, vp(8), vp(8),
+                                   vp(8), vp(8), None) == EARG
+    assert L.keys_exchange_noalloc(2, 4097, 8, ptrs, ptrs, two, ptrs, two, ptrs, two, vp(8),
+                                   vp(8), vp(8), vp(8), None) == EARG
+    assert L.keys_exchange_noalloc(2, 26, 8, ptrs, ptrs, two, ptrs, negr, ptrs, two, vp(8),
+                                   vp(8), vp(8), vp(8), None) == EARG
+    assert L.keys_exchange_noalloc(2, 26, -1, ptrs, ptrs, two, ptrs, two, ptrs, two, vp(8),
+                                   vp(8), vp(8), vp(8), None) == EARG
+    assert L.keys_exchange_noalloc(2, 26, 8, ptrs, ptrs, two, ptrs, two, ptrs, two, vp(8),
+                                   vp(8), vp(8), None, None) == EARG
 
 
 def test_workspace_formula(L):
