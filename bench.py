@@ -6,8 +6,9 @@ exchange -> offsets -> payload copy, three C-ABI calls on one stream. The
 default workload is W=4 ranks x 32 MiB (4096 rows x 4096 bf16, 8 KiB rows)
 with multinomial splits, the message size of the MoE region on the tuning
 page. The printed value is effective HBM throughput: payload bytes read plus
-bytes written (2 x row bytes x rows moved) per second of wall clock over the
-timed steps, inputs resident in HBM.
+bytes written (2 x row bytes x rows moved) per second of GPU time over the
+timed steps (HIP events on the launch stream, inside a region synchronized on
+both sides), inputs resident in HBM.
 
 Several independent buffer sets are cycled so that no step finds its inputs
 in the 256 MB Infinity Cache left behind by the step before.
@@ -20,9 +21,11 @@ Also reported on the same JSON line:
   cpu_baseline  the CPU oracle on the same workload on this host
   headline      W in {4, 8} x {32 MiB, 1 GiB} per rank, and W in {16, 64} at
                 32 MiB, payload kernel and step
+  sweep         W=4 at 1..4096 MiB per rank, uniform and 50%-zero splits
   ceilings      plain device copy of the same bytes (this library's copy loop
-                and torch's D2D copy), and the exchange as W*W separate
-                device-to-device copies (the library-call baseline)
+                and torch's D2D copy), read-only and write-only streams, and
+                the exchange as W*W separate device-to-device copies (the
+                library-call baseline)
 """
 from __future__ import annotations
 
@@ -39,7 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "a2av_wave_w4_32mib_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "embeddings_a2av_virtual_amd", "csrc", f)
-                  for f in ("a2av.hip", "common.hpp")]
+                  for f in ("a2av.hip", "common.hpp", "bounds.h")]
 
 
 def gbps(nbytes: float, seconds: float) -> float:
@@ -107,9 +110,12 @@ def run_config(torch, B, I, W, mib, steps, warmup, nsets, entry="fused", splits=
 
     The timed region holds the steps and nothing else: a barrier-free
     synchronize, host clock, one HIP event on the launch stream, the steps,
-    one more event, synchronize. Step throughput is payload bytes over the host
-    clock; the GPU time between the two events over `steps` is the average
-    launch duration (for the fused entry a step is one kernel). For the
+    one more event, synchronize. Step throughput is payload bytes over the GPU
+    time between the two events (device timing, not the host clock, which
+    adds the first launch's latency and the final wake-up to a region of a
+    millisecond); the host-clock figure is kept beside it. That time over
+    `steps` is also the average launch duration (for the fused entry a step
+    is one kernel). For the
     three-call entry a second pass times `steps` a2av_copy launches back to
     back (the offsets the first pass left in every set) to time that kernel
     alone."""
@@ -151,14 +157,14 @@ def run_config(torch, B, I, W, mib, steps, warmup, nsets, entry="fused", splits=
     res = {
         "W": W, "mib_per_rank": mib, "row_bytes": cols * 2, "steps": steps, "entry": entry,
         "bytes_per_step": statistics.mean(moved),
-        "step_ms": wall / steps * 1e3,
-        "step_gbs": gbps(sum(moved), wall),
-        "gpu_step_ms": gpu_ms / steps,
-        "gpu_step_gbs": gbps(sum(moved), gpu_ms / 1e3),
+        "step_ms": gpu_ms / steps,
+        "step_gbs": gbps(sum(moved), gpu_ms / 1e3),
+        "host_step_ms": wall / steps * 1e3,
+        "host_step_gbs": gbps(sum(moved), wall),
     }
     if entry == "fused":
         res["kernel_ms_mean"] = gpu_ms / steps
-        res["kernel_gbs"] = res["gpu_step_gbs"]
+        res["kernel_gbs"] = res["step_gbs"]
         # per-launch distribution from an event pair around each call (the
         # pair adds a little time of its own, so these read slightly high)
         n = min(steps, 100)
@@ -186,6 +192,20 @@ def run_config(torch, B, I, W, mib, steps, warmup, nsets, entry="fused", splits=
         copy_ms = e0.elapsed_time(e1)
         res["kernel_ms_mean"] = copy_ms / steps
         res["kernel_gbs"] = gbps(sum(moved), copy_ms / 1e3)
+        # control: the same copies, each after two launches of a kernel that
+        # writes one word (torch's fill of a one-element tensor), in place of
+        # the splits exchange and the offsets: what two dependent launches
+        # cost between copies, whatever they do
+        tiny = torch.zeros(1, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            tiny.fill_(i)
+            tiny.fill_(i + 1)
+            assert L.a2av_copy(*sets[i % nsets].copy_args) == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res["two_fills_then_copy_ms"] = e0.elapsed_time(e1) / steps
     for vs in sets:
         st = int(vs.st.status.item())
         if st != 0:
@@ -234,27 +254,59 @@ def naive_per_chunk(torch, I, W=4, mib=32, reps=50, nsets=8):
     return gbps(moved, a.elapsed_time(b) / 1e3)
 
 
+def _time_rotating(torch, fn, bufs, reps, nbytes):
+    """GB/s of reps calls fn(buf) over rotating buffers, between two events."""
+    n = len(bufs)
+    for i in range(3):
+        fn(bufs[i % n])
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(reps):
+        fn(bufs[i % n])
+    b.record()
+    torch.cuda.synchronize()
+    return gbps(nbytes * reps, a.elapsed_time(b) / 1e3)
+
+
 def ceilings(torch, B, nbytes, reps=50, nsets=8):
-    """Plain contiguous copies of the same byte count (read n + write n)."""
+    """Plain contiguous copies of the same byte count (read n/2 + write n/2),
+    and one-direction streams of n bytes (read only; written only, with
+    non-temporal and with ordinary stores), at that size and at 4 GiB, the
+    order of the MoE rows' traffic. Buffers rotate so the Infinity Cache
+    holds none of them."""
     half = nbytes // 2
     srcs = [torch.empty(half, dtype=torch.uint8, device="cuda").fill_(i) for i in range(nsets)]
     dsts = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
     out = {}
-    for name, fn in (("device_copy", lambda d, s: B.a2av_device_copy(d, s, half)),
-                     ("torch_d2d", lambda d, s: d.copy_(s))):
-        for i in range(5):
-            fn(dsts[i % nsets], srcs[i % nsets])
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for i in range(reps):
-            fn(dsts[i % nsets], srcs[i % nsets])
-        b.record()
-        torch.cuda.synchronize()
-        out[name + "_gbs"] = gbps(2 * half * reps, a.elapsed_time(b) / 1e3)
-    del srcs, dsts
+    pairs = list(zip(dsts, srcs))
+    out["device_copy_gbs"] = _time_rotating(
+        torch, lambda p: B.a2av_device_copy(p[0], p[1], half), pairs, reps, 2 * half)
+    out["torch_d2d_gbs"] = _time_rotating(torch, lambda p: p[0].copy_(p[1]), pairs, reps, 2 * half)
+    del srcs, dsts, pairs
     torch.cuda.empty_cache()
+    sink = torch.zeros(B.SINK_WORDS, dtype=torch.int64, device="cuda")
+    for tag, size, n, r in (("", nbytes, nsets, reps), ("_4gib", 4 << 30, 2, 6)):
+        bufs = [torch.empty(size, dtype=torch.uint8, device="cuda").fill_(i) for i in range(n)]
+        out[f"read_only{tag}_gbs"] = _time_rotating(
+            torch, lambda t: B.a2av_device_read(t, size, sink), bufs, r, size)
+        out[f"write_only_nt{tag}_gbs"] = _time_rotating(
+            torch, lambda t: B.a2av_device_fill(t, size, 0x5A5A5A5A, True), bufs, r, size)
+        out[f"write_only{tag}_gbs"] = _time_rotating(
+            torch, lambda t: B.a2av_device_fill(t, size, 0x5A5A5A5A, False), bufs, r, size)
+        del bufs
+        torch.cuda.empty_cache()
     return out
+
+
+def direction_ceiling(ceil, read_bytes, write_bytes):
+    """The ceiling a kernel moving read_bytes in and write_bytes out faces if
+    HBM serves the two directions one after the other at the one-direction
+    rates measured at 4 GiB: total bytes / (reads / read rate + writes /
+    write rate), the write rate being the better of the two store kinds."""
+    cr = ceil["read_only_4gib_gbs"]
+    cw = max(ceil["write_only_nt_4gib_gbs"], ceil["write_only_4gib_gbs"])
+    return (read_bytes + write_bytes) / (read_bytes / cr + write_bytes / cw)
 
 
 def host_cpu():
@@ -466,10 +518,11 @@ class KeyChain:
 def time_overlap(torch, fa, fb, sa, sb, reps=20):
     """GPU time (ms) per repetition of a then b on stream sa, and of a on sa
     alongside b on sb (b's stream waits for the repetition's start and sa for
-    b's end, so a repetition ends when both have)."""
-    def serial():
-        fa()
-        fb_s()
+    b's end, so a repetition ends when both have). Also b's latency: from the
+    repetition's start to b's end, median over the repetitions, when b is
+    queued behind a on one stream and when it runs on its own stream."""
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
 
     fb_s = fb["on_a"]
     fb_b = fb["on_b"]
@@ -477,15 +530,21 @@ def time_overlap(torch, fa, fb, sa, sb, reps=20):
         fa()
         fb_s()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = ev(), ev()
+    starts = [ev() for _ in range(reps)]
+    b_done = [ev() for _ in range(reps)]
     e0.record(sa)
-    for _ in range(reps):
-        serial()
+    for i in range(reps):
+        starts[i].record(sa)
+        fa()
+        fb_s()
+        b_done[i].record(sa)
     e1.record(sa)
     torch.cuda.synchronize()
     t_serial = e0.elapsed_time(e1) / reps
-    starts = [torch.cuda.Event() for _ in range(reps)]
-    ends = [torch.cuda.Event() for _ in range(reps)]
+    lat_serial = statistics.median(starts[i].elapsed_time(b_done[i]) for i in range(reps))
+    starts = [ev() for _ in range(reps)]
+    b_done = [ev() for _ in range(reps)]
     torch.cuda.synchronize()
     e0.record(sa)
     for i in range(reps):
@@ -493,15 +552,16 @@ def time_overlap(torch, fa, fb, sa, sb, reps=20):
         sb.wait_event(starts[i])
         fa()
         fb_b()
-        ends[i].record(sb)
-        sa.wait_event(ends[i])
+        b_done[i].record(sb)
+        sa.wait_event(b_done[i])
     e1.record(sa)
     torch.cuda.synchronize()
     t_over = e0.elapsed_time(e1) / reps
-    return t_serial, t_over
+    lat_own = statistics.median(starts[i].elapsed_time(b_done[i]) for i in range(reps))
+    return t_serial, t_over, lat_serial, lat_own
 
 
-def moe_rows(torch, B, I, o, out):
+def moe_rows(torch, B, I, o, out, ceil=None):
     """MoE dispatch workload: W=8, 8192 tokens x 7168 bf16 per rank, top-8 of
     256 Zipf(1.1) experts. pack -> dispatch a2av -> regroup to expert-major
     and back -> return a2av -> combine (weighted) and un-pack."""
@@ -533,6 +593,8 @@ def moe_rows(torch, B, I, o, out):
         cpu = dict(cpu_bytes=Ts * R + Ts * k * R + Ts * k * 12, cpu_s=cs,
                    note="one rank, 1024 tokens")
     out["moe_pack"] = row_entry(pack_bytes, ms, **cpu)
+    # one token row read, k written (plus ids, perm written and read back)
+    pack_rw = (W * (T * R + Q * 4 + Q * 8), W * (Q * R + Q * 8))
     # ---- dispatch a2av with the pack's splits (rank 0 receives ~66 % of all rows)
     fwd = A2av(W)
     fwd.S.copy_(S)
@@ -620,6 +682,11 @@ def moe_rows(torch, B, I, o, out):
                                       1, pdws, pdst)
     out["moe_pack_dispatch"] = row_entry(pack_bytes, time_events(torch, pd0, 5))
     out["moe_pack_dispatch_grouped"] = row_entry(pack_bytes, time_events(torch, pd1, 5))
+    if ceil:
+        dc = direction_ceiling(ceil, *pack_rw)
+        for key in ("moe_pack", "moe_pack_dispatch", "moe_pack_dispatch_grouped"):
+            out[key]["direction_ceiling_gbs"] = round(dc, 1)
+            out[key]["frac_of_direction_ceiling"] = round(out[key]["gbs"] / dc, 4)
     urws = torch.empty(B.moe_unpack_return_workspace_bytes(W, E), dtype=torch.uint8,
                        device="cuda")
     urst = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -798,19 +865,45 @@ def overlap_rows(torch, B, I, moe, out):
     disp = lambda: L.a2av_all_to_all_vdev(*disp_args)
     small = VSet(torch, B, I, 4, 4096, 4096, seed=77, stream_handle=sa.cuda_stream)
     a32 = lambda: L.a2av_all_to_all_vdev(*small.fused_args)
-    for name, fa in (("dispatch_a2av", disp), ("a2av_w4_32mib", a32)):
-        t_a = time_events(torch, fa, 10)
-        ts, to = time_overlap(torch, fa, {"on_a": ka.fused, "on_b": kb.fused}, sa, sb)
+    # an expert-sized bf16 GEMM (2048 rows x 7168 -> 4096): compute-bound, so
+    # it leaves HBM time for the key exchange to fill
+    ga = torch.randn(2048, 7168, device="cuda").to(torch.bfloat16)
+    gb = torch.randn(7168, 4096, device="cuda").to(torch.bfloat16).contiguous()
+    gc = torch.empty(2048, 4096, dtype=torch.bfloat16, device="cuda")
+    gemm = lambda: torch.matmul(ga, gb, out=gc)
+    cases = (("dispatch_a2av", disp, None), ("a2av_w4_32mib", a32, None),
+             ("gemm_expert", gemm, None),
+             # the same a2av neighbours without the occupancy cap (no unused LDS
+             # reserved per workgroup): how much of any loss the cap causes
+             ("dispatch_a2av_no_cap", disp, "0"), ("a2av_w4_32mib_no_cap", a32, "0"))
+    for name, fa, lds in cases:
+        old = os.environ.get("A2AV_WAVE_LDS")
+        if lds is not None:
+            os.environ["A2AV_WAVE_LDS"] = lds
+        try:
+            t_a = time_events(torch, fa, 10)
+            ts, to, ls, lo = time_overlap(torch, fa, {"on_a": ka.fused, "on_b": kb.fused}, sa, sb)
+        finally:
+            if lds is not None:
+                if old is None:
+                    del os.environ["A2AV_WAVE_LDS"]
+                else:
+                    os.environ["A2AV_WAVE_LDS"] = old
         res[name] = {"a_us": round(t_a * 1e3, 2), "keys_us": round(t_keys * 1e3, 2),
                      "serial_us": round(ts * 1e3, 2), "overlapped_us": round(to * 1e3, 2),
-                     "hidden_frac_of_keys": round((ts - to) / t_keys, 3)}
+                     "hidden_frac_of_keys": round((ts - to) / t_keys, 3),
+                     # when the keys are ready: behind the neighbour on its stream,
+                     # or on a stream of their own
+                     "keys_done_us_same_stream": round(ls * 1e3, 2),
+                     "keys_done_us_own_stream": round(lo * 1e3, 2)}
+        log("bench: overlap", name, json.dumps(res[name]))
     torch.cuda.synchronize()
     _check_status(B, [("keys a", ka.fstatus), ("keys b", kb.fstatus), ("a2av", small.st.status),
                       ("dispatch", fwd.status)])
     out["key_exchange_overlap"] = res
 
 
-def row_benchmarks(torch, B, I, with_cpu=True):
+def row_benchmarks(torch, B, I, with_cpu=True, ceil=None):
     """The other steps of the path, each at its full size. GB/s counts
     algorithmic bytes (payload read + written, plus index and weight bytes
     where a kernel reads them)."""
@@ -820,7 +913,7 @@ def row_benchmarks(torch, B, I, with_cpu=True):
     if with_cpu:
         from oracle.ref import Oracle
         o = Oracle()
-    moe = moe_rows(torch, B, I, o, out)
+    moe = moe_rows(torch, B, I, o, out, ceil)
     key_rows(torch, B, I, o, out)
     overlap_rows(torch, B, I, moe, out)
     del moe
@@ -848,8 +941,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the MoE pack / un-pack and key-exchange measurements")
-    ap.add_argument("--sweep", action="store_true",
-                    help="also time W=4 at 1..4096 MiB per rank, uniform and 50%%-zero splits")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the size sweep (W=4 at 1..4096 MiB per rank, uniform and "
+                         "50%%-zero splits)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -891,9 +985,12 @@ def main(argv=None):
                     "step_us": round(r["step_ms"] * 1e3, 2)}
                 if "per_launch_us" in r:
                     headline[key]["per_launch_us"] = r["per_launch_us"]
+                if "two_fills_then_copy_ms" in r:
+                    headline[key]["two_fills_then_copy_us"] = round(
+                        r["two_fills_then_copy_ms"] * 1e3, 2)
                 log("bench: headline", key, json.dumps(headline[key]))
     sweep = {}
-    if args.sweep:
+    if not args.no_sweep:
         for splits in ("uniform", "half_zero"):
             for mib in [1 << i for i in range(13)]:
                 per_step = 2 * 4 * mib << 20
@@ -902,7 +999,8 @@ def main(argv=None):
                 r = run_config(torch, B, I, 4, mib, steps, 3, nsets, "fused", splits)
                 sweep[f"{splits}_{mib}mib"] = {"kernel_gbs": round(r["kernel_gbs"], 1),
                                                "kernel_us": round(r["kernel_ms_mean"] * 1e3, 2),
-                                               "step_gbs": round(r["step_gbs"], 1)}
+                                               "frac": round(r["kernel_gbs"] / HBM_PEAK_GBS, 4),
+                                               "steps": steps}
                 log("bench: sweep", splits, mib, json.dumps(sweep[f"{splits}_{mib}mib"]))
     ceil = ceilings(torch, B, int(main_res["bytes_per_step"]))
     ceil["naive_w2_memcpy_gbs"] = naive_per_chunk(torch, I)
@@ -910,7 +1008,7 @@ def main(argv=None):
 
     rows = {}
     if not args.no_rows:
-        rows = row_benchmarks(torch, B, I, with_cpu=not args.no_cpu)
+        rows = row_benchmarks(torch, B, I, with_cpu=not args.no_cpu, ceil=ceil)
         log("bench: rows", json.dumps(rows))
 
     cpu = None if args.no_cpu else cpu_baseline(torch, I)
@@ -940,9 +1038,15 @@ def main(argv=None):
                    "W": 4, "rows_per_rank": 4096, "row_bytes": 8192, "payload": "bf16",
                    "rotating_sets": args.sets,
                    "frac_of_hbm_peak": round(main_res["step_gbs"] / HBM_PEAK_GBS, 4),
+                   "timing": "HIP events on the launch stream around the K steps, inside the "
+                             "synchronized region",
+                   "host_clock_gbs": round(main_res["host_step_gbs"], 1),
+                   "host_clock_ms_per_step": round(main_res["host_step_ms"], 5),
                    "three_call_step_gbs": round(three["step_gbs"], 1),
                    "three_call_copy_kernel_gbs": round(three["kernel_gbs"], 1),
                    "three_call_copy_kernel_frac": round(three["kernel_gbs"] / HBM_PEAK_GBS, 4),
+                   "three_call_step_us": round(three["step_ms"] * 1e3, 2),
+                   "two_fills_then_copy_us": round(three["two_fills_then_copy_ms"] * 1e3, 2),
                    "per_launch_us": main_res.get("per_launch_us")},
         "roofline": {"bound": "hbm", "kernel": "k_a2av_wave (one launch: exchange+offsets+copy)",
                      "achieved": round(achieved, 1),

@@ -31,6 +31,7 @@ __all__ = [
     "keys_bucketize_workspace_bytes",
     "keys_bucketize", "keys_exchange_workspace_bytes", "keys_exchange",
     "keys_exchange_noalloc", "NOALLOC_SCRATCH_BYTES", "a2av_device_copy",
+    "a2av_device_read", "a2av_device_fill", "SINK_WORDS",
     "MAX_TABLES",
 ]
 
@@ -42,6 +43,7 @@ MAX_SPLIT = 1 << 40
 MAX_EXPERTS = 4096
 MAX_TABLES = 4096
 NOALLOC_SCRATCH_BYTES = 1 << 20
+SINK_WORDS = 4096
 ST_BAD_SPLIT = 1
 ST_SEND_OVERRUN = 2
 ST_RECV_OVERFLOW = 4
@@ -116,12 +118,14 @@ def lib():
         L.keys_exchange_noalloc.argtypes = [i32, i32, i64, vpp, vpp, i64p, vpp, i64p, vpp, i64p,
                                             vp, vp, vp, vp, vp]
         L.a2av_device_copy.argtypes = [vp, vp, sz, vp]
+        L.a2av_device_read.argtypes = [vp, sz, vp, vp]
+        L.a2av_device_fill.argtypes = [vp, sz, ctypes.c_uint32, i32, vp]
         for f in ("a2av_exchange_splits", "a2av_offsets", "a2av_copy", "a2av_all_to_all_vdev",
                   "moe_pack", "moe_unpack", "moe_combine", "moe_regroup", "moe_dispatch_grouped",
                   "moe_combine_grouped", "moe_pack_dispatch", "moe_unpack_return",
                   "moe_combine_return",
                   "keys_bucketize", "keys_exchange", "keys_exchange_noalloc",
-                  "a2av_device_copy"):
+                  "a2av_device_copy", "a2av_device_read", "a2av_device_fill"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -439,3 +443,19 @@ def a2av_device_copy(dst, src, nbytes, stream=None):
            lib().a2av_device_copy(_dev(dst, "dst"), _dev(src, "src"), int(nbytes),
                                   _stream(stream, dst)))
 
+
+def a2av_device_read(src, nbytes, sink, stream=None):
+    """Read nbytes of src once (read-only bandwidth ceiling); each wave XORs
+    the fold of what it read into one word of sink (SINK_WORDS int64)."""
+    if sink.numel() * sink.element_size() < SINK_WORDS * 8:
+        raise ValueError("sink needs SINK_WORDS int64 words")
+    _check("a2av_device_read",
+           lib().a2av_device_read(_dev(src, "src"), int(nbytes), _dev(sink, "sink"),
+                                  _stream(stream, src)))
+
+
+def a2av_device_fill(dst, nbytes, pattern, nontemporal=True, stream=None):
+    """Write the 32-bit pattern over nbytes of dst (write-only bandwidth ceiling)."""
+    _check("a2av_device_fill",
+           lib().a2av_device_fill(_dev(dst, "dst"), int(nbytes), int(pattern) & 0xFFFFFFFF,
+                                  1 if nontemporal else 0, _stream(stream, dst)))

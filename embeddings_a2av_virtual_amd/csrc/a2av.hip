@@ -671,6 +671,79 @@ __global__ __launch_bounds__(256) void k_device_copy_wave(unsigned char *dst, co
     }
 }
 
+// ====================================================================== one-direction ceilings
+// Streams that only read or only write, with the piece structure of the
+// plain copy (one piece per wave, 16-byte accesses, U of them in flight per
+// lane): the HBM ceilings for kernels whose traffic runs mostly one way,
+// such as the pack's row scatter, which writes k bytes for every byte it
+// reads.
+constexpr int kSinkWords = 4096;
+
+// Every 16-byte vector of src is read once. Each wave XOR-folds what it read
+// into one 64-bit word and XORs that into sink[wave mod kSinkWords] (one
+// atomic per wave, spread over 32 KiB), so the XOR of all sink words is the
+// fold of the XOR of every vector: the loads cannot be dropped and a test can
+// check that each was made.
+template <int U>
+__global__ __launch_bounds__(256) void k_device_read_wave(const unsigned char *src, uint64_t bytes,
+                                                          uint64_t piece, uint64_t *sink) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t wpb = blockDim.x / kWave;
+    const uint64_t gw = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave;
+    const uint64_t TW = (uint64_t)gridDim.x * wpb;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (uint64_t p = gw; p * piece < bytes; p += TW) {
+        const uint64_t lo = p * piece;
+        const uint64_t hi = lo + piece < bytes ? lo + piece : bytes;
+        const u32x4 *s = (const u32x4 *)(src + lo);
+        const uint64_t nv = (hi - lo) / 16;
+        for (uint64_t base = 0; base < nv; base += (uint64_t)kWave * U) {
+            u32x4 r[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const uint64_t i = base + (uint64_t)u * kWave + lane;
+                r[u] = ld<true>(s + (i < nv ? i : nv - 1));
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                // a clamped index re-read the last vector: it is not counted
+                const uint32_t m = base + (uint64_t)u * kWave + lane < nv ? ~0u : 0u;
+                acc.x ^= r[u].x & m;
+                acc.y ^= r[u].y & m;
+                acc.z ^= r[u].z & m;
+                acc.w ^= r[u].w & m;
+            }
+        }
+    }
+    uint64_t x = ((uint64_t)(acc.x ^ acc.z) << 32) | (uint64_t)(acc.y ^ acc.w);
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) x ^= (uint64_t)__shfl_xor((long long)x, o, kWave);
+    if (lane == 0 && x != 0) atomicXor((unsigned long long *)&sink[gw % kSinkWords], x);
+}
+
+// Every 16-byte vector of dst is written once with the pattern.
+template <int U, bool NT>
+__global__ __launch_bounds__(256) void k_device_fill_wave(unsigned char *dst, uint64_t bytes,
+                                                          uint64_t piece, uint32_t pattern) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t wpb = blockDim.x / kWave;
+    const uint64_t TW = (uint64_t)gridDim.x * wpb;
+    const u32x4 v = {pattern, pattern, pattern, pattern};
+    for (uint64_t p = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave; p * piece < bytes; p += TW) {
+        const uint64_t lo = p * piece;
+        const uint64_t hi = lo + piece < bytes ? lo + piece : bytes;
+        u32x4 *d = (u32x4 *)(dst + lo);
+        const uint64_t nv = (hi - lo) / 16;
+        for (uint64_t base = 0; base < nv; base += (uint64_t)kWave * U) {
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const uint64_t i = base + (uint64_t)u * kWave + lane;
+                st<NT>(d + (i < nv ? i : nv - 1), v);
+            }
+        }
+    }
+}
+
 // ====================================================================== launch config
 struct CopyTuning {
     int blocks_per_cu;
@@ -1004,6 +1077,50 @@ A2AV_API int a2av_all_to_all_vdev(int W, size_t row_bytes, const void *const *in
         return launch_status();
     }
     launch_payload<kFused>(a, payload_grid(t, stream), t, stream);
+    return launch_status();
+}
+
+A2AV_API int a2av_device_read(const void *src, size_t bytes, uint64_t *sink, hipStream_t stream) {
+    if (bytes == 0) return A2AV_OK;
+    if (!src || !sink || bytes % 16 != 0 || (uintptr_t)src % 16 != 0) return A2AV_EARG;
+    // the shapes of the plain copy moving as many bytes (read + write)
+    const WaveTuning wt = wave_tuning(2 * (uint64_t)bytes, bytes >= kShortTraffic, true);
+    const int grid = wave_grid(bytes, wt.piece);
+    const unsigned char *s = (const unsigned char *)src;
+    if (wt.unroll == 16)
+        hipLaunchKernelGGL((k_device_read_wave<16>), dim3(grid), dim3(256), wt.lds, stream, s,
+                           (uint64_t)bytes, wt.piece, sink);
+    else if (wt.unroll == 4)
+        hipLaunchKernelGGL((k_device_read_wave<4>), dim3(grid), dim3(256), wt.lds, stream, s,
+                           (uint64_t)bytes, wt.piece, sink);
+    else
+        hipLaunchKernelGGL((k_device_read_wave<8>), dim3(grid), dim3(256), wt.lds, stream, s,
+                           (uint64_t)bytes, wt.piece, sink);
+    return launch_status();
+}
+
+A2AV_API int a2av_device_fill(void *dst, size_t bytes, uint32_t pattern, int nontemporal,
+                              hipStream_t stream) {
+    if (bytes == 0) return A2AV_OK;
+    if (!dst || bytes % 16 != 0 || (uintptr_t)dst % 16 != 0) return A2AV_EARG;
+    const WaveTuning wt = wave_tuning(2 * (uint64_t)bytes, bytes >= kShortTraffic, true);
+    const int grid = wave_grid(bytes, wt.piece);
+    unsigned char *d = (unsigned char *)dst;
+#define A2AV_FILL(U)                                                                            \
+    if (nontemporal)                                                                            \
+        hipLaunchKernelGGL((k_device_fill_wave<U, true>), dim3(grid), dim3(256), wt.lds, stream, \
+                           d, (uint64_t)bytes, wt.piece, pattern);                              \
+    else                                                                                        \
+        hipLaunchKernelGGL((k_device_fill_wave<U, false>), dim3(grid), dim3(256), wt.lds,        \
+                           stream, d, (uint64_t)bytes, wt.piece, pattern);
+    if (wt.unroll == 16) {
+        A2AV_FILL(16)
+    } else if (wt.unroll == 4) {
+        A2AV_FILL(4)
+    } else {
+        A2AV_FILL(8)
+    }
+#undef A2AV_FILL
     return launch_status();
 }
 

@@ -598,6 +598,29 @@ int keys_exchange_noalloc(int W, int n_tables, int64_t batch, const int32_t *con
  */
 int a2av_device_copy(void *dst, const void *src, size_t bytes, hipStream_t stream);
 
+/* Words of the sink array a2av_device_read XORs into. */
+#define A2AV_SINK_WORDS 4096
+
+/*
+ * One-direction bandwidth ceilings, with the pieces, access width and launch
+ * shapes of a2av_device_copy moving as many bytes; for measurement, as the
+ * ceilings of kernels whose traffic runs mostly one way (the pack's row
+ * scatter writes k bytes for each byte it reads). Both want `bytes` a
+ * multiple of 16 and a 16-byte-aligned buffer (else A2AV_EARG).
+ *   a2av_device_read   reads every byte of src once and writes only the
+ *                      device int64 sink[A2AV_SINK_WORDS] (caller-zeroed): each
+ *                      wave XORs the 64-bit fold of what it read into one
+ *                      sink word, so the XOR of all of them equals, for the
+ *                      XOR X of all 16-byte vectors of src taken as four
+ *                      32-bit words (x, y, z, w), the word
+ *                      ((x ^ z) << 32) | (y ^ w).
+ *   a2av_device_fill   writes the 32-bit pattern to every 4-byte word of dst,
+ *                      with non-temporal stores when nontemporal != 0.
+ */
+int a2av_device_read(const void *src, size_t bytes, uint64_t *sink, hipStream_t stream);
+int a2av_device_fill(void *dst, size_t bytes, uint32_t pattern, int nontemporal,
+                     hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -187,6 +187,14 @@ def test_host_argument_errors(L):
                                    vp(8), vp(8), vp(8), None) == EARG
     assert L.keys_exchange_noalloc(2, 26, 8, ptrs, ptrs, two, ptrs, two, ptrs, two, vp(8),
                                    vp(8), vp(8), None, None) == EARG
+    # one-direction ceilings: sizes and bases that are not 16-byte multiples, null buffers
+    assert L.a2av_device_read(vp(16), 24, vp(16), None) == EARG
+    assert L.a2av_device_read(vp(20), 32, vp(16), None) == EARG
+    assert L.a2av_device_read(vp(16), 32, None, None) == EARG
+    assert L.a2av_device_fill(vp(16), 8, 1, 1, None) == EARG
+    assert L.a2av_device_fill(vp(24), 32, 1, 0, None) == EARG
+    assert L.a2av_device_fill(None, 32, 1, 0, None) == EARG
+    assert L.a2av_device_read(None, 0, None, None) == 0 and L.a2av_device_fill(None, 0, 1, 0, None) == 0
 
 
 def test_workspace_formula(L):
