@@ -15,6 +15,7 @@
 #include <mutex>
 
 #include "common.hpp"
+#include "wave_walk.h"
 
 namespace a2av {
 
@@ -586,74 +587,47 @@ __global__ __launch_bounds__(1024) void k_a2av_prep(const CopyArgs a) {
     if (tid == 0 && lbits) atomicOr(a.status, lbits);
 }
 
-// Lane l of a wave holds entry l of the rank-indexed vector v[0..W) (W <= 64).
-__device__ __forceinline__ int64_t lane_load(const int64_t *v, int W, int lane) {
-    return lane < W ? v[lane] : 0;
-}
+// The GPU's wave for walk_pieces_any (wave_walk.h): one lane per thread,
+// cross-lane operations from the hardware, uniform loads through the scalar
+// cache (send_off is not written during the copy), the payload moved with the
+// wave copies.
+template <int U, bool ALIGNED>
+struct DeviceWave {
+    int ln;
+    __device__ int lane() const { return ln; }
+    __device__ int64_t load(const int64_t *p) const { return *p; }
+    __device__ int64_t load_uniform(const int64_t *p) const {
+        // the address taken from the first lane, so that the load is a
+        // scalar one whatever the compiler could prove about it
+        const uint64_t x = (uint64_t)(uintptr_t)p;
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+        return *(const const_i64 *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    }
+    __device__ void copy(unsigned char *d, const unsigned char *s, uint64_t n) const {
+        if constexpr (ALIGNED) wave_copy16<U>(d, s, n, ln);
+        else wave_copy_any<U>(d, s, n, ln);
+    }
+    __device__ uint64_t ballot(int, bool b) const { return __ballot(b); }
+    __device__ uint64_t readlane(int, uint64_t v, int l) const { return readlane_u64(v, l); }
+    __device__ int uniform(int, int x) const { return __builtin_amdgcn_readfirstlane(x); }
+    __device__ uint64_t incl_scan(int, uint64_t v) const { return wave_incl_scan_u64(v); }
+};
 
-// The copy after k_a2av_prep, one piece per wave. Lane d holds the rows
-// destination d receives (recv_off[d][W]) and, while the wave works inside
-// destination d, lane s holds recv_off[d][s], S[s][d] and send_off[s][d].
+// The copy after k_a2av_prep, one piece per wave (walk_pieces_any): lane d
+// holds the rows destination d receives and, while the wave works inside
+// destination d, lane s holds recv_off[d][s] and S[s][d] from two coalesced
+// loads of that row; the chunk it copies from takes one uniform load of
+// send_off.
 template <int U, bool ALIGNED>
 __global__ __launch_bounds__(256) void k_a2av_wave_any(const CopyArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint64_t wpb = blockDim.x / kWave;
     const uint64_t gw = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave;
     const uint64_t TW = (uint64_t)gridDim.x * wpb;
-    const int W = a.W, W1 = W + 1;
     if (status_at_entry(a.status)) return;  // final: the prep launch wrote it
-    const uint64_t R = a.R;
-    const uint64_t tot = lane < W ? (uint64_t)a.recv_off[lane * W1 + W] : 0;
-    const uint64_t incl = wave_incl_scan_u64(tot);
-    const uint64_t pre = incl - tot;  // rows of destinations before lane d
-    const uint64_t B = readlane_u64(incl, kWave - 1) * R;
-    const uint64_t piece = a.piece;
-    for (uint64_t p = gw; p * piece < B; p += TW) {
-        const uint64_t lo = p * piece;
-        const uint64_t hi = lo + piece < B ? lo + piece : B;
-        const uint64_t mask_d = __ballot(lane < W && pre * R <= lo);
-        if (mask_d == 0) break;  // cannot happen: pre[0] == 0
-        int d = 63 - __clzll(mask_d);
-        uint64_t dbase = readlane_u64(pre, d) * R;
-        uint64_t ro = (uint64_t)lane_load(a.recv_off + d * W1, W, lane);
-        uint64_t n = lane < W ? (uint64_t)a.S[lane * W + d] : 0;
-        uint64_t so = lane < W ? (uint64_t)a.send_off[lane * W1 + d] : 0;
-        const uint64_t mask_s = __ballot(lane < W && dbase + ro * R <= lo);
-        if (mask_s == 0) break;  // cannot happen: recv_off[d][0] == 0
-        int s = 63 - __clzll(mask_s);
-        uint64_t x = lo;
-        while (x < hi && d < W) {
-            const uint64_t nn = readlane_u64(n, s);
-            const uint64_t r0 = readlane_u64(ro, s);
-            const uint64_t F = dbase + r0 * R;
-            const uint64_t L = nn * R;
-            if (nn > 0 && x < F + L) {
-                const uint64_t e = hi < F + L ? hi : F + L;
-                const uint64_t off = x - F;
-                const uint64_t s0 = readlane_u64(so, s);
-                // checked offsets always pass; the check keeps every access
-                // inside the caller's buffers regardless (no sum that can
-                // wrap; the offsets are re-read from the caller's memory)
-                if (span_fits(r0, nn, (uint64_t)a.cap[d]) &&
-                    span_fits(s0, nn, (uint64_t)a.in_rows[s])) {
-                    unsigned char *dst = a.out[d] + r0 * R + off;
-                    const unsigned char *src = a.in[s] + s0 * R + off;
-                    if constexpr (ALIGNED) wave_copy16<U>(dst, src, e - x, lane);
-                    else wave_copy_any<U>(dst, src, e - x, lane);
-                }
-                x = e;
-            }
-            if (++s == W) {
-                s = 0;
-                if (++d < W && x < hi) {
-                    dbase = readlane_u64(pre, d) * R;
-                    ro = (uint64_t)lane_load(a.recv_off + d * W1, W, lane);
-                    n = lane < W ? (uint64_t)a.S[lane * W + d] : 0;
-                    so = lane < W ? (uint64_t)a.send_off[lane * W1 + d] : 0;
-                }
-            }
-        }
-    }
+    DeviceWave<U, ALIGNED> wv{lane};
+    walk_pieces_any(wv, a, gw, TW);
 }
 
 // Plain copy with the same one-piece-per-wave structure.
