@@ -261,3 +261,54 @@ def test_keys_exchange_full(ref):
     got = gpu_keys_exchange(W, NT, batch, lengths, keys, ref=ref)
     _compare_exchange(got, want, "full")
     _say("keys_exchange full: keys received", [k.size for k in got[2]])
+
+
+def test_keys_exchange_workspace_contents_do_not_matter(ref):
+    """The two-launch exchange counts its workgroups in the workspace: whatever
+    the workspace held before (zeros, all ones, random bytes, what the last
+    call or a poisoned call left) the result is the oracle's, call after call
+    on one workspace, and on a larger one."""
+    W, NT, batch = 8, 26, 300
+    g = I.rng(77)
+    lengths, keys = _inputs(g, W, NT, batch, lam=4.0, cap=20)
+    want = ref.keys_exchange(W, NT, batch, lengths, keys)
+    lcap = [x.size for x in want[1]]
+    kcap = [x.size for x in want[2]]
+    need = B.keys_exchange_workspace_bytes(W, NT)
+    ws = torch.empty(need + 4096, dtype=torch.uint8, device="cuda")
+    lin = [upload_rows(l.reshape(-1).view(np.uint8)) for l in lengths]
+    kin = [upload_rows(k.view(np.uint8)) for k in keys]
+
+    def call(status_init=0, wsv=None):
+        lout = [GuardedBuffer(c * 4) for c in lcap]
+        kout = [GuardedBuffer(c * 8) for c in kcap]
+        z = dict(dtype=torch.int64, device="cuda")
+        sk, sl, ro = torch.full((W, W), -7, **z), torch.full((W, W), -7, **z), torch.full((W, W + 1), -7, **z)
+        status = torch.full((1,), status_init, dtype=torch.int32, device="cuda")
+        B.keys_exchange(W, NT, batch, [b.view for b in lin], [b.view for b in kin],
+                        [k.size for k in keys], [b.view for b in lout], lcap, [b.view for b in kout],
+                        kcap, sk, sl, ro, ws if wsv is None else wsv, status)
+        torch.cuda.synchronize()
+        return (int(status.item()), [b.host().view(np.int32) for b in lout],
+                [b.host().view(np.int64) for b in kout], sk.cpu().numpy(), sl.cpu().numpy(),
+                ro.cpu().numpy(), all(b.guards_intact() for b in lin + kin + lout + kout))
+
+    fills = [("zeros", lambda: ws.zero_()), ("ones", lambda: ws.fill_(0xFF)),
+             ("random", lambda: ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8,
+                                                       device="cuda"))),
+             ("as left", lambda: None)]
+    for name, fill in fills:
+        fill()
+        torch.cuda.synchronize()
+        for rep in range(2):
+            _say("workspace", name, rep)
+            _compare_exchange(call(), want, f"{name} {rep}")
+    # a poisoned call leaves the counter as it was; the next call is whole
+    st = call(status_init=8)
+    assert st[0] == 8
+    _compare_exchange(call(), want, "after a poisoned call")
+    # a larger workspace holding other bytes, twice
+    big = torch.empty(B.keys_exchange_workspace_bytes(W, 60), dtype=torch.uint8, device="cuda")
+    big.fill_(0x5A)
+    _compare_exchange(call(wsv=big), want, "larger workspace")
+    _compare_exchange(call(wsv=big), want, "larger workspace again")
