@@ -38,7 +38,8 @@ def test_stored_traffic_is_consistent():
     alg = rec["algorithmic_bytes_per_launch"]
     assert alg == 2 * 4 * 32 * 2 ** 20          # W=4 x 32 MiB read + written
     assert abs(rec["hbm_bytes_per_launch"] / alg - 1) < 0.01
-    assert abs(rec["copy_kernel_hbm_bytes_per_launch"] / alg - 1) < 0.01
+    assert abs(rec["copy_only_kernel_hbm_bytes_per_launch"] / alg - 1) < 0.01
+    assert abs(rec["plain_copy_kernel_hbm_bytes_per_launch"] / alg - 1) < 0.01
 
 
 def test_traffic_is_dropped_when_the_kernel_changes(tmp_path, monkeypatch):
