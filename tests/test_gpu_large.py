@@ -90,14 +90,23 @@ def test_four_gib_per_rank(ref):
 
 
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "3call"])
-@pytest.mark.parametrize("W,mib,R", [
-    (4, 160, 8196),  # rows 4 bytes past a multiple of 16: every source phase 0, 4, 8, 12
-    (8, 80, 8),      # 8-byte rows (keys): source phases 0 and 8
-    (12, 48, 8196),  # more than 8 ranks: the prep workgroup, then the wave copy
+@pytest.mark.parametrize("W,mib,R,shape", [
+    # rows 4 bytes past a multiple of 16: every source phase 0, 4, 8, 12
+    (4, 160, 8196, "default"), (4, 160, 8196, "u16"),
+    # 8-byte rows (keys): source phases 0 and 8
+    (8, 80, 8, "default"), (8, 80, 8, "u16"),
+    # more than 8 ranks: the prep workgroup, then the wave copy
+    (12, 48, 8196, "default"),
 ])
-def test_misaligned_rows_past_512_mib(ref, W, mib, R, fused):
-    """More than 512 MiB on each side, so the copy runs 16 vectors per lane in
-    flight, with rows that are not 16-byte multiples: chunks start at every
-    4-byte phase of the 16-byte grid and take the one-load misaligned path."""
-    _say("large misaligned", W, mib, R, fused)
+def test_misaligned_rows_past_512_mib(ref, monkeypatch, W, mib, R, shape, fused):
+    """More than 512 MiB on each side with rows that are not 16-byte
+    multiples: chunks start at every 4-byte phase of the 16-byte grid and take
+    the one-load misaligned path. In the default shapes, up to 8 ranks move
+    4 KiB pieces with 4 vectors per lane in flight (every exchange of 64 MiB
+    or more), and more ranks 32 KiB pieces with 16 in flight; "u16" sets the
+    knobs so that up to 8 ranks take 32 KiB pieces with 16 in flight too."""
+    if shape == "u16":
+        monkeypatch.setenv("A2AV_WAVE_UNROLL", "16")
+        monkeypatch.setenv("A2AV_WAVE_PIECE", "32768")
+    _say("large misaligned", W, mib, R, shape, fused)
     run_large(ref, W, mib, "uniform", 90 + W + R % 7, fused=fused, R=R)
