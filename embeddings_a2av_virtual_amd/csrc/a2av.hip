@@ -318,45 +318,148 @@ __global__ __launch_bounds__(BS) void k_device_copy(unsigned char *dst, const un
 }
 
 // ====================================================================== wave-level payload (W <= 8)
-// For up to 8 ranks every wave is self-contained. It reads the status word
-// and the split matrix through the scalar cache (a few s_load bursts; the
-// scalar path does not queue behind the vector stream that older waves keep
-// in flight on the same CU, which starves the vector loads of a young wave),
-// computes every offset it needs with wave64 shuffles in registers (lane
-// s*W + d holds the (s, d) entry), and copies one piece of the destination
-// space. No LDS and no barrier: the grid is sized to the traffic so that the
-// hardware dispatcher hands pieces to waves as older ones retire, which evens
-// out the unequal bandwidth that waves of different age get.
+// For up to 8 ranks every wave is self-contained. It reads the status word,
+// the split matrix and the per-rank rows and capacities through the scalar
+// cache (the scalar path does not queue behind the vector stream that older
+// waves keep in flight on the same CU, which starves the vector loads of a
+// young wave), computes every offset it needs in registers, and copies one
+// piece of the destination space. No LDS and no barrier: the grid is sized to
+// the traffic so that the hardware dispatcher hands pieces to waves as older
+// ones retire, which evens out the unequal bandwidth that waves of different
+// age get.
+//
+// Every wave spends its first instructions on the offsets, so their latency
+// is paid once per piece and, at the start of a launch, before any payload
+// byte moves. Two layouts of groups of P lanes (P the power of two at or
+// above W, so that no group straddles a 16-lane DPP row) keep that short:
+//   row layout     lane s*P + d holds the (s, d) entry: S[s][d], send_off[s][d]
+//   column layout  lane d*P + s holds the (s, d) entry: recv_off[d][s]
+// S enters the row layout by v_writelane from the scalar loads (two
+// instructions per entry), scans inside groups are DPP row shifts (no LDS
+// round trip), and one ds_bpermute round turns S and send_off into the
+// column layout, where the scans give recv_off and the rows before each
+// destination. Lane g*P + W-1, the last of group g, holds group g's totals
+// and rank g's rows and capacity, so the range checks are vector compares.
 constexpr int kWaveMaxW = 8;
+
+template <int W>
+constexpr int group_lanes() {
+    return W <= 1 ? 1 : W <= 2 ? 2 : W <= 4 ? 4 : 8;
+}
+
+// x of the lane O below in the same 16-lane row (0 for the first O lanes of
+// a row); every lane must be active.
+template <int O>
+__device__ __forceinline__ uint64_t dpp_row_shr(uint64_t x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, 0x110 + O, 0xf, 0xf, true);
+    const uint32_t hi =
+        (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), 0x110 + O, 0xf, 0xf, true);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive scan inside aligned groups of P lanes (P = 1, 2, 4 or 8); k is
+// the lane's index in its group. A lane adds the value O lanes below only
+// when that lane is in its own group, which is then in its own DPP row.
+template <int P>
+__device__ __forceinline__ uint64_t group_incl_scan(uint64_t x, int k) {
+    static_assert(P == 1 || P == 2 || P == 4 || P == 8, "groups inside a DPP row");
+    if constexpr (P > 1) {
+        const uint64_t t = dpp_row_shr<1>(x);
+        if (k >= 1) x += t;
+    }
+    if constexpr (P > 2) {
+        const uint64_t t = dpp_row_shr<2>(x);
+        if (k >= 2) x += t;
+    }
+    if constexpr (P > 4) {
+        const uint64_t t = dpp_row_shr<4>(x);
+        if (k >= 4) x += t;
+    }
+    return x;
+}
+
+// x of lane src (any lane; every lane must be active).
+__device__ __forceinline__ uint64_t lane_gather(uint64_t x, int src) {
+    const int addr = src << 2;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)x);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// v_writelane_b32 (this compiler has no builtin for it): old with lane l set
+// to the uniform value val.
+__device__ int amdgcn_writelane(int val, int l, int old) __asm("llvm.amdgcn.writelane.i32");
+
+// Sixteen 64-bit values of array t from index o, as scalar-register operands
+// of an asm statement.
+#define A2AV_SREG16(t, o)                                                                        \
+    "s"(t[o + 0]), "s"(t[o + 1]), "s"(t[o + 2]), "s"(t[o + 3]), "s"(t[o + 4]), "s"(t[o + 5]),       \
+        "s"(t[o + 6]), "s"(t[o + 7]), "s"(t[o + 8]), "s"(t[o + 9]), "s"(t[o + 10]), "s"(t[o + 11]), \
+        "s"(t[o + 12]), "s"(t[o + 13]), "s"(t[o + 14]), "s"(t[o + 15])
+
+// v with lane l (a constant) set to the uniform value x.
+__device__ __forceinline__ uint64_t writelane_u64(uint64_t v, uint64_t x, int l) {
+    const uint32_t lo = (uint32_t)amdgcn_writelane((int)(uint32_t)x, l, (int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)amdgcn_writelane((int)(uint32_t)(x >> 32), l, (int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
 
 template <int W, int U, bool ALIGNED, int MODE>
 __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
     static_assert(W >= 1 && W <= kWaveMaxW, "one (s, d) entry per lane");
-    constexpr int N = W * W;
+    constexpr int P = group_lanes<W>();
+    constexpr int Q = W - 1;  // index in a group of the lane holding the group's totals
+    constexpr uint32_t wpb = 256 / kWave;  // the launch's block size
     const int lane = threadIdx.x & (kWave - 1);
-    const uint64_t wpb = blockDim.x / kWave;
-    const uint64_t gw = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave;
+    // the wave's index, said to be uniform so that the piece loop runs on the
+    // scalar unit
+    const uint64_t gw = __builtin_amdgcn_readfirstlane(blockIdx.x * wpb + threadIdx.x / kWave);
     const uint64_t TW = (uint64_t)gridDim.x * wpb;
+    const int gi = lane / P, gk = lane % P;  // group, index in the group
+    const bool act = gi < W && gk < W;       // holds an (s, d) entry
+    const bool last = gi < W && gk == Q;     // holds group gi's totals
 
-    // ---- scalar loads: status word, S, and in copy mode the given offsets
-    const int32_t st0 = status_at_entry(a.status);
-    const const_i64 *Sc = (const const_i64 *)a.S;
-    uint64_t v = 0;
+    // ---- scalar loads into lanes: the kernel arguments in one burst, then
+    // the status word and S (at most 32 entries a burst: 64 scalar
+    // registers). Empty asm statements that need every value of a burst make
+    // the compiler issue all of its loads before the first use.
+    const uint64_t R = a.R;
+    const uint64_t piece = a.piece;
+    const int64_t *Sp = a.S;
+    const int32_t *stp = a.status;
+    asm volatile("" ::"s"(R), "s"(piece), "s"(TW), "s"(Sp), "s"(stp));
+    uint64_t lim_in = 0, lim_cap = 0;  // lane r*P + Q: in_rows[r], cap[r]
 #pragma unroll
-    for (int i = 0; i < N; i++) {
-        const uint64_t x = (uint64_t)Sc[i];
-        v = lane == i ? x : v;
+    for (int r = 0; r < W; r++) {
+        lim_in = writelane_u64(lim_in, (uint64_t)a.in_rows[r], r * P + Q);
+        lim_cap = writelane_u64(lim_cap, (uint64_t)a.cap[r], r * P + Q);
     }
-    uint64_t gso = 0, gro = 0, gso_t = 0, gro_t = 0;  // given send_off[s][d], recv_off[d][s], totals
+    const int32_t st0 = status_at_entry(stp);
+    const const_i64 *Sc = (const const_i64 *)Sp;
+    uint64_t v = 0;  // row layout: S[s][d]
+#pragma unroll
+    for (int b = 0; b < W * W; b += 32) {
+        uint64_t t[32];
+#pragma unroll
+        for (int i = 0; i < 32; i++) t[i] = b + i < W * W ? (uint64_t)Sc[b + i] : t[0];
+        if (b == 0) asm volatile("" ::A2AV_SREG16(t, 0), A2AV_SREG16(t, 16), "s"(st0));
+        else asm volatile("" ::A2AV_SREG16(t, 0), A2AV_SREG16(t, 16));
+#pragma unroll
+        for (int i = 0; i < 32; i++)
+            if (b + i < W * W) v = writelane_u64(v, t[i], (b + i) / W * P + (b + i) % W);
+    }
+    // copy mode: the given send_off[s][d] (row layout) and recv_off[d][s]
+    // (column layout) share one index, row gi entry gk of each matrix, and
+    // the last lane of a group also takes the row's total
+    uint64_t gso = 0, gro = 0, gso_t = 0, gro_t = 0;
     auto load_given = [&]() {
-        // lane s*W + d fetches its own entries: four vector loads in flight
-        // together, one round trip for the whole wave
-        if (lane < N) {
-            const int s = lane / W, d = lane - (lane / W) * W;
-            gso = (uint64_t)a.send_off[s * (W + 1) + d];
-            gro = (uint64_t)a.recv_off[d * (W + 1) + s];
-            if (d == W - 1) gso_t = (uint64_t)a.send_off[s * (W + 1) + W];
-            if (s == W - 1) gro_t = (uint64_t)a.recv_off[d * (W + 1) + W];
+        if (act) {
+            gso = (uint64_t)a.send_off[gi * (W + 1) + gk];
+            gro = (uint64_t)a.recv_off[gi * (W + 1) + gk];
+            if (gk == Q) {
+                gso_t = (uint64_t)a.send_off[gi * (W + 1) + W];
+                gro_t = (uint64_t)a.recv_off[gi * (W + 1) + W];
+            }
         }
     };
     // copy mode: with aligned rows and 8 vectors in flight per lane the
@@ -368,32 +471,20 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
     if constexpr (MODE == kCopyGiven && !kDeferred) load_given();
     if (st0) return;
 
-    // ---- offsets from S, in registers (wrapping arithmetic, as the checks
-    // compare modulo 2^64)
-    const int s_ = lane / W, d_ = lane - (lane / W) * W;
-    const bool act = lane < N;
-    uint64_t inc = v;   // send_off[s][d + 1]
-#pragma unroll
-    for (int o = 1; o < W; o <<= 1) {
-        const uint64_t t = __shfl_up(inc, o, kWave);
-        if (d_ >= o) inc += t;
-    }
-    uint64_t inc2 = v;  // recv_off[d][s + 1]
-#pragma unroll
-    for (int o = 1; o < W; o <<= 1) {
-        const uint64_t t = __shfl_up(inc2, o * W, kWave);
-        if (s_ >= o) inc2 += t;
-    }
-    const uint64_t so = inc - v, ro = inc2 - v;
-    const uint64_t ct = __shfl(inc2, (W - 1) * W + d_, kWave);  // rows destination d_ receives
-    uint64_t pinc = ct;
-#pragma unroll
-    for (int o = 1; o < W; o <<= 1) {
-        const uint64_t t = __shfl_up(pinc, o, kWave);
-        if (d_ >= o) pinc += t;
-    }
-    const uint64_t pre = pinc - ct;  // rows of destinations before d_
-    const uint64_t total = readlane_u64(pinc, W - 1);
+    // ---- offsets from S (wrapping arithmetic, as the checks compare modulo
+    // 2^64); lanes outside the entries hold zeros, so a group's scan reaches
+    // its total at index Q
+    const uint64_t inc = group_incl_scan<P>(v, gk);  // row layout: send_off[s][d + 1]
+    const uint64_t so = inc - v;                     // row layout: send_off[s][d]
+    const int tsrc = gk * P + gi;                    // the row-layout lane of this column-layout lane
+    const uint64_t vt = lane_gather(v, tsrc);        // column layout: S[s][d]
+    const uint64_t sot = lane_gather(so, tsrc);      // column layout: send_off[s][d]
+    const uint64_t inc2 = group_incl_scan<P>(vt, gk);  // column layout: recv_off[d][s + 1]
+    const uint64_t ro = inc2 - vt;                     // column layout: recv_off[d][s]
+    // lane d*P + Q: rows of the destinations before d, the sum over s of
+    // send_off[s][d]
+    const uint64_t pre = group_incl_scan<P>(sot, gk);
+    const uint64_t total = readlane_u64(pre, Q * P + Q) + readlane_u64(inc2, Q * P + Q);
 
     // ---- checks, identical in every wave
     int bits = __ballot(act && split_invalid((int64_t)v)) ? A2AV_ST_BAD_SPLIT : 0;
@@ -403,14 +494,10 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
     // check costs no round trip of its own; otherwise it runs here.
     auto given_bits = [&]() -> int {
         int b = bits;
-        const bool bad_off = act && (gso != so || gro != ro || (d_ == W - 1 && gso_t != inc) ||
-                                     (s_ == W - 1 && gro_t != inc2));
+        const bool bad_off = act && (gso != so || gro != ro || (gk == Q && (gso_t != inc || gro_t != inc2)));
         if (__ballot(bad_off)) b |= A2AV_ST_BAD_OFFSETS;
-#pragma unroll
-        for (int r = 0; r < W; r++) {
-            if ((int64_t)readlane_u64(gso_t, r * W + W - 1) > a.in_rows[r]) b |= A2AV_ST_SEND_OVERRUN;
-            if ((int64_t)readlane_u64(gro_t, (W - 1) * W + r) > a.cap[r]) b |= A2AV_ST_RECV_OVERFLOW;
-        }
+        if (__ballot(last && (int64_t)gso_t > (int64_t)lim_in)) b |= A2AV_ST_SEND_OVERRUN;
+        if (__ballot(last && (int64_t)gro_t > (int64_t)lim_cap)) b |= A2AV_ST_RECV_OVERFLOW;
         return b;
     };
     bool pending = kDeferred;  // the gate has not run yet
@@ -426,22 +513,21 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
         if (kDeferred && bits) load_given();
         if (!kDeferred || bits) bits = given_bits();
     } else {
-#pragma unroll
-        for (int r = 0; r < W; r++) {
-            if ((int64_t)readlane_u64(inc, r * W + W - 1) > a.in_rows[r]) bits |= A2AV_ST_SEND_OVERRUN;
-            if ((int64_t)readlane_u64(inc2, (W - 1) * W + r) > a.cap[r]) bits |= A2AV_ST_RECV_OVERFLOW;
-        }
+        if (__ballot(last && (int64_t)inc > (int64_t)lim_in)) bits |= A2AV_ST_SEND_OVERRUN;
+        if (__ballot(last && (int64_t)inc2 > (int64_t)lim_cap)) bits |= A2AV_ST_RECV_OVERFLOW;
         // invalid splits stop the sequence at the exchange
         if (bits & A2AV_ST_BAD_SPLIT) bits = A2AV_ST_BAD_SPLIT;
     }
     if (gw == 0) {
         if constexpr (MODE == kFused) {
             if (!(bits & A2AV_ST_BAD_SPLIT) && act) {
-                a.O_out[d_ * W + s_] = (int64_t)v;
-                a.send_off_out[s_ * (W + 1) + d_] = (int64_t)so;
-                if (d_ == W - 1) a.send_off_out[s_ * (W + 1) + W] = (int64_t)inc;
-                a.recv_off_out[d_ * (W + 1) + s_] = (int64_t)ro;
-                if (s_ == W - 1) a.recv_off_out[d_ * (W + 1) + W] = (int64_t)inc2;
+                a.O_out[gi * W + gk] = (int64_t)vt;  // O[d][s] = S[s][d]
+                a.send_off_out[gi * (W + 1) + gk] = (int64_t)so;
+                a.recv_off_out[gi * (W + 1) + gk] = (int64_t)ro;
+                if (gk == Q) {
+                    a.send_off_out[gi * (W + 1) + W] = (int64_t)inc;
+                    a.recv_off_out[gi * (W + 1) + W] = (int64_t)inc2;
+                }
             }
         }
         if (bits && lane == 0) atomicOr(a.status, bits);
@@ -449,9 +535,7 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
     if (bits) return;
 
     // ---- pieces of the destination space: out[0] rows, then out[1] rows, ...
-    const uint64_t R = a.R;
     const uint64_t B = total * R;
-    const uint64_t piece = a.piece;
     for (uint64_t p = gw; p * piece < B; p += TW) {
         uint64_t lo = p * piece;
         uint64_t hi = lo + piece < B ? lo + piece : B;
@@ -460,39 +544,42 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
             // address is 128-byte aligned, so no cache line is split between
             // two waves' partial writes (neighbouring pieces move the same
             // boundary, so the pieces still tile the space)
-            lo = snap_to_line(lo, B, pre * R, lane, W, a.out);
-            hi = snap_to_line(hi, B, pre * R, lane, W, a.out);
+            lo = snap_to_line<P, Q>(lo, B, pre * R, lane, W, a.out);
+            hi = snap_to_line<P, Q>(hi, B, pre * R, lane, W, a.out);
             if (lo >= hi) continue;
         }
-        // last destination starting at or before lo (lanes 0..W-1 hold pre[d]),
-        // then the last source chunk inside it starting at or before lo
-        const uint64_t mask_d = __ballot(lane < W && pre * R <= lo);
+        // last destination starting at or before lo (lane d*P + Q holds its
+        // rows before), then the last source chunk inside it starting at or
+        // before lo (lane d*P + s holds recv_off[d][s])
+        const uint64_t mask_d = __ballot(last && pre * R <= lo);
         if (mask_d == 0) break;  // cannot happen: pre[0] == 0
-        int d = 63 - __clzll(mask_d);
-        uint64_t dbase = readlane_u64(pre, d) * R;
-        const uint64_t mask_s = __ballot(act && d_ == d && dbase + ro * R <= lo);
+        int d = (63 - __clzll(mask_d)) / P;
+        uint64_t dbase = readlane_u64(pre, d * P + Q) * R;
+        const uint64_t mask_s = __ballot(gi == d && gk < W && dbase + ro * R <= lo);
         if (mask_s == 0) break;  // cannot happen: recv_off[d][0] == 0
-        int s = (63 - __clzll(mask_s)) / W;
+        int s = (63 - __clzll(mask_s)) % P;
         uint64_t x = lo;
         while (x < hi && d < W) {
-            const int li = s * W + d;
-            const uint64_t n = readlane_u64(v, li);
-            const uint64_t r0 = readlane_u64(ro, li);
+            const int lr = s * P + d, lc = d * P + s;  // row and column layout lanes
+            const uint64_t n = readlane_u64(v, lr);
+            const uint64_t r0 = readlane_u64(ro, lc);
             const uint64_t F = dbase + r0 * R;
             const uint64_t L = n * R;
             if (n > 0 && x < F + L) {
                 const uint64_t e = hi < F + L ? hi : F + L;
                 const uint64_t off = x - F;
-                const uint64_t s0 = readlane_u64(so, li);
+                const uint64_t s0 = readlane_u64(so, lr);
                 // d and s are wave-uniform; saying so keeps the argument
                 // reads below scalar (a vector read would wait behind the
                 // payload traffic of older waves on the CU)
                 const int du = __builtin_amdgcn_readfirstlane(d);
                 const int su = __builtin_amdgcn_readfirstlane(s);
                 // validated offsets always pass; the check keeps every access
-                // inside the caller's buffers regardless (no sum that can wrap)
-                if (span_fits(r0, n, (uint64_t)a.cap[du]) &&
-                    span_fits(s0, n, (uint64_t)a.in_rows[su])) {
+                // inside the caller's buffers regardless (no sum that can
+                // wrap); the capacities and rows come from the lanes that
+                // hold them, and both sides are evaluated (no short cut)
+                if (span_fits(r0, n, readlane_u64(lim_cap, du * P + Q)) &
+                    span_fits(s0, n, readlane_u64(lim_in, su * P + Q))) {
                     unsigned char *dst = a.out[du] + r0 * R + off;
                     const unsigned char *src = a.in[su] + s0 * R + off;
                     if constexpr (kDeferred) {
@@ -508,7 +595,7 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
             if (++s == W) {
                 s = 0;
                 ++d;
-                if (d < W) dbase = readlane_u64(pre, d) * R;
+                if (d < W) dbase = readlane_u64(pre, d * P + Q) * R;
             }
         }
     }

@@ -336,15 +336,16 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
 
 // ------------------------------------------------------------ piece boundaries
 // A flat position of the destination space (destination d's bytes start at
-// start_d, held by lane d) moved up to the next 128-byte boundary of its
+// start_d, held by lane d*P + Q) moved up to the next 128-byte boundary of its
 // destination's address, or to that destination's end; 0 and B stay put.
+template <int P = 1, int Q = 0>
 __device__ __forceinline__ uint64_t snap_to_line(uint64_t x, uint64_t B, uint64_t start_d,
                                                  int lane, int W, unsigned char *const *out) {
     if (x == 0 || x >= B) return x < B ? x : B;
-    const uint64_t md = __ballot(lane < W && start_d <= x);
-    const int d = 63 - __clzll(md);
-    const uint64_t db = readlane_u64(start_d, d);
-    const uint64_t de = d + 1 < W ? readlane_u64(start_d, d + 1) : B;
+    const uint64_t md = __ballot(lane % P == Q && lane / P < W && start_d <= x);
+    const int d = (63 - __clzll(md)) / P;
+    const uint64_t db = readlane_u64(start_d, d * P + Q);
+    const uint64_t de = d + 1 < W ? readlane_u64(start_d, (d + 1) * P + Q) : B;
     const uint64_t addr = (uint64_t)(uintptr_t)out[d] + (x - db);
     const uint64_t up = ((addr + 127) & ~(uint64_t)127) - addr;
     return x + up < de ? x + up : de;
