@@ -29,6 +29,10 @@ FLAGS = [
     "-fno-gpu-flush-denormals-to-zero",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first five kernel arguments arrive in scalar registers at wave
+    # launch (kernels whose leading arguments are pointers and sizes skip a
+    # memory round trip before their first load)
+    "-mllvm", "-amdgpu-kernarg-preload-count=5",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

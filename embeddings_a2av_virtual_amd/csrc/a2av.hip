@@ -397,6 +397,11 @@ __device__ int amdgcn_writelane(int val, int l, int old) __asm("llvm.amdgcn.writ
         "s"(t[o + 6]), "s"(t[o + 7]), "s"(t[o + 8]), "s"(t[o + 9]), "s"(t[o + 10]), "s"(t[o + 11]), \
         "s"(t[o + 12]), "s"(t[o + 13]), "s"(t[o + 14]), "s"(t[o + 15])
 
+#define A2AV_SREG4(t, o) "s"(t[o + 0]), "s"(t[o + 1]), "s"(t[o + 2]), "s"(t[o + 3])
+#define A2AV_SREG8(t, o)                                                                        \
+    "s"(t[o + 0]), "s"(t[o + 1]), "s"(t[o + 2]), "s"(t[o + 3]), "s"(t[o + 4]), "s"(t[o + 5]),       \
+        "s"(t[o + 6]), "s"(t[o + 7])
+
 // v with lane l (a constant) set to the uniform value x.
 __device__ __forceinline__ uint64_t writelane_u64(uint64_t v, uint64_t x, int l) {
     const uint32_t lo = (uint32_t)amdgcn_writelane((int)(uint32_t)x, l, (int)(uint32_t)v);
@@ -404,8 +409,14 @@ __device__ __forceinline__ uint64_t writelane_u64(uint64_t v, uint64_t x, int l)
     return ((uint64_t)hi << 32) | lo;
 }
 
+// The first five arguments repeat fields of a (S, status, R, piece and the
+// grid's wave count) so that the compiler preloads them into scalar
+// registers at wave launch (the library is built with
+// -amdgpu-kernarg-preload-count=5): the first scalar burst can go out at
+// once.
 template <int W, int U, bool ALIGNED, int MODE>
-__global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
+__global__ __launch_bounds__(256) void k_a2av_wave(const int64_t *Sp, int32_t *stp, uint64_t R,
+                                                   uint64_t piece, uint32_t waves, const CopyArgs a) {
     static_assert(W >= 1 && W <= kWaveMaxW, "one (s, d) entry per lane");
     constexpr int P = group_lanes<W>();
     constexpr int Q = W - 1;  // index in a group of the lane holding the group's totals
@@ -414,39 +425,69 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
     // the wave's index, said to be uniform so that the piece loop runs on the
     // scalar unit
     const uint64_t gw = __builtin_amdgcn_readfirstlane(blockIdx.x * wpb + threadIdx.x / kWave);
-    const uint64_t TW = (uint64_t)gridDim.x * wpb;
+    const uint64_t TW = waves;
     const int gi = lane / P, gk = lane % P;  // group, index in the group
     const bool act = gi < W && gk < W;       // holds an (s, d) entry
     const bool last = gi < W && gk == Q;     // holds group gi's totals
 
-    // ---- scalar loads into lanes: the kernel arguments in one burst, then
-    // the status word and S (at most 32 entries a burst: 64 scalar
-    // registers). Empty asm statements that need every value of a burst make
-    // the compiler issue all of its loads before the first use.
-    const uint64_t R = a.R;
-    const uint64_t piece = a.piece;
-    const int64_t *Sp = a.S;
-    const int32_t *stp = a.status;
-    asm volatile("" ::"s"(R), "s"(piece), "s"(TW), "s"(Sp), "s"(stp));
-    uint64_t lim_in = 0, lim_cap = 0;  // lane r*P + Q: in_rows[r], cap[r]
-#pragma unroll
-    for (int r = 0; r < W; r++) {
-        lim_in = writelane_u64(lim_in, (uint64_t)a.in_rows[r], r * P + Q);
-        lim_cap = writelane_u64(lim_cap, (uint64_t)a.cap[r], r * P + Q);
-    }
-    const int32_t st0 = status_at_entry(stp);
+    // ---- scalar loads into lanes, in bursts: every load of a burst is in
+    // flight together, forced by an empty asm statement that needs all of
+    // its values. The first burst is the only one that can miss the scalar
+    // cache (at the start of a launch every line it touches is cold, and a
+    // miss costs a memory round trip before any payload byte moves).
+    //   W <= 4: one burst: the status word, S (16 entries at most), the rows,
+    //     capacities and buffer addresses; the walk then reads the buffer
+    //     addresses from lanes.
+    //   W > 4: the status word with S, up to 32 entries (64 scalar
+    //     registers) a burst, then the rows and capacities; the walk loads
+    //     the two buffer addresses it needs.
+    constexpr int N = W * W;
+    constexpr bool kOneBurst = W <= 4;
     const const_i64 *Sc = (const const_i64 *)Sp;
+    const int32_t st0 = status_at_entry(stp);
     uint64_t v = 0;  // row layout: S[s][d]
+    // lane r*P + Q: in_rows[r], cap[r], and for W <= 4 in[r] and out[r]
+    uint64_t lim_in = 0, lim_cap = 0, lane_in = 0, lane_out = 0;
+    if constexpr (kOneBurst) {
+        uint64_t t[16], ir[4], cp[4], pin[4], pout[4];  // entries past N or W repeat entry 0
 #pragma unroll
-    for (int b = 0; b < W * W; b += 32) {
-        uint64_t t[32];
+        for (int i = 0; i < 16; i++) t[i] = (uint64_t)Sc[i < N ? i : 0];
 #pragma unroll
-        for (int i = 0; i < 32; i++) t[i] = b + i < W * W ? (uint64_t)Sc[b + i] : t[0];
-        if (b == 0) asm volatile("" ::A2AV_SREG16(t, 0), A2AV_SREG16(t, 16), "s"(st0));
-        else asm volatile("" ::A2AV_SREG16(t, 0), A2AV_SREG16(t, 16));
+        for (int r = 0; r < 4; r++) {
+            const int q = r < W ? r : 0;
+            ir[r] = (uint64_t)a.in_rows[q];
+            cp[r] = (uint64_t)a.cap[q];
+            pin[r] = (uint64_t)(uintptr_t)a.in[q];
+            pout[r] = (uint64_t)(uintptr_t)a.out[q];
+        }
+        asm volatile("" ::A2AV_SREG16(t, 0), "s"(st0), A2AV_SREG4(ir, 0), A2AV_SREG4(cp, 0),
+                     A2AV_SREG4(pin, 0), A2AV_SREG4(pout, 0));
 #pragma unroll
-        for (int i = 0; i < 32; i++)
-            if (b + i < W * W) v = writelane_u64(v, t[i], (b + i) / W * P + (b + i) % W);
+        for (int i = 0; i < N; i++) v = writelane_u64(v, t[i], i / W * P + i % W);
+#pragma unroll
+        for (int r = 0; r < W; r++) {
+            lim_in = writelane_u64(lim_in, ir[r], r * P + Q);
+            lim_cap = writelane_u64(lim_cap, cp[r], r * P + Q);
+            lane_in = writelane_u64(lane_in, pin[r], r * P + Q);
+            lane_out = writelane_u64(lane_out, pout[r], r * P + Q);
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < N; b += 32) {
+            uint64_t t[32];
+#pragma unroll
+            for (int i = 0; i < 32; i++) t[i] = (uint64_t)Sc[b + i < N ? b + i : b];
+            if (b == 0) asm volatile("" ::A2AV_SREG16(t, 0), A2AV_SREG16(t, 16), "s"(st0));
+            else asm volatile("" ::A2AV_SREG16(t, 0), A2AV_SREG16(t, 16));
+#pragma unroll
+            for (int i = 0; i < 32; i++)
+                if (b + i < N) v = writelane_u64(v, t[i], (b + i) / W * P + (b + i) % W);
+        }
+#pragma unroll
+        for (int r = 0; r < W; r++) {
+            lim_in = writelane_u64(lim_in, (uint64_t)a.in_rows[r], r * P + Q);
+            lim_cap = writelane_u64(lim_cap, (uint64_t)a.cap[r], r * P + Q);
+        }
     }
     // copy mode: the given send_off[s][d] (row layout) and recv_off[d][s]
     // (column layout) share one index, row gi entry gk of each matrix, and
@@ -506,7 +547,7 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
         pending = false;
         load_given();
         const int b = given_bits();
-        if (b && gw == 0 && lane == 0) atomicOr(a.status, b);
+        if (b && gw == 0 && lane == 0) atomicOr(stp, b);
         return b == 0;
     };
     if constexpr (MODE == kCopyGiven) {
@@ -530,7 +571,7 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
                 }
             }
         }
-        if (bits && lane == 0) atomicOr(a.status, bits);
+        if (bits && lane == 0) atomicOr(stp, bits);
     }
     if (bits) return;
 
@@ -580,8 +621,12 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const CopyArgs a) {
                 // hold them, and both sides are evaluated (no short cut)
                 if (span_fits(r0, n, readlane_u64(lim_cap, du * P + Q)) &
                     span_fits(s0, n, readlane_u64(lim_in, su * P + Q))) {
-                    unsigned char *dst = a.out[du] + r0 * R + off;
-                    const unsigned char *src = a.in[su] + s0 * R + off;
+                    unsigned char *const ob =
+                        kOneBurst ? (unsigned char *)(uintptr_t)readlane_u64(lane_out, du * P + Q) : a.out[du];
+                    const unsigned char *const ib =
+                        kOneBurst ? (const unsigned char *)(uintptr_t)readlane_u64(lane_in, su * P + Q) : a.in[su];
+                    unsigned char *dst = ob + r0 * R + off;
+                    const unsigned char *src = ib + s0 * R + off;
                     if constexpr (kDeferred) {
                         if (!wave_copy16<U>(dst, src, e - x, lane, gate)) return;
                     } else if constexpr (ALIGNED) {
@@ -919,15 +964,22 @@ template <int W, int MODE>
 static void launch_wave_w(const CopyArgs &a, bool aligned, const WaveTuning &wt, int grid,
                           hipStream_t st) {
     const unsigned lds = wt.lds;
+    const uint32_t waves = (uint32_t)grid * (256 / kWave);
     if (wt.unroll == 16) {
-        if (aligned) hipLaunchKernelGGL((k_a2av_wave<W, 16, true, MODE>), dim3(grid), dim3(256), lds, st, a);
-        else hipLaunchKernelGGL((k_a2av_wave<W, 16, false, MODE>), dim3(grid), dim3(256), lds, st, a);
+        if (aligned) hipLaunchKernelGGL((k_a2av_wave<W, 16, true, MODE>), dim3(grid), dim3(256), lds, st, a.S,
+                                     a.status, a.R, a.piece, waves, a);
+        else hipLaunchKernelGGL((k_a2av_wave<W, 16, false, MODE>), dim3(grid), dim3(256), lds, st, a.S,
+                                     a.status, a.R, a.piece, waves, a);
     } else if (wt.unroll == 4) {
-        if (aligned) hipLaunchKernelGGL((k_a2av_wave<W, 4, true, MODE>), dim3(grid), dim3(256), lds, st, a);
-        else hipLaunchKernelGGL((k_a2av_wave<W, 4, false, MODE>), dim3(grid), dim3(256), lds, st, a);
+        if (aligned) hipLaunchKernelGGL((k_a2av_wave<W, 4, true, MODE>), dim3(grid), dim3(256), lds, st, a.S,
+                                     a.status, a.R, a.piece, waves, a);
+        else hipLaunchKernelGGL((k_a2av_wave<W, 4, false, MODE>), dim3(grid), dim3(256), lds, st, a.S,
+                                     a.status, a.R, a.piece, waves, a);
     } else {
-        if (aligned) hipLaunchKernelGGL((k_a2av_wave<W, 8, true, MODE>), dim3(grid), dim3(256), lds, st, a);
-        else hipLaunchKernelGGL((k_a2av_wave<W, 8, false, MODE>), dim3(grid), dim3(256), lds, st, a);
+        if (aligned) hipLaunchKernelGGL((k_a2av_wave<W, 8, true, MODE>), dim3(grid), dim3(256), lds, st, a.S,
+                                     a.status, a.R, a.piece, waves, a);
+        else hipLaunchKernelGGL((k_a2av_wave<W, 8, false, MODE>), dim3(grid), dim3(256), lds, st, a.S,
+                                     a.status, a.R, a.piece, waves, a);
     }
 }
 
