@@ -342,6 +342,10 @@ __global__ __launch_bounds__(BS) void k_device_copy(unsigned char *dst, const un
 // and rank g's rows and capacity, so the range checks are vector compares.
 constexpr int kWaveMaxW = 8;
 
+// LDS the kernel declares for W > 4: S in the row layout and the four
+// per-rank arrays.
+constexpr unsigned kWaveOwnLds = (64 + 4 * 8) * sizeof(uint64_t);
+
 template <int W>
 constexpr int group_lanes() {
     return W <= 1 ? 1 : W <= 2 ? 2 : W <= 4 ? 4 : 8;
@@ -430,23 +434,25 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const int64_t *Sp, int32_t *s
     const bool act = gi < W && gk < W;       // holds an (s, d) entry
     const bool last = gi < W && gk == Q;     // holds group gi's totals
 
-    // ---- scalar loads into lanes, in bursts: every load of a burst is in
-    // flight together, forced by an empty asm statement that needs all of
-    // its values. The first burst is the only one that can miss the scalar
-    // cache (at the start of a launch every line it touches is cold, and a
-    // miss costs a memory round trip before any payload byte moves).
-    //   W <= 4: one burst: the status word, S (16 entries at most), the rows,
-    //     capacities and buffer addresses; the walk then reads the buffer
-    //     addresses from lanes.
-    //   W > 4: the status word with S, up to 32 entries (64 scalar
-    //     registers) a burst, then the rows and capacities; the walk loads
-    //     the two buffer addresses it needs.
+    // ---- scalar loads into lanes. Every load of a burst is in flight
+    // together, forced by an empty asm statement that needs all of its
+    // values, and each wave makes one burst: at the start of a launch every
+    // line it touches is cold, and each miss costs a memory round trip before
+    // any payload byte moves. Afterwards the buffer addresses stay in lanes
+    // and the piece walk reads them with v_readlane.
+    //   W <= 4: each wave loads the status word, S (16 entries at most) and
+    //     the rows, capacities and buffer addresses of every rank.
+    //   W > 4: the workgroup's four waves share the work: wave k loads the
+    //     status word, rows k and k + 4 of S and the k-th of the four
+    //     per-rank arrays (input addresses, output addresses, rows,
+    //     capacities), and the waves exchange them through LDS.
     constexpr int N = W * W;
     constexpr bool kOneBurst = W <= 4;
     const const_i64 *Sc = (const const_i64 *)Sp;
     const int32_t st0 = status_at_entry(stp);
     uint64_t v = 0;  // row layout: S[s][d]
-    // lane r*P + Q: in_rows[r], cap[r], and for W <= 4 in[r] and out[r]
+    // lane r*P + Q (for W > 4 every lane of group r): in_rows[r], cap[r],
+    // in[r], out[r]
     uint64_t lim_in = 0, lim_cap = 0, lane_in = 0, lane_out = 0;
     if constexpr (kOneBurst) {
         uint64_t t[16], ir[4], cp[4], pin[4], pout[4];  // entries past N or W repeat entry 0
@@ -472,22 +478,43 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const int64_t *Sp, int32_t *s
             lane_out = writelane_u64(lane_out, pout[r], r * P + Q);
         }
     } else {
+        static_assert(P == 8, "rows of S in groups of 8 lanes");
+        __shared__ uint64_t sh_s[64];    // S in the row layout
+        __shared__ uint64_t sh_a[4][8];  // in[], out[], in_rows[], cap[]
+        const int k = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+        // the k-th per-rank array: CopyArgs holds in, out, in_rows and cap
+        // back to back, 64 entries each (entries past W are not used)
+        const const_i64 *arr = (const const_i64 *)&a.in[0] + 64 * k;
+        uint64_t ar[8];
 #pragma unroll
-        for (int b = 0; b < N; b += 32) {
-            uint64_t t[32];
+        for (int r = 0; r < 8; r++) ar[r] = (uint64_t)arr[r];
+        // rows k and k + 4 of S (a row past W loads row 0 and is dropped)
+        const bool hi_row = k + 4 < W;
+        const const_i64 *r0p = Sc + k * W;
+        const const_i64 *r1p = Sc + (hi_row ? (k + 4) * W : 0);
+        uint64_t t[16];
 #pragma unroll
-            for (int i = 0; i < 32; i++) t[i] = (uint64_t)Sc[b + i < N ? b + i : b];
-            if (b == 0) asm volatile("" ::A2AV_SREG16(t, 0), A2AV_SREG16(t, 16), "s"(st0));
-            else asm volatile("" ::A2AV_SREG16(t, 0), A2AV_SREG16(t, 16));
+        for (int d = 0; d < 8; d++) {
+            t[d] = (uint64_t)r0p[d < W ? d : 0];
+            t[8 + d] = (uint64_t)r1p[d < W ? d : 0];
+        }
+        asm volatile("" ::A2AV_SREG16(t, 0), "s"(st0), A2AV_SREG8(ar, 0));
+        uint64_t part = 0, apart = 0;  // lanes 0..7: row k, 8..15: row k + 4
 #pragma unroll
-            for (int i = 0; i < 32; i++)
-                if (b + i < N) v = writelane_u64(v, t[i], (b + i) / W * P + (b + i) % W);
+        for (int d = 0; d < W; d++) {
+            part = writelane_u64(part, t[d], d);
+            part = writelane_u64(part, hi_row ? t[8 + d] : 0, 8 + d);
         }
 #pragma unroll
-        for (int r = 0; r < W; r++) {
-            lim_in = writelane_u64(lim_in, (uint64_t)a.in_rows[r], r * P + Q);
-            lim_cap = writelane_u64(lim_cap, (uint64_t)a.cap[r], r * P + Q);
-        }
+        for (int r = 0; r < W; r++) apart = writelane_u64(apart, ar[r], r);
+        if (lane < 16) sh_s[8 * k + lane + (lane >= 8 ? 24 : 0)] = part;
+        if (lane < 8) sh_a[k][lane] = apart;
+        __syncthreads();
+        v = sh_s[lane];
+        lane_in = sh_a[0][gi];
+        lane_out = sh_a[1][gi];
+        lim_in = sh_a[2][gi];
+        lim_cap = sh_a[3][gi];
     }
     // copy mode: the given send_off[s][d] (row layout) and recv_off[d][s]
     // (column layout) share one index, row gi entry gk of each matrix, and
@@ -621,12 +648,10 @@ __global__ __launch_bounds__(256) void k_a2av_wave(const int64_t *Sp, int32_t *s
                 // hold them, and both sides are evaluated (no short cut)
                 if (span_fits(r0, n, readlane_u64(lim_cap, du * P + Q)) &
                     span_fits(s0, n, readlane_u64(lim_in, su * P + Q))) {
-                    unsigned char *const ob =
-                        kOneBurst ? (unsigned char *)(uintptr_t)readlane_u64(lane_out, du * P + Q) : a.out[du];
-                    const unsigned char *const ib =
-                        kOneBurst ? (const unsigned char *)(uintptr_t)readlane_u64(lane_in, su * P + Q) : a.in[su];
-                    unsigned char *dst = ob + r0 * R + off;
-                    const unsigned char *src = ib + s0 * R + off;
+                    unsigned char *dst =
+                        (unsigned char *)(uintptr_t)readlane_u64(lane_out, du * P + Q) + r0 * R + off;
+                    const unsigned char *src =
+                        (const unsigned char *)(uintptr_t)readlane_u64(lane_in, su * P + Q) + s0 * R + off;
                     if constexpr (kDeferred) {
                         if (!wave_copy16<U>(dst, src, e - x, lane, gate)) return;
                     } else if constexpr (ALIGNED) {
@@ -963,7 +988,10 @@ static int wave_grid(uint64_t bmax, uint64_t piece) {
 template <int W, int MODE>
 static void launch_wave_w(const CopyArgs &a, bool aligned, const WaveTuning &wt, int grid,
                           hipStream_t st) {
-    const unsigned lds = wt.lds;
+    // the LDS the kernel declares itself (W > 4) counts against the
+    // occupancy cap
+    constexpr unsigned own = W > 4 ? kWaveOwnLds : 0;
+    const unsigned lds = wt.lds > own ? wt.lds - own : wt.lds;
     const uint32_t waves = (uint32_t)grid * (256 / kWave);
     if (wt.unroll == 16) {
         if (aligned) hipLaunchKernelGGL((k_a2av_wave<W, 16, true, MODE>), dim3(grid), dim3(256), lds, st, a.S,
