@@ -42,7 +42,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "a2av_wave_w4_32mib_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "embeddings_a2av_virtual_amd", "csrc", f)
-                  for f in ("a2av.hip", "common.hpp", "bounds.h")]
+                  for f in ("a2av.hip", "common.hpp", "bounds.h")] + [
+                      os.path.join(ROOT, "embeddings_a2av_virtual_amd", "build.py")]
 
 
 def gbps(nbytes: float, seconds: float) -> float:
