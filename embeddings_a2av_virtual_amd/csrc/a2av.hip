@@ -351,68 +351,6 @@ constexpr int group_lanes() {
     return W <= 1 ? 1 : W <= 2 ? 2 : W <= 4 ? 4 : 8;
 }
 
-// x of the lane O below in the same 16-lane row (0 for the first O lanes of
-// a row); every lane must be active.
-template <int O>
-__device__ __forceinline__ uint64_t dpp_row_shr(uint64_t x) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, 0x110 + O, 0xf, 0xf, true);
-    const uint32_t hi =
-        (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), 0x110 + O, 0xf, 0xf, true);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// Inclusive scan inside aligned groups of P lanes (P = 1, 2, 4 or 8); k is
-// the lane's index in its group. A lane adds the value O lanes below only
-// when that lane is in its own group, which is then in its own DPP row.
-template <int P>
-__device__ __forceinline__ uint64_t group_incl_scan(uint64_t x, int k) {
-    static_assert(P == 1 || P == 2 || P == 4 || P == 8, "groups inside a DPP row");
-    if constexpr (P > 1) {
-        const uint64_t t = dpp_row_shr<1>(x);
-        if (k >= 1) x += t;
-    }
-    if constexpr (P > 2) {
-        const uint64_t t = dpp_row_shr<2>(x);
-        if (k >= 2) x += t;
-    }
-    if constexpr (P > 4) {
-        const uint64_t t = dpp_row_shr<4>(x);
-        if (k >= 4) x += t;
-    }
-    return x;
-}
-
-// x of lane src (any lane; every lane must be active).
-__device__ __forceinline__ uint64_t lane_gather(uint64_t x, int src) {
-    const int addr = src << 2;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)x);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)(x >> 32));
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// v_writelane_b32 (this compiler has no builtin for it): old with lane l set
-// to the uniform value val.
-__device__ int amdgcn_writelane(int val, int l, int old) __asm("llvm.amdgcn.writelane.i32");
-
-// Sixteen 64-bit values of array t from index o, as scalar-register operands
-// of an asm statement.
-#define A2AV_SREG16(t, o)                                                                        \
-    "s"(t[o + 0]), "s"(t[o + 1]), "s"(t[o + 2]), "s"(t[o + 3]), "s"(t[o + 4]), "s"(t[o + 5]),       \
-        "s"(t[o + 6]), "s"(t[o + 7]), "s"(t[o + 8]), "s"(t[o + 9]), "s"(t[o + 10]), "s"(t[o + 11]), \
-        "s"(t[o + 12]), "s"(t[o + 13]), "s"(t[o + 14]), "s"(t[o + 15])
-
-#define A2AV_SREG4(t, o) "s"(t[o + 0]), "s"(t[o + 1]), "s"(t[o + 2]), "s"(t[o + 3])
-#define A2AV_SREG8(t, o)                                                                        \
-    "s"(t[o + 0]), "s"(t[o + 1]), "s"(t[o + 2]), "s"(t[o + 3]), "s"(t[o + 4]), "s"(t[o + 5]),       \
-        "s"(t[o + 6]), "s"(t[o + 7])
-
-// v with lane l (a constant) set to the uniform value x.
-__device__ __forceinline__ uint64_t writelane_u64(uint64_t v, uint64_t x, int l) {
-    const uint32_t lo = (uint32_t)amdgcn_writelane((int)(uint32_t)x, l, (int)(uint32_t)v);
-    const uint32_t hi = (uint32_t)amdgcn_writelane((int)(uint32_t)(x >> 32), l, (int)(uint32_t)(v >> 32));
-    return ((uint64_t)hi << 32) | lo;
-}
-
 // The first five arguments repeat fields of a (S, status, R, piece and the
 // grid's wave count) so that the compiler preloads them into scalar
 // registers at wave launch (the library is built with

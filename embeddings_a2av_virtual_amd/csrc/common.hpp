@@ -303,20 +303,100 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint64_t t = __shfl_up(v, o, kWave);
-        if (lane >= o) v += t;
-    }
-    return v;
-}
 
 __device__ __forceinline__ int32_t wave_or(int32_t v) {
 #pragma unroll
     for (int o = kWave / 2; o >= 1; o >>= 1) v |= __shfl_xor(v, o, kWave);
     return v;
+}
+
+// ------------------------------------------------------------ lanes, DPP and bursts
+// x of the lane O below in the same 16-lane row (0 for the first O lanes of
+// a row); every lane must be active.
+template <int O>
+__device__ __forceinline__ uint64_t dpp_row_shr(uint64_t x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, 0x110 + O, 0xf, 0xf, true);
+    const uint32_t hi =
+        (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), 0x110 + O, 0xf, 0xf, true);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive scan inside aligned groups of P lanes (P = 1, 2, 4, 8 or 16); k
+// is the lane's index in its group. A lane adds the value O lanes below only
+// when that lane is in its own group, which is then in its own DPP row.
+template <int P>
+__device__ __forceinline__ uint64_t group_incl_scan(uint64_t x, int k) {
+    static_assert(P == 1 || P == 2 || P == 4 || P == 8 || P == 16, "groups inside a DPP row");
+    if constexpr (P > 1) {
+        const uint64_t t = dpp_row_shr<1>(x);
+        if (k >= 1) x += t;
+    }
+    if constexpr (P > 2) {
+        const uint64_t t = dpp_row_shr<2>(x);
+        if (k >= 2) x += t;
+    }
+    if constexpr (P > 4) {
+        const uint64_t t = dpp_row_shr<4>(x);
+        if (k >= 4) x += t;
+    }
+    if constexpr (P > 8) {
+        const uint64_t t = dpp_row_shr<8>(x);
+        if (k >= 8) x += t;
+    }
+    return x;
+}
+
+// x of the last lane of the row before (DPP row_bcast: lane 15 into row 1
+// and lane 47 into row 3 for ROWS = 0xa; lane 31 into rows 2 and 3 for
+// ROWS = 0xc), 0 in the other rows; every lane must be active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_row_bcast(uint64_t x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, ROWS, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, ROWS, 0xf, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive scan over the 64 lanes: inside each 16-lane row, then the rows'
+// totals carried forward (lane 15 into row 1, lane 31 into rows 2 and 3,
+// lane 47 into row 3); DPP moves only, no LDS round trip. Every lane must be
+// active.
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x) {
+    const int lane = threadIdx.x & (kWave - 1);
+    x = group_incl_scan<16>(x, lane & 15);
+    x += dpp_row_bcast<0x142, 0xa>(x);
+    x += dpp_row_bcast<0x143, 0xc>(x);
+    return x;
+}
+
+// x of lane src (any lane; every lane must be active).
+__device__ __forceinline__ uint64_t lane_gather(uint64_t x, int src) {
+    const int addr = src << 2;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)x);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// v_writelane_b32 (this compiler has no builtin for it): old with lane l set
+// to the uniform value val.
+__device__ int amdgcn_writelane(int val, int l, int old) __asm("llvm.amdgcn.writelane.i32");
+
+// Sixteen 64-bit values of array t from index o, as scalar-register operands
+// of an asm statement.
+#define A2AV_SREG16(t, o)                                                                        \
+    "s"(t[o + 0]), "s"(t[o + 1]), "s"(t[o + 2]), "s"(t[o + 3]), "s"(t[o + 4]), "s"(t[o + 5]),       \
+        "s"(t[o + 6]), "s"(t[o + 7]), "s"(t[o + 8]), "s"(t[o + 9]), "s"(t[o + 10]), "s"(t[o + 11]), \
+        "s"(t[o + 12]), "s"(t[o + 13]), "s"(t[o + 14]), "s"(t[o + 15])
+
+#define A2AV_SREG4(t, o) "s"(t[o + 0]), "s"(t[o + 1]), "s"(t[o + 2]), "s"(t[o + 3])
+#define A2AV_SREG8(t, o)                                                                        \
+    "s"(t[o + 0]), "s"(t[o + 1]), "s"(t[o + 2]), "s"(t[o + 3]), "s"(t[o + 4]), "s"(t[o + 5]),       \
+        "s"(t[o + 6]), "s"(t[o + 7])
+
+// v with lane l (a constant) set to the uniform value x.
+__device__ __forceinline__ uint64_t writelane_u64(uint64_t v, uint64_t x, int l) {
+    const uint32_t lo = (uint32_t)amdgcn_writelane((int)(uint32_t)x, l, (int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)amdgcn_writelane((int)(uint32_t)(x >> 32), l, (int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // ------------------------------------------------------------ bfloat16

@@ -55,6 +55,10 @@ def test_tiny_workload_and_round_trip(ref, seed, fused):
     (3, 128, 20000, 0.0, 6),
     (16, 512, 257, 0.5, 7),
     (64, 48, 40, 0.3, 8),
+    (6, 2048, 400, 0.3, 13),   # W > 4: the four waves of a workgroup share the loads
+    (7, 1024, 600, 0.5, 14),   # rows k + 4 past W are dropped
+    (2, 16, 9000, 0.0, 15),
+    (1, 32, 5000, 0.0, 16),
 ])
 @pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
 def test_random_splits_many_tiles(ref, W, R, max_rows, zero_frac, seed, fused):
@@ -116,7 +120,7 @@ ERROR_ENVS = {"wave": {}, "wave_u16": {"A2AV_WAVE_UNROLL": "16"},
 
 @pytest.mark.parametrize("env", list(ERROR_ENVS), ids=list(ERROR_ENVS))
 @pytest.mark.parametrize("R", [16, 24])
-@pytest.mark.parametrize("W", [4, 12, 20])
+@pytest.mark.parametrize("W", [4, 5, 6, 8, 12, 20])
 @pytest.mark.parametrize("fused", [False, True], ids=["3call", "fused"])
 def test_error_paths_match_oracle(ref, monkeypatch, fused, W, R, env):
     for k, v in ERROR_ENVS[env].items():
@@ -152,7 +156,7 @@ def test_error_paths_match_oracle(ref, monkeypatch, fused, W, R, env):
 
 @pytest.mark.parametrize("env", list(ERROR_ENVS), ids=list(ERROR_ENVS))
 @pytest.mark.parametrize("R", [16, 24])
-@pytest.mark.parametrize("W", [4, 12, 20])
+@pytest.mark.parametrize("W", [4, 6, 8, 12, 20])
 def test_copy_rejects_foreign_offsets(ref, monkeypatch, W, R, env):
     """Offsets that are not the scans of S: the copy refuses and writes nothing."""
     from embeddings_a2av_virtual_amd.vranks import A2av
