@@ -2,7 +2,8 @@
 against keys_exchange (a caller's workspace) on the same inputs, through the
 C ABI: every output byte, split, offset and status word identical, on calls
 in a row whose second is smaller than the first (the array keeps the first
-call's contents), on an error case, and against the oracle."""
+call's contents), on an error case, against the oracle, and captured into a
+HIP graph and replayed."""
 import numpy as np
 import pytest
 import torch
@@ -110,3 +111,52 @@ def test_noalloc_refuses_sizes_beyond_its_scratch():
     assert e.value.code == B.EARG
     torch.cuda.synchronize()
     assert int(status.item()) == 0
+
+
+def test_noalloc_under_graph_capture(ref):
+    """The callers it is for include code under HIP graph capture: the entry
+    captured once (after an eager call has looked up the scratch's address)
+    and replayed four times, with unrelated eager work between replays, gives
+    the workspace entry's bytes every time."""
+    W, NT, batch = 8, 26, 256
+    lengths, keys = _inputs(W, NT, batch, 31)
+    rst, wlo, wko, wsk, wsl, wro = ref.keys_exchange(W, NT, batch, lengths, keys)
+    assert rst == 0
+    want = _run(False, W, NT, batch, lengths, keys, [x.size for x in wlo], [x.size for x in wko])
+    assert want[0] == 0
+    lin = [torch.from_numpy(l.reshape(-1)).cuda() for l in lengths]
+    kin = [torch.from_numpy(k).cuda() for k in keys]
+    lo = [torch.zeros(x.size, dtype=torch.int32, device="cuda") for x in wlo]
+    ko = [torch.zeros(x.size, dtype=torch.int64, device="cuda") for x in wko]
+    z = dict(dtype=torch.int64, device="cuda")
+    sk, sl, ro = torch.zeros((W, W), **z), torch.zeros((W, W), **z), torch.zeros((W, W + 1), **z)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def call():
+        B.keys_exchange_noalloc(W, NT, batch, lin, kin, [k.size for k in keys], lo,
+                                [x.size for x in wlo], ko, [x.size for x in wko], sk, sl, ro, status)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        call()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            call()
+    torch.cuda.synchronize()
+    for i in range(4):
+        for x in lo + ko + [sk, sl, ro]:
+            x.zero_()
+        status.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _say("graph replay", i)
+        got = (int(status.item()), [x.cpu().numpy().view(np.uint8) for x in lo],
+               [x.cpu().numpy().view(np.uint8) for x in ko], sk.cpu().numpy(), sl.cpu().numpy(),
+               ro.cpu().numpy())
+        _same(got, want, f"replay {i}")
+        x = torch.randn(1 << 20, device="cuda")
+        (x * 2).sum().item()
+        torch.cuda.synchronize()
