@@ -46,48 +46,77 @@ long env_long(const char *name, long dflt, long lo, long hi) {
 }
 
 // ====================================================================== exchange
+// One block. The status word comes through the scalar cache (this launch's
+// one block is its only writer) and S is loaded by every thread before
+// anything waits, so the word and the matrix take one memory round trip.
 __global__ __launch_bounds__(256) void k_exchange(int W, const int64_t *__restrict__ S,
                                                   int64_t *__restrict__ O, int32_t *status) {
-    if (status_poisoned(status)) return;
+    constexpr int kPer = (A2AV_MAX_W * A2AV_MAX_W + 255) / 256;  // entries per thread at most
     const int n = W * W;
+    const int32_t st0 = status_at_entry(status);
+    int64_t v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        const int i = threadIdx.x + k * 256;
+        v[k] = i < n ? S[i] : 0;
+    }
+    if (st0) return;
     int bad = 0;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) bad |= split_invalid(S[i]);
+#pragma unroll
+    for (int k = 0; k < kPer; k++) bad |= split_invalid(v[k]);
     if (__syncthreads_or(bad)) {
         if (threadIdx.x == 0) atomicOr(status, A2AV_ST_BAD_SPLIT);
         return;
     }
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        const int s = i / W, d = i - s * W;
-        O[d * W + s] = S[i];
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        const int i = threadIdx.x + k * 256;
+        if (i < n) {
+            const int s = i / W, d = i - s * W;
+            O[d * W + s] = v[k];
+        }
     }
 }
 
 // ====================================================================== offsets
 // Row r < W scans S row r into send_off; row W + r scans O row r into
-// recv_off. One wave per row (W <= 64 entries fit one wave64 scan).
+// recv_off. One wave per row (W <= 64 entries fit one wave64 scan), at most
+// 16 waves, each loading all of its rows (and the status word, through the
+// scalar cache: one block, the only writer) before anything waits.
 __global__ __launch_bounds__(1024) void k_offsets(int W, const int64_t *__restrict__ S,
                                                   const int64_t *__restrict__ O,
                                                   int64_t *__restrict__ send_off,
                                                   int64_t *__restrict__ recv_off,
                                                   int32_t *status) {
-    if (status_poisoned(status)) return;
-    const int n = W * W;
+    constexpr int kRows = (2 * A2AV_MAX_W + 15) / 16;  // rows per wave at most
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nwaves = blockDim.x / kWave;
+    const int32_t st0 = status_at_entry(status);
+    int64_t v[kRows];
+#pragma unroll
+    for (int k = 0; k < kRows; k++) {
+        const int row = wave + k * nwaves;
+        const int64_t *src = row < W ? S + (size_t)row * W : O + (size_t)(row - W) * W;
+        v[k] = row < 2 * W && lane < W ? src[lane] : 0;
+    }
+    if (st0) return;
     int bad = 0;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) bad |= (int)split_invalid(S[i]) | (int)split_invalid(O[i]);
+#pragma unroll
+    for (int k = 0; k < kRows; k++) bad |= split_invalid(v[k]);
     if (__syncthreads_or(bad)) {
         if (threadIdx.x == 0) atomicOr(status, A2AV_ST_BAD_SPLIT);
         return;
     }
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int nwaves = blockDim.x / kWave;
-    for (int row = wave; row < 2 * W; row += nwaves) {
-        const int64_t *src = row < W ? S + (size_t)row * W : O + (size_t)(row - W) * W;
-        int64_t *dst = row < W ? send_off + (size_t)row * (W + 1) : recv_off + (size_t)(row - W) * (W + 1);
-        const int64_t v = lane < W ? src[lane] : 0;
-        const int64_t incl = wave_incl_scan(v);
-        if (lane < W) dst[lane] = incl - v;
-        if (lane == W - 1) dst[W] = incl;
+#pragma unroll
+    for (int k = 0; k < kRows; k++) {
+        const int row = wave + k * nwaves;  // the same in every lane of the wave
+        if (row < 2 * W) {
+            int64_t *dst = row < W ? send_off + (size_t)row * (W + 1) : recv_off + (size_t)(row - W) * (W + 1);
+            const int64_t incl = (int64_t)wave_incl_scan_u64((uint64_t)v[k]);
+            if (lane < W) dst[lane] = incl - v[k];
+            if (lane == W - 1) dst[W] = incl;
+        }
     }
 }
 
