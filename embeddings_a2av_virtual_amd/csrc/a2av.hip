@@ -714,12 +714,24 @@ __global__ __launch_bounds__(1024) void k_a2av_prep(const CopyArgs a) {
 // The GPU's wave for walk_pieces_any (wave_walk.h): one lane per thread,
 // cross-lane operations from the hardware, uniform loads through the scalar
 // cache (send_off is not written during the copy), the payload moved with the
-// wave copies.
+// wave copies. The destination totals and one receive-offset row come from
+// the workgroup's scalar loads (k_a2av_wave_any); any other row is loaded by
+// the lanes.
+typedef __attribute__((address_space(3))) const uint64_t lds_u64;
+
+// The entry off bytes past p (a scalar load with a register offset).
+__device__ __forceinline__ int64_t at_byte(const const_i64 *p, uint32_t off) {
+    typedef __attribute__((address_space(4))) const char const_c;
+    return *(const const_i64 *)((const const_c *)p + off);
+}
+
 template <int U, bool ALIGNED>
 struct DeviceWave {
     int ln;
+    uint64_t tot;       // lane d < W: recv_off[d][W]
+    int d_row;          // the destination whose row is in row_lds
+    const lds_u64 *row_lds;  // recv_off[d_row][0..W]
     __device__ int lane() const { return ln; }
-    __device__ int64_t load(const int64_t *p) const { return *p; }
     __device__ int64_t load_uniform(const int64_t *p) const {
         // the address taken from the first lane, so that the load is a
         // scalar one whatever the compiler could prove about it
@@ -736,21 +748,86 @@ struct DeviceWave {
     __device__ uint64_t readlane(int, uint64_t v, int l) const { return readlane_u64(v, l); }
     __device__ int uniform(int, int x) const { return __builtin_amdgcn_readfirstlane(x); }
     __device__ uint64_t incl_scan(int, uint64_t v) const { return wave_incl_scan_u64(v); }
+    __device__ uint64_t dest_totals(int, const CopyArgs &) const { return tot; }
+    __device__ void row(int, const CopyArgs &a, int d, uint64_t &ro, uint64_t &n) const {
+        const int W = a.W;
+        if (d == d_row) {
+            ro = ln < W ? row_lds[ln] : 0;
+            n = ln < W ? row_lds[ln + 1] - ro : 0;
+        } else {
+            const int64_t *rrow = a.recv_off + (uint64_t)d * (W + 1);
+            ro = ln < W ? (uint64_t)rrow[ln] : 0;
+            n = ln < W ? (uint64_t)rrow[ln + 1] - ro : 0;
+        }
+    }
 };
 
-// The copy after k_a2av_prep, one piece per wave (walk_pieces_any): lane d
-// holds the rows destination d receives and, while the wave works inside
-// destination d, lane s holds recv_off[d][s] and S[s][d] from two coalesced
-// loads of that row; the chunk it copies from takes one uniform load of
-// send_off.
+// LDS the W > 8 wave kernel declares itself: the destination totals and one
+// receive-offset row, in one array whose size is a multiple of 16 bytes (so
+// that the size the launch subtracts from the occupancy cap is the size the
+// kernel is given).
+constexpr int kAnyLdsWords = 2 * A2AV_MAX_W + 2;
+constexpr unsigned kAnyOwnLds = kAnyLdsWords * 8;
+static_assert(kAnyOwnLds % 16 == 0, "LDS rounded to 16 bytes");
+
+// The copy after k_a2av_prep, one piece per wave (walk_pieces_any). Before
+// the walk, the workgroup loads what its waves look up first, through the
+// scalar cache in two bursts (a vector load of a young wave waits behind the
+// payload traffic older waves keep in flight on the CU; a scalar load does
+// not), and shares it through LDS:
+//   1. the status word and the destination totals recv_off[d][W], wave k
+//      taking d = 16k .. 16k + 15;
+//   2. the receive-offset row of the destination holding the workgroup's
+//      first byte (its four waves' pieces are neighbours, so they nearly
+//      always start in it), wave k taking entries 16k .. 16k + 16.
+// Every wave reaches both barriers before it looks at the status word.
 template <int U, bool ALIGNED>
 __global__ __launch_bounds__(256) void k_a2av_wave_any(const CopyArgs a) {
+    __shared__ uint64_t sh_meta[kAnyLdsWords];
+    uint64_t *const sh_tot = sh_meta;               // [A2AV_MAX_W]
+    uint64_t *const sh_row = sh_meta + A2AV_MAX_W;  // [A2AV_MAX_W + 1]
     const int lane = threadIdx.x & (kWave - 1);
-    const uint64_t wpb = blockDim.x / kWave;
-    const uint64_t gw = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave;
-    const uint64_t TW = (uint64_t)gridDim.x * wpb;
-    if (status_at_entry(a.status)) return;  // final: the prep launch wrote it
-    DeviceWave<U, ALIGNED> wv{lane};
+    const int k = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint64_t gw = (uint64_t)blockIdx.x * 4 + k;
+    const uint64_t TW = (uint64_t)gridDim.x * 4;
+    const int W = a.W, W1 = W + 1;
+    const const_i64 *rc = (const const_i64 *)a.recv_off;
+    const int32_t st0 = status_at_entry(a.status);
+    // entries past the matrix repeat its last one and are not stored; each
+    // load takes the matrix address and a 32-bit byte offset (the matrix is
+    // at most 64 x 65 entries), so the burst needs one address, not sixteen
+    uint64_t t[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const int e = 16 * k + i < W ? 16 * k + i : W - 1;
+        t[i] = (uint64_t)at_byte(rc, (uint32_t)(e * W1 + W) * 8u);
+    }
+    asm volatile("" : A2AV_SREG16_IO(t, 0) : "s"(st0));
+    uint64_t part = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) part = writelane_u64(part, t[i], i);
+    if (lane < 16 && 16 * k + lane < W) sh_tot[16 * k + lane] = part;
+    __syncthreads();
+    const uint64_t tot = lane < W ? sh_tot[lane] : 0;
+    const uint64_t incl = wave_incl_scan_u64(tot);
+    const uint64_t pre = incl - tot;
+    // the last destination starting at or before the workgroup's first byte
+    // (the same in its four waves: they scan the same totals)
+    const uint64_t lo0 = (uint64_t)blockIdx.x * 4 * a.piece;
+    const uint64_t mask = __ballot(lane < W && pre * a.R <= lo0);
+    const int dw = __builtin_amdgcn_readfirstlane(mask ? 63 - (int)__clzll(mask) : 0);
+    uint64_t u[17];
+#pragma unroll
+    for (int i = 0; i < 17; i++)
+        u[i] = (uint64_t)at_byte(rc, (uint32_t)(dw * W1 + (16 * k + i <= W ? 16 * k + i : W)) * 8u);
+    asm volatile("" : A2AV_SREG16_IO(u, 0), "+s"(u[16]));
+    part = 0;
+#pragma unroll
+    for (int i = 0; i < 17; i++) part = writelane_u64(part, u[i], i);
+    if (lane < 17 && 16 * k + lane <= W) sh_row[16 * k + lane] = part;
+    __syncthreads();
+    if (st0) return;  // final: the prep launch wrote it
+    DeviceWave<U, ALIGNED> wv{lane, tot, dw, (const lds_u64 *)sh_row};
     walk_pieces_any(wv, a, gw, TW);
 }
 
@@ -1003,15 +1080,17 @@ static void launch_wave_any(CopyArgs a, bool aligned, const WaveTuning &wt, int 
         a.send_off = a.send_off_out;
         a.recv_off = a.recv_off_out;
     }
+    // the kernel's own LDS counts against the occupancy cap
+    const unsigned lds = wt.lds > kAnyOwnLds ? wt.lds - kAnyOwnLds : wt.lds;
     if (wt.unroll == 16) {
-        if (aligned) hipLaunchKernelGGL((k_a2av_wave_any<16, true>), dim3(grid), dim3(256), wt.lds, st, a);
-        else hipLaunchKernelGGL((k_a2av_wave_any<16, false>), dim3(grid), dim3(256), wt.lds, st, a);
+        if (aligned) hipLaunchKernelGGL((k_a2av_wave_any<16, true>), dim3(grid), dim3(256), lds, st, a);
+        else hipLaunchKernelGGL((k_a2av_wave_any<16, false>), dim3(grid), dim3(256), lds, st, a);
     } else if (wt.unroll == 4) {
-        if (aligned) hipLaunchKernelGGL((k_a2av_wave_any<4, true>), dim3(grid), dim3(256), wt.lds, st, a);
-        else hipLaunchKernelGGL((k_a2av_wave_any<4, false>), dim3(grid), dim3(256), wt.lds, st, a);
+        if (aligned) hipLaunchKernelGGL((k_a2av_wave_any<4, true>), dim3(grid), dim3(256), lds, st, a);
+        else hipLaunchKernelGGL((k_a2av_wave_any<4, false>), dim3(grid), dim3(256), lds, st, a);
     } else {
-        if (aligned) hipLaunchKernelGGL((k_a2av_wave_any<8, true>), dim3(grid), dim3(256), wt.lds, st, a);
-        else hipLaunchKernelGGL((k_a2av_wave_any<8, false>), dim3(grid), dim3(256), wt.lds, st, a);
+        if (aligned) hipLaunchKernelGGL((k_a2av_wave_any<8, true>), dim3(grid), dim3(256), lds, st, a);
+        else hipLaunchKernelGGL((k_a2av_wave_any<8, false>), dim3(grid), dim3(256), lds, st, a);
     }
 }
 

@@ -387,6 +387,15 @@ __device__ int amdgcn_writelane(int val, int l, int old) __asm("llvm.amdgcn.writ
         "s"(t[o + 6]), "s"(t[o + 7]), "s"(t[o + 8]), "s"(t[o + 9]), "s"(t[o + 10]), "s"(t[o + 11]), \
         "s"(t[o + 12]), "s"(t[o + 13]), "s"(t[o + 14]), "s"(t[o + 15])
 
+// The same as operands the asm statement reads and writes: what uses the
+// values afterwards cannot be scheduled before the statement, so no use of
+// an early value splits the burst with a wait for the loads issued so far.
+#define A2AV_SREG16_IO(t, o)                                                                     \
+    "+s"(t[o + 0]), "+s"(t[o + 1]), "+s"(t[o + 2]), "+s"(t[o + 3]), "+s"(t[o + 4]),                \
+        "+s"(t[o + 5]), "+s"(t[o + 6]), "+s"(t[o + 7]), "+s"(t[o + 8]), "+s"(t[o + 9]),            \
+        "+s"(t[o + 10]), "+s"(t[o + 11]), "+s"(t[o + 12]), "+s"(t[o + 13]), "+s"(t[o + 14]),       \
+        "+s"(t[o + 15])
+
 #define A2AV_SREG4(t, o) "s"(t[o + 0]), "s"(t[o + 1]), "s"(t[o + 2]), "s"(t[o + 3])
 #define A2AV_SREG8(t, o)                                                                        \
     "s"(t[o + 0]), "s"(t[o + 1]), "s"(t[o + 2]), "s"(t[o + 3]), "s"(t[o + 4]), "s"(t[o + 5]),       \

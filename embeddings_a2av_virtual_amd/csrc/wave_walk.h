@@ -9,15 +9,23 @@
 //
 // The wave type Wv provides, per lane:
 //   lane()                 this lane's index, 0..63
-//   load(p)                a load of *p by this lane
 //   load_uniform(p)        a load of *p at an address every lane holds the same
 //   copy(dst, src, n)      a copy of n bytes that all 64 lanes make together
-// and cross-lane operations, each called by all 64 lanes at one place (site
-// names the place, for the host model's check):
+// and operations each called by all 64 lanes at one place (site names the
+// place, for the host model's check):
 //   ballot(site, b)        the 64-bit mask of lanes with b set
 //   readlane(site, v, l)   lane l's v
 //   uniform(site, x)       x of the first lane (every lane holds the same x)
 //   incl_scan(site, v)     the inclusive prefix sum of v over lanes 0..lane
+//   dest_totals(site, a)   lane d < W: recv_off[d][W] (the rows destination d
+//                          receives); other lanes 0
+//   row(site, a, d, ro, n) lane s < W: ro = recv_off[d][s] and
+//                          n = recv_off[d][s + 1] - ro; other lanes 0 (d is
+//                          the same in every lane)
+// How a wave comes by the offsets is its own affair: the GPU's wave takes the
+// totals, and the row of the destination its workgroup starts in, from what
+// the workgroup loaded once through the scalar cache; the host model loads
+// them lane by lane.
 //
 // The argument block A provides W, R (row bytes), piece (bytes per piece),
 // in[], out[], in_rows[], cap[] (per rank) and the device matrices
@@ -25,11 +33,10 @@
 // the launch before (so recv_off[d][s+1] - recv_off[d][s] is S[s][d]).
 //
 // Per piece, a wave finds the destination d whose rows hold the piece's first
-// byte (lanes 0..W-1 hold the rows of destinations before them), then loads
-// row d of recv_off twice, lane s taking entries s and s+1, so that lane s
-// holds the first output row of source s's chunk and its row count (their
-// difference) from two coalesced loads; the chunk's send offset is one
-// uniform load when the wave copies from it.
+// byte (lanes 0..W-1 hold the rows of destinations before them), then takes
+// row d of recv_off, lane s holding the first output row of source s's chunk
+// and its row count; the chunk's send offset is one uniform load when the
+// wave copies from it.
 #pragma once
 
 #include <stdint.h>
@@ -45,7 +52,7 @@ A2AV_HD inline void walk_pieces_any(Wv &wv, const A &a, uint64_t gw, uint64_t TW
     const uint64_t R = a.R;
     const uint64_t piece = a.piece;
     // lane d: rows destination d receives, and (scanned) the rows before it
-    const uint64_t tot = lane < W ? (uint64_t)wv.load(a.recv_off + (uint64_t)lane * W1 + W) : 0;
+    const uint64_t tot = wv.dest_totals(11, a);
     const uint64_t incl = wv.incl_scan(1, tot);
     const uint64_t pre = incl - tot;
     const uint64_t B = wv.readlane(2, incl, 63) * R;
@@ -59,10 +66,9 @@ A2AV_HD inline void walk_pieces_any(Wv &wv, const A &a, uint64_t gw, uint64_t TW
         int d = 63 - __builtin_clzll(mask_d);
         uint64_t dbase = wv.readlane(4, pre, d) * R;
         // lane s: first output row of source s's chunk in destination d, and
-        // its rows (the next entry minus this one)
-        const int64_t *rrow = a.recv_off + (uint64_t)d * W1;
-        uint64_t ro = lane < W ? (uint64_t)wv.load(rrow + lane) : 0;
-        uint64_t n = lane < W ? (uint64_t)wv.load(rrow + lane + 1) - ro : 0;
+        // its rows
+        uint64_t ro, n;
+        wv.row(12, a, d, ro, n);
         // last source chunk starting at or before lo
         const uint64_t mask_s = wv.ballot(5, lane < W && dbase + ro * R <= lo);
         if (mask_s == 0) break;
@@ -95,9 +101,7 @@ A2AV_HD inline void walk_pieces_any(Wv &wv, const A &a, uint64_t gw, uint64_t TW
                 s = 0;
                 if (++d < W && x < hi) {
                     dbase = wv.readlane(10, pre, d) * R;
-                    rrow = a.recv_off + (uint64_t)d * W1;
-                    ro = lane < W ? (uint64_t)wv.load(rrow + lane) : 0;
-                    n = lane < W ? (uint64_t)wv.load(rrow + lane + 1) - ro : 0;
+                    wv.row(13, a, d, ro, n);
                 }
             }
         }

@@ -131,6 +131,17 @@ class HostWave {
         return exchange(site, v, [l](const uint64_t *x, int) { return x[l]; });
     }
     int uniform(int site, int x) { return (int)same(site, (uint64_t)(int64_t)x, "uniform value"); }
+    uint64_t dest_totals(int site, const Args &a) {
+        same(site, 0, "destination totals");
+        return ln_ < a.W ? (uint64_t)load(a.recv_off + (uint64_t)ln_ * (a.W + 1) + a.W) : 0;
+    }
+    void row(int site, const Args &a, int d, uint64_t &ro, uint64_t &n) {
+        same(site, (uint64_t)(int64_t)d, "row destination");
+        if (d < 0 || d >= a.W) die(4, "row of destination %d", d);
+        const int64_t *rrow = a.recv_off + (uint64_t)d * (a.W + 1);
+        ro = ln_ < a.W ? (uint64_t)load(rrow + ln_) : 0;
+        n = ln_ < a.W ? (uint64_t)load(rrow + ln_ + 1) - ro : 0;
+    }
     uint64_t incl_scan(int site, uint64_t v) {
         return exchange(site, v, [](const uint64_t *x, int lane) {
             uint64_t s = 0;
