@@ -368,6 +368,22 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x) {
     return x;
 }
 
+// The same for 32-bit values.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+    const int k = threadIdx.x & 15;
+    uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);
+    if (k >= 1) x += t;
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);
+    if (k >= 2) x += t;
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);
+    if (k >= 4) x += t;
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);
+    if (k >= 8) x += t;
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);
+    return x;
+}
+
 // x of lane src (any lane; every lane must be active).
 __device__ __forceinline__ uint64_t lane_gather(uint64_t x, int src) {
     const int addr = src << 2;

@@ -77,61 +77,66 @@ __global__ __launch_bounds__(256) void k_moe_hist(const MoeArgs a) {
 }
 
 // ------------------------------------------------------------------ scan
-// One block per rank. Each thread scans a contiguous run of the E*nseg
-// counters; run totals are scanned across the block through LDS.
+// One block per rank, in passes of kScanPass counters: thread t loads
+// counters t, t + 1024, ... of the pass (coalesced, all in flight together),
+// each wave scans every group of 64 with DPP moves, and one wave scans the
+// 256 group totals of the pass, in counter order, through LDS. (A form where
+// each thread scanned a contiguous run of 16 counters made every load and
+// store instruction touch 64 cache lines: 18.3 us per call against 6.1 us at
+// 8 ranks x 256 experts x 64 segments.)
+constexpr int kScanPer = 16;                     // counters per thread per pass
+constexpr int kScanWaves = 1024 / kWave;         // 16
+constexpr int kScanPass = kScanPer * 1024;       // counters per pass
+static_assert(kScanPer * kScanWaves == 4 * kWave, "one wave scans the group totals, 4 per lane");
+
 __global__ __launch_bounds__(1024) void k_moe_scan(const MoeArgs a) {
-    __shared__ int32_t wave_tot[1024 / kWave];
+    __shared__ int32_t part[kScanPer * kScanWaves];  // group totals of a pass, counter order
+    __shared__ int32_t carry_sh;
     if (status_poisoned(a.status)) return;
     const int r = blockIdx.x;
     const int64_t N = (int64_t)a.E * a.nseg;
     int32_t *H = a.hist + (size_t)r * N;
-    const int nthr = blockDim.x;
-    const int64_t per = (N + nthr - 1) / nthr;
-    const int64_t b0 = (int64_t)threadIdx.x * per;
-    const int64_t b1 = b0 + per < N ? b0 + per : N;
-    // a run of up to kScanRegs counters is read once into registers, all
-    // loads in flight together; longer runs are walked twice
-    constexpr int kScanRegs = 32;
-    const bool in_regs = per <= kScanRegs;
-    int32_t vals[kScanRegs];
-    int32_t sum = 0;
-    if (in_regs) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    int32_t carry = 0;  // counters of the passes before
+    for (int64_t base = 0; base < N; base += kScanPass) {
+        int32_t v[kScanPer], inc[kScanPer];
 #pragma unroll
-        for (int u = 0; u < kScanRegs; u++) vals[u] = b0 + u < b1 ? H[b0 + u] : 0;
-#pragma unroll
-        for (int u = 0; u < kScanRegs; u++) sum += vals[u];
-    } else {
-        for (int64_t i = b0; i < b1; i++) sum += H[i];
-    }
-    // block exclusive scan of `sum`
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int32_t incl = wave_incl_scan32(sum);
-    if (lane == kWave - 1) wave_tot[wave] = incl;
-    __syncthreads();
-    if (wave == 0) {
-        const int nw = nthr / kWave;
-        const int32_t t = lane < nw ? wave_tot[lane] : 0;
-        const int32_t ti = wave_incl_scan32(t);
-        if (lane < nw) wave_tot[lane] = ti - t;
-    }
-    __syncthreads();
-    int32_t run = wave_tot[wave] + incl - sum;
-    if (in_regs) {
-#pragma unroll
-        for (int u = 0; u < kScanRegs; u++) {
-            if (b0 + u < b1) H[b0 + u] = run;
-            run += vals[u];
+        for (int u = 0; u < kScanPer; u++) {
+            const int64_t i = base + (int64_t)u * 1024 + tid;
+            v[u] = i < N ? H[i] : 0;
         }
-    } else {
-        for (int64_t i = b0; i < b1; i++) {
-            const int32_t c = H[i];
-            H[i] = run;
-            run += c;
+#pragma unroll
+        for (int u = 0; u < kScanPer; u++) {
+            inc[u] = (int32_t)wave_incl_scan_u32((uint32_t)v[u]);
+            if (lane == kWave - 1) part[u * kScanWaves + wave] = inc[u];
         }
+        __syncthreads();
+        if (wave == 0) {
+            int32_t t[4], sum = 0;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                t[j] = part[lane * 4 + j];
+                sum += t[j];
+            }
+            int32_t run = (int32_t)wave_incl_scan_u32((uint32_t)sum) - sum + carry;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                part[lane * 4 + j] = run;
+                run += t[j];
+            }
+            if (lane == kWave - 1) carry_sh = run;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kScanPer; u++) {
+            const int64_t i = base + (int64_t)u * 1024 + tid;
+            if (i < N) H[i] = part[u * kScanWaves + wave] + inc[u] - v[u];
+        }
+        carry = carry_sh;
+        __syncthreads();  // part and carry_sh are rewritten by the next pass
     }
-    __syncthreads();
     // base of expert e = H[e][0]; the count is the gap to the next base
-    const int E = a.E;
+    const int E = a.E, nthr = blockDim.x;
     for (int e = threadIdx.x; e < E; e += nthr) {
         const int64_t b = H[(size_t)e * a.nseg];
         const int64_t nb = e + 1 < E ? (int64_t)H[(size_t)(e + 1) * a.nseg] : a.Q;

@@ -77,6 +77,7 @@ def _moe_inputs(g, W, T, k, E, R, dist="zipf"):
     (4, 1500, 3, 12, 10, "uniform", 0),        # unaligned rows, repeated experts
     (2, 700, 2, 2, 16, "uniform", 4),          # one expert per rank, misaligned bases
     (4, 2048, 1, 4096, 64, "uniform", 0),      # k = 1, the most experts
+    (4, 4000, 4, 4092, 16, "uniform", 0),      # four passes of the histogram scan, the last ragged
     (1, 100, 4, 7, 32, "uniform", 0),          # one rank
 ])
 def test_moe_pack_round_trip_matches_oracle(ref, W, T, k, E, R, dist, pad):
