@@ -719,11 +719,6 @@ __global__ __launch_bounds__(1024) void k_a2av_prep(const CopyArgs a) {
 // the lanes.
 typedef __attribute__((address_space(3))) const uint64_t lds_u64;
 
-// The entry off bytes past p (a scalar load with a register offset).
-__device__ __forceinline__ int64_t at_byte(const const_i64 *p, uint32_t off) {
-    typedef __attribute__((address_space(4))) const char const_c;
-    return *(const const_i64 *)((const const_c *)p + off);
-}
 
 template <int U, bool ALIGNED>
 struct DeviceWave {

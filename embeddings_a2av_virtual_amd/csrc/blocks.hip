@@ -65,37 +65,109 @@ __device__ __forceinline__ int find_last_le(const int64_t *v, int n, uint64_t ke
     return lo + 63 - __clzll(m);
 }
 
+// LDS the block copy declares itself: the ranks' rows and row bytes, one
+// plan row, the waves' error bits; a multiple of 16 bytes, so that the size
+// the launch subtracts from the occupancy cap is the size the kernel is given.
+constexpr int kCopyRowMax = kWave - 1;  // plans of up to this many blocks per rank stage a row
+struct CopyLds {
+    uint64_t rows[A2AV_MAX_W];      // rank r: rows it receives (dst_start[r][B])
+    uint64_t row[kCopyRowMax + 1];  // dst_start row of the workgroup's first rank, lane b: entry b
+    uint32_t rb[A2AV_MAX_W];        // rank r: row bytes (MIXED)
+    int32_t bits[4];                // OR of the planning bits each wave loaded
+};
+constexpr unsigned kCopyOwnLds = sizeof(CopyLds);
+static_assert(kCopyOwnLds % 16 == 0, "LDS rounded to 16 bytes");
+
 // MIXED: every rank has its own row size (Rr), so two exchanges with
 // different rows (keys and lengths) run as one launch over 2W ranks.
+//
+// Before its pieces, the workgroup loads what its waves look up first
+// through the scalar cache, in two bursts shared in LDS (a vector load of a
+// young wave waits behind the payload traffic older waves keep in flight on
+// the CU; a scalar load does not): (1) the status word, and for ranks
+// 16k .. 16k + 15 (wave k) the planning bits, the rows each rank receives and
+// (MIXED) the row bytes; (2) with at most kCopyRowMax blocks per rank, the
+// dst_start row of the rank holding the workgroup's first byte, wave k taking
+// entries 16k .. 16k + 16. A piece in that rank searches the row in LDS; any
+// other searches the plan in global memory. Every wave reaches both barriers
+// before it looks at the status word or the bits.
 template <int U, bool ALIGNED, bool MIXED = false>
 __global__ __launch_bounds__(256) void k_block_copy(const BlockArgs a) {
+    __shared__ CopyLds sh;
     const int lane = threadIdx.x & (kWave - 1);
-    const uint64_t wpb = blockDim.x / kWave;
-    const uint64_t gw = (uint64_t)blockIdx.x * wpb + threadIdx.x / kWave;
-    const uint64_t TW = (uint64_t)gridDim.x * wpb;
-    const int W = a.W, B = a.B;
-    // lane r: rank r's row bytes
-    const uint64_t Rl = MIXED ? (lane < W ? (uint64_t)a.Rr[lane] : 1) : a.R;
+    const int k = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint64_t gw = (uint64_t)blockIdx.x * 4 + k;
+    const uint64_t TW = (uint64_t)gridDim.x * 4;
+    const int W = a.W, B = a.B, B1 = B + 1;
+    const const_i64 *dsc = (const const_i64 *)a.dst_start;
+    const const_i32 *bic = (const const_i32 *)a.bits;
 
     const int32_t st0 = status_at_entry(a.status);
-    int32_t rb = 0;
-    uint64_t rows = 0;
-    if (lane < W) {
-        rb = a.bits[lane];
-        rows = (uint64_t)a.dst_start[(uint64_t)lane * (B + 1) + B];
+    // entries past W repeat rank W - 1 and are not stored
+    uint64_t t[16];
+    int32_t bb[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const int e = 16 * k + i < W ? 16 * k + i : W - 1;
+        t[i] = (uint64_t)at_byte(dsc, (uint32_t)(e * B1 + B) * 8u);
+        bb[i] = at_byte(bic, (uint32_t)e * 4u);
     }
-    if (st0) return;
-    const int32_t bad = wave_or(rb);
-    if (bad) {
-        if (gw == 0 && lane == 0) atomicOr(a.status, bad);
-        return;
+    uint32_t rr[16];  // MIXED: row bytes of ranks 16k .. 16k + 15 (the array holds 64)
+    if constexpr (MIXED) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) rr[i] = a.Rr[16 * k + i];
+        asm volatile("" : A2AV_SREG16_IO(t, 0), A2AV_SREG16_IO(bb, 0), A2AV_SREG16_IO(rr, 0) : "s"(st0));
+    } else {
+        asm volatile("" : A2AV_SREG16_IO(t, 0), A2AV_SREG16_IO(bb, 0) : "s"(st0));
     }
+    int32_t ob = 0;
+    uint64_t part = 0;
+    uint32_t rpart = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        ob |= 16 * k + i < W ? bb[i] : 0;
+        part = writelane_u64(part, t[i], i);
+        if constexpr (MIXED) rpart = (uint32_t)amdgcn_writelane((int)rr[i], i, (int)rpart);
+    }
+    if (lane < 16 && 16 * k + lane < W) sh.rows[16 * k + lane] = part;
+    if (MIXED && lane < 16) sh.rb[16 * k + lane] = rpart;
+    if (lane == 0) sh.bits[k] = ob;
+    __syncthreads();
+    // lane r: rank r's rows, row bytes, and bytes
+    const uint64_t rows = lane < W ? sh.rows[lane] : 0;
+    const uint64_t Rl = MIXED ? (lane < W ? (uint64_t)sh.rb[lane] : 1) : a.R;
+    const int32_t bad = sh.bits[0] | sh.bits[1] | sh.bits[2] | sh.bits[3];
     // lane r: bytes of rank r and where they start in the flat space
     const uint64_t bytes = rows * Rl;
     const uint64_t incl = wave_incl_scan_u64(bytes);
     const uint64_t base = incl - bytes;
     const uint64_t total = readlane_u64(incl, kWave - 1);
     const uint64_t piece = a.piece;
+    // the rank holding the workgroup's first byte (the same in its four
+    // waves: they scan the same rows) and, with few blocks, its plan row
+    const bool staged = B <= kCopyRowMax;
+    const uint64_t x0 = (uint64_t)blockIdx.x * 4 * piece;
+    const uint64_t m0 = __ballot(lane < W && base <= x0);
+    const int d0 = __builtin_amdgcn_readfirstlane(m0 ? 63 - (int)__clzll(m0) : 0);
+    if (staged) {
+        uint64_t u[17];
+#pragma unroll
+        for (int i = 0; i < 17; i++)
+            u[i] = (uint64_t)at_byte(dsc, (uint32_t)(d0 * B1 + (16 * k + i <= B ? 16 * k + i : B)) * 8u);
+        asm volatile("" : A2AV_SREG16_IO(u, 0), "+s"(u[16]));
+        part = 0;
+#pragma unroll
+        for (int i = 0; i < 17; i++) part = writelane_u64(part, u[i], i);
+        if (lane < 17 && 16 * k + lane <= B) sh.row[16 * k + lane] = part;
+        __syncthreads();
+    }
+    if (st0) return;
+    if (bad) {
+        if (gw == 0 && lane == 0) atomicOr(a.status, bad);
+        return;
+    }
+    // lane b: entry b of the staged row (b <= B < 64)
+    const uint64_t srow = staged && lane <= B ? sh.row[lane] : 0;
     for (uint64_t p = gw; p * piece < total; p += TW) {
         uint64_t x = p * piece;
         uint64_t hi = x + piece < total ? x + piece : total;
@@ -116,32 +188,37 @@ __global__ __launch_bounds__(256) void k_block_copy(const BlockArgs a) {
             const uint64_t xr = x - rbase;
             const uint64_t hr = (hi < rend ? hi : rend) - rbase;
             const uint64_t R = MIXED ? readlane_u64(Rl, d) : a.R;
-            const int64_t *ds = a.dst_start + (uint64_t)d * (B + 1);
-            const int b = find_last_le(ds, B, xr / R, lane);
-            if (b < 0) return;  // not a valid plan
-            // d and b are the same in every lane: the block's plan entries
-            // (written by the launch before, not during this one) come
-            // through the scalar cache, where they do not wait behind the
-            // payload traffic older waves keep in flight on the CU (fused key
-            // exchange 107.0 -> 104.8 us, grouped dispatch 320.6 -> 314.7 us
-            // at 1 GB moved, same-process A/B; a binary search of the plan
-            // through the same cache, instead of the ballot search above, was
-            // 4-12 % slower: its loads depend on one another)
+            // d and b are the same in every lane; the block's plan entries
+            // (written by the launch before, not during this one) come from
+            // the staged row or through the scalar cache
             const int du = __builtin_amdgcn_readfirstlane(d);
-            const int bu = __builtin_amdgcn_readfirstlane(b);
-            const const_i64 *dsu = (const const_i64 *)(a.dst_start + (uint64_t)du * (B + 1));
-            const uint64_t r0 = (uint64_t)dsu[bu], r1 = (uint64_t)dsu[bu + 1];
-            const uint64_t s0 = (uint64_t)((const const_i64 *)a.src_start)[(uint64_t)du * B + bu];
-            const int sr = a.src_rank ? ((const const_i32 *)a.src_rank)[(uint64_t)du * B + bu] : du;
+            int b;
+            uint64_t r0, r1;
+            if (staged && du == d0) {
+                const uint64_t mb = __ballot(lane < B && srow <= xr / R);
+                if (mb == 0) return;  // not a valid plan
+                b = __builtin_amdgcn_readfirstlane(63 - (int)__clzll(mb));
+                r0 = readlane_u64(srow, b);
+                r1 = readlane_u64(srow, b + 1);
+            } else {
+                const int64_t *ds = a.dst_start + (uint64_t)d * (B + 1);
+                b = __builtin_amdgcn_readfirstlane(find_last_le(ds, B, xr / R, lane));
+                if (b < 0) return;  // not a valid plan
+                const const_i64 *dsu = (const const_i64 *)(a.dst_start + (uint64_t)du * (B + 1));
+                r0 = (uint64_t)dsu[b];
+                r1 = (uint64_t)dsu[b + 1];
+            }
+            const uint64_t s0 = (uint64_t)((const const_i64 *)a.src_start)[(uint64_t)du * B + b];
+            const int sr = a.src_rank ? ((const const_i32 *)a.src_rank)[(uint64_t)du * B + b] : du;
             const uint64_t e = hr < r1 * R ? hr : r1 * R;
             if (e <= xr || sr < 0 || sr >= W) return;  // not a valid plan
             // a valid plan always passes; the check keeps every access inside
             // the caller's buffers regardless (rows [r0, r1) of the
             // destination and [s0, s0 + r1 - r0) of the source, with no sum
             // that can wrap)
-            if (r0 <= r1 && span_fits(r0, r1 - r0, (uint64_t)a.cap[d]) &&
+            if (r0 <= r1 && span_fits(r0, r1 - r0, (uint64_t)a.cap[du]) &&
                 span_fits(s0, r1 - r0, (uint64_t)a.in_rows[sr])) {
-                unsigned char *dst = a.out[d] + xr;
+                unsigned char *dst = a.out[du] + xr;
                 const unsigned char *src = a.in[sr] + s0 * R + (xr - r0 * R);
                 if constexpr (ALIGNED) wave_copy16<U>(dst, src, e - xr, lane);
                 else wave_copy_any<U>(dst, src, e - xr, lane);
@@ -385,6 +462,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_bucket_plan(const BucketArgs a
 // never written.
 constexpr int kKxPer = 5;  // blocks per planning thread: up to 5120 per receiver
 constexpr int kKxMaxB = A2AV_MAX_TABLES + A2AV_MAX_W;
+// the block copy reads plan entries at 32-bit byte offsets
+static_assert((uint64_t)A2AV_MAX_W * (kKxMaxB + 1) * 8 < (1ull << 31) &&
+                  (uint64_t)A2AV_MAX_W * (A2AV_MAX_EXPERTS + 1) * 8 < (1ull << 31),
+              "plan offsets fit 32 bits");
 
 struct KeyxArgs {
     int64_t n_keys[A2AV_MAX_W];
@@ -703,6 +784,8 @@ static void launch_block_copy(const BlockArgs &a, uint64_t bmax, bool aligned, h
     uint64_t piece;
     unsigned lds;
     piece_policy(bmax, aligned, &unroll, &piece, &lds);
+    // the kernel's own LDS counts against the occupancy cap
+    if (lds > kCopyOwnLds) lds -= kCopyOwnLds;
     BlockArgs b = a;
     b.piece = piece;
     const int grid = copy_grid(bmax, piece);
@@ -724,6 +807,7 @@ static void launch_block_copy_mixed(const BlockArgs &a, uint64_t bmax, hipStream
     uint64_t piece;
     unsigned lds;
     piece_policy(bmax, false, &unroll, &piece, &lds);
+    if (lds > kCopyOwnLds) lds -= kCopyOwnLds;
     BlockArgs b = a;
     b.piece = piece;
     const int grid = copy_grid(bmax, piece);

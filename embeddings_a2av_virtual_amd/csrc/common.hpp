@@ -281,6 +281,18 @@ __device__ __forceinline__ bool wave_copy16(unsigned char *dst, const unsigned c
 typedef __attribute__((address_space(4))) const int64_t const_i64;
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 
+// The entry off bytes past p, through the scalar cache: a scalar load with a
+// register offset, so that a burst of loads from one array at computed
+// offsets needs one address pair, not one per load.
+__device__ __forceinline__ int64_t at_byte(const const_i64 *p, uint32_t off) {
+    typedef __attribute__((address_space(4))) const char const_c;
+    return *(const const_i64 *)((const const_c *)p + off);
+}
+__device__ __forceinline__ int32_t at_byte(const const_i32 *p, uint32_t off) {
+    typedef __attribute__((address_space(4))) const char const_c;
+    return *(const const_i32 *)((const const_c *)p + off);
+}
+
 // The status word as a wave finds it at entry, read once through the scalar
 // cache (a uniform load that does not queue behind the vector traffic older
 // waves keep in flight on the CU). The constant address space tells the

@@ -73,6 +73,8 @@ def _random_counts(g, W, E, hi, zero_frac=0.3):
     (2, 4096, 16, 2, 0, 0),        # the most experts: two search levels
     (1, 5, 48, 9, 0, 0),           # one rank
     (5, 5, 64, 300, 0, 1),         # one expert per rank
+    (7, 63, 48, 9, 0, 0),          # the most blocks whose plan row a workgroup stages
+    (8, 64, 48, 9, 0, 1),          # one block more: the row is searched in global memory
 ])
 def test_regroup_matches_oracle(ref, W, E, R, hi, pad, direction):
     _say("regroup", W, E, R, hi, pad, direction)
@@ -246,6 +248,7 @@ def _check_grouped(ref, W, E, R, counts, X, in_rows, cap, direction, got):
 @pytest.mark.parametrize("W,E,R,hi,pad", [
     (8, 256, 1024, 3, 0), (4, 16, 7168 * 2, 40, 0), (3, 12, 10, 50, 0), (3, 12, 10, 50, 4),
     (2, 4096, 16, 2, 0), (1, 5, 48, 9, 0), (5, 5, 64, 300, 0), (64, 128, 32, 3, 0),
+    (7, 63, 48, 9, 0), (8, 64, 48, 9, 0),
 ])
 @pytest.mark.parametrize("direction", [0, 1])
 def test_grouped_matches_oracle(ref, W, E, R, hi, pad, direction):
