@@ -336,15 +336,32 @@ __global__ __launch_bounds__(256) void k_bucket_sums(const BucketArgs a) {
     const int32_t *L = a.lengths[r] + (int64_t)t * a.batch;
     int64_t s = 0;
     int n = 0;
-    if ((a.batch & 3) == 0 && ((uintptr_t)L & 15) == 0) {
-        // four lengths per load, several loads in flight per thread
+    if ((a.batch & 3) == 0 && ((uintptr_t)L & 15) == 0 && a.batch > 0) {
+        // four lengths per load, eight loads in flight per thread (a batch
+        // of 8192: all of the table's); indices past the end load the last
+        // vector again and count nothing
+        constexpr int kPer = 8;
+        static_assert(kPer == 8, "the asm statement below names eight vectors");
         const u32x4 *L4 = (const u32x4 *)L;
         const int64_t n4 = a.batch / 4;
-#pragma unroll 4
-        for (int64_t i = tid; i < n4; i += 256) {
-            const u32x4 v = L4[i];
-            s += (int64_t)(int32_t)v.x + (int32_t)v.y + (int32_t)v.z + (int32_t)v.w;
-            n |= (int32_t)(v.x | v.y | v.z | v.w) < 0;
+        for (int64_t i0 = tid; i0 < n4; i0 += 256 * kPer) {
+            u32x4 v[kPer];
+#pragma unroll
+            for (int u = 0; u < kPer; u++) {
+                const int64_t i = i0 + (int64_t)u * 256;
+                v[u] = L4[i < n4 ? i : n4 - 1];
+            }
+            // every load in flight before the first sum uses one (without
+            // this the compiler reused registers and issued the last two
+            // after the first results came back)
+            asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                         "+v"(v[6]), "+v"(v[7]));
+#pragma unroll
+            for (int u = 0; u < kPer; u++) {
+                if (i0 + (int64_t)u * 256 >= n4) v[u] = u32x4{0, 0, 0, 0};
+                s += (int64_t)(int32_t)v[u].x + (int32_t)v[u].y + (int32_t)v[u].z + (int32_t)v[u].w;
+                n |= (int32_t)(v[u].x | v[u].y | v[u].z | v[u].w) < 0;
+            }
         }
     } else {
         for (int64_t i = tid; i < a.batch; i += 256) {
@@ -376,24 +393,25 @@ __global__ __launch_bounds__(256) void k_bucket_sums(const BucketArgs a) {
 // (tables owned by ranks < t mod W) + t / W.
 __global__ __launch_bounds__(kPlanThreads) void k_bucket_plan(const BucketArgs a) {
     __shared__ ScanLds lds;
-    __shared__ int poisoned;
     __shared__ unsigned long long owner_keys[A2AV_MAX_W];
     const int r = blockIdx.x, tid = threadIdx.x;
     const int W = a.W, NT = a.n_tables;
-    if (tid == 0) poisoned = *a.status != 0;
+    // the word as the operation found it (no kernel of it has written it
+    // yet), loaded beside the key counts (a vector load: a scalar one would
+    // hold the counts' address, which waits for every scalar load in
+    // flight); it and the counts are judged together at the first barrier
+    const int32_t st0 = status_poisoned(a.status);
     if (tid < A2AV_MAX_W) owner_keys[tid] = 0;
-    __syncthreads();
-    if (poisoned) return;
-    if (a.merged && tid == 0) a.bits[W + r] = 0;  // the plan's verdict sits in bits[r]
     const int64_t *tk = a.tk + (int64_t)r * NT;
     // by position in destination order: the table there, its key count
     int64_t nd[kPlanPer], nt[kPlanPer];
     int64_t sd = 0, st = 0;
     int bad = 0;
+    int tpos[kPlanPer];
 #pragma unroll
     for (int u = 0; u < kPlanPer; u++) {
         const int i = tid * kPlanPer + u;
-        nd[u] = nt[u] = 0;
+        tpos[u] = 0;
         if (i < NT) {
             // the table at position i: owner o is the largest with first(o) <= i,
             // first(o) = sum over o' < o of ceil((NT - o') / W)
@@ -404,15 +422,30 @@ __global__ __launch_bounds__(kPlanThreads) void k_bucket_plan(const BucketArgs a
                 first += cnt;
                 o++;
             }
-            const int t = o + (i - first) * W;
-            nd[u] = tk[t];
-            nt[u] = tk[i];  // table order, for the source starts
-            bad |= nt[u] < 0;
+            tpos[u] = o + (i - first) * W;
         }
+    }
+    if (NT > 0) {
+        // every load in flight together: positions past NT read table 0 and
+        // count nothing
+#pragma unroll
+        for (int u = 0; u < kPlanPer; u++) {
+            const int i = tid * kPlanPer + u;
+            nd[u] = tk[i < NT ? tpos[u] : 0];
+            nt[u] = tk[i < NT ? i : 0];  // table order, for the source starts
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kPlanPer; u++) {
+        if (NT == 0 || tid * kPlanPer + u >= NT) nd[u] = nt[u] = 0;
+        bad |= nt[u] < 0;
         sd += nd[u];
         st += nt[u];
     }
-    if (__syncthreads_or(bad)) {
+    const int flags = __syncthreads_or((st0 != 0 ? 2 : 0) | bad);
+    if (flags & 2) return;
+    if (a.merged && tid == 0) a.bits[W + r] = 0;  // the plan's verdict sits in bits[r]
+    if (flags & 1) {
         if (tid == 0) a.bits[r] = A2AV_ST_BAD_SPLIT;
         return;
     }
@@ -494,21 +527,23 @@ struct KeyxArgs {
 __global__ __launch_bounds__(kPlanThreads) void k_keyx_plan(const KeyxArgs a) {
     __shared__ ScanLds lds;
     __shared__ int64_t tst[kKxMaxB];           // start of (s, i) in source s's keys
+    __shared__ int64_t tnk[kKxMaxB];           // keys of (s, i)
     __shared__ int64_t sstart[A2AV_MAX_W + 1];  // first key of source s at this receiver
-    __shared__ int poisoned, sbits;
+    constexpr int NWV = kPlanThreads / kWave;
+    __shared__ int wbits[NWV];                   // the sources' bits, per wave
+    __shared__ int32_t st_sh;
     const int d = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = tid / kWave;
-    constexpr int NWV = kPlanThreads / kWave;
     const int W = a.W, NT = a.NT, cmax = a.cmax, B = a.B;
-    if (tid == 0) {
-        poisoned = *a.status != 0;
-        sbits = 0;
-    }
-    __syncthreads();
-    if (poisoned) return;
-    if (a.merged && tid == 0) a.bits[W + d] = 0;  // the plan's verdict sits in bits[d]
+    // the word as the operation found it (no kernel of it has written it
+    // yet), loaded beside the key counts (a vector load: a scalar one would
+    // hold the counts' address, which waits for every scalar load in flight);
+    // the scan below only writes LDS, so it may run first; the first wave's
+    // read decides for the block
+    const int32_t st0 = status_poisoned(a.status);
     // every source's table-order scan (one wave per source): where the tables
     // d owns start, and the source's own checks (as its bucketing makes them)
+    int wb = 0;
     for (int s = wave; s < W; s += NWV) {
         int64_t run = 0;
         bool neg = false;
@@ -518,15 +553,22 @@ __global__ __launch_bounds__(kPlanThreads) void k_keyx_plan(const KeyxArgs a) {
             neg = neg || __ballot(v < 0) != 0;
             v = v < 0 ? 0 : v;
             const int64_t incl = wave_incl_scan(v);
-            if (t < NT && t % W == d) tst[s * cmax + t / W] = run + incl - v;
+            if (t < NT && t % W == d) {
+                tst[s * cmax + t / W] = run + incl - v;
+                tnk[s * cmax + t / W] = v;
+            }
             run += (int64_t)readlane_u64((uint64_t)incl, kWave - 1);
         }
-        if (lane == 0) {
-            const int b = neg ? A2AV_ST_BAD_SPLIT : run > a.n_keys[s] ? A2AV_ST_SEND_OVERRUN : 0;
-            if (b) atomicOr(&sbits, b);
-        }
+        wb |= neg ? A2AV_ST_BAD_SPLIT : run > a.n_keys[s] ? A2AV_ST_SEND_OVERRUN : 0;
     }
+    if (lane == 0) wbits[wave] = wb;
+    if (tid == 0) st_sh = st0;
     __syncthreads();
+    if (st_sh) return;
+    if (a.merged && tid == 0) a.bits[W + d] = 0;  // the plan's verdict sits in bits[d]
+    int sbits = 0;
+#pragma unroll
+    for (int w = 0; w < NWV; w++) sbits |= wbits[w];
     if (sbits) {
         if (tid == 0) a.bits[d] = sbits;
         return;
@@ -541,7 +583,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_keyx_plan(const KeyxArgs a) {
         if (b < B) {
             const int s = b / cmax, i = b - (b / cmax) * cmax;
             if (i < cnt) {
-                nk[u] = a.tk[(int64_t)s * NT + d + i * W];
+                nk[u] = tnk[s * cmax + i];
                 nl[u] = a.batch;
             }
         }

@@ -33,27 +33,6 @@ __device__ __forceinline__ bool split_invalid(int64_t v) {
     return v < 0 || v > A2AV_MAX_SPLIT;
 }
 
-// ------------------------------------------------------------ wave64 scans
-__device__ __forceinline__ int64_t wave_incl_scan(int64_t v) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int64_t t = __shfl_up(v, o, kWave);
-        if (lane >= o) v += t;
-    }
-    return v;
-}
-
-__device__ __forceinline__ int32_t wave_incl_scan32(int32_t v) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int32_t t = __shfl_up(v, o, kWave);
-        if (lane >= o) v += t;
-    }
-    return v;
-}
-
 // ------------------------------------------------------------ loads / stores
 template <bool NT, typename V>
 __device__ __forceinline__ V ld(const V *p) {
@@ -316,12 +295,6 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
 }
 
 
-__device__ __forceinline__ int32_t wave_or(int32_t v) {
-#pragma unroll
-    for (int o = kWave / 2; o >= 1; o >>= 1) v |= __shfl_xor(v, o, kWave);
-    return v;
-}
-
 // ------------------------------------------------------------ lanes, DPP and bursts
 // x of the lane O below in the same 16-lane row (0 for the first O lanes of
 // a row); every lane must be active.
@@ -378,6 +351,11 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x) {
     x += dpp_row_bcast<0x142, 0xa>(x);
     x += dpp_row_bcast<0x143, 0xc>(x);
     return x;
+}
+
+// The same for signed values (the sum modulo 2^64 is the same bits).
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t v) {
+    return (int64_t)wave_incl_scan_u64((uint64_t)v);
 }
 
 // The same for 32-bit values.
