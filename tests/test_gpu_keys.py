@@ -207,6 +207,9 @@ def _compare_exchange(got, want, what=""):
     (1, 5, 33, 0), (16, 300, 7, 0), (64, 100, 3, 0), (3, 4096, 2, 0),
     # keys and lengths in one block copy over 2W ranks up to W = 32, two above
     (32, 40, 5, 4), (33, 50, 4, 0),
+    # 63 blocks per receiver (the block copy stages the plan row), 64 and 72
+    # (it searches the plan in global memory); more ranks than a DPP row
+    (7, 63, 6, 4), (8, 64, 5, 0), (8, 65, 5, 0), (16, 32, 3, 0), (17, 20, 3, 0),
 ])
 def test_keys_exchange_matches_oracle(ref, W, NT, batch, pad):
     _say("keys_exchange", W, NT, batch, pad)
@@ -219,8 +222,8 @@ def test_keys_exchange_matches_oracle(ref, W, NT, batch, pad):
 
 
 @pytest.mark.parametrize("case", ["negative", "overrun", "keys_room", "lengths_room", "poisoned"])
-def test_keys_exchange_errors(ref, case):
-    W, NT, batch = 4, 9, 50
+@pytest.mark.parametrize("W,NT,batch", [(4, 9, 50), (8, 66, 6)])  # staged plan rows; searched in memory
+def test_keys_exchange_errors(ref, case, W, NT, batch):
     g = I.rng(13)
     lengths, keys = _inputs(g, W, NT, batch)
     _, lo, ko, _, _, _ = ref.keys_exchange(W, NT, batch, lengths, keys)
@@ -264,10 +267,10 @@ def test_keys_exchange_full(ref):
 
 
 def test_keys_exchange_workspace_contents_do_not_matter(ref):
-    """The two-launch exchange counts its workgroups in the workspace: whatever
-    the workspace held before (zeros, all ones, random bytes, what the last
-    call or a poisoned call left) the result is the oracle's, call after call
-    on one workspace, and on a larger one."""
+    """The exchange keeps its key counts (and, with a plan launch, the plan) in
+    the workspace: whatever the workspace held before (zeros, all ones, random
+    bytes, what the last call or a poisoned call left) the result is the
+    oracle's, call after call on one workspace, and on a larger one."""
     W, NT, batch = 8, 26, 300
     g = I.rng(77)
     lengths, keys = _inputs(g, W, NT, batch, lam=4.0, cap=20)
