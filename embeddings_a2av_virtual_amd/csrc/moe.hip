@@ -49,30 +49,41 @@ struct MoeArgs {
 };
 
 // ------------------------------------------------------------------ histogram
-__global__ __launch_bounds__(256) void k_moe_hist(const MoeArgs a) {
+constexpr int kHistThreads = 256;
+
+__global__ __launch_bounds__(kHistThreads) void k_moe_hist(const MoeArgs a) {
     extern __shared__ int32_t hist[];
     __shared__ int poisoned;
-    // blocks of this launch set the word; one read per block keeps its waves
-    // in agreement
-    if (threadIdx.x == 0) poisoned = status_poisoned(a.status);
     const int r = blockIdx.y, seg = blockIdx.x, E = a.E;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
-    __syncthreads();
-    if (poisoned) return;
     const int32_t *ids = a.ids[r];
     const int64_t q0 = (int64_t)seg * kSeg;
+    // the segment's ids, every load in flight together, and then the word
+    // (blocks of this launch set it; one read per block keeps its waves in
+    // agreement)
+    constexpr int kPer = kSeg / kHistThreads;
+    int32_t idv[kPer];
+    const bool any = q0 < a.Q;  // the same in the whole block
+#pragma unroll
+    for (int j = 0; j < kPer; j++) {
+        const int64_t q = q0 + threadIdx.x + j * kHistThreads;
+        idv[j] = any ? ids[q < a.Q ? q : a.Q - 1] : 0;
+    }
+    if (threadIdx.x == 0) poisoned = status_poisoned(a.status);
+    for (int e = threadIdx.x; e < E; e += kHistThreads) hist[e] = 0;
+    __syncthreads();
+    if (poisoned) return;
     int bad = 0;
-    for (int i = threadIdx.x; i < kSeg; i += blockDim.x) {
-        const int64_t q = q0 + i;
-        if (q < a.Q) {
-            const int e = ids[q];
+#pragma unroll
+    for (int j = 0; j < kPer; j++) {
+        if (q0 + threadIdx.x + j * kHistThreads < a.Q) {
+            const int e = idv[j];
             if ((unsigned)e >= (unsigned)E) bad = 1;
             else atomicAdd(&hist[e], 1);
         }
     }
     bad = __syncthreads_or(bad);
     int32_t *H = a.hist + (size_t)r * E * a.nseg;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) H[(size_t)e * a.nseg + seg] = hist[e];
+    for (int e = threadIdx.x; e < E; e += kHistThreads) H[(size_t)e * a.nseg + seg] = hist[e];
     if (bad && threadIdx.x == 0) atomicOr(a.status, A2AV_ST_BAD_EXPERT);
 }
 
@@ -157,30 +168,47 @@ __global__ __launch_bounds__(1024) void k_moe_scan(const MoeArgs a) {
 // counter. After a barrier, the counts of earlier waves are added.
 __global__ __launch_bounds__(256) void k_moe_rank(const MoeArgs a) {
     extern __shared__ int32_t cnt[];  // [kRankWaves][E]
-    if (status_poisoned(a.status)) return;
     const int r = blockIdx.y, seg = blockIdx.x, E = a.E;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    constexpr int kChunks = kSlotsPerWave / kWave;
+    const int32_t *ids = a.ids[r];
+    const int32_t *H = a.hist + (size_t)r * E * a.nseg;
+    const int64_t qbase = (int64_t)seg * kSeg + wave * kSlotsPerWave;
+    // the wave's ids, then their experts' bases for this segment (written by
+    // the scan), all loaded before any ballot; slots past Q (the launch has
+    // Q >= 1) read the last one and count nothing. The word is read beside
+    // them: no kernel of this launch writes it, so every thread finds the
+    // same value.
+    int e_of[kChunks];
+    int32_t hb[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; c++) {
+        const int64_t q = qbase + c * kWave + lane;
+        e_of[c] = ids[q < a.Q ? q : a.Q - 1];
+    }
+#pragma unroll
+    for (int c = 0; c < kChunks; c++) {
+        const int e = (unsigned)e_of[c] < (unsigned)E ? e_of[c] : 0;
+        hb[c] = H[(size_t)e * a.nseg + seg];
+    }
+    if (status_poisoned(a.status)) return;
     for (int i = threadIdx.x; i < kRankWaves * E; i += blockDim.x) cnt[i] = 0;
     __syncthreads();
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     const uint64_t below = (1ull << lane) - 1;
-    const int32_t *ids = a.ids[r];
     int32_t *mine = cnt + wave * E;
-    int e_of[kSlotsPerWave / kWave];
-    int rank_of[kSlotsPerWave / kWave];
-    const int64_t qbase = (int64_t)seg * kSeg + wave * kSlotsPerWave;
+    int rank_of[kChunks];
 #pragma unroll
-    for (int c = 0; c < kSlotsPerWave / kWave; c++) {
+    for (int c = 0; c < kChunks; c++) {
         const int64_t q = qbase + c * kWave + lane;
         const bool ok = q < a.Q;
-        const int e = ok ? ids[q] : 0;
+        const int e = ok ? e_of[c] : 0;
         uint64_t peers = __ballot(ok);
         for (int b = 0; b < nbits; b++) {
             const int bit = (e >> b) & 1;
             const uint64_t m = __ballot(bit);
             peers &= bit ? m : ~m;
         }
-        e_of[c] = e;
         rank_of[c] = 0;
         if (ok) {
             const int before = mine[e];
@@ -190,16 +218,15 @@ __global__ __launch_bounds__(256) void k_moe_rank(const MoeArgs a) {
         }
     }
     __syncthreads();
-    const int32_t *H = a.hist + (size_t)r * E * a.nseg;
     int64_t *perm = a.perm[r];
 #pragma unroll
-    for (int c = 0; c < kSlotsPerWave / kWave; c++) {
+    for (int c = 0; c < kChunks; c++) {
         const int64_t q = qbase + c * kWave + lane;
         if (q < a.Q) {
             const int e = e_of[c];
             int32_t pre = 0;
             for (int w = 0; w < wave; w++) pre += cnt[w * E + e];
-            perm[q] = (int64_t)H[(size_t)e * a.nseg + seg] + pre + rank_of[c];
+            perm[q] = (int64_t)hb[c] + pre + rank_of[c];
         }
     }
 }
@@ -324,43 +351,66 @@ __global__ __launch_bounds__(kPlanThreads) void k_shift_plan(const ShiftArgs a) 
     __shared__ int64_t yb[A2AV_MAX_W + 1];  // Y_s(d*P)
     __shared__ uint64_t base[A2AV_MAX_W];
     __shared__ int64_t limit[A2AV_MAX_W];
-    __shared__ int poisoned;
     const int s = blockIdx.x, tid = threadIdx.x;
     const int W = a.W, E = a.E, P = E / W;
-    if (tid == 0) {
-        poisoned = status_poisoned(a.status);
-        for (int d = 0; d < W; d++) {
-            base[d] = (uint64_t)(uintptr_t)a.base[d];
-            limit[d] = a.limit[d];
-        }
-    }
-    __syncthreads();
-    if (poisoned) return;
-    if (a.check_counts) {
-        int bad = 0;
-        for (int i = tid; i < W * E; i += kPlanThreads) bad |= (int)split_invalid(a.counts[i]);
-        if (__syncthreads_or(bad)) {
-            if (s == 0 && tid == 0) {
-                a.words[0] = A2AV_ST_BAD_SPLIT;
-                a.words[1] = 0;
-            }
-            return;
-        }
-    }
+    // thread tid: experts tid * kPlanPer + u, every source's count of them,
+    // read in groups of 8 sources with all of a group's loads in flight
+    // together (entries past W or E read entry 0 and count nothing); with
+    // them the owners' bases and limits and the status word. Every count is
+    // read by exactly one thread, which also range-checks it.
+    constexpr int kGroup = 8;
     int64_t col[kPlanPer], before[kPlanPer], mine[kPlanPer];
+    int bad = 0;
+#pragma unroll
+    for (int u = 0; u < kPlanPer; u++) col[u] = before[u] = mine[u] = 0;
+    const uint64_t my_base = (uint64_t)(uintptr_t)a.base[tid < W ? tid : 0];
+    const int64_t my_limit = a.limit[tid < W ? tid : 0];
+    const int poisoned = status_poisoned(a.status);
+    auto group = [&](int s0) {
+        int64_t c[kPlanPer][kGroup];
+#pragma unroll
+        for (int u = 0; u < kPlanPer; u++)
+#pragma unroll
+            for (int j = 0; j < kGroup; j++) {
+                const int e = tid * kPlanPer + u, s2 = s0 + j;
+                c[u][j] = a.counts[e < E && s2 < W ? (int64_t)s2 * E + e : 0];
+            }
+#pragma unroll
+        for (int u = 0; u < kPlanPer; u++)
+#pragma unroll
+            for (int j = 0; j < kGroup; j++) {
+                const int e = tid * kPlanPer + u, s2 = s0 + j;
+                if (e < E && s2 < W) {
+                    const int64_t v = c[u][j];
+                    bad |= (int)split_invalid(v);
+                    col[u] += v;
+                    if (s2 < s) before[u] += v;
+                    if (s2 == s) mine[u] = v;
+                }
+            }
+    };
+    // the first group in line with the loads above, so that no loop head
+    // waits for them first; threads past the experts load nothing
+    if (tid * kPlanPer < E) {
+        group(0);
+        for (int s0 = kGroup; s0 < W; s0 += kGroup) group(s0);
+    }
+    if (tid < W) {
+        base[tid] = my_base;
+        limit[tid] = my_limit;
+    }
+    const int flags = __syncthreads_or(poisoned * 2 | (a.check_counts ? bad : 0));
+    if (flags & 2) return;
+    if (flags & 1) {
+        if (s == 0 && tid == 0) {
+            a.words[0] = A2AV_ST_BAD_SPLIT;
+            a.words[1] = 0;
+        }
+        return;
+    }
     int64_t scol = 0, sbef = 0, smine = 0;
 #pragma unroll
     for (int u = 0; u < kPlanPer; u++) {
-        const int e = tid * kPlanPer + u;
-        col[u] = before[u] = mine[u] = 0;
-        if (e < E) {
-            for (int s2 = 0; s2 < W; s2++) {
-                const int64_t c = a.counts[(int64_t)s2 * E + e];
-                col[u] += c;
-                if (s2 < s) before[u] += c;
-            }
-            mine[u] = a.counts[(int64_t)s * E + e];
-        }
         scol += col[u];
         sbef += before[u];
         smine += mine[u];
@@ -451,20 +501,26 @@ struct ReturnArgs {
 // expert's block, so every row the gather reads lies in the owner's buffer;
 // for the combine, also the address of the slot's row.
 __global__ __launch_bounds__(256) void k_slot_check(const ReturnArgs a) {
-    if (status_poisoned(a.status)) return;
     const int s = blockIdx.y;
     const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // the slot's id and pack row beside the word (the launch has Q >= 1;
+    // threads past Q read slot 0 and check nothing), then the entries of its
+    // expert together
+    const int64_t qc = q < a.Q ? q : 0;
+    const int32_t e = a.ids[s][qc];
+    const int64_t pq = a.perm[s][qc];
+    if (status_poisoned(a.status)) return;
     int bad = 0;
     if (q < a.Q) {
-        const int32_t e = a.ids[s][q];
         if (e < 0 || e >= a.E) {
             bad = A2AV_ST_BAD_EXPERT;
         } else {
-            const int64_t p = a.perm[s][q] - a.ystart[(int64_t)s * a.E + e];
-            if (p < 0 || p >= a.counts[(int64_t)s * a.E + e]) bad = A2AV_ST_BAD_PERM;
-            else if (a.xaddr)
-                a.xaddr[(int64_t)s * a.Q + q] =
-                    a.row_addr[(int64_t)s * a.E + e] + (uint64_t)a.perm[s][q] * a.R;
+            const int64_t ys = a.ystart[(int64_t)s * a.E + e];
+            const int64_t cn = a.counts[(int64_t)s * a.E + e];
+            const uint64_t ra = a.xaddr ? a.row_addr[(int64_t)s * a.E + e] : 0;
+            const int64_t p = pq - ys;
+            if (p < 0 || p >= cn) bad = A2AV_ST_BAD_PERM;
+            else if (a.xaddr) a.xaddr[(int64_t)s * a.Q + q] = ra + (uint64_t)pq * a.R;
         }
     }
     const int be = __ballot(bad & A2AV_ST_BAD_EXPERT) != 0, bp = __ballot(bad & A2AV_ST_BAD_PERM) != 0;
@@ -717,10 +773,10 @@ static void launch_pack_sort(MoeArgs &a, hipStream_t stream) {
     a.nseg = (int)n_segments(a.Q);
     const int nseg_grid = a.nseg > 0 ? a.nseg : 1;
     if (a.nseg > 0) {
-        hipLaunchKernelGGL(k_moe_hist, dim3(a.nseg, W), dim3(256), E * sizeof(int32_t), stream, a);
+        hipLaunchKernelGGL(k_moe_hist, dim3(a.nseg, W), dim3(kHistThreads), E * sizeof(int32_t), stream, a);
     } else {
         a.nseg = 1;  // no slots: one empty segment so counts and splits come out zero
-        hipLaunchKernelGGL(k_moe_hist, dim3(1, W), dim3(256), E * sizeof(int32_t), stream, a);
+        hipLaunchKernelGGL(k_moe_hist, dim3(1, W), dim3(kHistThreads), E * sizeof(int32_t), stream, a);
     }
     hipLaunchKernelGGL(k_moe_scan, dim3(W), dim3(1024), 0, stream, a);
     if (a.Q > 0)
