@@ -120,6 +120,52 @@ __global__ __launch_bounds__(1024) void k_offsets(int W, const int64_t *__restri
     }
 }
 
+// ====================================================================== W <= 8
+// The same two steps in one wave each (no barrier): lane i < W * W holds
+// S[i / W][i % W] for the exchange; for the offsets, the eight lanes of
+// group r hold row r of S and row r of O, scanned inside the group.
+__global__ __launch_bounds__(64) void k_exchange_w8(int W, const int64_t *__restrict__ S,
+                                                    int64_t *__restrict__ O, int32_t *status) {
+    const int lane = threadIdx.x, n = W * W;
+    const int32_t st0 = status_at_entry(status);
+    const int64_t v = lane < n ? S[lane] : 0;
+    if (st0) return;
+    if (__ballot(split_invalid(v))) {
+        if (lane == 0) atomicOr(status, A2AV_ST_BAD_SPLIT);
+        return;
+    }
+    if (lane < n) {
+        const int s = lane / W, d = lane - s * W;
+        O[d * W + s] = v;
+    }
+}
+
+__global__ __launch_bounds__(64) void k_offsets_w8(int W, const int64_t *__restrict__ S,
+                                                   const int64_t *__restrict__ O,
+                                                   int64_t *__restrict__ send_off,
+                                                   int64_t *__restrict__ recv_off, int32_t *status) {
+    const int lane = threadIdx.x, r = lane / 8, k = lane % 8;
+    const bool act = r < W && k < W;
+    const int32_t st0 = status_at_entry(status);
+    const int64_t vs = act ? S[r * W + k] : 0;
+    const int64_t vo = act ? O[r * W + k] : 0;
+    if (st0) return;
+    if (__ballot(split_invalid(vs) || split_invalid(vo))) {
+        if (lane == 0) atomicOr(status, A2AV_ST_BAD_SPLIT);
+        return;
+    }
+    const int64_t is = (int64_t)group_incl_scan<8>((uint64_t)vs, k);
+    const int64_t io = (int64_t)group_incl_scan<8>((uint64_t)vo, k);
+    if (act) {
+        send_off[r * (W + 1) + k] = is - vs;
+        recv_off[r * (W + 1) + k] = io - vo;
+        if (k == W - 1) {
+            send_off[r * (W + 1) + W] = is;
+            recv_off[r * (W + 1) + W] = io;
+        }
+    }
+}
+
 // ====================================================================== payload copy
 // A block stages the split and offset matrices in LDS when W <= kMetaW (one
 // global round trip for all of its metadata); above that it reads them from
@@ -1163,13 +1209,19 @@ A2AV_API const char *a2av_strerror(int code) {
 A2AV_API int a2av_exchange_splits(int W, const int64_t *S, int64_t *O, int32_t *status,
                                   hipStream_t stream) {
     if (W < 1 || W > A2AV_MAX_W || !S || !O || !status) return A2AV_EARG;
-    hipLaunchKernelGGL(k_exchange, dim3(1), dim3(256), 0, stream, W, S, O, status);
+    if (W <= kWaveMaxW) hipLaunchKernelGGL(k_exchange_w8, dim3(1), dim3(kWave), 0, stream, W, S, O, status);
+    else hipLaunchKernelGGL(k_exchange, dim3(1), dim3(256), 0, stream, W, S, O, status);
     return launch_status();
 }
 
 A2AV_API int a2av_offsets(int W, const int64_t *S, const int64_t *O, int64_t *send_off,
                           int64_t *recv_off, int32_t *status, hipStream_t stream) {
     if (W < 1 || W > A2AV_MAX_W || !S || !O || !send_off || !recv_off || !status) return A2AV_EARG;
+    if (W <= kWaveMaxW) {
+        hipLaunchKernelGGL(k_offsets_w8, dim3(1), dim3(kWave), 0, stream, W, S, O, send_off, recv_off,
+                           status);
+        return launch_status();
+    }
     const int threads = 2 * W * kWave < 1024 ? 2 * W * kWave : 1024;
     hipLaunchKernelGGL(k_offsets, dim3(1), dim3(threads), 0, stream, W, S, O, send_off, recv_off,
                        status);
