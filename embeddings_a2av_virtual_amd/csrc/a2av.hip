@@ -1048,14 +1048,14 @@ static WaveTuning wave_tuning(uint64_t bmax, bool short_pieces = false, bool cap
 }
 
 // The tuning of the W <= 8 wave kernel, the one-call kernel and a2av_copy
-// alike. Rows that are not 16-byte multiples take the short pieces too,
-// without the cap (keys a2av, 8-byte rows: 91.6 -> 89.9 us; with the cap it
-// was slower). The copy-only kernel takes the cap as the one-call kernel
-// does (W = 4 x 32 MiB 44.76 -> 43.47 us, x 256 MiB 345.7 -> 335.7 us,
-// same-process A/B).
-static WaveTuning wave_tuning_w8(uint64_t bmax, bool aligned) {
+// alike, rows of any width: from kShortTraffic up, short pieces and the
+// occupancy cap. (Measured on the current prologue: the copy-only kernel
+// W = 4 x 32 MiB 44.76 -> 43.47 us, x 256 MiB 345.7 -> 335.7 us, same-process
+// A/B; the keys a2av, 8-byte rows, 87.5 -> 86.2 us, where with the older
+// prologue the cap had made both slower.)
+static WaveTuning wave_tuning_w8(uint64_t bmax) {
     const bool short_pieces = bmax >= kShortTraffic;
-    return wave_tuning(bmax, short_pieces, aligned);
+    return wave_tuning(bmax, short_pieces, true);
 }
 
 // The tuning of the more-than-8-ranks wave kernel: short pieces and the cap
@@ -1249,7 +1249,7 @@ A2AV_API int a2av_copy(int W, size_t row_bytes, const void *const *in, const int
         uint64_t bmax;
         bool aligned;
         traffic_bound(a, &bmax, &aligned);
-        const WaveTuning wt = W <= kWaveMaxW ? wave_tuning_w8(bmax, aligned)
+        const WaveTuning wt = W <= kWaveMaxW ? wave_tuning_w8(bmax)
                                              : wave_tuning_any(bmax, aligned);
         a.piece = wt.piece;
         if (W <= kWaveMaxW) launch_wave<kCopyGiven>(a, aligned, wt, wave_grid(bmax, wt.piece), stream);
@@ -1308,7 +1308,7 @@ A2AV_API int a2av_all_to_all_vdev(int W, size_t row_bytes, const void *const *in
         uint64_t bmax;
         bool aligned;
         traffic_bound(a, &bmax, &aligned);
-        const WaveTuning wt = wave_tuning_w8(bmax, aligned);
+        const WaveTuning wt = wave_tuning_w8(bmax);
         a.piece = wt.piece;
         launch_wave<kFused>(a, aligned, wt, wave_grid(bmax, wt.piece), stream);
         return launch_status();
