@@ -129,14 +129,17 @@ int a2av_offsets(int W, const int64_t *S, const int64_t *O, int64_t *send_off,
  * accesses (realigned in registers when source and destination differ mod
  * 16), and the grid is sized to min(sum in_rows, sum out_cap_rows) *
  * row_bytes. For W <= 8 this is one kernel: every wave reads S and the
- * offsets through the scalar cache and checks them itself. For larger W a
+ * per-rank arrays through the scalar cache, scans S itself, and checks the
+ * given offsets against its scans before its first store. For larger W a
  * single workgroup checks everything first and the copy kernel follows (two
- * launches); each wave then reads, per destination it works in, one row of
- * recv_off and the matching columns of S and send_off.
- * The one-call kernel, the plain copy and the block copies (from 64 MiB per
- * side, with 16-byte rows) and the weighted combine (always) reserve LDS
- * they do not use, to run fewer workgroups per CU; a kernel on another stream
- * then finds less LDS free on the CUs they occupy.
+ * launches); its workgroups take the destination totals and one row of
+ * recv_off from two scalar bursts shared through LDS, and a wave in another
+ * destination loads that destination's row of recv_off.
+ * The wave kernels of a2av_copy and a2av_all_to_all_vdev (from 64 MiB per
+ * side; above 8 ranks only with 16-byte rows), the plain copy, the block copies
+ * (from 64 MiB per side, with 16-byte rows) and the weighted combine (always)
+ * reserve LDS they do not use, to run fewer workgroups per CU; a kernel on
+ * another stream then finds less LDS free on the CUs they occupy.
  * Tuning (read on every call; defaults are compiled in): A2AV_WAVE_PIECE,
  * A2AV_WAVE_UNROLL (4, 8 or 16), A2AV_WAVE_LDS (bytes of LDS per workgroup
  * the kernel does not use, which limits workgroups per CU) for the wave
