@@ -274,8 +274,9 @@ def ceilings(torch, B, nbytes, reps=50, nsets=8):
     """Plain contiguous copies of the same byte count (read n/2 + write n/2),
     and one-direction streams of n bytes (read only; written only, with
     non-temporal and with ordinary stores), at that size and at 4 GiB, the
-    order of the MoE rows' traffic. Buffers rotate so the Infinity Cache
-    holds none of them."""
+    order of the MoE rows' traffic; and a plain copy of 4 GiB (8 GiB moved,
+    the bytes of a W = 4 x 1 GiB exchange). Buffers rotate so the Infinity
+    Cache holds none of them."""
     half = nbytes // 2
     srcs = [torch.empty(half, dtype=torch.uint8, device="cuda").fill_(i) for i in range(nsets)]
     dsts = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
@@ -295,6 +296,11 @@ def ceilings(torch, B, nbytes, reps=50, nsets=8):
             torch, lambda t: B.a2av_device_fill(t, size, 0x5A5A5A5A, True), bufs, r, size)
         out[f"write_only{tag}_gbs"] = _time_rotating(
             torch, lambda t: B.a2av_device_fill(t, size, 0x5A5A5A5A, False), bufs, r, size)
+        if tag:
+            # one buffer into the other, then back
+            out[f"device_copy{tag}_gbs"] = _time_rotating(
+                torch, lambda p: B.a2av_device_copy(p[0], p[1], size),
+                [(bufs[1], bufs[0]), (bufs[0], bufs[1])], r, 2 * size)
         del bufs
         torch.cuda.empty_cache()
     return out
