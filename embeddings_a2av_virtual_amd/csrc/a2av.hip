@@ -45,6 +45,11 @@ long env_long(const char *name, long dflt, long lo, long hi) {
     return x;
 }
 
+// Largest grid, in workgroups, of the kernels whose waves loop over their
+// work (the loops stride over what the grid does not cover). A2AV_MAX_GRID
+// lowers it, so that small inputs run the loops' later passes too.
+unsigned max_grid() { return (unsigned)env_long("A2AV_MAX_GRID", 1L << 22, 1, 1L << 22); }
+
 // ====================================================================== exchange
 // One block. The status word comes through the scalar cache (this launch's
 // one block is its only writer) and S is loaded by every thread before
@@ -1069,7 +1074,7 @@ static int wave_grid(uint64_t bmax, uint64_t piece) {
     const uint64_t per_block = piece * 4;  // 4 waves per 256-thread block
     uint64_t g = (bmax + per_block - 1) / per_block;
     if (g < 1) g = 1;
-    if (g > (1u << 22)) g = 1u << 22;  // the piece loop strides over the rest
+    if (g > max_grid()) g = max_grid();  // the piece loop strides over the rest
     return (int)g;
 }
 

@@ -816,7 +816,7 @@ static void piece_policy(uint64_t bmax, bool aligned, int *unroll, uint64_t *pie
 static int copy_grid(uint64_t bmax, uint64_t piece) {
     uint64_t g = (bmax + piece * 4 - 1) / (piece * 4);  // 4 waves per block
     if (g < 1) g = 1;  // one wave always runs, to report the planning bits
-    if (g > (1u << 22)) g = 1u << 22;  // the piece loop strides over the rest
+    if (g > max_grid()) g = max_grid();  // the piece loop strides over the rest
     return (int)g;
 }
 

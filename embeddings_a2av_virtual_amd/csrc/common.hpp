@@ -520,5 +520,6 @@ __device__ __forceinline__ void block_excl_scan3(const int64_t (&v)[3], ScanLds3
 // ------------------------------------------------------------ host helpers
 int device_cu_count(hipStream_t stream);
 long env_long(const char *name, long dflt, long lo, long hi);
+unsigned max_grid();
 
 }  // namespace a2av

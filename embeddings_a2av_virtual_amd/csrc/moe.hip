@@ -793,7 +793,7 @@ static void launch_scatter(const MoeArgs &a, bool aligned, hipStream_t stream) {
     const uint64_t ntok = (uint64_t)a.W * (uint64_t)a.T;
     if (!aligned || a.k > kWave) {
         uint64_t blocks = (ntok + 3) / 4;
-        if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
+        if (blocks > max_grid()) blocks = max_grid();  // the wave loop strides over the rest
         hipLaunchKernelGGL((k_moe_scatter<4, false, DIRECT>), dim3((unsigned)blocks), dim3(256), 0,
                            stream, a, (uint64_t)1);
         return;
@@ -802,7 +802,7 @@ static void launch_scatter(const MoeArgs &a, bool aligned, hipStream_t stream) {
     const uint64_t nch = (nv + 8 * kWave - 1) / (8 * kWave);
     const int U = (int)((nv + nch * kWave - 1) / (nch * kWave));
     uint64_t blocks = (ntok * nch + 3) / 4;
-    if (blocks > (1u << 22)) blocks = 1u << 22;
+    if (blocks > max_grid()) blocks = max_grid();
     const dim3 g((unsigned)blocks), b(256);
     switch (U) {
     case 1: hipLaunchKernelGGL((k_moe_scatter<1, true, DIRECT>), g, b, 0, stream, a, nch); break;
@@ -997,7 +997,7 @@ A2AV_API int moe_unpack_return(int W, int64_t T, int k, int E, size_t row_bytes,
     // at least one wave, so that a verdict of the plan is reported
     uint64_t blocks = ((uint64_t)W * (uint64_t)c.Q + 3) / 4;
     if (blocks < 1) blocks = 1;
-    if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
+    if (blocks > max_grid()) blocks = max_grid();  // the wave loop strides over the rest
     if (aligned)
         hipLaunchKernelGGL((k_moe_gather_home<16, true>), dim3((unsigned)blocks), dim3(256), 0,
                            stream, c);
@@ -1093,13 +1093,13 @@ A2AV_API int moe_combine_return(int W, int64_t T, int k, int E, int64_t H,
     if (!aligned || row_bytes >= (1ull << 32)) {
         uint64_t blocks = ((uint64_t)W * (uint64_t)T + 3) / 4;
         if (blocks < 1) blocks = 1;
-        if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
+        if (blocks > max_grid()) blocks = max_grid();  // the wave loop strides over the rest
         hipLaunchKernelGGL(k_moe_combine_any<true>, dim3((unsigned)blocks), dim3(256), 0, stream, m);
     } else {
         const uint64_t nchunk = ((uint64_t)H / 8 + kWave - 1) / kWave;
         uint64_t blocks = ((uint64_t)W * (uint64_t)T * nchunk + 3) / 4;
         if (blocks < 1) blocks = 1;
-        if (blocks > (1u << 22)) blocks = 1u << 22;
+        if (blocks > max_grid()) blocks = max_grid();
         hipLaunchKernelGGL((k_moe_combine<true, true>), dim3((unsigned)blocks), dim3(256),
                            (unsigned)env_long("A2AV_COMBINE_LDS", kCombineHomeLds, 0, 65536),
                            stream, m, nchunk);
@@ -1133,7 +1133,7 @@ A2AV_API int moe_unpack(int W, int64_t T, int k, size_t row_bytes, const void *c
     const int64_t check_blocks = (a.Q + 255) / 256;
     if (check_blocks > INT32_MAX) return A2AV_EARG;
     uint64_t gather_blocks = ((uint64_t)W * (uint64_t)a.Q + 3) / 4;
-    if (gather_blocks > (1u << 22)) gather_blocks = 1u << 22;  // the wave loop strides over the rest
+    if (gather_blocks > max_grid()) gather_blocks = max_grid();  // the wave loop strides over the rest
     hipLaunchKernelGGL(k_perm_check, dim3((unsigned)check_blocks, W), dim3(256), 0, stream, a);
     const int gu = (int)env_long("A2AV_MOE_GATHER_UNROLL", 16, 4, 16);
     if (aligned && gu >= 16)
@@ -1188,12 +1188,12 @@ A2AV_API int moe_combine(int W, int64_t T, int k, int64_t H, const void *const *
     // the fast path needs 16-byte vectors and rows under 4 GiB (32-bit lane offsets)
     if (!aligned || (uint64_t)H * 2 >= (1ull << 32)) {
         uint64_t blocks = ((uint64_t)W * (uint64_t)T + 3) / 4;
-        if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
+        if (blocks > max_grid()) blocks = max_grid();  // the wave loop strides over the rest
         hipLaunchKernelGGL(k_moe_combine_any<false>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     } else {
         const uint64_t nchunk = ((uint64_t)H / 8 + kWave - 1) / kWave;
         uint64_t blocks = ((uint64_t)W * (uint64_t)T * nchunk + 3) / 4;
-        if (blocks > (1u << 22)) blocks = 1u << 22;  // the wave loop strides over the rest
+        if (blocks > max_grid()) blocks = max_grid();  // the wave loop strides over the rest
         // tuning knob: A2AV_COMBINE_STORE_NT (non-temporal stores, 0/1)
         if (env_long("A2AV_COMBINE_STORE_NT", 1, 0, 1))
             hipLaunchKernelGGL((k_moe_combine<true, false>), dim3((unsigned)blocks), dim3(256),

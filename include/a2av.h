@@ -38,6 +38,10 @@
  *     after synchronising the stream.
  *   - Calls that overlap in time on buffers they share race; calls on
  *     disjoint buffers may run concurrently on different streams.
+ *   - The copy, scatter, gather and combine kernels launch one wave per
+ *     piece, row or slot, up to A2AV_MAX_GRID workgroups (environment,
+ *     read on every call; default and maximum 2^22); their waves loop over
+ *     what a smaller grid leaves. The setting changes only the schedule.
  */
 #ifndef A2AV_H
 #define A2AV_H
