@@ -115,6 +115,40 @@ MUTANTS = {
          "(void *const *)lengths_out,\n                               lengths_cap, Sk, O, so, ro);", 0)],
     "bucketize_length_split_counts_keys": [
         ("split_lengths[d] += batch;", "split_lengths[d] += tk[t];", 0)],
+    # totals, counts and offsets beside the payload
+    "send_total_drops_last": [
+        ("        send_off[s * (W + 1) + W] = run;",
+         "        send_off[s * (W + 1) + W] = run - S[s * W + W - 1];", 0)],
+    "recv_total_from_send_row": [
+        ("        recv_off[d * (W + 1) + W] = run;",
+         "        recv_off[d * (W + 1) + W] = send_off[d * (W + 1) + W];", 0)],
+    "expert_counts_shifted": [
+        ("for (int e = 0; e < E; e++) expert_counts[e] = count[e];",
+         "for (int e = 0; e < E; e++) expert_counts[e] = count[(e + 1) % E];", 0)],
+    "regroup_offsets_total_wrong": [
+        ("    expert_offsets[P] = run;", "    expert_offsets[P] = expert_offsets[P - 1];", 0)],
+    "regroup_offsets_inclusive": [
+        ("        expert_offsets[j] = run;\n        for (int s = 0; s < W; s++) run += counts[s * E + d * P + j];",
+         "        for (int s = 0; s < W; s++) run += counts[s * E + d * P + j];\n        expert_offsets[j] = run;", 0)],
+    "keys_recv_total_short": [
+        ("        recv_off_keys[d * (W + 1) + W] = run;",
+         "        recv_off_keys[d * (W + 1) + W] = run - Sk[(W - 1) * W + d];", 0)],
+    "keys_split_lengths_transposed": [
+        ("            split_lengths[s * W + d] = Sl[s * W + d];",
+         "            split_lengths[s * W + d] = Sl[d * W + s];", 0)],
+    # bounds one off
+    "bucketize_overrun_slack": [
+        ("    if (run > n_keys) { free(tk); free(tstart); return REF_SEND_OVERRUN; }",
+         "    if (run > n_keys + 1) { free(tk); free(tstart); return REF_SEND_OVERRUN; }", 0)],
+    "keys_capacity_slack": [
+        ("        if (rk > keys_cap[d] || rl > lengths_cap[d])",
+         "        if (rk > keys_cap[d] + 1 || rl > lengths_cap[d])", 0)],
+    "regroup_overflow_slack": [
+        ("    if (total > out_cap) st |= REF_RECV_OVERFLOW;",
+         "    if (total > out_cap + 1) st |= REF_RECV_OVERFLOW;", 0)],
+    "pack_expert_bound_slack": [
+        ("        if (ids[q] < 0 || ids[q] >= E) return REF_BAD_EXPERT;",
+         "        if (ids[q] < 0 || ids[q] > E) return REF_BAD_EXPERT;", 0)],
 }
 
 # cheap pins first; the brute-force enumeration last
